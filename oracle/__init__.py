@@ -1,0 +1,190 @@
+"""Python access to the plain-C CPU oracle (oracle/moe_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this module.  The GPU library and
+its Python binding never import it.
+
+Arrays are numpy; bf16 data travels as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = os.environ.get("MOE_ORACLE_LIB")  # a planted-mistake build (mutation tests)
+        if path is None:
+            path = _build.LIB
+            if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+                _build.build()
+        L = C.CDLL(path)
+        P = C.c_void_p
+        i = C.c_int
+        L.oracle_e4m3_encode.argtypes = [P, i, P]
+        L.oracle_bf16_round.argtypes = [P, i, P]
+        L.oracle_quant_int8.argtypes = [P, i, P, P]
+        L.oracle_quant_mxfp8.argtypes = [P, i, P, P]
+        L.oracle_update_expert.argtypes = [P, P, P, P, P, i, i, i, i, i, P, P, P]
+        L.oracle_route.argtypes = [P, P, i, i, P, P, P, P, P]
+        L.oracle_dispatch.argtypes = [P, P, P, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
+        L.oracle_combine_add_rmsnorm.argtypes = [P, P, P, P, P, P, C.c_float, i, i, i, i,
+                                                 P, P, P]
+        for f in (L.oracle_update_expert, L.oracle_route, L.oracle_dispatch,
+                  L.oracle_combine_add_rmsnorm):
+            f.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def bf16_bits(t) -> np.ndarray:
+    """bf16 torch tensor -> uint16 numpy bit patterns."""
+    import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32).reshape(-1)
+    out = np.empty(v.size, dtype=np.uint8)
+    lib().oracle_e4m3_encode(_p(v), v.size, _p(out))
+    return out
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float64).reshape(-1)
+    out = np.empty(v.size, dtype=np.uint16)
+    lib().oracle_bf16_round(_p(v), v.size, _p(out))
+    return out
+
+
+def quant_int8(x_bits: np.ndarray):
+    x = _c(x_bits, np.uint16).reshape(-1)
+    q = np.empty(x.size, dtype=np.int8)
+    s = np.zeros(1, dtype=np.float32)
+    lib().oracle_quant_int8(_p(x), x.size, _p(q), _p(s))
+    return q, float(s[0])
+
+
+def quant_mxfp8(x_bits: np.ndarray):
+    x = _c(x_bits, np.uint16).reshape(-1)
+    q = np.empty(x.size, dtype=np.uint8)
+    s = np.zeros(1, dtype=np.uint8)
+    lib().oracle_quant_mxfp8(_p(x), x.size, _p(q), _p(s))
+    return q, int(s[0])
+
+
+def update_expert(ids, scores, table, thr, token_mask, n_instances: int):
+    ids = _c(ids, np.int32)
+    Bs, K = ids.shape
+    table = _c(table, np.int32)
+    n_logical, F = table.shape
+    scores = _c(scores, np.float32)
+    thr = _c(thr, np.float32)
+    token_mask = _c(token_mask, np.uint8)
+    out_ids = np.empty((Bs, K), dtype=np.int32)
+    out_mask = np.empty((Bs, K), dtype=np.uint8)
+    err = np.zeros(1, dtype=np.int32)
+    rc = lib().oracle_update_expert(_p(ids), _p(scores), _p(table), _p(thr), _p(token_mask),
+                                    Bs, K, n_logical, F, n_instances, _p(out_ids),
+                                    _p(out_mask), _p(err))
+    if rc:
+        raise ValueError(f"oracle_update_expert rc={rc}")
+    return out_ids, out_mask, int(err[0])
+
+
+def route(ids, mask, E: int):
+    ids = _c(ids, np.int32).reshape(-1)
+    mask = _c(mask, np.uint8)
+    mask = None if mask is None else mask.reshape(-1)
+    N = ids.size
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    assist = np.empty(N, dtype=np.int32)
+    src = np.empty(N, dtype=np.int32)
+    err = np.zeros(1, dtype=np.int32)
+    rc = lib().oracle_route(_p(ids), _p(mask), N, E, _p(counts), _p(offsets), _p(assist),
+                            _p(src), _p(err))
+    if rc:
+        raise ValueError(f"oracle_route rc={rc}")
+    return counts, offsets, assist, src, int(err[0])
+
+
+def n_scales(quant_mode: int, H: int, tile: int) -> int:
+    return {0: 0, 2: 1, 3: -(-H // tile) if tile > 0 else 0, 4: H // 32}[quant_mode]
+
+
+def dispatch(x_bits, ids, mask, n_ranks: int, local_experts: int, quant_mode: int,
+             tile: int = 0):
+    """Returns dict(expand_x, scales, counts, offsets, src, assist, err).
+    Rows past offsets[E] are zero (never written)."""
+    x = _c(x_bits, np.uint16)
+    Bs, H = x.shape
+    ids = _c(ids, np.int32)
+    K = ids.shape[1]
+    mask = _c(mask, np.uint8)
+    N = Bs * K
+    E = n_ranks * local_experts
+    if quant_mode == 0:
+        ex = np.zeros((N, H), dtype=np.uint16)
+    elif quant_mode == 4:
+        ex = np.zeros((N, H), dtype=np.uint8)
+    else:
+        ex = np.zeros((N, H), dtype=np.int8)
+    ns = n_scales(quant_mode, H, tile)
+    if quant_mode == 4:
+        sc = np.zeros((N, ns), dtype=np.uint8)
+    elif quant_mode in (2, 3):
+        sc = np.zeros((N, ns), dtype=np.float32)
+    else:
+        sc = None
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    src = np.empty(N, dtype=np.int32)
+    assist = np.empty(N, dtype=np.int32)
+    err = np.zeros(1, dtype=np.int32)
+    rc = lib().oracle_dispatch(_p(x), _p(ids), _p(mask), Bs, H, K, n_ranks, local_experts,
+                               quant_mode, tile, _p(ex), _p(sc), _p(counts), _p(offsets),
+                               _p(src), _p(assist), _p(err))
+    if rc:
+        raise ValueError(f"oracle_dispatch rc={rc}")
+    return dict(expand_x=ex, scales=sc, counts=counts, offsets=offsets, src=src,
+                assist=assist, err=int(err[0]))
+
+
+def combine(expert_out_bits, assist, scales, shared_bits, residual_bits, gamma_bits,
+            eps: float, shared_mode: int = 0):
+    """Returns (y_bits, x_out_bits, rstd) with y/x_out as uint16 bf16 patterns."""
+    eo = _c(expert_out_bits, np.uint16)
+    res = _c(residual_bits, np.uint16)
+    Bs, H = res.shape
+    assist = _c(assist, np.int32).reshape(Bs, -1)
+    K = assist.shape[1]
+    scales = _c(scales, np.float32).reshape(Bs, K)
+    sh = _c(shared_bits, np.uint16)
+    gamma = _c(gamma_bits, np.uint16)
+    y = np.empty((Bs, H), dtype=np.uint16)
+    xo = np.empty((Bs, H), dtype=np.uint16)
+    rstd = np.empty(Bs, dtype=np.float32)
+    rc = lib().oracle_combine_add_rmsnorm(_p(eo), _p(assist), _p(scales), _p(sh), _p(res),
+                                          _p(gamma), eps, Bs, H, K, shared_mode, _p(y),
+                                          _p(xo), _p(rstd))
+    if rc:
+        raise ValueError(f"oracle_combine rc={rc}")
+    return y, xo, rstd

@@ -1,0 +1,429 @@
+/*
+ * moe_oracle.c -- plain CPU oracle for the single-GPU share of an MoE layer's
+ * expert mapping, token dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the slow, obviously-correct reference the
+ * GPU library is checked against.  Only the test suite, the package smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or helper with the GPU library, and the GPU library never
+ * calls it.
+ *
+ * Sources (Ascend CANN operator documentation pages):
+ *   [UPD] "aclnnMoeUpdateExpert": load balancing (map each token's top-K
+ *         logical expert ids to deployed instances), expert pruning by a
+ *         threshold broadcast over the batch, and the mapping-table format
+ *         (column 0 = replica count > 0, columns 1.. = instance ids).
+ *   [DSP] "aclnnMoeDistributeDispatchV2", 计算公式 (formula): case 1
+ *         (quantMode 0, no quantisation), case 3 (quantMode 2, per-token
+ *         dynamic int8), case 4 (quantMode 3, per-tile dynamic int8), case 5
+ *         (quantMode 4, mxfp8), and the note that emax is the exponent of
+ *         the target type's largest normal number; 约束说明 (constraints) for
+ *         the 1-D / 2-D active mask.
+ *   [CMB] "aclnnMoeDistributeCombineAddRmsNorm", 计算公式 (formula): the
+ *         weighted sum of expert outputs and shared-expert output, the
+ *         residual add and RMSNorm.
+ *
+ * Readings where the pages are silent or garbled (each also listed with its
+ * reason in the design notes of this repository):
+ *   - instance ids are global: instance = rank * local_experts + local slot;
+ *   - the replica used by token i is column 1 + (i mod replica count);
+ *   - pruning keeps an entry unless score < threshold[k] (NaN is kept);
+ *   - rows of one instance are ordered by ascending flat index f = i*K + k;
+ *   - int8: dstTypeMax = 127, round half to even, clamp to [-127, 127],
+ *     scale written = 1 / dynamicScales, all-zero segment -> codes 0, scale 0;
+ *   - per-tile mode: tiles of `tile` elements along H (128 in the workloads);
+ *   - mxfp8: blocks of 32 along H, max(x) read as max |x|, emax = 8 (E4M3),
+ *     fp8 cast rounds to nearest even and saturates at +-448, the scale byte
+ *     is the E8M0 code of 2^sharedExp (the dequantisation multiplier),
+ *     all-zero block -> exponent -127;
+ *   - the shared-expert term is weighted by the sum of the token's active
+ *     scales (the formula's literal reading) or by 1 (selectable);
+ *   - RMS is taken over the unrounded x; y = x * (1 / RMS(x)) * gamma.
+ *
+ * Precision: the quantisers work in fp32 exactly as the dispatch formula's
+ * CastToFp32 prescribes (IEEE division, no contraction; build with
+ * -ffp-contract=off -fno-fast-math).  The combine is computed in fp64 and
+ * rounded once to bf16.
+ *
+ * Parity pins: every exported function is pinned by CPU tests against brute
+ * force, library routines, closed forms and invariants (tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_ERR_ID = 1, ORC_ERR_TABLE = 2, ORC_ERR_MASK1D = 4 };
+
+/* ---------------------------------------------------------------- numbers */
+
+/* bf16 bit pattern -> value (exact: bf16 is the top half of an fp32). */
+static float bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Nearest bf16 to a double, ties to even.  bf16 keeps 8 significant bits,
+ * normal exponents [-126, 127], subnormal spacing 2^-133. */
+static uint16_t bf16_from_double(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    double a = fabs(v), r = 0.0;
+    if (a != 0.0) {
+        int e = ilogb(a);          /* a in [2^e, 2^(e+1)) */
+        int q = e - 7;             /* exponent of one unit in the last place */
+        if (q < -133)
+            q = -133;              /* subnormal grid */
+        r = ldexp(nearbyint(ldexp(a, -q)), q);
+    }
+    float f = (r >= 0x1p128) ? INFINITY : (float)r;  /* r is exact in fp32 */
+    if (signbit(v))
+        f = -f;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* OCP FP8 E4M3 code of an fp32 value: bias 7, 3 mantissa bits, largest
+ * finite 448 = 1.75 * 2^8, no infinities, 0x7F/0xFF = NaN.  Rounds to nearest
+ * with ties to the even code and saturates at +-448.  Codes increase
+ * monotonically with magnitude, so the subnormal grid m * 2^-9 and each
+ * binade's grid (8 + m) * 2^(e-3) map to consecutive codes. */
+static uint8_t e4m3_from_float(float v)
+{
+    uint8_t s = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v))
+        return s | 0x7F;
+    float a = fabsf(v);
+    if (a >= 448.0f)
+        return s | 0x7E;
+    if (a < 0x1p-6f)                            /* below the smallest normal */
+        return s | (uint8_t)nearbyintf(a * 512.0f);  /* 0..8; 8 is 2^-6 */
+    int e = ilogbf(a);                          /* -6 .. 8 */
+    int q = (int)nearbyintf(ldexpf(a, 3 - e));  /* 8 .. 16 */
+    return s | (uint8_t)((e + 7) * 8 + (q - 8));
+}
+
+/* ---------------------------------------------------------------- quantisers */
+
+/* [DSP] cases 3/4: dynamicScales = 127 / max|x| over the segment;
+ * code = CastToInt8(x * dynamicScales); the scale sent is 1 / dynamicScales. */
+static void quant_int8_segment(const uint16_t *x, int n, int8_t *q, float *scale)
+{
+    float m = 0.0f;
+    for (int j = 0; j < n; ++j) {
+        float a = fabsf(bf16_value(x[j]));
+        if (a > m)
+            m = a;
+    }
+    if (m == 0.0f) {
+        for (int j = 0; j < n; ++j)
+            q[j] = 0;
+        *scale = 0.0f;
+        return;
+    }
+    float d = 127.0f / m;
+    for (int j = 0; j < n; ++j) {
+        float v = bf16_value(x[j]) * d;
+        float r = nearbyintf(v);
+        if (r > 127.0f)
+            r = 127.0f;
+        if (r < -127.0f)
+            r = -127.0f;
+        q[j] = (int8_t)r;
+    }
+    *scale = 1.0f / d;
+}
+
+/* [DSP] case 5: sharedExp = floor(log2(max|x|)) - emax with emax = 8;
+ * code = CastToFp8(x / 2^sharedExp); scale byte = E8M0(2^sharedExp). */
+static void quant_mxfp8_block(const uint16_t *x, int n, uint8_t *codes, uint8_t *scale_byte)
+{
+    float m = 0.0f;
+    for (int j = 0; j < n; ++j) {
+        float a = fabsf(bf16_value(x[j]));
+        if (a > m)
+            m = a;
+    }
+    int se = -127;
+    if (m != 0.0f) {
+        se = ilogbf(m) - 8;   /* exact floor(log2 m), subnormals included */
+        if (se < -127)
+            se = -127;
+        if (se > 127)
+            se = 127;
+    }
+    for (int j = 0; j < n; ++j)
+        codes[j] = e4m3_from_float(ldexpf(bf16_value(x[j]), -se));
+    *scale_byte = (uint8_t)(se + 127);
+}
+
+/* ---------------------------------------------------------------- exports */
+
+void oracle_e4m3_encode(const float *v, int n, uint8_t *out)
+{
+    for (int j = 0; j < n; ++j)
+        out[j] = e4m3_from_float(v[j]);
+}
+
+void oracle_bf16_round(const double *v, int n, uint16_t *out)
+{
+    for (int j = 0; j < n; ++j)
+        out[j] = bf16_from_double(v[j]);
+}
+
+void oracle_quant_int8(const uint16_t *x, int n, int8_t *q, float *scale)
+{
+    quant_int8_segment(x, n, q, scale);
+}
+
+void oracle_quant_mxfp8(const uint16_t *x, int n, uint8_t *codes, uint8_t *scale_byte)
+{
+    quant_mxfp8_block(x, n, codes, scale_byte);
+}
+
+/* [UPD] map + prune.  For entry f = i*K + k with logical id e:
+ *   keep      = token_mask[i] (if given) and not (score[f] < thr[k]) (if given)
+ *   instance  = table[e][1 + (i mod table[e][0])]
+ * An entry whose lookup fails (id, replica count or instance out of range)
+ * gets instance -1 and keep 0; it raises an error bit only if it would have
+ * been kept.  A 1-D token mask that is not all-true-then-all-false raises
+ * bit 4 and is still applied as given. */
+int oracle_update_expert(const int32_t *ids, const float *scores, const int32_t *table,
+                         const float *thr, const uint8_t *token_mask, int Bs, int K,
+                         int n_logical, int F, int n_instances, int32_t *out_ids,
+                         uint8_t *out_mask, int32_t *err)
+{
+    if (Bs <= 0 || K <= 0 || n_logical <= 0 || F < 2 || n_instances <= 0)
+        return -1;
+    int32_t bits = 0;
+    if (token_mask)
+        for (int i = 1; i < Bs; ++i)
+            if (token_mask[i] && !token_mask[i - 1])
+                bits |= ORC_ERR_MASK1D;
+    for (int i = 0; i < Bs; ++i) {
+        for (int k = 0; k < K; ++k) {
+            int f = i * K + k;
+            int keep = (token_mask == NULL) || token_mask[i] != 0;
+            if (scores && thr && scores[f] < thr[k])
+                keep = 0;
+            int e = ids[f], inst = -1, fail = 0;
+            if (e < 0 || e >= n_logical) {
+                fail = ORC_ERR_ID;
+            } else {
+                int n = table[(size_t)e * F];
+                if (n < 1 || n > F - 1) {
+                    fail = ORC_ERR_TABLE;
+                } else {
+                    inst = table[(size_t)e * F + 1 + (i % n)];
+                    if (inst < 0 || inst >= n_instances) {
+                        fail = ORC_ERR_TABLE;
+                        inst = -1;
+                    }
+                }
+            }
+            if (fail) {
+                if (keep)
+                    bits |= fail;
+                keep = 0;
+            }
+            out_ids[f] = inst;
+            out_mask[f] = (uint8_t)keep;
+        }
+    }
+    if (err)
+        *err |= bits;
+    return 0;
+}
+
+/* Expert-major routing of N = Bs*K entries over E instances: a stable
+ * counting sort by instance id.
+ *   counts[e]   = number of active entries with id e
+ *   offsets     = exclusive prefix sum of counts, offsets[E] = total rows
+ *   assist[f]   = destination row of entry f (-1 if not active)
+ *   src[r]      = entry f placed in row r (-1 for r >= total)
+ * Within an instance, rows follow ascending f.  An active entry whose id is
+ * outside [0, E) raises bit 1 and is treated as inactive. */
+int oracle_route(const int32_t *ids, const uint8_t *mask, int N, int E, int32_t *counts,
+                 int32_t *offsets, int32_t *assist, int32_t *src, int32_t *err)
+{
+    if (N <= 0 || E <= 0)
+        return -1;
+    int32_t bits = 0;
+    uint8_t *act = (uint8_t *)malloc((size_t)N);
+    int32_t *cursor = (int32_t *)malloc((size_t)E * sizeof(int32_t));
+    if (!act || !cursor) {
+        free(act);
+        free(cursor);
+        return -2;
+    }
+    for (int f = 0; f < N; ++f) {
+        act[f] = (mask == NULL) || mask[f] != 0;
+        if (act[f] && (ids[f] < 0 || ids[f] >= E)) {
+            bits |= ORC_ERR_ID;
+            act[f] = 0;
+        }
+    }
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int f = 0; f < N; ++f)
+        if (act[f])
+            counts[ids[f]] += 1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    for (int e = 0; e < E; ++e)
+        cursor[e] = offsets[e];
+    for (int f = 0; f < N; ++f) {
+        if (act[f]) {
+            int r = cursor[ids[f]]++;
+            assist[f] = r;
+            src[r] = f;
+        } else {
+            assist[f] = -1;
+        }
+    }
+    for (int r = offsets[E]; r < N; ++r)
+        src[r] = -1;
+    free(act);
+    free(cursor);
+    if (err)
+        *err |= bits;
+    return 0;
+}
+
+/* [DSP] dispatch on one device: route, then quantise each token once and copy
+ * its coded row (and scales) into each of its destination rows.
+ *   quant_mode 0: expand_x is bf16 [N, H], bit copies of x; no scales
+ *   quant_mode 2: expand_x int8 [N, H]; scales f32 [N]
+ *   quant_mode 3: expand_x int8 [N, H]; scales f32 [N, ceil(H / tile)]
+ *   quant_mode 4: expand_x e4m3 [N, H]; scales E8M0 u8 [N, H / 32]
+ * Rows at or past offsets[E] are not written. */
+int oracle_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs, int H,
+                    int K, int n_ranks, int local_experts, int quant_mode, int tile,
+                    void *expand_x, void *expand_scales, int32_t *counts, int32_t *offsets,
+                    int32_t *expand_src, int32_t *assist_dst, int32_t *err)
+{
+    if (Bs <= 0 || H <= 0 || K <= 0 || n_ranks <= 0 || local_experts <= 0)
+        return -1;
+    if (quant_mode == 3 && tile <= 0)
+        return -1;
+    if (quant_mode == 4 && H % 32 != 0)
+        return -1;
+    if (quant_mode != 0 && quant_mode != 2 && quant_mode != 3 && quant_mode != 4)
+        return -1;
+    int E = n_ranks * local_experts, N = Bs * K;
+    int rc = oracle_route(ids, mask, N, E, counts, offsets, assist_dst, expand_src, err);
+    if (rc)
+        return rc;
+
+    int n_sc = 0;  /* scale entries per row */
+    if (quant_mode == 2)
+        n_sc = 1;
+    else if (quant_mode == 3)
+        n_sc = (H + tile - 1) / tile;
+    else if (quant_mode == 4)
+        n_sc = H / 32;
+
+    int8_t *q = (int8_t *)malloc((size_t)H);
+    float *fs = (float *)malloc((size_t)(n_sc > 0 ? n_sc : 1) * sizeof(float));
+    uint8_t *bs = (uint8_t *)malloc((size_t)(n_sc > 0 ? n_sc : 1));
+    if (!q || !fs || !bs) {
+        free(q);
+        free(fs);
+        free(bs);
+        return -2;
+    }
+    for (int i = 0; i < Bs; ++i) {
+        const uint16_t *xi = x + (size_t)i * H;
+        if (quant_mode == 2) {
+            quant_int8_segment(xi, H, q, &fs[0]);
+        } else if (quant_mode == 3) {
+            for (int t = 0; t < n_sc; ++t) {
+                int n = H - t * tile < tile ? H - t * tile : tile;
+                quant_int8_segment(xi + (size_t)t * tile, n, q + (size_t)t * tile, &fs[t]);
+            }
+        } else if (quant_mode == 4) {
+            for (int b = 0; b < n_sc; ++b)
+                quant_mxfp8_block(xi + (size_t)b * 32, 32, (uint8_t *)q + (size_t)b * 32, &bs[b]);
+        }
+        for (int k = 0; k < K; ++k) {
+            int r = assist_dst[i * K + k];
+            if (r < 0)
+                continue;
+            if (quant_mode == 0) {
+                memcpy((uint16_t *)expand_x + (size_t)r * H, xi, (size_t)H * sizeof(uint16_t));
+            } else {
+                memcpy((int8_t *)expand_x + (size_t)r * H, q, (size_t)H);
+                if (quant_mode == 4)
+                    memcpy((uint8_t *)expand_scales + (size_t)r * n_sc, bs, (size_t)n_sc);
+                else
+                    memcpy((float *)expand_scales + (size_t)r * n_sc, fs,
+                           (size_t)n_sc * sizeof(float));
+            }
+        }
+    }
+    free(q);
+    free(fs);
+    free(bs);
+    return 0;
+}
+
+/* [CMB] combine + add + RMSNorm for each token i, in fp64:
+ *   acc  = sum over active k of s[i,k] * Eout[assist[i,k]]
+ *   acc += w * shared[i]   with w = sum of active s[i,k] (shared_mode 0)
+ *                          or w = 1 (shared_mode 1); skipped without shared
+ *   x    = acc + residual[i]                 -> x_out = bf16(x)
+ *   rstd = 1 / sqrt(mean(x^2) + eps)         -> y = bf16(x * rstd * gamma)
+ * An entry with assist < 0 was not dispatched and contributes nothing. */
+int oracle_combine_add_rmsnorm(const uint16_t *expert_out, const int32_t *assist,
+                               const float *scales, const uint16_t *shared,
+                               const uint16_t *residual, const uint16_t *gamma, float eps,
+                               int Bs, int H, int K, int shared_mode, uint16_t *y,
+                               uint16_t *x_out, float *rstd_out)
+{
+    if (Bs <= 0 || H <= 0 || K <= 0 || (shared_mode != 0 && shared_mode != 1))
+        return -1;
+    double *xf = (double *)malloc((size_t)H * sizeof(double));
+    if (!xf)
+        return -2;
+    for (int i = 0; i < Bs; ++i) {
+        double ws = 0.0;
+        for (int h = 0; h < H; ++h)
+            xf[h] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int r = assist[i * K + k];
+            if (r < 0)
+                continue;
+            double s = scales[i * K + k];
+            ws += s;
+            const uint16_t *row = expert_out + (size_t)r * H;
+            for (int h = 0; h < H; ++h)
+                xf[h] += s * (double)bf16_value(row[h]);
+        }
+        if (shared) {
+            double w = shared_mode == 0 ? ws : 1.0;
+            for (int h = 0; h < H; ++h)
+                xf[h] += w * (double)bf16_value(shared[(size_t)i * H + h]);
+        }
+        double ss = 0.0;
+        for (int h = 0; h < H; ++h) {
+            xf[h] += (double)bf16_value(residual[(size_t)i * H + h]);
+            ss += xf[h] * xf[h];
+        }
+        double rstd = 1.0 / sqrt(ss / H + (double)eps);
+        for (int h = 0; h < H; ++h) {
+            if (x_out)
+                x_out[(size_t)i * H + h] = bf16_from_double(xf[h]);
+            y[(size_t)i * H + h] = bf16_from_double(xf[h] * rstd * (double)bf16_value(gamma[h]));
+        }
+        if (rstd_out)
+            rstd_out[i] = (float)rstd;
+    }
+    free(xf);
+    return 0;
+}

@@ -1,0 +1,66 @@
+"""The oracle's pins must catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a temporary copy of oracle/moe_oracle.c
+(a dropped term, a wrong sign, index, rounding mode or comparison), builds
+it, and runs the oracle pin suite against that build in a subprocess.  The
+suite must fail for every planted mistake.  Nothing here touches the GPU
+library.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, exact text in the oracle, replacement); each text must occur once
+MUTANTS = [
+    ("replica_index", "1 + (i % n)", "1 + (k % n)"),
+    ("prune_compare", "scores[f] < thr[k]", "scores[f] <= thr[k]"),
+    ("mask1d_rule", "token_mask[i] && !token_mask[i - 1]", "!token_mask[i] && token_mask[i - 1]"),
+    ("unstable_order", "for (int f = 0; f < N; ++f) {\n        if (act[f]) {",
+     "for (int f = N - 1; f >= 0; --f) {\n        if (act[f]) {"),
+    ("scan_short_total", "offsets[e + 1] = offsets[e] + counts[e];",
+     "offsets[e + 1] = offsets[e] + counts[e] - (e == E - 1 && counts[e] > 0);"),
+    ("histogram_drops_first", "counts[ids[f]] += 1;", "counts[ids[f]] += (f > 0);"),
+    ("int8_truncate", "float r = nearbyintf(v);", "float r = truncf(v);"),
+    ("int8_scale_direction", "*scale = 1.0f / d;", "*scale = d;"),
+    ("int8_no_abs", "float a = fabsf(bf16_value(x[j]));\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {",
+     "float a = bf16_value(x[j]);\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {"),
+    ("int8_dst_max", "float d = 127.0f / m;", "float d = 128.0f / m;"),
+    ("mx_emax", "se = ilogbf(m) - 8;", "se = ilogbf(m) - 7;"),
+    ("mx_scale_direction", "*scale_byte = (uint8_t)(se + 127);", "*scale_byte = (uint8_t)(127 - se);"),
+    ("e4m3_no_saturation", "return s | 0x7E;", "return s | 0x7F;"),
+    ("e4m3_ties_away", "int q = (int)nearbyintf(ldexpf(a, 3 - e));", "int q = (int)roundf(ldexpf(a, 3 - e));"),
+    ("e4m3_bias", "(e + 7) * 8 + (q - 8)", "(e + 8) * 8 + (q - 8)"),
+    ("bf16_ties_away", "r = ldexp(nearbyint(ldexp(a, -q)), q);", "r = ldexp(floor(ldexp(a, -q) + 0.5), q);"),
+    ("shared_weight_one", "double w = shared_mode == 0 ? ws : 1.0;", "double w = 1.0;"),
+    ("residual_dropped", "xf[h] += (double)bf16_value(residual[(size_t)i * H + h]);",
+     "xf[h] += 0.0 * (double)bf16_value(residual[(size_t)i * H + h]);"),
+    ("rms_mean_n_minus_1", "sqrt(ss / H + (double)eps)", "sqrt(ss / (H - 1) + (double)eps)"),
+    ("eps_outside_sqrt", "1.0 / sqrt(ss / H + (double)eps)", "1.0 / (sqrt(ss / H) + (double)eps)"),
+    ("gamma_dropped", "xf[h] * rstd * (double)bf16_value(gamma[h])", "xf[h] * rstd"),
+    ("pruned_weight_counted", "int r = assist[i * K + k];\n            if (r < 0)\n                continue;\n            double s = scales[i * K + k];\n            ws += s;",
+     "int r = assist[i * K + k];\n            double s = scales[i * K + k];\n            ws += s;\n            if (r < 0)\n                continue;"),
+]
+
+PIN_FILES = ["tests/test_oracle_numbers.py", "tests/test_oracle_route.py",
+             "tests/test_oracle_dispatch_combine.py", "tests/test_golden.py"]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, old, new, tmp_path):
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+    mut_src = tmp_path / "moe_oracle_mutant.c"
+    mut_src.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmoe_oracle_mutant.so")
+    obuild.build(src=str(mut_src), lib=lib)
+    env = dict(os.environ, MOE_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *PIN_FILES], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode == 1, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
