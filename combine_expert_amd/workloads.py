@@ -176,7 +176,7 @@ def make_c3(seed: int = 3000, quant_mode: int = QUANT_MXFP8, with_expert_out: bo
 
 def _c4_table(rng, n_logical: int, two_replicas: np.ndarray, n_slots: int) -> np.ndarray:
     """Place each logical expert's replicas on distinct seeded-random instance slots."""
-    slots = rng.permutation(n_slots).astype(np.int32)
+    slots = rng.permutation(n_slots).astype(np.int32)  # unused slots stay empty
     table = np.full((n_logical, 3), -1, dtype=np.int32)
     pos = 0
     for e in range(n_logical):
@@ -184,7 +184,7 @@ def _c4_table(rng, n_logical: int, two_replicas: np.ndarray, n_slots: int) -> np
         table[e, 0] = n
         table[e, 1:1 + n] = slots[pos:pos + n]
         pos += n
-    assert pos == n_slots
+    assert pos <= n_slots
     return table
 
 

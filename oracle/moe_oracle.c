@@ -31,6 +31,8 @@
  *   - rows of one instance are ordered by ascending flat index f = i*K + k;
  *   - int8: dstTypeMax = 127, round half to even, clamp to [-127, 127],
  *     scale written = 1 / dynamicScales, all-zero segment -> codes 0, scale 0;
+ *     if 127 / max overflows fp32 (max below about 3.7e-38), zero elements
+ *     code to 0 and the others saturate to +-127 (scale 1/inf = 0);
  *   - per-tile mode: tiles of `tile` elements along H (128 in the workloads);
  *   - mxfp8: blocks of 32 along H, max(x) read as max |x|, emax = 8 (E4M3),
  *     fp8 cast rounds to nearest even and saturates at +-448, the scale byte
@@ -126,10 +128,10 @@ static void quant_int8_segment(const uint16_t *x, int n, int8_t *q, float *scale
         *scale = 0.0f;
         return;
     }
-    float d = 127.0f / m;
+    float d = 127.0f / m;  /* +inf when m < 127 / FLT_MAX (a tiny subnormal maximum) */
     for (int j = 0; j < n; ++j) {
         float v = bf16_value(x[j]) * d;
-        float r = nearbyintf(v);
+        float r = (v != v) ? 0.0f : nearbyintf(v);  /* 0 * inf: a zero element stays 0 */
         if (r > 127.0f)
             r = 127.0f;
         if (r < -127.0f)

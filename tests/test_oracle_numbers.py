@@ -212,6 +212,12 @@ def test_int8_invariants():
 def test_int8_zero_segment_and_worked_values():
     q, s = oracle.quant_int8(np.zeros(64, dtype=np.uint16))
     assert s == 0.0 and not q.any()
+    # maximum a tiny subnormal: 127 / m overflows to +inf in fp32, so nonzero
+    # elements saturate, zeros (0 * inf) stay 0 and the scale 1/inf is 0
+    xb = np.array([0x0001, 0x8003, 0x0000, 0x8000, 0x0002], np.uint16)
+    assert np.isinf(np.float32(127.0) / bits_to_f32(xb[1:2])[0].__abs__())
+    q, s = oracle.quant_int8(xb)
+    assert list(q) == [127, -127, 0, 0, 127] and s == 0.0
     # x = [1, -2, 0.5, 4]: m = 4, d = 127/4 = 31.75 (exact);
     # x*d = [31.75, -63.5, 15.875, 127] -> [32, -64 (tie to even), 16, 127]
     q, s = oracle.quant_int8(bf16_bits_of(np.array([1.0, -2.0, 0.5, 4.0])))
