@@ -1,0 +1,139 @@
+// api.hip -- C ABI of libmoe_expert.so (declared in include/moe_expert.h).
+//
+// Each entry point checks every host-visible argument (the pages' first-phase
+// parameter check) and returns a non-zero status before anything is
+// enqueued; otherwise it enqueues its kernels on the caller's stream and
+// returns.  Nothing is allocated, synchronised or kept between calls.
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "moe_expert.h"
+
+namespace {
+
+constexpr int kMaxBs = 512;       // combine / update-expert pages: 0 < Bs <= 512
+constexpr int kMaxK = 16;         // 0 < K <= 16
+constexpr int kMinH = 1024;       // combine page: H in [1024, 8192]
+constexpr int kMaxH = 8192;
+constexpr int kMaxExperts = 1024; // update-expert page: at most 1024 instances
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool bad_bs_k(int Bs, int K) { return Bs <= 0 || Bs > kMaxBs || K <= 0 || K > kMaxK; }
+
+bool bad_h(int H) { return H < kMinH || H > kMaxH || H % 32 != 0; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_EINVAL: return "MOE_EINVAL: argument out of range, NULL or misaligned";
+    case MOE_ENOTSUP: return "MOE_ENOTSUP: option not implemented";
+    case MOE_ELAUNCH: return "MOE_ELAUNCH: kernel launch failed";
+    default: return "unknown moe_status";
+    }
+}
+
+int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
+                      const int32_t *table, const float *prune_thr, const uint8_t *token_mask,
+                      int Bs, int K, int n_logical, int F, int n_instances,
+                      int32_t *balanced_ids, uint8_t *balanced_mask, int32_t *dev_err,
+                      void *stream)
+{
+    if (!expert_ids || !table || !balanced_ids || !balanced_mask)
+        return MOE_EINVAL;
+    if (bad_bs_k(Bs, K) || n_logical <= 0 || n_logical > kMaxExperts || K > n_logical)
+        return MOE_EINVAL;
+    if (F < 2 || F > n_logical + 1 || n_instances <= 0 || n_instances > kMaxExperts)
+        return MOE_EINVAL;
+    if (!aligned(expert_ids, 4) || !aligned(table, 4) || !aligned(balanced_ids, 4) ||
+        (expert_scales && !aligned(expert_scales, 4)) || (prune_thr && !aligned(prune_thr, 4)) ||
+        (dev_err && !aligned(dev_err, 4)))
+        return MOE_EINVAL;
+    return from_hip(moe::launch_update_expert(expert_ids, expert_scales, table, prune_thr,
+                                              token_mask, Bs, K, n_logical, F, n_instances,
+                                              balanced_ids, balanced_mask, dev_err,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask, int Bs,
+                 int H, int K, int n_ranks, int local_experts, int quant_mode, int tile,
+                 void *expand_x, void *expand_scales, int32_t *expert_counts,
+                 int32_t *expert_offsets, int32_t *expand_src, int32_t *assist_dst,
+                 int32_t *dev_err, void *stream)
+{
+    if (!x || !expert_ids || !expand_x || !expert_counts || !expert_offsets || !expand_src ||
+        !assist_dst)
+        return MOE_EINVAL;
+    if (bad_bs_k(Bs, K) || bad_h(H) || n_ranks < 1 || local_experts < 1)
+        return MOE_EINVAL;
+    const long long E = (long long)n_ranks * local_experts;
+    if (E > kMaxExperts || K > E)
+        return MOE_EINVAL;
+    switch (quant_mode) {
+    case MOE_Q_NONE:
+        break;
+    case MOE_Q_STATIC:
+        return MOE_ENOTSUP;
+    case MOE_Q_INT8_TOKEN:
+    case MOE_Q_MXFP8:
+        if (!expand_scales)
+            return MOE_EINVAL;
+        break;
+    case MOE_Q_INT8_TILE:
+        if (!expand_scales || tile <= 0)
+            return MOE_EINVAL;
+        if (tile < 16 || tile > 1024 || (tile & (tile - 1)) != 0)
+            return MOE_ENOTSUP;
+        break;
+    default:
+        return MOE_EINVAL;
+    }
+    if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(expert_ids, 16) ||
+        (active_mask && !aligned(active_mask, 4)) || !aligned(expert_counts, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(expand_src, 4) || !aligned(assist_dst, 4) ||
+        (dev_err && !aligned(dev_err, 4)) ||
+        ((quant_mode == MOE_Q_INT8_TOKEN || quant_mode == MOE_Q_INT8_TILE) &&
+         !aligned(expand_scales, 4)))
+        return MOE_EINVAL;
+    return from_hip(moe::launch_dispatch(
+        static_cast<const uint16_t *>(x), expert_ids, active_mask, Bs, H, K, (int)E, quant_mode,
+        quant_mode == MOE_Q_INT8_TILE ? tile : 0, expand_x, expand_scales, expert_counts,
+        expert_offsets, expand_src, assist_dst, dev_err, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
+                            const float *expert_scales, const void *shared_x,
+                            const void *residual_x, const void *gamma, float eps, int Bs,
+                            int H, int K, int shared_mode, void *y, void *x_out, float *rstd,
+                            int32_t *dev_err, void *stream)
+{
+    if (!expert_out || !assist_dst || !expert_scales || !residual_x || !gamma || !y)
+        return MOE_EINVAL;
+    if (bad_bs_k(Bs, K) || bad_h(H))
+        return MOE_EINVAL;
+    if (!(eps >= 0.0f) || !isfinite(eps) || (shared_mode != MOE_SHARED_PAGE &&
+                                            shared_mode != MOE_SHARED_ADD))
+        return MOE_EINVAL;
+    if (!aligned(expert_out, 16) || !aligned(residual_x, 16) || !aligned(gamma, 16) ||
+        !aligned(y, 16) || (shared_x && !aligned(shared_x, 16)) ||
+        (x_out && !aligned(x_out, 16)) || !aligned(assist_dst, 4) ||
+        !aligned(expert_scales, 4) || (rstd && !aligned(rstd, 4)) ||
+        (dev_err && !aligned(dev_err, 4)))
+        return MOE_EINVAL;
+    return from_hip(moe::launch_combine(
+        static_cast<const uint16_t *>(expert_out), assist_dst, expert_scales,
+        static_cast<const uint16_t *>(shared_x), static_cast<const uint16_t *>(residual_x),
+        static_cast<const uint16_t *>(gamma), eps, Bs, H, K, shared_mode,
+        static_cast<uint16_t *>(y), static_cast<uint16_t *>(x_out), rstd, dev_err,
+        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

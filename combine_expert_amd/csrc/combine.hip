@@ -1,0 +1,181 @@
+// combine.hip -- weighted gather of expert outputs + shared expert + residual,
+// fused with RMSNorm ("aclnnMoeDistributeCombineAddRmsNorm", 计算公式:
+// combineOut = Sum(expertScales*ataOut + expertScales*sharedExpertX),
+// x = combineOut + residualX, y = x / RMS(x) * gamma with
+// RMS(x) = sqrt(mean(x^2) + normEps)).
+//
+// One block per token, one thread per 16 elements of the row: every input
+// row is read once with 16-byte loads, the fp32 sum stays in registers, the
+// sum of squares is a wave butterfly plus one LDS step, and y / x_out are
+// written once.  The kernel is bound by HBM bandwidth: per token it moves
+// (n_dispatched + 2 or 3) rows in and 2 rows out.
+//
+// The token's dispatched entries (assist_dst >= 0) are compacted by wave 0
+// with a ballot, in k order, so row loads are issued back to back, CH rows
+// at a time, with no loads for pruned entries.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <int CH>
+__global__ __launch_bounds__(kMaxThreads) void k_combine(
+    const uint16_t *__restrict__ eo, const int32_t *__restrict__ assist,
+    const float *__restrict__ scales, const uint16_t *__restrict__ shared,
+    const uint16_t *__restrict__ residual, const uint16_t *__restrict__ gamma, float eps,
+    int Bs, int H, int K, int shared_mode, uint16_t *__restrict__ y,
+    uint16_t *__restrict__ x_out, float *__restrict__ rstd_out, int32_t *__restrict__ dev_err)
+{
+    __shared__ int s_row[16];
+    __shared__ float s_w[16];
+    __shared__ int s_n;
+    __shared__ float s_ws;
+    __shared__ float s_part[kMaxWaves];
+
+    const int i = blockIdx.x;
+    const int t = threadIdx.x, T = blockDim.x;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
+    const bool has = t * kChunk < H;
+    const size_t rowoff = (size_t)i * H;
+
+    // residual, shared and gamma do not depend on the routing: start them first
+    uint4 ra = make_uint4(0, 0, 0, 0), rb = ra, sa = ra, sb = ra, ga = ra, gb = ra;
+    if (has) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(residual + rowoff) + 2 * t;
+        ra = p[0];
+        rb = p[1];
+        const uint4 *q = reinterpret_cast<const uint4 *>(gamma) + 2 * t;
+        ga = q[0];
+        gb = q[1];
+        if (shared) {
+            const uint4 *s = reinterpret_cast<const uint4 *>(shared + rowoff) + 2 * t;
+            sa = s[0];
+            sb = s[1];
+        }
+    }
+
+    if (w == 0) {
+        int r = -1;
+        float s = 0.0f;
+        if (lane < K) {
+            r = assist[i * K + lane];
+            s = scales[i * K + lane];
+        }
+        const bool bad = r >= Bs * K;
+        if (bad)
+            r = -1;
+        const bool on = r >= 0;
+        const unsigned long long bal = __ballot(on);
+        const int slot = __popcll(bal & ((1ull << lane) - 1ull));
+        if (on) {
+            s_row[slot] = r;
+            s_w[slot] = s;
+        }
+        const float ws = wave_sum_f32(on ? s : 0.0f);
+        if (lane == 0) {
+            s_n = __popcll(bal);
+            s_ws = ws;
+        }
+        if (bad && dev_err)
+            atomicOr(dev_err, 8);
+    }
+    __syncthreads();
+    const int n = s_n;
+
+    float acc[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        acc[j] = 0.0f;
+    for (int j0 = 0; j0 < n; j0 += CH) {
+        uint4 ea[CH], eb[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (j0 + j < n && has) {
+                const uint4 *p =
+                    reinterpret_cast<const uint4 *>(eo + (size_t)s_row[j0 + j] * H) + 2 * t;
+                ea[j] = p[0];
+                eb[j] = p[1];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            if (j0 + j < n) {
+                const float s = s_w[j0 + j];
+                float v[16];
+                unpack16(ea[j], eb[j], v);
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[e] = fmaf(s, v[e], acc[e]);
+            }
+        }
+    }
+
+    float xf[16];
+    {
+        float rv[16];
+        unpack16(ra, rb, rv);
+        if (shared) {
+            const float wsh = shared_mode == 0 ? s_ws : 1.0f;
+            float sv[16];
+            unpack16(sa, sb, sv);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[e] = fmaf(wsh, sv[e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            xf[e] = acc[e] + rv[e];
+    }
+
+    // lanes past the row end loaded nothing: they add nothing to the sum of squares
+    float ss = 0.0f;
+    if (has) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            ss = fmaf(xf[e], xf[e], ss);
+    }
+    ss = wave_sum_f32(ss);
+    if (lane == 0)
+        s_part[w] = ss;
+
+    if (has && x_out) {
+        uint4 *p = reinterpret_cast<uint4 *>(x_out + rowoff) + 2 * t;
+        p[0] = make_uint4(pack_bf16x2(xf[0], xf[1]), pack_bf16x2(xf[2], xf[3]),
+                          pack_bf16x2(xf[4], xf[5]), pack_bf16x2(xf[6], xf[7]));
+        p[1] = make_uint4(pack_bf16x2(xf[8], xf[9]), pack_bf16x2(xf[10], xf[11]),
+                          pack_bf16x2(xf[12], xf[13]), pack_bf16x2(xf[14], xf[15]));
+    }
+    __syncthreads();
+    float tot = 0.0f;
+    for (int j = 0; j < nw; ++j)
+        tot += s_part[j];
+    const float rstd = 1.0f / __builtin_sqrtf(tot / (float)H + eps);
+    if (t == 0 && rstd_out)
+        rstd_out[i] = rstd;
+    if (!has)
+        return;
+    float g[16], o[16];
+    unpack16(ga, gb, g);
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        o[e] = xf[e] * rstd * g[e];
+    uint4 *p = reinterpret_cast<uint4 *>(y + rowoff) + 2 * t;
+    p[0] = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                      pack_bf16x2(o[6], o[7]));
+    p[1] = make_uint4(pack_bf16x2(o[8], o[9]), pack_bf16x2(o[10], o[11]),
+                      pack_bf16x2(o[12], o[13]), pack_bf16x2(o[14], o[15]));
+}
+
+hipError_t launch_combine(const uint16_t *expert_out, const int32_t *assist,
+                          const float *scales, const uint16_t *shared,
+                          const uint16_t *residual, const uint16_t *gamma, float eps, int Bs,
+                          int H, int K, int shared_mode, uint16_t *y, uint16_t *x_out,
+                          float *rstd, int32_t *dev_err, hipStream_t stream)
+{
+    hipLaunchKernelGGL((k_combine<8>), dim3(Bs), dim3(row_threads(H)), 0, stream, expert_out,
+                       assist, scales, shared, residual, gamma, eps, Bs, H, K, shared_mode, y,
+                       x_out, rstd, dev_err);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,116 @@
+// device.h -- gfx950 device helpers for the MoE mapping / dispatch / combine
+// kernels: bf16 and OCP E4M3 conversions, wave64 reductions and scans.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxThreads = 512;        // H <= 8192 elements / 16 per thread
+constexpr int kMaxWaves = kMaxThreads / kWave;
+constexpr int kChunk = 16;              // row elements owned by one thread
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// 16 bf16 (two uint4) -> 16 fp32
+__device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float *v)
+{
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        v[2 * j] = bf16_lo(w[j]);
+        v[2 * j + 1] = bf16_hi(w[j]);
+    }
+}
+
+// Largest |x| bit pattern among 16 bf16 (sign cleared).  For non-negative
+// values the integer order of bf16 patterns is the numeric order.
+__device__ __forceinline__ uint32_t amax_bits16(const uint4 &a, const uint4 &b)
+{
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        m = max(m, w[j] & 0x7fffu);
+        m = max(m, (w[j] >> 16) & 0x7fffu);
+    }
+    return m;
+}
+
+// ---------------------------------------------------------------- E4M3
+
+// OCP FP8 E4M3 code of v: round to nearest even, saturate at +-448
+// (0x7E), NaN -> 0x7F with the sign kept, -0 -> 0x80.
+//   |v| <  2^-6 : subnormal grid m * 2^-9, code = rint(|v| * 512) in [0, 8]
+//   |v| >= 2^-6 : keep 3 of the 23 fp32 mantissa bits with round-half-even on
+//                 the 20 dropped bits; the carry moves into the exponent and
+//                 the fp32 exponent bias 127 becomes the E4M3 bias 7.
+__device__ __forceinline__ uint32_t e4m3_code(float v)
+{
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    const float af = __uint_as_float(a);
+    const uint32_t sub = (uint32_t)__builtin_rintf(af * 512.0f);
+    const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    uint32_t code = af < 0x1p-6f ? sub : nrm;
+    code = af >= 448.0f ? 0x7eu : code;
+    code = af != af ? 0x7fu : code;
+    return sign | code;
+}
+
+// ---------------------------------------------------------------- wave ops
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+// Every lane gets the same bits: the butterfly adds the same pairs in every lane.
+__device__ __forceinline__ float wave_sum_f32(float v)
+{
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int t = __shfl_up(v, o);
+        if (lane >= o)
+            v += t;
+    }
+    return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,388 @@
+// dispatch.hip -- quantise tokens and scatter them expert-major
+// ("aclnnMoeDistributeDispatchV2", 计算公式 cases 1, 3, 4 and 5: the rows
+// this device sends, laid out [rank][local expert][token] exactly as the
+// all-to-all would deliver them).
+//
+// One launch, Bs + 1 blocks, no inter-block communication:
+//   block 0      histogram of the active entries (LDS atomics; counts are
+//                order-free), exclusive scan, counts/offsets, and -1 for the
+//                unused tail of expand_src;
+//   block 1 + i  token i: loads its row once, computes the stable row of
+//                each of its K entries, codes the row once and writes it K
+//                times.
+// The stable row of entry f is the number of active entries g whose key
+// (instance id, g) is smaller than f's, i.e. offsets[id] plus the number of
+// earlier entries with the same id.  Each token block counts it directly
+// over all N = Bs*K keys (at most 8192 four-byte ids, L2-resident), which
+// costs a few hundred ALU operations per thread and overlaps the HBM load
+// of the token's row, instead of a serial routing kernel between two
+// launches.  The result does not depend on scheduling: bitwise repeatable.
+//
+// Row layout: one thread owns 16 consecutive elements (two 16-byte loads of
+// bf16), so a 32-element mxfp8 block is a lane pair and a 128-element int8
+// tile is 8 lanes; per-block maxima are lane shuffles, the per-token maximum
+// is a wave reduction plus one LDS step.
+#include "device.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kKeyShift = 13;  // flat entry index g < Bs*K <= 8192 = 2^13
+constexpr int kInactiveKey = 0x7fffffff;
+
+// ------------------------------------------------------------------ block 0
+
+__device__ void route_summary(const int32_t *__restrict__ ids, const uint8_t *__restrict__ mask,
+                              int N, int E, int32_t *__restrict__ counts,
+                              int32_t *__restrict__ offsets, int32_t *__restrict__ expand_src,
+                              int32_t *__restrict__ dev_err, int *s_hist, int *s_wave)
+{
+    const int t = threadIdx.x, T = blockDim.x;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
+    for (int e = t; e < E; e += T)
+        s_hist[e] = 0;
+    __syncthreads();
+    int bad = 0;
+    for (int g = t; g < N; g += T) {
+        const int id = ids[g];
+        if (mask == nullptr || mask[g] != 0) {
+            if (id >= 0 && id < E)
+                atomicAdd(&s_hist[id], 1);
+            else
+                bad = 1;
+        }
+    }
+    if (bad && dev_err)
+        atomicOr(dev_err, 1);
+    __syncthreads();
+
+    // exclusive scan: each thread owns a contiguous run of counters
+    const int per = (E + T - 1) / T;
+    const int e0 = min(t * per, E), e1 = min(e0 + per, E);
+    int local = 0;
+    for (int e = e0; e < e1; ++e)
+        local += s_hist[e];
+    const int incl = wave_incl_scan(local);
+    if (lane == kWave - 1)
+        s_wave[w] = incl;
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int j = 0; j < nw; ++j) {
+        const int v = s_wave[j];
+        base += j < w ? v : 0;
+        total += v;
+    }
+    int run = base + incl - local;
+    for (int e = e0; e < e1; ++e) {
+        const int c = s_hist[e];
+        counts[e] = c;
+        offsets[e] = run;
+        run += c;
+    }
+    if (t == 0)
+        offsets[E] = total;
+    for (int r = total + t; r < N; r += T)
+        expand_src[r] = -1;
+}
+
+// ------------------------------------------------------------------ token blocks
+
+__device__ __forceinline__ int entry_key(int id, bool on, int g, int E)
+{
+    return (on && id >= 0 && id < E) ? (id << kKeyShift) | g : kInactiveKey;
+}
+
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d)
+{
+    return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+           ((uint32_t)d << 24);
+}
+
+// int8 codes of 16 values with multiplier d: clamp(rint(v * d), -127, 127).
+// d is +inf when 127 / max overflows (a tiny subnormal maximum): zeros then
+// give 0 * inf = NaN and are coded 0, the rest saturate.
+__device__ __forceinline__ uint4 int8_codes(const float *v, float d)
+{
+    int q[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        float r = __builtin_rintf(v[j] * d);
+        r = r != r ? 0.0f : r;
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q[j] = (int)r;
+    }
+    return make_uint4(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]),
+                      pack_i8x4(q[8], q[9], q[10], q[11]), pack_i8x4(q[12], q[13], q[14], q[15]));
+}
+
+// E4M3 codes of 16 values multiplied by the power of two f (exact product)
+__device__ __forceinline__ uint4 e4m3_codes(const float *v, float f)
+{
+    uint32_t c[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+        c[j] = e4m3_code(v[j] * f);
+    return make_uint4(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
+                      c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24,
+                      c[8] | c[9] << 8 | c[10] << 16 | c[11] << 24,
+                      c[12] | c[13] << 8 | c[14] << 16 | c[15] << 24);
+}
+
+// floor(log2(m)) of a positive bf16 magnitude pattern (normal or subnormal)
+__device__ __forceinline__ int bf16_ilogb(uint32_t m)
+{
+    const int ex = (int)(m >> 7);
+    return ex ? ex - 127 : (31 - __clz((int)(m & 0x7f))) - 133;
+}
+
+template <int MODE, int KMAX>
+__global__ __launch_bounds__(kMaxThreads) void k_dispatch(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ ids,
+    const uint8_t *__restrict__ mask, int Bs, int H, int K, int E, int tile,
+    void *__restrict__ expand_x, void *__restrict__ expand_scales, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ expand_src,
+    int32_t *__restrict__ assist_dst, int32_t *__restrict__ dev_err)
+{
+    __shared__ int s_hist[1024];
+    __shared__ int s_part[kMaxWaves][KMAX / 2 + 1];
+    __shared__ int s_rank[KMAX];
+    __shared__ uint32_t s_amax;
+
+    const int N = Bs * K;
+    if (blockIdx.x == 0) {
+        route_summary(ids, mask, N, E, counts, offsets, expand_src, dev_err, s_hist,
+                      &s_part[0][0]);
+        return;
+    }
+    const int i = blockIdx.x - 1;
+    const int t = threadIdx.x, T = blockDim.x;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
+    const bool has = t * kChunk < H;
+
+    // 1. this thread's 16 elements of x[i] (in flight while ranks are counted)
+    uint4 xa = make_uint4(0, 0, 0, 0), xb = xa;
+    if (has) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)i * H) + 2 * t;
+        xa = src[0];
+        xb = src[1];
+    }
+
+    // 2. stable rows of the token's entries: count smaller keys over all entries
+    int tkey[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        tkey[k] = -1;  // inactive target: no key is smaller
+        if (k < K) {
+            const int f = i * K + k;
+            const int key = entry_key(ids[f], mask == nullptr || mask[f] != 0, f, E);
+            if (key != kInactiveKey)
+                tkey[k] = key;
+        }
+    }
+    int cnt[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        cnt[k] = 0;
+    const int N4 = N >> 2;
+    const int4 *ids4 = reinterpret_cast<const int4 *>(ids);
+    const uint32_t *mask4 = reinterpret_cast<const uint32_t *>(mask);
+#pragma unroll 4
+    for (int g4 = t; g4 < N4; g4 += T) {
+        const int4 v = ids4[g4];
+        const uint32_t m = mask ? mask4[g4] : 0x01010101u;
+        const int g = g4 * 4;
+        const int k0 = entry_key(v.x, (m & 0xffu) != 0, g, E);
+        const int k1 = entry_key(v.y, (m & 0xff00u) != 0, g + 1, E);
+        const int k2 = entry_key(v.z, (m & 0xff0000u) != 0, g + 2, E);
+        const int k3 = entry_key(v.w, (m & 0xff000000u) != 0, g + 3, E);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            cnt[k] += (k0 < tkey[k]) + (k1 < tkey[k]) + (k2 < tkey[k]) + (k3 < tkey[k]);
+    }
+    for (int g = N4 * 4 + t; g < N; g += T) {
+        const int key = entry_key(ids[g], mask == nullptr || mask[g] != 0, g, E);
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+            cnt[k] += key < tkey[k];
+    }
+
+    // 3. block sums: two 16-bit counters per word (each sum <= 8192)
+    constexpr int P = KMAX / 2;
+    int pk[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        pk[j] = wave_sum_i32(cnt[2 * j] | (cnt[2 * j + 1] << 16));
+    uint32_t amax = 0;
+    if (MODE == 2) {
+        amax = wave_max_u32(amax_bits16(xa, xb));
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            s_part[w][j] = pk[j];
+        if (MODE == 2)
+            s_part[w][P] = (int)amax;
+    }
+    __syncthreads();
+    if (t < P) {
+        int s = 0;
+        for (int j = 0; j < nw; ++j)
+            s += s_part[j][t];
+        s_rank[2 * t] = tkey[2 * t] < 0 ? -1 : (s & 0xffff);
+        s_rank[2 * t + 1] = tkey[2 * t + 1] < 0 ? -1 : (s >> 16);
+    }
+    if (MODE == 2 && t == P) {
+        uint32_t m = 0;
+        for (int j = 0; j < nw; ++j)
+            m = max(m, (uint32_t)s_part[j][P]);
+        s_amax = m;
+    }
+    __syncthreads();
+    int rank[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+        rank[k] = k < K ? s_rank[k] : -1;
+    if (t < K) {
+        const int f = i * K + t;
+        const int r = s_rank[t];
+        assist_dst[f] = r;
+        if (r >= 0)
+            expand_src[r] = f;
+    }
+
+    // 4. code the row once, write it to each destination row
+    if (MODE == 0) {
+        if (!has)
+            return;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (rank[k] < 0)
+                continue;
+            uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(expand_x) +
+                                                   (size_t)rank[k] * H) + 2 * t;
+            dst[0] = xa;
+            dst[1] = xb;
+        }
+        return;
+    }
+
+    float v[16];
+    unpack16(xa, xb, v);
+    uint4 code;
+    if (MODE == 2) {
+        const uint32_t m = s_amax;
+        const float mf = __uint_as_float(m << 16);
+        const float d = m ? 127.0f / mf : 0.0f;
+        const float scale = m ? 1.0f / d : 0.0f;
+        code = int8_codes(v, d);
+        if (has) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (rank[k] < 0)
+                    continue;
+                reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
+                                          (size_t)rank[k] * H)[t] = code;
+                if (t == 0)
+                    static_cast<float *>(expand_scales)[rank[k]] = scale;
+            }
+        }
+    } else if (MODE == 3) {
+        const int lanes = tile / kChunk;  // lanes per tile: 1 .. 64
+        uint32_t m = amax_bits16(xa, xb);
+        for (int o = 1; o < lanes; o <<= 1)
+            m = max(m, (uint32_t)__shfl_xor((int)m, o));
+        const float mf = __uint_as_float(m << 16);
+        const float d = m ? 127.0f / mf : 0.0f;
+        const float scale = m ? 1.0f / d : 0.0f;
+        code = int8_codes(v, d);
+        const int nt = (H + tile - 1) / tile;
+        const bool lead = has && (t & (lanes - 1)) == 0;
+        if (has) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (rank[k] < 0)
+                    continue;
+                reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
+                                          (size_t)rank[k] * H)[t] = code;
+                if (lead)
+                    static_cast<float *>(expand_scales)[(size_t)rank[k] * nt +
+                                                        (t * kChunk) / tile] = scale;
+            }
+        }
+    } else {  // MODE == 4
+        uint32_t m = amax_bits16(xa, xb);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        int se = -127;
+        if (m) {
+            se = bf16_ilogb(m) - 8;
+            se = max(-127, min(127, se));
+        }
+        const float f = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, normal
+        code = e4m3_codes(v, f);
+        const int nb = H / 32;
+        const bool lead = has && (t & 1) == 0;
+        if (has) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (rank[k] < 0)
+                    continue;
+                reinterpret_cast<uint4 *>(static_cast<uint8_t *>(expand_x) +
+                                          (size_t)rank[k] * H)[t] = code;
+                if (lead)
+                    static_cast<uint8_t *>(expand_scales)[(size_t)rank[k] * nb + t / 2] =
+                        (uint8_t)(se + 127);
+            }
+        }
+    }
+}
+
+template <int MODE>
+static hipError_t launch_mode(int kmax, dim3 grid, dim3 block, hipStream_t stream,
+                              const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
+                              int H, int K, int E, int tile, void *expand_x, void *expand_scales,
+                              int32_t *counts, int32_t *offsets, int32_t *expand_src,
+                              int32_t *assist_dst, int32_t *dev_err)
+{
+#define MOE_DISPATCH_LAUNCH(KM)                                                                \
+    hipLaunchKernelGGL((k_dispatch<MODE, KM>), grid, block, 0, stream, x, ids, mask, Bs, H, K, \
+                       E, tile, expand_x, expand_scales, counts, offsets, expand_src,          \
+                       assist_dst, dev_err)
+    switch (kmax) {
+    case 2: MOE_DISPATCH_LAUNCH(2); break;
+    case 4: MOE_DISPATCH_LAUNCH(4); break;
+    case 8: MOE_DISPATCH_LAUNCH(8); break;
+    default: MOE_DISPATCH_LAUNCH(16); break;
+    }
+#undef MOE_DISPATCH_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
+                           int H, int K, int E, int quant_mode, int tile, void *expand_x,
+                           void *expand_scales, int32_t *counts, int32_t *offsets,
+                           int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err,
+                           hipStream_t stream)
+{
+    const int kmax = K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : 16;
+    const dim3 grid(Bs + 1), block(row_threads(H));
+    switch (quant_mode) {
+    case 0:
+        return launch_mode<0>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
+                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
+                              dev_err);
+    case 2:
+        return launch_mode<2>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
+                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
+                              dev_err);
+    case 3:
+        return launch_mode<3>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
+                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
+                              dev_err);
+    default:
+        return launch_mode<4>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
+                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
+                              dev_err);
+    }
+}
+
+}  // namespace moe

@@ -1,0 +1,31 @@
+// kernels.h -- launchers shared between the C ABI (api.hip) and the kernel
+// translation units.  Arguments are already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_update_expert(const int32_t *ids, const float *scores, const int32_t *table,
+                                const float *thr, const uint8_t *token_mask, int Bs, int K,
+                                int n_logical, int F, int n_instances, int32_t *out_ids,
+                                uint8_t *out_mask, int32_t *dev_err, hipStream_t stream);
+
+hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
+                           int H, int K, int E, int quant_mode, int tile, void *expand_x,
+                           void *expand_scales, int32_t *counts, int32_t *offsets,
+                           int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err,
+                           hipStream_t stream);
+
+hipError_t launch_combine(const uint16_t *expert_out, const int32_t *assist,
+                          const float *scales, const uint16_t *shared,
+                          const uint16_t *residual, const uint16_t *gamma, float eps, int Bs,
+                          int H, int K, int shared_mode, uint16_t *y, uint16_t *x_out,
+                          float *rstd, int32_t *dev_err, hipStream_t stream);
+
+// Threads per row block: one thread per 16 row elements, rounded up to
+// whole waves (64 .. 512 threads for H in [1024, 8192]).
+inline int row_threads(int H) { return ((H / 16 + 63) / 64) * 64; }
+
+}  // namespace moe

@@ -1,0 +1,161 @@
+"""Thin ctypes binding of libmoe_expert.so (include/moe_expert.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the path runs in the library's kernels.
+Output tensors may be passed in (nothing is allocated then) or are allocated
+with torch.empty.  There is no fallback: importing this module raises if the
+library is missing, and each call raises MoeError on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ELAUNCH = 0, 1, 2, 3
+QUANT_NONE, QUANT_STATIC, QUANT_INT8_TOKEN, QUANT_INT8_TILE, QUANT_MXFP8 = 0, 1, 2, 3, 4
+SHARED_PAGE, SHARED_ADD = 0, 1
+ERR_ID, ERR_TABLE, ERR_MASK1D, ERR_ROW = 1, 2, 4, 8
+
+EXPORTS = ("moe_update_expert", "moe_dispatch", "moe_combine_add_rmsnorm", "moe_status_string")
+
+if not os.path.exists(_build.LIB):
+    raise ImportError(f"{_build.LIB} is not built: run `python -m combine_expert_amd.build`")
+
+_lib = C.CDLL(_build.LIB)
+_P, _I = C.c_void_p, C.c_int
+_lib.moe_update_expert.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
+_lib.moe_dispatch.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
+                              _P, _P]
+_lib.moe_combine_add_rmsnorm.argtypes = [_P, _P, _P, _P, _P, _P, C.c_float, _I, _I, _I, _I,
+                                         _P, _P, _P, _P, _P]
+for _f in (_lib.moe_update_expert, _lib.moe_dispatch, _lib.moe_combine_add_rmsnorm):
+    _f.restype = C.c_int
+_lib.moe_status_string.argtypes = [_I]
+_lib.moe_status_string.restype = C.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {moe_status_string(status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def moe_status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def n_scale_entries(quant_mode: int, H: int, tile: int = 0) -> int:
+    """Scale entries per expand_x row for a quantisation mode."""
+    if quant_mode == QUANT_INT8_TOKEN:
+        return 1
+    if quant_mode == QUANT_INT8_TILE:
+        return -(-H // tile)
+    if quant_mode == QUANT_MXFP8:
+        return H // 32
+    return 0
+
+
+def moe_update_expert(expert_ids, table, n_instances: int, expert_scales=None, prune_thr=None,
+                      token_mask=None, balanced_ids=None, balanced_mask=None, dev_err=None,
+                      stream=None):
+    Bs, K = expert_ids.shape
+    n_logical, F = table.shape
+    dev = expert_ids.device
+    if balanced_ids is None:
+        balanced_ids = torch.empty((Bs, K), dtype=torch.int32, device=dev)
+    if balanced_mask is None:
+        balanced_mask = torch.empty((Bs, K), dtype=torch.uint8, device=dev)
+    rc = _lib.moe_update_expert(_ptr(expert_ids), _ptr(expert_scales), _ptr(table),
+                                _ptr(prune_thr), _ptr(token_mask), Bs, K, n_logical, F,
+                                n_instances, _ptr(balanced_ids), _ptr(balanced_mask),
+                                _ptr(dev_err), _stream(stream))
+    _check("moe_update_expert", rc)
+    return balanced_ids, balanced_mask
+
+
+def dispatch_buffers(Bs: int, H: int, K: int, E: int, quant_mode: int, tile: int = 0,
+                     device="cuda"):
+    """Allocate the dispatch outputs for a shape (capacity Bs*K rows)."""
+    N = Bs * K
+    dt = {QUANT_NONE: torch.bfloat16, QUANT_INT8_TOKEN: torch.int8,
+          QUANT_INT8_TILE: torch.int8, QUANT_MXFP8: torch.uint8}[quant_mode]
+    ns = n_scale_entries(quant_mode, H, tile)
+    sdt = torch.uint8 if quant_mode == QUANT_MXFP8 else torch.float32
+    return dict(
+        expand_x=torch.empty((N, H), dtype=dt, device=device),
+        expand_scales=torch.empty((N, ns), dtype=sdt, device=device) if ns else None,
+        expert_counts=torch.empty((E,), dtype=torch.int32, device=device),
+        expert_offsets=torch.empty((E + 1,), dtype=torch.int32, device=device),
+        expand_src=torch.empty((N,), dtype=torch.int32, device=device),
+        assist_dst=torch.empty((N,), dtype=torch.int32, device=device),
+    )
+
+
+def moe_dispatch(x, expert_ids, n_ranks: int, local_experts: int, quant_mode: int = 0,
+                 tile: int = 0, active_mask=None, out: Optional[dict] = None, dev_err=None,
+                 stream=None) -> dict:
+    Bs, H = x.shape
+    K = expert_ids.shape[1]
+    if out is None:
+        out = dispatch_buffers(Bs, H, K, n_ranks * local_experts, quant_mode, tile, x.device)
+    rc = _lib.moe_dispatch(_ptr(x), _ptr(expert_ids), _ptr(active_mask), Bs, H, K, n_ranks,
+                           local_experts, quant_mode, tile, _ptr(out["expand_x"]),
+                           _ptr(out.get("expand_scales")), _ptr(out["expert_counts"]),
+                           _ptr(out["expert_offsets"]), _ptr(out["expand_src"]),
+                           _ptr(out["assist_dst"]), _ptr(dev_err), _stream(stream))
+    _check("moe_dispatch", rc)
+    return out
+
+
+def moe_combine_add_rmsnorm(expert_out, assist_dst, expert_scales, residual_x, gamma,
+                            eps: float = 1e-6, shared_x=None, shared_mode: int = SHARED_PAGE,
+                            y=None, x_out=None, rstd=None, want_x: bool = True,
+                            want_rstd: bool = True, dev_err=None, stream=None):
+    Bs, H = residual_x.shape
+    K = expert_scales.shape[1]
+    dev = residual_x.device
+    if y is None:
+        y = torch.empty((Bs, H), dtype=torch.bfloat16, device=dev)
+    if x_out is None and want_x:
+        x_out = torch.empty((Bs, H), dtype=torch.bfloat16, device=dev)
+    if rstd is None and want_rstd:
+        rstd = torch.empty((Bs,), dtype=torch.float32, device=dev)
+    rc = _lib.moe_combine_add_rmsnorm(_ptr(expert_out), _ptr(assist_dst), _ptr(expert_scales),
+                                      _ptr(shared_x), _ptr(residual_x), _ptr(gamma), eps, Bs, H,
+                                      K, shared_mode, _ptr(y), _ptr(x_out), _ptr(rstd),
+                                      _ptr(dev_err), _stream(stream))
+    _check("moe_combine_add_rmsnorm", rc)
+    return y, x_out, rstd
+
+
+def raw():
+    """The ctypes library handle (for tests of the C ABI itself)."""
+    return _lib

@@ -1,0 +1,196 @@
+/*
+ * moe_expert.h -- C ABI of the MI355X (gfx950) MoE expert-mapping, dispatch
+ * and combine library (libmoe_expert.so).
+ *
+ * One device's share of a Mixture-of-Experts layer's token dispatch and
+ * combine, as described by the Ascend CANN operator pages
+ * "aclnnMoeUpdateExpert", "aclnnMoeDistributeDispatchV2" and
+ * "aclnnMoeDistributeCombineAddRmsNorm".  The three calls run in that fixed
+ * order for a layer (update-expert page, calling-sequence constraint).
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is DEVICE memory owned by the caller.  The library
+ *     allocates, frees, synchronises and retains nothing; each call only
+ *     validates its scalar arguments on the host and enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the legacy default stream).  Calls are
+ *     asynchronous, safe to capture in a HIP graph, reentrant across streams
+ *     and deterministic (bitwise-repeatable), as the pages require
+ *     (确定性计算 / "deterministic computation" notes).
+ *   - All arrays are dense row-major.  bf16 data is IEEE bfloat16 bit
+ *     patterns; fp8 data is OCP FP8 E4M3 bytes; int8 is two's complement.
+ *   - Row pointers (x, expand_x, expert_out, shared_x, residual_x, y, x_out,
+ *     gamma) must be 16-byte aligned.
+ *   - Host-checkable errors return a non-zero moe_status BEFORE anything is
+ *     enqueued (the role of the pages' first-phase parameter check).
+ *     Data-dependent errors that cannot be seen without reading device
+ *     memory set bits in the optional device word *dev_err (atomic OR,
+ *     sticky until the caller clears it); the offending entry is then
+ *     treated as pruned.  MOE_ELAUNCH reports a HIP launch failure.
+ *
+ * Shape limits (combine page 约束说明 item 4; update-expert page shape
+ * restrictions): 0 < Bs <= 512, 0 < K <= 16, 1024 <= H <= 8192, at most
+ * 1024 expert instances in total.  This library also requires H % 32 == 0
+ * (whole 16-byte row chunks and whole 32-element mxfp8 blocks).
+ */
+#ifndef MOE_EXPERT_H
+#define MOE_EXPERT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,   /* a scalar out of range, a NULL required pointer, misalignment */
+    MOE_ENOTSUP = 2,  /* a valid option this library does not implement */
+    MOE_ELAUNCH = 3   /* the HIP runtime rejected a kernel launch */
+} moe_status;
+
+/* Dispatch quantisation modes (dispatch page 计算公式 cases 1, 3, 4, 5). */
+typedef enum {
+    MOE_Q_NONE = 0,        /* expand_x rows are bit copies of x (bf16)                  */
+    MOE_Q_STATIC = 1,      /* static quantisation: not implemented -> MOE_ENOTSUP       */
+    MOE_Q_INT8_TOKEN = 2,  /* per-token dynamic int8                                    */
+    MOE_Q_INT8_TILE = 3,   /* per-tile dynamic int8 ("pertile" / "pergroup")            */
+    MOE_Q_MXFP8 = 4        /* mxfp8: E4M3 codes, one E8M0 exponent per 32 elements      */
+} moe_quant;
+
+/* Weight of the shared-expert output in the combine (combine page 计算公式). */
+typedef enum {
+    MOE_SHARED_PAGE = 0,   /* sum over the token's dispatched k of expertScales[i,k]     */
+    MOE_SHARED_ADD = 1     /* 1                                                         */
+} moe_shared_mode;
+
+/* dev_err bits */
+#define MOE_ERR_ID 1        /* an active expert / instance id outside its range          */
+#define MOE_ERR_TABLE 2     /* mapping-table replica count not in [1, F-1], or an
+                               instance id in the table outside [0, n_instances)         */
+#define MOE_ERR_MASK1D 4    /* a 1-D token mask that is not all-true-then-all-false      */
+#define MOE_ERR_ROW 8       /* combine: an assist_dst entry >= Bs*K                      */
+
+/*
+ * moe_update_expert -- load balancing and expert pruning
+ * ("aclnnMoeUpdateExpert": map each token's top-K logical expert ids to
+ * deployed instances; prune entries by a threshold broadcast over the batch).
+ *
+ * For entry f = i*K + k with logical id e = expert_ids[f]:
+ *   n                = table[e*F + 0]                (replica count, 1 <= n <= F-1)
+ *   balanced_ids[f]  = table[e*F + 1 + (i mod n)]    (global instance id,
+ *                                                     rank * local_experts + slot)
+ *   balanced_mask[f] = token_mask[i] (1 if token_mask is NULL)
+ *                      AND NOT (expert_scales[f] < prune_thr[k])
+ *                      (the threshold test is skipped if either pointer is NULL;
+ *                       a NaN score is kept)
+ * An entry whose lookup fails gets id -1 and mask 0, and raises MOE_ERR_ID /
+ * MOE_ERR_TABLE only if it would otherwise have been kept.  A token_mask that
+ * is not all-true-then-all-false (dispatch page: {true,false,true} is
+ * illegal) raises MOE_ERR_MASK1D and is still applied as given.
+ *
+ *   expert_ids    int32 [Bs, K]            logical ids in [0, n_logical)
+ *   expert_scales f32   [Bs, K] or NULL     routing scores
+ *   table         int32 [n_logical, F]      col 0 = replica count, cols 1.. = instance ids
+ *   prune_thr     f32   [K] or NULL         threshold for column k
+ *   token_mask    u8    [Bs] or NULL        1 = token takes part
+ *   balanced_ids  int32 [Bs, K]   (out)
+ *   balanced_mask u8    [Bs, K]   (out)     1 = dispatch, 0 = pruned
+ *   dev_err       int32 [1] or NULL
+ * Limits: 0 < Bs <= 512, 0 < K <= 16, K <= n_logical <= 1024,
+ *         2 <= F <= n_logical + 1, 0 < n_instances <= 1024.
+ */
+int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
+                      const int32_t *table, const float *prune_thr, const uint8_t *token_mask,
+                      int Bs, int K, int n_logical, int F, int n_instances,
+                      int32_t *balanced_ids, uint8_t *balanced_mask, int32_t *dev_err,
+                      void *stream);
+
+/*
+ * moe_dispatch -- quantise tokens and scatter them expert-major
+ * ("aclnnMoeDistributeDispatchV2" 计算公式: expandX = AllToAllV(quantOut);
+ * here the single device's share: the rows this device would send, laid out
+ * [rank][local expert][token] as the all-to-all delivers them).
+ *
+ * E = n_ranks * local_experts instances; N = Bs*K entries f = i*K + k.
+ * Entry f is active if active_mask is NULL or active_mask[f] != 0, and its
+ * id is in [0, E) (else MOE_ERR_ID and it is dropped).
+ *   expert_counts[e]  = number of active entries with id e
+ *   expert_offsets    = exclusive prefix sum of counts; offsets[E] = rows written
+ *   assist_dst[f]     = row of entry f: offsets[id] + number of active g < f
+ *                       with the same id (stable, ascending f); -1 if inactive
+ *   expand_src[r]     = entry placed in row r; -1 for r >= offsets[E]
+ *   expand_x[r]       = token i = f / K, coded once per token:
+ *     MOE_Q_NONE       bf16 [N, H] bit copy of x[i]
+ *     MOE_Q_INT8_TOKEN int8 [N, H]: m = max|x[i]|, d = 127/m (fp32, IEEE),
+ *                      code = clamp(round_half_even(x*d), -127, 127);
+ *                      expand_scales f32 [N] = 1/d  (m == 0: codes 0, scale 0)
+ *     MOE_Q_INT8_TILE  the same per tile of `tile` elements along H (the last
+ *                      tile may be partial); expand_scales f32 [N, ceil(H/tile)];
+ *                      tile must be a power of two in [16, 1024]
+ *     MOE_Q_MXFP8      E4M3 [N, H]: per block of 32, se = floor(log2 max|x|) - 8
+ *                      clamped to [-127, 127] (-127 for an all-zero block),
+ *                      code = E4M3(x / 2^se) rounded to nearest even and
+ *                      saturated at +-448; expand_scales u8 [N, H/32] = se + 127
+ *                      (E8M0 code of the dequantisation multiplier 2^se)
+ * Rows at or past offsets[E] of expand_x / expand_scales are not written.
+ *
+ *   x              bf16 [Bs, H]
+ *   expert_ids     int32 [Bs, K]     instance ids (e.g. balanced_ids)
+ *   active_mask    u8 [Bs, K] or NULL (e.g. balanced_mask)
+ *   expand_x       [N, H] elements of the mode's type (out)
+ *   expand_scales  see above; NULL for MOE_Q_NONE (out)
+ *   expert_counts  int32 [E]  (out)      expert_offsets int32 [E+1] (out)
+ *   expand_src     int32 [N]  (out)      assist_dst     int32 [N]   (out)
+ *   dev_err        int32 [1] or NULL
+ * Limits: 0 < Bs <= 512, 0 < K <= 16, K <= E <= 1024, H in [1024, 8192] with
+ *         H % 32 == 0, n_ranks >= 1, local_experts >= 1.
+ */
+int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask,
+                 int Bs, int H, int K, int n_ranks, int local_experts, int quant_mode,
+                 int tile, void *expand_x, void *expand_scales, int32_t *expert_counts,
+                 int32_t *expert_offsets, int32_t *expand_src, int32_t *assist_dst,
+                 int32_t *dev_err, void *stream);
+
+/*
+ * moe_combine_add_rmsnorm -- weighted gather of expert outputs, shared
+ * expert and residual add, RMSNorm ("aclnnMoeDistributeCombineAddRmsNorm"
+ * 计算公式: combineOut = Sum(expertScales*ataOut + expertScales*sharedExpertX),
+ * x = combineOut + residualX, y = x / RMS(x) * gamma,
+ * RMS(x) = sqrt(mean(x^2) + normEps)).
+ *
+ * For token i, with fp32 accumulation:
+ *   acc  = sum over k with r = assist_dst[i*K+k] >= 0 of
+ *          expert_scales[i*K+k] * expert_out[r]
+ *   acc += w * shared_x[i]   (w = sum of those scales for MOE_SHARED_PAGE,
+ *                             1 for MOE_SHARED_ADD; skipped if shared_x is NULL)
+ *   x    = acc + residual_x[i];  x_out[i] = bf16(x)
+ *   rstd = 1 / sqrt(mean(x^2) + eps);  y[i] = bf16(x * rstd * gamma)
+ * The RMS is taken over the fp32 x before rounding.
+ *
+ *   expert_out   bf16 [Bs*K, H]   rows in dispatch order (expert FFN output)
+ *   assist_dst   int32 [Bs, K]    from moe_dispatch (-1 = not dispatched)
+ *   expert_scales f32 [Bs, K]
+ *   shared_x     bf16 [Bs, H] or NULL
+ *   residual_x   bf16 [Bs, H]
+ *   gamma        bf16 [H]
+ *   y            bf16 [Bs, H] (out)
+ *   x_out        bf16 [Bs, H] or NULL (out)
+ *   rstd         f32 [Bs] or NULL (out)
+ *   dev_err      int32 [1] or NULL: MOE_ERR_ROW for an entry >= Bs*K (skipped)
+ * Limits: 0 < Bs <= 512, 0 < K <= 16, H in [1024, 8192] with H % 32 == 0,
+ *         eps >= 0 and finite, shared_mode in {0, 1}.
+ */
+int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
+                            const float *expert_scales, const void *shared_x,
+                            const void *residual_x, const void *gamma, float eps, int Bs,
+                            int H, int K, int shared_mode, void *y, void *x_out, float *rstd,
+                            int32_t *dev_err, void *stream);
+
+/* A static, human-readable name for a moe_status value. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EXPERT_H */

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Routing, counts, offsets, permutation, rows, int8 / fp8
+codes and scales are compared bit for bit; the combine's bf16 outputs within
+abs 2e-2 + rel 1e-2 (fp32 accumulation vs the oracle's fp64).
+
+Cases: the five workloads at full size (c1 .. c4, c4b and the first c5
+layer), small ragged shapes that span several row chunks, tiles and a
+partial last tile, the shape limits (H = 1024 / 8192, K = 1 / 16, 1024
+instances), everything pruned, a prefix token mask, bf16 extremes
+(subnormals, the largest finite values) and determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_expert_amd import workloads as W
+from tests.gpu_common import (M, bits, check_combine, check_dispatch, cuda, gpu_combine,
+                              gpu_dispatch, gpu_update, np_, oracle_combine, oracle_dispatch,
+                              oracle_update, say)
+
+pytestmark = pytest.mark.gpu
+
+
+def full_chain(wl):
+    """update -> dispatch -> combine on the GPU and in the oracle; each GPU
+    stage is compared with the oracle stage fed the oracle's own inputs."""
+    say(f"[parity] {wl.name} Bs={wl.Bs} H={wl.H} K={wl.K} E={wl.E} q={wl.quant_mode}")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gids, gmask = gpu_update(wl, dev_err=err)
+    oids, omask, oerr = oracle_update(wl)
+    np.testing.assert_array_equal(np_(gids), oids)
+    np.testing.assert_array_equal(np_(gmask), omask)
+    gd = gpu_dispatch(wl, gids, gmask, dev_err=err)
+    od = oracle_dispatch(wl, oids, omask)
+    total = check_dispatch(wl, gd, od)
+    assert int(err.item()) == (oerr | od["err"])
+    eout = wl.expert_out
+    if eout is None:  # identity + bias expert on the dispatched rows
+        eout = W.identity_bias_expert(gd["expand_x"].cpu(), gd["expert_offsets"].cpu(),
+                                      wl.expert_bias)
+    g = gpu_combine(wl, gd["assist_dst"], eout)
+    o = oracle_combine(wl, od["assist"], eout)
+    check_combine(g, o)
+    return total
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c4b"])
+def test_workload_full_size(name):
+    wl = W.make(name)
+    total = full_chain(wl)
+    assert total > 0
+
+
+def test_c5_first_layer():
+    wl = W.make_c5_layers(n_layers=1)[0]
+    full_chain(wl)
+
+
+SMALL = [
+    # seed, Bs, H, K, ranks, local, mode, tile, prune, shared, token-mask prefix, replicas
+    (101, 37, 1056, 5, 3, 4, 0, 0, True, True, None, False),
+    (102, 37, 1056, 5, 3, 4, 2, 0, True, True, None, False),
+    (103, 37, 1056, 5, 3, 4, 3, 128, True, True, None, False),
+    (104, 37, 1056, 5, 3, 4, 4, 0, True, True, None, False),
+    (105, 19, 2080, 3, 2, 3, 3, 16, False, False, None, False),
+    (106, 19, 2080, 3, 2, 3, 3, 32, False, True, None, False),
+    (107, 19, 2048, 3, 2, 3, 3, 1024, False, True, None, False),
+    (108, 64, 4128, 7, 5, 5, 3, 64, True, True, 40, True),
+    (109, 3, 1024, 1, 1, 1, 2, 0, False, True, None, False),
+    (110, 512, 8192, 16, 64, 16, 4, 0, True, True, None, True),
+    (111, 512, 1024, 16, 1, 16, 2, 0, False, True, 300, False),
+    (112, 1, 8192, 16, 128, 8, 3, 256, True, False, None, False),
+    (113, 200, 1024, 2, 8, 128, 0, 0, False, True, None, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_small_and_edge_shapes(case):
+    seed, Bs, H, K, R, L, mode, tile, prune, shared, prefix, rep = case
+    wl = W.make_small(seed, Bs, H, K, R, L, mode, tile, prune=prune, shared=shared,
+                      token_mask_prefix=prefix, replicas=rep)
+    full_chain(wl)
+
+
+@pytest.mark.parametrize("mode", [0, 2, 3, 4])
+def test_everything_pruned(mode):
+    wl = W.make_small(7, 16, 1024, 4, 2, 4, mode, 128)
+    say(f"[parity] all pruned mode={mode}")
+    ids = cuda(wl.logical_ids)
+    mask = torch.zeros((wl.Bs, wl.K), dtype=torch.uint8, device="cuda")
+    gd = gpu_dispatch(wl, ids, mask)
+    od = oracle_dispatch(wl, wl.logical_ids.numpy(), np.zeros((wl.Bs, wl.K), np.uint8))
+    assert check_dispatch(wl, gd, od) == 0
+    g = gpu_combine(wl, gd["assist_dst"], wl.expert_out)
+    o = oracle_combine(wl, od["assist"], wl.expert_out)
+    check_combine(g, o)
+
+
+def extreme_x(Bs, H, seed):
+    """bf16 rows mixing every finite bf16 magnitude class: subnormals, tiny
+    and huge normals, signed zeros and blocks of all zeros."""
+    rng = np.random.default_rng(seed)
+    pats = np.arange(65536, dtype=np.uint32)
+    fin = pats[((pats >> 7) & 0xFF) != 0xFF]  # drop inf / NaN
+    b = rng.choice(fin, size=(Bs, H)).astype(np.uint16)
+    b[:, 64:96] = 0x8000  # an all-(-0) block
+    b[:, 96:128] = 0      # an all-zero block
+    sub = rng.integers(1, 128, size=(Bs, 32)).astype(np.uint16)
+    b[:, 128:160] = sub | (rng.integers(0, 2, size=(Bs, 32)) << 15).astype(np.uint16)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode,tile", [(2, 0), (3, 32), (3, 128), (4, 0)])
+def test_quantisers_on_bf16_extremes(mode, tile):
+    wl = W.make_small(9, 32, 2048, 2, 2, 2, mode, tile or 128)
+    wl.x = extreme_x(wl.Bs, wl.H, 99 + mode + tile)
+    say(f"[parity] extremes mode={mode} tile={tile}")
+    ids = wl.logical_ids
+    gd = gpu_dispatch(wl, cuda(ids), None)
+    od = oracle_dispatch(wl, ids.numpy(), None)
+    check_dispatch(wl, gd, od)
+
+
+def test_mxfp8_every_bf16_value():
+    # every finite bf16 pattern appears once, in blocks whose maxima vary
+    pats = np.arange(65536, dtype=np.uint32)
+    fin = pats[((pats >> 7) & 0xFF) != 0xFF].astype(np.uint16)
+    H = 8192
+    Bs = -(-fin.size // H)
+    b = np.zeros(Bs * H, np.uint16)
+    b[:fin.size] = np.random.default_rng(1).permutation(fin)
+    wl = W.make_small(11, Bs, H, 1, 1, 1, 4)
+    wl.x = torch.from_numpy(b.reshape(Bs, H).view(np.int16)).view(torch.bfloat16)
+    say(f"[parity] mxfp8 all bf16 values Bs={Bs}")
+    gd = gpu_dispatch(wl, cuda(wl.logical_ids), None)
+    od = oracle_dispatch(wl, wl.logical_ids.numpy(), None)
+    check_dispatch(wl, gd, od)
+
+
+def test_shared_modes_differ_with_unnormalised_scales():
+    wl = W.make_small(12, 64, 2048, 4, 2, 4, 0)
+    wl.scales = wl.scales * 3.0
+    ids = cuda(wl.logical_ids)
+    gd = gpu_dispatch(wl, ids, None)
+    od = oracle_dispatch(wl, wl.logical_ids.numpy(), None)
+    check_dispatch(wl, gd, od)
+    for mode in (0, 1):
+        say(f"[parity] shared mode {mode}")
+        g = gpu_combine(wl, gd["assist_dst"], wl.expert_out, shared_mode=mode)
+        o = oracle_combine(wl, od["assist"], wl.expert_out, shared_mode=mode)
+        check_combine(g, o)
+
+
+def test_determinism_bitwise():
+    wl = W.make("c3")
+    say("[parity] determinism c3")
+    ids = cuda(wl.logical_ids)
+    a = gpu_dispatch(wl, ids, None)
+    b = gpu_dispatch(wl, ids, None)
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), k
+    g1 = gpu_combine(wl, a["assist_dst"], wl.expert_out)
+    g2 = gpu_combine(wl, a["assist_dst"], wl.expert_out)
+    for u, v in zip(g1, g2):
+        assert torch.equal(u.view(torch.uint8), v.view(torch.uint8))
+
+
+def test_device_error_bits():
+    m = M()
+    say("[parity] device error bits")
+    wl = W.make_small(13, 8, 1024, 2, 2, 2, 0)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids = wl.logical_ids.clone()
+    ids[3, 1] = 99  # out of range, active
+    gd = gpu_dispatch(wl, cuda(ids), None, dev_err=err)
+    od = oracle_dispatch(wl, ids.numpy(), None)
+    check_dispatch(wl, gd, od)
+    assert int(err.item()) == 1 == od["err"]
+    # combine: an assist entry beyond Bs*K is skipped and flagged
+    err.zero_()
+    assist = od["assist"].copy()
+    assist[5] = wl.Bs * wl.K + 3
+    y, xo, rstd = m.moe_combine_add_rmsnorm(
+        cuda(wl.expert_out), cuda(torch.from_numpy(assist)).reshape(wl.Bs, wl.K),
+        cuda(wl.scales), cuda(wl.residual), cuda(wl.gamma), wl.eps, shared_x=cuda(wl.shared),
+        dev_err=err)
+    assert int(err.item()) == 8
+    assist[5] = -1
+    o = oracle_combine(wl, assist, wl.expert_out)
+    check_combine((y, xo, rstd), o)
+    # update-expert: illegal 1-D mask and a bad table entry
+    err.zero_()
+    table = W.identity_table(wl.E)
+    table[1, 0] = 0
+    tmask = torch.tensor([1, 0, 1, 1, 0, 0, 0, 0], dtype=torch.uint8)
+    gi, gm = m.moe_update_expert(cuda(wl.logical_ids), cuda(torch.from_numpy(table)), wl.E,
+                                 token_mask=cuda(tmask), dev_err=err)
+    oi, om, oe = oracle.update_expert(wl.logical_ids.numpy(), None, table, None, tmask.numpy(),
+                                      wl.E)
+    np.testing.assert_array_equal(np_(gi), oi)
+    np.testing.assert_array_equal(np_(gm), om)
+    assert int(err.item()) == oe and oe & 4
+
+
+def test_identity_expert_round_trip_closed_form():
+    # mode-0 dispatch, identity experts, residual 0, no shared expert:
+    # x_out = bf16(sum_k s_k * x_i) (spec invariant), on the GPU path only
+    wl = W.make_small(14, 128, 4096, 8, 4, 8, 0, shared=False)
+    say("[parity] identity round trip")
+    gd = gpu_dispatch(wl, cuda(wl.logical_ids), None)
+    zero = torch.zeros_like(wl.residual)
+    y, xo, _ = gpu_combine(wl, gd["assist_dst"], gd["expand_x"], residual=zero)
+    expect = (wl.scales.double().sum(1, keepdim=True) * wl.x.double())
+    got = xo.double().cpu()
+    assert torch.all((got - expect).abs() <= 2e-2 + 1e-2 * expect.abs())
