@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark one MoE layer step on one MI355X: expert mapping, dispatch
+(histogram, scan, stable scatter, mxfp8 quantisation) and combine + shared
+expert + residual + RMSNorm, on the DeepSeek-V3-shaped workload
+(Bs=512 tokens, H=7168, 256 expert instances = 32 ranks x 8, top-8,
+Zipf(1.2) routing, one shared expert).
+
+    python bench.py [--steps 500] [--warmup 50] [--sets 5] [--cpu-seconds 10]
+
+Prints one JSON line.  `value` is whole-step throughput in GB/s of
+algorithmic bytes (each input read once, each output written once) with all
+inputs resident in HBM; input and output buffers rotate over --sets copies
+(about 125 MB each) so that the 256 MB Infinity Cache cannot serve a step from
+the previous use of its buffers.  The combine kernel dominates the step; its
+per-launch duration is taken with HIP events on the stream it runs on,
+bracketing a run of back-to-back launches over the rotating
+buffer sets (events between the kernels of a step would add their own
+packets to the step).  The CPU oracle runs the same step on the host cores as
+a reference point.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine HBM GB/s (% of peak) and tokens/s, Bs=512 H=7168 K=8"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--sets", type=int, default=5, help="rotating buffer sets")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="time budget of the CPU oracle baseline (0 = skip)")
+    p.add_argument("--no-check", action="store_true", help="skip the parity check of step 0")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="instead of the step, time a plain device copy of this many MB "
+                        "(the reference kernel for counter scaling and achievable bandwidth)")
+    return p.parse_args()
+
+
+def copy_calibration(mb, steps, warmup):
+    """Plain bf16 device-to-device copy of a known size: read mb MB, write mb MB."""
+    import torch
+    n = mb * (1 << 20) // 2
+    nset = max(2, -(-1024 // (2 * mb)))  # rotate so the set pair exceeds the Infinity Cache
+    src = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(nset)]
+    dst = [torch.empty_like(s) for s in src]
+    for k in range(warmup):
+        dst[k % nset].copy_(src[k % nset])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for k in range(steps):
+        ev[2 * k].record()
+        dst[k % nset].copy_(src[k % nset])
+        ev[2 * k + 1].record()
+    torch.cuda.synchronize()
+    t = statistics.mean(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(steps)) * 1e-3
+    nbytes = 2 * n * 2
+    print(json.dumps({"copy_mb": mb, "bytes_per_launch": nbytes, "read_bytes": n * 2,
+                      "write_bytes": n * 2, "avg_us": round(t * 1e6, 3),
+                      "GBps": round(nbytes / t / 1e9, 1)}), flush=True)
+
+
+# ----------------------------------------------------------------- bytes
+
+def algorithmic_bytes(Bs, H, K, E, rows, n_logical, F, quant_mode, n_scale, shared=True):
+    """Bytes each kernel must move: every input read once, every output written once."""
+    N = Bs * K
+    upd = N * 4 + n_logical * F * 4 + N * 4 + N  # ids, table, balanced ids, mask
+    code_b = 2 if quant_mode == 0 else 1
+    scale_b = {0: 0, 2: 4, 3: 4, 4: 1}[quant_mode] * n_scale
+    dsp = (Bs * H * 2 + N * 4 + N                 # x, ids, mask
+           + rows * H * code_b + rows * scale_b   # coded rows and their scales
+           + E * 4 + (E + 1) * 4 + 2 * N * 4)     # counts, offsets, src, assist
+    cmb = (rows * H * 2 + 2 * N * 4               # expert rows, assist, scales
+           + (Bs * H * 2 if shared else 0) + Bs * H * 2 + H * 2   # shared, residual, gamma
+           + 2 * Bs * H * 2 + Bs * 4)             # y, x_out, rstd
+    return dict(update_expert=upd, dispatch=dsp, combine=cmb)
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "combine_expert_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_file, digest_names):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they
+    were taken on the current kernel source."""
+    path = os.path.join(PROFILES, kernel_file)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_digest") != source_digest(*digest_names):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------- GPU side
+
+def make_set(wl, torch, moe):
+    dev = torch.device("cuda")
+    c = lambda t: t.contiguous().to(dev)
+    s = dict(x=c(wl.x), ids=c(wl.logical_ids), scales=c(wl.scales), table=c(wl.table),
+             eout=c(wl.expert_out), shared=c(wl.shared), residual=c(wl.residual),
+             gamma=c(wl.gamma))
+    s["bal_ids"] = torch.empty((wl.Bs, wl.K), dtype=torch.int32, device=dev)
+    s["bal_mask"] = torch.empty((wl.Bs, wl.K), dtype=torch.uint8, device=dev)
+    s["d"] = moe.dispatch_buffers(wl.Bs, wl.H, wl.K, wl.E, wl.quant_mode, wl.tile, dev)
+    s["y"] = torch.empty((wl.Bs, wl.H), dtype=torch.bfloat16, device=dev)
+    s["x_out"] = torch.empty((wl.Bs, wl.H), dtype=torch.bfloat16, device=dev)
+    s["rstd"] = torch.empty((wl.Bs,), dtype=torch.float32, device=dev)
+    return s
+
+
+def step_args(wl, s, stream):
+    """Pre-marshalled C-ABI argument tuples for one step on buffer set s."""
+    d = s["d"]
+    p = lambda t: None if t is None else t.data_ptr()
+    n_logical, F = wl.table.shape
+    upd = (p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.K, n_logical, F, wl.E,
+           p(s["bal_ids"]), p(s["bal_mask"]), None, stream)
+    dsp = (p(s["x"]), p(s["bal_ids"]), p(s["bal_mask"]), wl.Bs, wl.H, wl.K, wl.n_ranks,
+           wl.local_experts, wl.quant_mode, wl.tile, p(d["expand_x"]), p(d["expand_scales"]),
+           p(d["expert_counts"]), p(d["expert_offsets"]), p(d["expand_src"]),
+           p(d["assist_dst"]), None, stream)
+    cmb = (p(s["eout"]), p(d["assist_dst"]), p(s["scales"]), p(s["shared"]), p(s["residual"]),
+           p(s["gamma"]), wl.eps, wl.Bs, wl.H, wl.K, wl.shared_mode, p(s["y"]), p(s["x_out"]),
+           p(s["rstd"]), None, stream)
+    return upd, dsp, cmb
+
+
+def check_parity(wl, s, oracle, np):
+    """Step-0 outputs against the oracle: routing/codes exact, y within tolerance."""
+    oi, om, _ = oracle.update_expert(wl.logical_ids.numpy(), None, wl.table.numpy(), None, None,
+                                     wl.E)
+    od = oracle.dispatch(oracle.bf16_bits(wl.x), oi, om, wl.n_ranks, wl.local_experts,
+                         wl.quant_mode, wl.tile)
+    d = s["d"]
+    total = int(od["offsets"][-1])
+    ok = (np.array_equal(d["assist_dst"].cpu().numpy(), od["assist"])
+          and np.array_equal(d["expert_offsets"].cpu().numpy(), od["offsets"])
+          and np.array_equal(d["expand_x"].view(__import__("torch").uint8).cpu().numpy()[:total],
+                             od["expand_x"].view(np.uint8)[:total])
+          and np.array_equal(d["expand_scales"].cpu().numpy()[:total], od["scales"][:total]))
+    oy, _, _ = oracle.combine(oracle.bf16_bits(wl.expert_out), od["assist"], wl.scales.numpy(),
+                              oracle.bf16_bits(wl.shared), oracle.bf16_bits(wl.residual),
+                              oracle.bf16_bits(wl.gamma), wl.eps, wl.shared_mode)
+    ref = (oy.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got = s["y"].float().cpu().numpy()
+    ok = ok and bool(np.all(np.abs(got - ref) <= 2e-2 + 1e-2 * np.abs(ref)))
+    return ok
+
+
+def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
+    """The oracle as it stands: single-threaded C, whole step on the same inputs."""
+    ids = wl.logical_ids.numpy()
+    table = wl.table.numpy()
+    xb = oracle.bf16_bits(wl.x)
+    eob = oracle.bf16_bits(wl.expert_out)
+    shb, rsb, gmb = (oracle.bf16_bits(wl.shared), oracle.bf16_bits(wl.residual),
+                     oracle.bf16_bits(wl.gamma))
+    sc = wl.scales.numpy()
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        oi, om, _ = oracle.update_expert(ids, None, table, None, None, wl.E)
+        od = oracle.dispatch(xb, oi, om, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile)
+        oracle.combine(eob, od["assist"], sc, shb, rsb, gmb, wl.eps, wl.shared_mode)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end or len(times) >= 50:
+            break
+    t = statistics.median(times)
+    return {"value": round(step_bytes / t / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full step (update + dispatch + combine) on all {wl.Bs} tokens of the "
+                      f"workload, {len(times)} repetitions, median {t * 1e3:.1f} ms; "
+                      f"{wl.Bs / t:.0f} tokens/s",
+            "tokens_per_s": round(wl.Bs / t, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU share of the MoE layer; runs on more than one "
+              "GPU are not part of this build (see the sharding notes in DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_mb:
+        copy_calibration(args.copy_mb, args.steps, args.warmup)
+        return
+
+    import numpy as np
+    import torch
+
+    from combine_expert_amd import build as hip_build
+    if hip_build.stale():
+        hip_build.build()
+    from combine_expert_amd import moe
+    from combine_expert_amd import workloads as W
+
+    wl = W.make_c3()
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    lib = moe.raw()
+    f_upd, f_dsp, f_cmb = lib.moe_update_expert, lib.moe_dispatch, lib.moe_combine_add_rmsnorm
+
+    sets = [make_set(wl, torch, moe) for _ in range(args.sets)]
+    argv = [step_args(wl, s, sp) for s in sets]
+    torch.cuda.synchronize()
+
+    def run_steps(n):
+        for k in range(n):
+            a_u, a_d, a_c = argv[k % len(argv)]
+            if f_upd(*a_u) | f_dsp(*a_d) | f_cmb(*a_c):
+                raise RuntimeError("a library call returned a non-zero status")
+
+    def kernel_us(which, n):
+        """Average launch duration of one kernel: HIP events on the launch stream
+        bracket n back-to-back launches that rotate over the buffer sets."""
+        f = (f_upd, f_dsp, f_cmb)[which]
+        for k in range(len(argv)):
+            f(*argv[k][which])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(n):
+            f(*argv[k % len(argv)][which])
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    ok = True
+    if not args.no_check:
+        import oracle
+        ok = check_parity(wl, sets[0], oracle, np)
+
+    # timed region: exactly K steps, synchronised on both sides
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(K)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-kernel launch durations (the dominant kernel's feeds the roofline)
+    n_k = max(K, 100)
+    us_upd, us_dsp, us_cmb = (kernel_us(j, n_k) for j in range(3))
+    rows = int(sets[0]["d"]["expert_offsets"][-1].item())
+    nb = algorithmic_bytes(wl.Bs, wl.H, wl.K, wl.E, rows, wl.table.shape[0], wl.table.shape[1],
+                           wl.quant_mode, moe.n_scale_entries(wl.quant_mode, wl.H, wl.tile),
+                           shared=True)
+    step_bytes = sum(nb.values())
+    t_step = wall / K
+    gbs = step_bytes / t_step / 1e9
+    a_cmb = nb["combine"] / (us_cmb * 1e-6) / 1e9
+    a_dsp = nb["dispatch"] / (us_dsp * 1e-6) / 1e9
+    a_upd = nb["update_expert"] / (us_upd * 1e-6) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "DeepSeek-V3-shaped MoE layer: Bs=512, H=7168, 256 instances "
+                               "(32 ranks x 8), K=8, Zipf(1.2) routing, mxfp8 dispatch, "
+                               "1 shared expert, combine + residual + RMSNorm (bf16 in/out)",
+                   "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E, "quant": "mxfp8",
+                   "rows_dispatched": rows, "buffer_sets": args.sets},
+        "tokens_per_s": round(wl.Bs / t_step, 1),
+        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "kernel": "k_combine", "bound": "hbm", "achieved": round(a_cmb, 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a_cmb / HBM_PEAK_GBS, 4),
+            "traffic": counter_traffic("combine_c3_traffic.json", ("combine.hip", "device.h")),
+            "algorithmic_bytes_per_launch": nb["combine"],
+            "avg_launch_us": round(us_cmb, 3),
+        },
+        "kernels": {
+            "update_expert": {"avg_us": round(us_upd, 3), "bytes": nb["update_expert"],
+                              "GBps": round(a_upd, 1)},
+            "dispatch": {"avg_us": round(us_dsp, 3), "bytes": nb["dispatch"],
+                         "GBps": round(a_dsp, 1), "frac": round(a_dsp / HBM_PEAK_GBS, 4),
+                         "traffic": counter_traffic("dispatch_c3_traffic.json",
+                                                    ("dispatch.hip", "device.h"))},
+            "combine": {"avg_us": round(us_cmb, 3), "bytes": nb["combine"],
+                        "GBps": round(a_cmb, 1), "frac": round(a_cmb / HBM_PEAK_GBS, 4)},
+        },
+        "step_bytes": step_bytes,
+        "parity_step0": "ok" if ok else "MISMATCH",
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        line["cpu_baseline"] = cpu_baseline(wl, oracle, np, args.cpu_seconds, step_bytes)
+    print(json.dumps(line), flush=True)
+    if not ok:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()
