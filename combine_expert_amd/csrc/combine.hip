@@ -10,9 +10,10 @@
 // written once.  The kernel is bound by HBM bandwidth: per token it moves
 // (n_dispatched + 2 or 3) rows in and 2 rows out.
 //
-// The token's dispatched entries (assist_dst >= 0) are compacted by wave 0
-// with a ballot, in k order, so row loads are issued back to back, CH rows
-// at a time, with no loads for pruned entries.
+// Every wave reads the token's K (row, weight) pairs itself, one per lane,
+// and broadcasts them with readlane, so the only block barrier is the one of
+// the sum of squares.  Row loads are issued back to back, CH rows at a time,
+// with no loads for entries that were not dispatched.
 #include "device.h"
 #include "kernels.h"
 
@@ -26,10 +27,6 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
     int Bs, int H, int K, int shared_mode, uint16_t *__restrict__ y,
     uint16_t *__restrict__ x_out, float *__restrict__ rstd_out, int32_t *__restrict__ dev_err)
 {
-    __shared__ int s_row[16];
-    __shared__ float s_w[16];
-    __shared__ int s_n;
-    __shared__ float s_ws;
     __shared__ float s_part[kMaxWaves];
 
     const int i = blockIdx.x;
@@ -38,74 +35,61 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
     const bool has = t * kChunk < H;
     const size_t rowoff = (size_t)i * H;
 
-    // residual, shared and gamma do not depend on the routing: start them first
-    uint4 ra = make_uint4(0, 0, 0, 0), rb = ra, sa = ra, sb = ra, ga = ra, gb = ra;
-    if (has) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(residual + rowoff) + 2 * t;
-        ra = p[0];
-        rb = p[1];
-        const uint4 *q = reinterpret_cast<const uint4 *>(gamma) + 2 * t;
-        ga = q[0];
-        gb = q[1];
-        if (shared) {
-            const uint4 *s = reinterpret_cast<const uint4 *>(shared + rowoff) + 2 * t;
-            sa = s[0];
-            sb = s[1];
-        }
-    }
+    // 1. the token's K entries, one per lane, loaded first: the expert-row
+    //    loads depend on them, and wait counters retire in issue order
+    //    (all loads here are unconditional -- lanes past K or past the row end
+    //    re-read a valid address -- so that waiting for one load never has to
+    //    assume a shorter queue on some other path and wait for later ones)
+    const int kk = min(lane, K - 1);
+    int my_r = assist[i * K + kk];
+    float my_s = scales[i * K + kk];
+    if (lane >= K)
+        my_r = -1;
 
-    if (w == 0) {
-        int r = -1;
-        float s = 0.0f;
-        if (lane < K) {
-            r = assist[i * K + lane];
-            s = scales[i * K + lane];
-        }
-        const bool bad = r >= Bs * K;
-        if (bad)
-            r = -1;
-        const bool on = r >= 0;
-        const unsigned long long bal = __ballot(on);
-        const int slot = __popcll(bal & ((1ull << lane) - 1ull));
-        if (on) {
-            s_row[slot] = r;
-            s_w[slot] = s;
-        }
-        const float ws = wave_sum_f32(on ? s : 0.0f);
-        if (lane == 0) {
-            s_n = __popcll(bal);
-            s_ws = ws;
-        }
-        if (bad && dev_err)
+    // 2. residual, shared and gamma do not depend on the routing
+    const int tc = has ? t : 0;
+    const uint16_t *shp = shared ? shared : residual;
+    const uint4 *pr = reinterpret_cast<const uint4 *>(residual + rowoff) + 2 * tc;
+    const uint4 *pg = reinterpret_cast<const uint4 *>(gamma) + 2 * tc;
+    const uint4 *ps = reinterpret_cast<const uint4 *>(shp + rowoff) + 2 * tc;
+    const uint4 ra = pr[0], rb = pr[1];
+    const uint4 ga = pg[0], gb = pg[1];
+    const uint4 sa = ps[0], sb = ps[1];
+
+    // 3. the dispatched entries' rows, CH at a time; entries that were not
+    //    dispatched (row -1) or point outside the buffer load nothing
+    if (my_r >= Bs * K) {
+        if (w == 0 && dev_err)
             atomicOr(dev_err, 8);
+        my_r = -1;
     }
-    __syncthreads();
-    const int n = s_n;
-
+    const float ws = wave_sum_f32(my_r >= 0 ? my_s : 0.0f);
     float acc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         acc[j] = 0.0f;
-    for (int j0 = 0; j0 < n; j0 += CH) {
+    for (int k0 = 0; k0 < K; k0 += CH) {
         uint4 ea[CH], eb[CH];
+        int rr[CH];
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            if (j0 + j < n && has) {
-                const uint4 *p =
-                    reinterpret_cast<const uint4 *>(eo + (size_t)s_row[j0 + j] * H) + 2 * t;
-                ea[j] = p[0];
-                eb[j] = p[1];
+            rr[j] = k0 + j < K ? __builtin_amdgcn_readlane(my_r, k0 + j) : -1;
+            if (rr[j] >= 0) {
+                const uint4 *p = reinterpret_cast<const uint4 *>(eo + (size_t)rr[j] * H) + 2 * tc;
+                ea[j] = load_nt16(p);
+                eb[j] = load_nt16(p + 1);
             }
         }
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
-            if (j0 + j < n) {
-                const float s = s_w[j0 + j];
+            if (rr[j] >= 0) {
+                const float sk =
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k0 + j));
                 float v[16];
                 unpack16(ea[j], eb[j], v);
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    acc[e] = fmaf(s, v[e], acc[e]);
+                    acc[e] = fmaf(sk, v[e], acc[e]);
             }
         }
     }
@@ -115,7 +99,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
         float rv[16];
         unpack16(ra, rb, rv);
         if (shared) {
-            const float wsh = shared_mode == 0 ? s_ws : 1.0f;
+            const float wsh = shared_mode == 0 ? ws : 1.0f;
             float sv[16];
             unpack16(sa, sb, sv);
 #pragma unroll
@@ -145,7 +129,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
         p[1] = make_uint4(pack_bf16x2(xf[8], xf[9]), pack_bf16x2(xf[10], xf[11]),
                           pack_bf16x2(xf[12], xf[13]), pack_bf16x2(xf[14], xf[15]));
     }
-    __syncthreads();
+    lds_barrier();
     float tot = 0.0f;
     for (int j = 0; j < nw; ++j)
         tot += s_part[j];

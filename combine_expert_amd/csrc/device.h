@@ -51,6 +51,25 @@ __device__ __forceinline__ uint32_t amax_bits16(const uint4 &a, const uint4 &b)
     return m;
 }
 
+// ---------------------------------------------------------------- streaming access
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte loads / stores marked non-temporal: data read or written exactly
+// once by this kernel (expert rows in, coded rows out) should not displace
+// reusable lines in the caches.
+__device__ __forceinline__ uint4 load_nt16(const void *p)
+{
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_nt16(void *p, const uint4 &v)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
+
 // ---------------------------------------------------------------- E4M3
 
 // OCP FP8 E4M3 code of v: round to nearest even, saturate at +-448
@@ -71,6 +90,19 @@ __device__ __forceinline__ uint32_t e4m3_code(float v)
     code = af >= 448.0f ? 0x7eu : code;
     code = af != af ? 0x7fu : code;
     return sign | code;
+}
+
+// ---------------------------------------------------------------- block barrier
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load and store of the wave (vmcnt(0)), which would
+// serialise the HBM traffic in flight behind each barrier; the barriers in
+// these kernels only publish LDS data, so global accesses stay in flight.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------- wave ops

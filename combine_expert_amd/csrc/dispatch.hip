@@ -7,16 +7,18 @@
 //   block 0      histogram of the active entries (LDS atomics; counts are
 //                order-free), exclusive scan, counts/offsets, and -1 for the
 //                unused tail of expand_src;
-//   block 1 + i  token i: loads its row once, computes the stable row of
-//                each of its K entries, codes the row once and writes it K
-//                times.
-// The stable row of entry f is the number of active entries g whose key
-// (instance id, g) is smaller than f's, i.e. offsets[id] plus the number of
-// earlier entries with the same id.  Each token block counts it directly
-// over all N = Bs*K keys (at most 8192 four-byte ids, L2-resident), which
-// costs a few hundred ALU operations per thread and overlaps the HBM load
-// of the token's row, instead of a serial routing kernel between two
-// launches.  The result does not depend on scheduling: bitwise repeatable.
+//   block 1 + i  token i: loads its row once, works out the destination row
+//                of each of its K entries, codes the row once and writes it
+//                K times.
+// The row of entry f with instance id e is offsets[e] plus the number of
+// active entries before f with the same id (a stable counting sort).  Each
+// token block derives it on its own from two LDS histograms of all N = Bs*K
+// ids (at most 8192 four-byte ids, read with 16-byte loads from L2): one over
+// every entry, one over the entries before its token.  offsets[e] is then a
+// sum over the smaller ids, the earlier same-id count is one LDS read plus
+// the token's own duplicates.  This replaces a serial routing kernel between
+// two launches with a little redundant LDS work that overlaps the HBM load of
+// the token's row.  Nothing depends on scheduling: bitwise repeatable.
 //
 // Row layout: one thread owns 16 consecutive elements (two 16-byte loads of
 // bf16), so a 32-element mxfp8 block is a lane pair and a 128-element int8
@@ -27,10 +29,56 @@
 
 namespace moe {
 
-constexpr int kKeyShift = 13;  // flat entry index g < Bs*K <= 8192 = 2^13
-constexpr int kInactiveKey = 0x7fffffff;
-
 // ------------------------------------------------------------------ block 0
+
+// Visits every entry g this thread owns -- int4 groups g4 = t, t + T, ...,
+// then the scalar tail -- as f(id, on, g).  Each batch issues four 16-byte
+// id loads (and their mask words) before using any; indices past the end
+// are clamped, so the loads are unconditional, and those groups are visited
+// as inactive entries.  after_first_issue() runs once, right after the first
+// batch is issued and before it is waited for: loads placed there stay in
+// flight while the batch is consumed (wait counters retire in issue order).
+template <typename F, typename G>
+__device__ __forceinline__ void for_each_entry(const int32_t *__restrict__ ids,
+                                               const uint8_t *__restrict__ mask, int N, F &&f,
+                                               G &&after_first_issue)
+{
+    const int t = threadIdx.x, T = blockDim.x;
+    const int N4 = N >> 2;
+    const int4 *ids4 = reinterpret_cast<const int4 *>(ids);
+    const uint32_t *mask4 = reinterpret_cast<const uint32_t *>(mask);
+    bool first = true;
+    for (int base = t; base < N4 || first; base += 4 * T) {
+        int4 v[4];
+        uint32_t m[4];
+        if (N4 > 0) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int g4 = min(base + u * T, N4 - 1);
+                v[u] = ids4[g4];
+                m[u] = mask ? mask4[g4] : 0x01010101u;
+            }
+        }
+        if (first) {
+            after_first_issue();
+            first = false;
+        }
+        if (N4 == 0)
+            break;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g4 = base + u * T;
+            const uint32_t mu = g4 < N4 ? m[u] : 0u;
+            const int g = g4 * 4;
+            f(v[u].x, (mu & 0xffu) != 0, g);
+            f(v[u].y, (mu & 0xff00u) != 0, g + 1);
+            f(v[u].z, (mu & 0xff0000u) != 0, g + 2);
+            f(v[u].w, (mu & 0xff000000u) != 0, g + 3);
+        }
+    }
+    for (int g = N4 * 4 + t; g < N; g += T)
+        f(ids[g], mask == nullptr || mask[g] != 0, g);
+}
 
 __device__ void route_summary(const int32_t *__restrict__ ids, const uint8_t *__restrict__ mask,
                               int N, int E, int32_t *__restrict__ counts,
@@ -41,20 +89,21 @@ __device__ void route_summary(const int32_t *__restrict__ ids, const uint8_t *__
     const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
     for (int e = t; e < E; e += T)
         s_hist[e] = 0;
-    __syncthreads();
     int bad = 0;
-    for (int g = t; g < N; g += T) {
-        const int id = ids[g];
-        if (mask == nullptr || mask[g] != 0) {
-            if (id >= 0 && id < E)
-                atomicAdd(&s_hist[id], 1);
-            else
-                bad = 1;
-        }
-    }
+    for_each_entry(
+        ids, mask, N,
+        [&](int id, bool on, int) {
+            if (on) {
+                if ((unsigned)id < (unsigned)E)
+                    atomicAdd(&s_hist[id], 1);
+                else
+                    bad = 1;
+            }
+        },
+        [] { lds_barrier(); });
     if (bad && dev_err)
         atomicOr(dev_err, 1);
-    __syncthreads();
+    lds_barrier();
 
     // exclusive scan: each thread owns a contiguous run of counters
     const int per = (E + T - 1) / T;
@@ -65,7 +114,7 @@ __device__ void route_summary(const int32_t *__restrict__ ids, const uint8_t *__
     const int incl = wave_incl_scan(local);
     if (lane == kWave - 1)
         s_wave[w] = incl;
-    __syncthreads();
+    lds_barrier();
     int base = 0, total = 0;
     for (int j = 0; j < nw; ++j) {
         const int v = s_wave[j];
@@ -86,11 +135,6 @@ __device__ void route_summary(const int32_t *__restrict__ ids, const uint8_t *__
 }
 
 // ------------------------------------------------------------------ token blocks
-
-__device__ __forceinline__ int entry_key(int id, bool on, int g, int E)
-{
-    return (on && id >= 0 && id < E) ? (id << kKeyShift) | g : kInactiveKey;
-}
 
 __device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d)
 {
@@ -115,17 +159,23 @@ __device__ __forceinline__ uint4 int8_codes(const float *v, float d)
                       pack_i8x4(q[8], q[9], q[10], q[11]), pack_i8x4(q[12], q[13], q[14], q[15]));
 }
 
-// E4M3 codes of 16 values multiplied by the power of two f (exact product)
+// E4M3 codes of 16 values multiplied by the power of two f (an exact product):
+// clamp to +-448 (saturation), then the gfx950 packed conversion, which
+// rounds to nearest even and keeps the sign of zero.
 __device__ __forceinline__ uint4 e4m3_codes(const float *v, float f)
 {
-    uint32_t c[16];
+    uint32_t w[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-        c[j] = e4m3_code(v[j] * f);
-    return make_uint4(c[0] | c[1] << 8 | c[2] << 16 | c[3] << 24,
-                      c[4] | c[5] << 8 | c[6] << 16 | c[7] << 24,
-                      c[8] | c[9] << 8 | c[10] << 16 | c[11] << 24,
-                      c[12] | c[13] << 8 | c[14] << 16 | c[15] << 24);
+    for (int q = 0; q < 4; ++q) {
+        const float a = fminf(fmaxf(v[4 * q] * f, -448.0f), 448.0f);
+        const float b = fminf(fmaxf(v[4 * q + 1] * f, -448.0f), 448.0f);
+        const float c = fminf(fmaxf(v[4 * q + 2] * f, -448.0f), 448.0f);
+        const float d = fminf(fmaxf(v[4 * q + 3] * f, -448.0f), 448.0f);
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
+        w[q] = (uint32_t)p;
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // floor(log2(m)) of a positive bf16 magnitude pattern (normal or subnormal)
@@ -144,6 +194,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
     int32_t *__restrict__ assist_dst, int32_t *__restrict__ dev_err)
 {
     __shared__ int s_hist[1024];
+    __shared__ int s_pre[1024];
     __shared__ int s_part[kMaxWaves][KMAX / 2 + 1];
     __shared__ int s_rank[KMAX];
     __shared__ uint32_t s_amax;
@@ -159,51 +210,58 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
     const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
     const bool has = t * kChunk < H;
 
-    // 1. this thread's 16 elements of x[i] (in flight while ranks are counted)
-    uint4 xa = make_uint4(0, 0, 0, 0), xb = xa;
-    if (has) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)i * H) + 2 * t;
-        xa = src[0];
-        xb = src[1];
+    // 1. the token's own K entries, one per lane (a single round trip)
+    //    (unconditional loads: lanes past K re-read entry K-1, and without a
+    //    mask the id word is read in its place, so no wait on them has to
+    //    cover loads issued after them on another path)
+    const int f0 = i * K;
+    const int kk = min(lane, K - 1);
+    const int raw_id = ids[f0 + kk];
+    const uint8_t *mp = mask ? mask : reinterpret_cast<const uint8_t *>(ids);
+    const uint8_t raw_on = mp[f0 + kk];
+    for (int e = t; e < E; e += T) {
+        s_hist[e] = 0;
+        s_pre[e] = 0;
     }
 
-    // 2. stable rows of the token's entries: count smaller keys over all entries
-    int tkey[KMAX];
+    // 2. stable rows of the token's entries.  Row of entry f with id e:
+    //    offsets[e] (active entries with a smaller id) + active entries g < f
+    //    with id e.  Both come from two LDS histograms of the active ids, one
+    //    over all entries and one over the entries before this token.  The
+    //    token's row (16 elements per thread) is loaded after the first batch
+    //    of ids, so it stays in flight while the histograms are built.
+    uint4 xa, xb;
+    for_each_entry(
+        ids, mask, N,
+        [&](int id, bool on, int g) {
+            if (on && (unsigned)id < (unsigned)E) {
+                atomicAdd(&s_hist[id], 1);
+                if (g < f0)
+                    atomicAdd(&s_pre[id], 1);
+            }
+        },
+        [&] {
+            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)i * H) + 2 * (has ? t : 0);
+            xa = src[0];
+            xb = src[1];
+            lds_barrier();  // histograms zeroed before the first increment
+        });
+    const bool my_on = lane < K && (mask == nullptr || raw_on != 0) && (unsigned)raw_id < (unsigned)E;
+    const int my_id = my_on ? raw_id : -1;
+    int tid[KMAX];  // instance id of each of the token's entries, -1 if inactive
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-        tkey[k] = -1;  // inactive target: no key is smaller
-        if (k < K) {
-            const int f = i * K + k;
-            const int key = entry_key(ids[f], mask == nullptr || mask[f] != 0, f, E);
-            if (key != kInactiveKey)
-                tkey[k] = key;
-        }
-    }
+    for (int k = 0; k < KMAX; ++k)
+        tid[k] = k < K ? __builtin_amdgcn_readlane(my_id, k) : -1;
+    lds_barrier();
     int cnt[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         cnt[k] = 0;
-    const int N4 = N >> 2;
-    const int4 *ids4 = reinterpret_cast<const int4 *>(ids);
-    const uint32_t *mask4 = reinterpret_cast<const uint32_t *>(mask);
-#pragma unroll 4
-    for (int g4 = t; g4 < N4; g4 += T) {
-        const int4 v = ids4[g4];
-        const uint32_t m = mask ? mask4[g4] : 0x01010101u;
-        const int g = g4 * 4;
-        const int k0 = entry_key(v.x, (m & 0xffu) != 0, g, E);
-        const int k1 = entry_key(v.y, (m & 0xff00u) != 0, g + 1, E);
-        const int k2 = entry_key(v.z, (m & 0xff0000u) != 0, g + 2, E);
-        const int k3 = entry_key(v.w, (m & 0xff000000u) != 0, g + 3, E);
+    for (int e = t; e < E; e += T) {
+        const int c = s_hist[e];
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            cnt[k] += (k0 < tkey[k]) + (k1 < tkey[k]) + (k2 < tkey[k]) + (k3 < tkey[k]);
-    }
-    for (int g = N4 * 4 + t; g < N; g += T) {
-        const int key = entry_key(ids[g], mask == nullptr || mask[g] != 0, g, E);
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            cnt[k] += key < tkey[k];
+            cnt[k] += e < tid[k] ? c : 0;
     }
 
     // 3. block sums: two 16-bit counters per word (each sum <= 8192)
@@ -223,13 +281,21 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
         if (MODE == 2)
             s_part[w][P] = (int)amax;
     }
-    __syncthreads();
+    lds_barrier();
     if (t < P) {
         int s = 0;
         for (int j = 0; j < nw; ++j)
             s += s_part[j][t];
-        s_rank[2 * t] = tkey[2 * t] < 0 ? -1 : (s & 0xffff);
-        s_rank[2 * t + 1] = tkey[2 * t + 1] < 0 ? -1 : (s >> 16);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int k = 2 * t + h;
+            int dup = 0;  // earlier entries of this token with the same id
+#pragma unroll
+            for (int q = 0; q < KMAX; ++q)
+                dup += (q < k && tid[q] == tid[k]) ? 1 : 0;
+            const int off = h ? (s >> 16) : (s & 0xffff);
+            s_rank[k] = tid[k] < 0 ? -1 : off + s_pre[tid[k]] + dup;
+        }
     }
     if (MODE == 2 && t == P) {
         uint32_t m = 0;
@@ -237,7 +303,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
             m = max(m, (uint32_t)s_part[j][P]);
         s_amax = m;
     }
-    __syncthreads();
+    lds_barrier();
     int rank[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
@@ -260,8 +326,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
                 continue;
             uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(expand_x) +
                                                    (size_t)rank[k] * H) + 2 * t;
-            dst[0] = xa;
-            dst[1] = xb;
+            store_nt16(dst, xa);
+            store_nt16(dst + 1, xb);
         }
         return;
     }
@@ -280,15 +346,17 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
             for (int k = 0; k < KMAX; ++k) {
                 if (rank[k] < 0)
                     continue;
-                reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
-                                          (size_t)rank[k] * H)[t] = code;
+                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
+                                                     (size_t)rank[k] * H) + t, code);
                 if (t == 0)
                     static_cast<float *>(expand_scales)[rank[k]] = scale;
             }
         }
     } else if (MODE == 3) {
         const int lanes = tile / kChunk;  // lanes per tile: 1 .. 64
-        uint32_t m = amax_bits16(xa, xb);
+        // lanes past the row end hold a copy of chunk 0: keep it out of the
+        // last (partial) tile's maximum
+        uint32_t m = has ? amax_bits16(xa, xb) : 0u;
         for (int o = 1; o < lanes; o <<= 1)
             m = max(m, (uint32_t)__shfl_xor((int)m, o));
         const float mf = __uint_as_float(m << 16);
@@ -302,8 +370,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
             for (int k = 0; k < KMAX; ++k) {
                 if (rank[k] < 0)
                     continue;
-                reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
-                                          (size_t)rank[k] * H)[t] = code;
+                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
+                                                     (size_t)rank[k] * H) + t, code);
                 if (lead)
                     static_cast<float *>(expand_scales)[(size_t)rank[k] * nt +
                                                         (t * kChunk) / tile] = scale;
@@ -326,8 +394,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
             for (int k = 0; k < KMAX; ++k) {
                 if (rank[k] < 0)
                     continue;
-                reinterpret_cast<uint4 *>(static_cast<uint8_t *>(expand_x) +
-                                          (size_t)rank[k] * H)[t] = code;
+                store_nt16(reinterpret_cast<uint4 *>(static_cast<uint8_t *>(expand_x) +
+                                                     (size_t)rank[k] * H) + t, code);
                 if (lead)
                     static_cast<uint8_t *>(expand_scales)[(size_t)rank[k] * nb + t / 2] =
                         (uint8_t)(se + 127);
