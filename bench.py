@@ -6,6 +6,11 @@ expert + residual + RMSNorm, on the DeepSeek-V3-shaped workload
 Zipf(1.2) routing, one shared expert).
 
     python bench.py [--steps 500] [--warmup 50] [--sets 5] [--cpu-seconds 10]
+    python bench.py --copy-mb 256                        # copy kernel for counter scaling
+    python bench.py --summarize-trace STATS.csv --out profiles/X.md --command CMD
+    python bench.py --summarize-counters FETCH.csv WRITE.csv --kernel NAME \
+                    --sources a.hip,b.h --out profiles/X.txt --command CMD1 --command CMD2
+    python bench.py --summarize-copy FETCH.csv WRITE.csv --copy-mb 256 --out profiles/X.txt ...
 
 Prints one JSON line.  `value` is whole-step throughput in GB/s of
 algorithmic bytes (each input read once, each output written once) with all
@@ -21,6 +26,7 @@ a reference point.
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -48,6 +54,19 @@ def parse():
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the step, time a plain device copy of this many MB "
                         "(the reference kernel for counter scaling and achievable bandwidth)")
+    g = p.add_argument_group("profile summaries (rocprofv3 CSV output -> profiles/*.txt|md)")
+    g.add_argument("--summarize-trace", metavar="STATS_CSV",
+                   help="kernel_stats.csv of a --kernel-trace --stats run")
+    g.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="counter_collection.csv of a FETCH_SIZE run and of a WRITE_SIZE run")
+    g.add_argument("--summarize-copy", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="the same for the --copy-mb kernel: derives the counter scales")
+    g.add_argument("--kernel", help="kernel name (prefix) to summarise")
+    g.add_argument("--sources", default="", help="comma-separated csrc files of that kernel")
+    g.add_argument("--out", help="summary file to write")
+    g.add_argument("--command", action="append", default=[],
+                   help="the command(s) that produced the CSV files")
+    g.add_argument("--title", default="rocprofv3 kernel statistics")
     return p.parse_args()
 
 
@@ -110,6 +129,71 @@ def counter_traffic(kernel_file, digest_names):
     if d.get("source_digest") != source_digest(*digest_names):
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------- profile summaries
+
+WORKLOAD_TAG = "Bs=512 H=7168 K=8 E=256 mxfp8 (bench.py)"
+COPY_CAL = "copy_calibration.txt"
+
+
+def _median_counter(path, kernel, counter):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(kernel)]
+    if not vals:
+        raise SystemExit(f"{path}: no {counter} rows for a kernel named {kernel}*")
+    return statistics.median(vals), len(vals)
+
+
+def summarize_trace(args):
+    rows = list(csv.DictReader(open(args.summarize_trace)))
+    lines = [f"# {args.title}", "", "Command (from the repository root, on one MI355X):", "",
+             "```", *args.command, "```", "",
+             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_counters(args):
+    """HBM bytes per launch = FETCH_SIZE KiB x 1024 x fetch_scale + WRITE_SIZE KiB x 1024 x
+    write_scale, the scales being what the counters read for a copy of known size."""
+    fetch, nf = _median_counter(args.summarize_counters[0], args.kernel, "FETCH_SIZE")
+    write, nw = _median_counter(args.summarize_counters[1], args.kernel, "WRITE_SIZE")
+    with open(os.path.join(PROFILES, COPY_CAL)) as f:
+        cal = json.load(f)
+    rd = round(fetch * 1024 * cal["fetch_scale"])
+    wr = round(write * 1024 * cal["write_scale"])
+    names = [n for n in args.sources.split(",") if n]
+    d = {"kernel": args.kernel, "workload": WORKLOAD_TAG, "source_digest": source_digest(*names),
+         "source_files": names, "FETCH_SIZE_KiB_per_dispatch": fetch,
+         "WRITE_SIZE_KiB_per_dispatch": write, "dispatches": [nf, nw],
+         "fetch_scale": cal["fetch_scale"], "write_scale": cal["write_scale"],
+         "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+         "hbm_bytes_per_launch": rd + wr, "commands": args.command,
+         "note": f"median over the profiled dispatches of the kernel; scales from {COPY_CAL}"}
+    with open(args.out, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+
+
+def summarize_copy(args):
+    kernel = args.kernel or "__amd_rocclr_copyBuffer"
+    fetch, _ = _median_counter(args.summarize_copy[0], kernel, "FETCH_SIZE")
+    write, _ = _median_counter(args.summarize_copy[1], kernel, "WRITE_SIZE")
+    nbytes = args.copy_mb * (1 << 20)
+    d = {"kernel": f"{kernel} (torch device-to-device copy of a bf16 tensor)",
+         "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+         "FETCH_SIZE_KiB_per_dispatch": fetch, "WRITE_SIZE_KiB_per_dispatch": write,
+         "fetch_scale": round(nbytes / (fetch * 1024), 4),
+         "write_scale": round(nbytes / (write * 1024), 4), "commands": args.command,
+         "note": "Kernel traffic = FETCH_SIZE*1024*fetch_scale + WRITE_SIZE*1024*write_scale."}
+    with open(args.out, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
 
 
 # ----------------------------------------------------------------- GPU side
@@ -198,10 +282,15 @@ def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
+    if args.summarize_copy:
+        return summarize_copy(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU share of the MoE layer; runs on more than one "
-              "GPU are not part of this build (see the sharding notes in DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py times the single-GPU share of the MoE layer and runs on one GPU only; "
+              "--gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_mb:
@@ -300,7 +389,7 @@ def main():
         "roofline": {
             "kernel": "k_combine", "bound": "hbm", "achieved": round(a_cmb, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a_cmb / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic("combine_c3_traffic.json", ("combine.hip", "device.h")),
+            "traffic": counter_traffic("combine_c3_traffic.txt", ("combine.hip", "device.h")),
             "algorithmic_bytes_per_launch": nb["combine"],
             "avg_launch_us": round(us_cmb, 3),
         },
@@ -309,7 +398,7 @@ def main():
                               "GBps": round(a_upd, 1)},
             "dispatch": {"avg_us": round(us_dsp, 3), "bytes": nb["dispatch"],
                          "GBps": round(a_dsp, 1), "frac": round(a_dsp / HBM_PEAK_GBS, 4),
-                         "traffic": counter_traffic("dispatch_c3_traffic.json",
+                         "traffic": counter_traffic("dispatch_c3_traffic.txt",
                                                     ("dispatch.hip", "device.h"))},
             "combine": {"avg_us": round(us_cmb, 3), "bytes": nb["combine"],
                         "GBps": round(a_cmb, 1), "frac": round(a_cmb / HBM_PEAK_GBS, 4)},

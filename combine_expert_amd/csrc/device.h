@@ -1,5 +1,6 @@
 // device.h -- gfx950 device helpers for the MoE mapping / dispatch / combine
-// kernels: bf16 and OCP E4M3 conversions, wave64 reductions and scans.
+// kernels: bf16 conversions, streaming loads/stores, an LDS-only block
+// barrier, wave64 reductions and scans.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -68,28 +69,6 @@ __device__ __forceinline__ void store_nt16(void *p, const uint4 &v)
 {
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
-}
-
-// ---------------------------------------------------------------- E4M3
-
-// OCP FP8 E4M3 code of v: round to nearest even, saturate at +-448
-// (0x7E), NaN -> 0x7F with the sign kept, -0 -> 0x80.
-//   |v| <  2^-6 : subnormal grid m * 2^-9, code = rint(|v| * 512) in [0, 8]
-//   |v| >= 2^-6 : keep 3 of the 23 fp32 mantissa bits with round-half-even on
-//                 the 20 dropped bits; the carry moves into the exponent and
-//                 the fp32 exponent bias 127 becomes the E4M3 bias 7.
-__device__ __forceinline__ uint32_t e4m3_code(float v)
-{
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    const float af = __uint_as_float(a);
-    const uint32_t sub = (uint32_t)__builtin_rintf(af * 512.0f);
-    const uint32_t nrm = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    uint32_t code = af < 0x1p-6f ? sub : nrm;
-    code = af >= 448.0f ? 0x7eu : code;
-    code = af != af ? 0x7fu : code;
-    return sign | code;
 }
 
 // ---------------------------------------------------------------- block barrier

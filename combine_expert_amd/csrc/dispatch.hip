@@ -5,48 +5,59 @@
 //
 // One launch, Bs + 1 blocks, no inter-block communication:
 //   block 0      histogram of the active entries (LDS atomics; counts are
-//                order-free), exclusive scan, counts/offsets, and -1 for the
-//                unused tail of expand_src;
+//                order-free), exclusive scan, counts/offsets, -1 for the
+//                unused tail of expand_src, and the device error bits;
 //   block 1 + i  token i: loads its row once, works out the destination row
 //                of each of its K entries, codes the row once and writes it
 //                K times.
 // The row of entry f with instance id e is offsets[e] plus the number of
 // active entries before f with the same id (a stable counting sort).  Each
 // token block derives it on its own from two LDS histograms of all N = Bs*K
-// ids (at most 8192 four-byte ids, read with 16-byte loads from L2): one over
-// every entry, one over the entries before its token.  offsets[e] is then a
-// sum over the smaller ids, the earlier same-id count is one LDS read plus
-// the token's own duplicates.  This replaces a serial routing kernel between
-// two launches with a little redundant LDS work that overlaps the HBM load of
-// the token's row.  Nothing depends on scheduling: bitwise repeatable.
+// entries (at most 8192 four-byte ids, read with 16-byte loads from L2): one
+// over every entry, one over the entries before its token.  offsets[e] is
+// then a sum over the smaller ids, the earlier same-id count is one LDS read
+// plus the token's own duplicates.  This replaces a serial routing kernel
+// between two launches with a little redundant LDS work that overlaps the HBM
+// load of the token's row.  Nothing depends on scheduling: bitwise repeatable.
 //
 // Row layout: one thread owns 16 consecutive elements (two 16-byte loads of
 // bf16), so a 32-element mxfp8 block is a lane pair and a 128-element int8
 // tile is 8 lanes; per-block maxima are lane shuffles, the per-token maximum
 // is a wave reduction plus one LDS step.
+//
+// Load order matters: wait counters retire in issue order, so the loads a
+// phase waits for are issued before the ones it does not (the token's row),
+// and loads are unconditional (clamped indices) so that no control-flow join
+// makes a wait cover loads issued after it on another path.
 #include "device.h"
 #include "kernels.h"
 
 namespace moe {
 
-// ------------------------------------------------------------------ block 0
+constexpr int kHistSlots = 1024;  // one LDS counter per instance (E <= 1024)
+
+// Where the entries come from: [Bs, K] instance ids and an optional mask.
+struct Entries {
+    const int32_t *ids;
+    const uint8_t *mask;  // null: every entry is active
+    int E;
+};
 
 // Visits every entry g this thread owns -- int4 groups g4 = t, t + T, ...,
-// then the scalar tail -- as f(id, on, g).  Each batch issues four 16-byte
-// id loads (and their mask words) before using any; indices past the end
-// are clamped, so the loads are unconditional, and those groups are visited
-// as inactive entries.  after_first_issue() runs once, right after the first
-// batch is issued and before it is waited for: loads placed there stay in
-// flight while the batch is consumed (wait counters retire in issue order).
-template <typename F, typename G>
-__device__ __forceinline__ void for_each_entry(const int32_t *__restrict__ ids,
-                                               const uint8_t *__restrict__ mask, int N, F &&f,
+// then the scalar tail -- as f(inst, on, g) with inst = -1 unless on.  Each
+// batch issues four 16-byte id loads (and mask words) before using any;
+// indices past the end are clamped and visited as inactive.  Ids outside
+// [0, E) of active entries raise error bit 1 in err.
+// after_first_issue() runs once, right after the first batch is issued:
+// loads placed there stay in flight while the batch is consumed.
+template <typename Fn, typename G>
+__device__ __forceinline__ void for_each_entry(const Entries &s, int N, int &err, Fn &&f,
                                                G &&after_first_issue)
 {
     const int t = threadIdx.x, T = blockDim.x;
     const int N4 = N >> 2;
-    const int4 *ids4 = reinterpret_cast<const int4 *>(ids);
-    const uint32_t *mask4 = reinterpret_cast<const uint32_t *>(mask);
+    const int4 *ids4 = reinterpret_cast<const int4 *>(s.ids);
+    const uint32_t *mask4 = reinterpret_cast<const uint32_t *>(s.mask);
     bool first = true;
     for (int base = t; base < N4 || first; base += 4 * T) {
         int4 v[4];
@@ -56,7 +67,7 @@ __device__ __forceinline__ void for_each_entry(const int32_t *__restrict__ ids,
             for (int u = 0; u < 4; ++u) {
                 const int g4 = min(base + u * T, N4 - 1);
                 v[u] = ids4[g4];
-                m[u] = mask ? mask4[g4] : 0x01010101u;
+                m[u] = s.mask ? mask4[g4] : 0x01010101u;
             }
         }
         if (first) {
@@ -68,41 +79,58 @@ __device__ __forceinline__ void for_each_entry(const int32_t *__restrict__ ids,
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int g4 = base + u * T;
-            const uint32_t mu = g4 < N4 ? m[u] : 0u;
             const int g = g4 * 4;
-            f(v[u].x, (mu & 0xffu) != 0, g);
-            f(v[u].y, (mu & 0xff00u) != 0, g + 1);
-            f(v[u].z, (mu & 0xff0000u) != 0, g + 2);
-            f(v[u].w, (mu & 0xff000000u) != 0, g + 3);
+            const int idv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            const uint32_t mu = g4 < N4 ? m[u] : 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool on = ((mu >> (8 * j)) & 0xffu) != 0;
+                const bool ok = (unsigned)idv[j] < (unsigned)s.E;
+                if (on && !ok)
+                    err |= 1;
+                f(on && ok ? idv[j] : -1, on && ok, g + j);
+            }
         }
     }
-    for (int g = N4 * 4 + t; g < N; g += T)
-        f(ids[g], mask == nullptr || mask[g] != 0, g);
+    for (int g = N4 * 4 + t; g < N; g += T) {
+        const int id = s.ids[g];
+        const bool on = s.mask == nullptr || s.mask[g] != 0;
+        const bool ok = (unsigned)id < (unsigned)s.E;
+        if (on && !ok)
+            err |= 1;
+        f(on && ok ? id : -1, on && ok, g);
+    }
 }
 
-__device__ void route_summary(const int32_t *__restrict__ ids, const uint8_t *__restrict__ mask,
-                              int N, int E, int32_t *__restrict__ counts,
-                              int32_t *__restrict__ offsets, int32_t *__restrict__ expand_src,
-                              int32_t *__restrict__ dev_err, int *s_hist, int *s_wave)
+struct DispatchArgs {
+    const uint16_t *x;
+    const int32_t *ids;
+    const uint8_t *mask;
+    int Bs, H, K, E, tile;
+    void *expand_x, *expand_scales;
+    int32_t *counts, *offsets, *expand_src, *assist_dst;
+    int32_t *dev_err;
+};
+
+// ------------------------------------------------------------------ block 0
+
+__device__ void route_summary(const DispatchArgs &a, const Entries &s, int *s_hist, int *s_wave)
 {
     const int t = threadIdx.x, T = blockDim.x;
     const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
+    const int N = a.Bs * a.K, E = a.E;
     for (int e = t; e < E; e += T)
         s_hist[e] = 0;
-    int bad = 0;
+    int err = 0;
     for_each_entry(
-        ids, mask, N,
-        [&](int id, bool on, int) {
-            if (on) {
-                if ((unsigned)id < (unsigned)E)
-                    atomicAdd(&s_hist[id], 1);
-                else
-                    bad = 1;
-            }
+        s, N, err,
+        [&](int inst, bool on, int) {
+            if (on)
+                atomicAdd(&s_hist[inst], 1);
         },
-        [] { lds_barrier(); });
-    if (bad && dev_err)
-        atomicOr(dev_err, 1);
+        [&] { lds_barrier(); });
+    if (err && a.dev_err)
+        atomicOr(a.dev_err, err);
     lds_barrier();
 
     // exclusive scan: each thread owns a contiguous run of counters
@@ -124,14 +152,14 @@ __device__ void route_summary(const int32_t *__restrict__ ids, const uint8_t *__
     int run = base + incl - local;
     for (int e = e0; e < e1; ++e) {
         const int c = s_hist[e];
-        counts[e] = c;
-        offsets[e] = run;
+        a.counts[e] = c;
+        a.offsets[e] = run;
         run += c;
     }
     if (t == 0)
-        offsets[E] = total;
+        a.offsets[E] = total;
     for (int r = total + t; r < N; r += T)
-        expand_src[r] = -1;
+        a.expand_src[r] = -1;
 }
 
 // ------------------------------------------------------------------ token blocks
@@ -185,24 +213,116 @@ __device__ __forceinline__ int bf16_ilogb(uint32_t m)
     return ex ? ex - 127 : (31 - __clz((int)(m & 0x7f))) - 133;
 }
 
+// Codes a token's row once (this thread's 16 elements in xa, xb) and writes it,
+// with its scales, to each destination row rank[k] >= 0.  amax_row is the
+// token's largest |x| pattern (per-token int8 only).
 template <int MODE, int KMAX>
-__global__ __launch_bounds__(kMaxThreads) void k_dispatch(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ ids,
-    const uint8_t *__restrict__ mask, int Bs, int H, int K, int E, int tile,
-    void *__restrict__ expand_x, void *__restrict__ expand_scales, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ expand_src,
-    int32_t *__restrict__ assist_dst, int32_t *__restrict__ dev_err)
+__device__ __forceinline__ void code_store(const DispatchArgs &a, int t, bool has, const uint4 &xa,
+                                           const uint4 &xb, const int *rank, uint32_t amax_row)
 {
-    __shared__ int s_hist[1024];
-    __shared__ int s_pre[1024];
+    const int H = a.H;
+    if (MODE == 0) {
+        if (!has)
+            return;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+            if (rank[k] < 0)
+                continue;
+            uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.expand_x) +
+                                                   (size_t)rank[k] * H) + 2 * t;
+            store_nt16(dst, xa);
+            store_nt16(dst + 1, xb);
+        }
+        return;
+    }
+
+    float v[16];
+    unpack16(xa, xb, v);
+    uint4 code;
+    if (MODE == 2) {
+        const uint32_t m = amax_row;
+        const float mf = __uint_as_float(m << 16);
+        const float d = m ? 127.0f / mf : 0.0f;
+        const float scale = m ? 1.0f / d : 0.0f;
+        code = int8_codes(v, d);
+        if (has) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (rank[k] < 0)
+                    continue;
+                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(a.expand_x) +
+                                                     (size_t)rank[k] * H) + t, code);
+                if (t == 0)
+                    static_cast<float *>(a.expand_scales)[rank[k]] = scale;
+            }
+        }
+    } else if (MODE == 3) {
+        const int tile = a.tile;
+        const int lanes = tile / kChunk;  // lanes per tile: 1 .. 64
+        // lanes past the row end hold a copy of chunk 0: keep it out of the
+        // last (partial) tile's maximum
+        uint32_t m = has ? amax_bits16(xa, xb) : 0u;
+        for (int o = 1; o < lanes; o <<= 1)
+            m = max(m, (uint32_t)__shfl_xor((int)m, o));
+        const float mf = __uint_as_float(m << 16);
+        const float d = m ? 127.0f / mf : 0.0f;
+        const float scale = m ? 1.0f / d : 0.0f;
+        code = int8_codes(v, d);
+        const int nt = (H + tile - 1) / tile;
+        const bool lead = has && (t & (lanes - 1)) == 0;
+        if (has) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (rank[k] < 0)
+                    continue;
+                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(a.expand_x) +
+                                                     (size_t)rank[k] * H) + t, code);
+                if (lead)
+                    static_cast<float *>(a.expand_scales)[(size_t)rank[k] * nt +
+                                                          (t * kChunk) / tile] = scale;
+            }
+        }
+    } else {  // MODE == 4
+        uint32_t m = amax_bits16(xa, xb);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        int se = -127;
+        if (m) {
+            se = bf16_ilogb(m) - 8;
+            se = max(-127, min(127, se));
+        }
+        const float f = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, normal
+        code = e4m3_codes(v, f);
+        const int nb = H / 32;
+        const bool lead = has && (t & 1) == 0;
+        if (has) {
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                if (rank[k] < 0)
+                    continue;
+                store_nt16(reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.expand_x) +
+                                                     (size_t)rank[k] * H) + t, code);
+                if (lead)
+                    static_cast<uint8_t *>(a.expand_scales)[(size_t)rank[k] * nb + t / 2] =
+                        (uint8_t)(se + 127);
+            }
+        }
+    }
+}
+
+template <int MODE, int KMAX>
+__global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
+{
+    __shared__ int s_hist[kHistSlots];
+    __shared__ int s_pre[kHistSlots];
     __shared__ int s_part[kMaxWaves][KMAX / 2 + 1];
     __shared__ int s_rank[KMAX];
     __shared__ uint32_t s_amax;
 
+    const int Bs = a.Bs, H = a.H, K = a.K, E = a.E;
     const int N = Bs * K;
+    const Entries s{a.ids, a.mask, E};
     if (blockIdx.x == 0) {
-        route_summary(ids, mask, N, E, counts, offsets, expand_src, dev_err, s_hist,
-                      &s_part[0][0]);
+        route_summary(a, s, s_hist, &s_part[0][0]);
         return;
     }
     const int i = blockIdx.x - 1;
@@ -210,14 +330,12 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
     const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
     const bool has = t * kChunk < H;
 
-    // 1. the token's own K entries, one per lane (a single round trip)
-    //    (unconditional loads: lanes past K re-read entry K-1, and without a
-    //    mask the id word is read in its place, so no wait on them has to
-    //    cover loads issued after them on another path)
+    // 1. the token's own K entries, one per lane: the first loads issued are
+    //    the first ones waited for
     const int f0 = i * K;
     const int kk = min(lane, K - 1);
-    const int raw_id = ids[f0 + kk];
-    const uint8_t *mp = mask ? mask : reinterpret_cast<const uint8_t *>(ids);
+    const int raw_id = a.ids[f0 + kk];
+    const uint8_t *mp = a.mask ? a.mask : reinterpret_cast<const uint8_t *>(a.ids);
     const uint8_t raw_on = mp[f0 + kk];
     for (int e = t; e < E; e += T) {
         s_hist[e] = 0;
@@ -231,22 +349,25 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
     //    token's row (16 elements per thread) is loaded after the first batch
     //    of ids, so it stays in flight while the histograms are built.
     uint4 xa, xb;
+    int err = 0;
     for_each_entry(
-        ids, mask, N,
-        [&](int id, bool on, int g) {
-            if (on && (unsigned)id < (unsigned)E) {
-                atomicAdd(&s_hist[id], 1);
+        s, N, err,
+        [&](int inst, bool on, int g) {
+            if (on) {
+                atomicAdd(&s_hist[inst], 1);
                 if (g < f0)
-                    atomicAdd(&s_pre[id], 1);
+                    atomicAdd(&s_pre[inst], 1);
             }
         },
         [&] {
-            const uint4 *src = reinterpret_cast<const uint4 *>(x + (size_t)i * H) + 2 * (has ? t : 0);
+            const uint4 *src =
+                reinterpret_cast<const uint4 *>(a.x + (size_t)i * H) + 2 * (has ? t : 0);
             xa = src[0];
             xb = src[1];
             lds_barrier();  // histograms zeroed before the first increment
         });
-    const bool my_on = lane < K && (mask == nullptr || raw_on != 0) && (unsigned)raw_id < (unsigned)E;
+    const bool my_on =
+        lane < K && (a.mask == nullptr || raw_on != 0) && (unsigned)raw_id < (unsigned)E;
     const int my_id = my_on ? raw_id : -1;
     int tid[KMAX];  // instance id of each of the token's entries, -1 if inactive
 #pragma unroll
@@ -283,9 +404,9 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
     }
     lds_barrier();
     if (t < P) {
-        int s = 0;
+        int sum = 0;
         for (int j = 0; j < nw; ++j)
-            s += s_part[j][t];
+            sum += s_part[j][t];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int k = 2 * t + h;
@@ -293,7 +414,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
 #pragma unroll
             for (int q = 0; q < KMAX; ++q)
                 dup += (q < k && tid[q] == tid[k]) ? 1 : 0;
-            const int off = h ? (s >> 16) : (s & 0xffff);
+            const int off = h ? (sum >> 16) : (sum & 0xffff);
             s_rank[k] = tid[k] < 0 ? -1 : off + s_pre[tid[k]] + dup;
         }
     }
@@ -309,119 +430,26 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(
     for (int k = 0; k < KMAX; ++k)
         rank[k] = k < K ? s_rank[k] : -1;
     if (t < K) {
-        const int f = i * K + t;
+        const int f = f0 + t;
         const int r = s_rank[t];
-        assist_dst[f] = r;
+        a.assist_dst[f] = r;
         if (r >= 0)
-            expand_src[r] = f;
+            a.expand_src[r] = f;
     }
 
-    // 4. code the row once, write it to each destination row
-    if (MODE == 0) {
-        if (!has)
-            return;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (rank[k] < 0)
-                continue;
-            uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(expand_x) +
-                                                   (size_t)rank[k] * H) + 2 * t;
-            store_nt16(dst, xa);
-            store_nt16(dst + 1, xb);
-        }
-        return;
-    }
-
-    float v[16];
-    unpack16(xa, xb, v);
-    uint4 code;
-    if (MODE == 2) {
-        const uint32_t m = s_amax;
-        const float mf = __uint_as_float(m << 16);
-        const float d = m ? 127.0f / mf : 0.0f;
-        const float scale = m ? 1.0f / d : 0.0f;
-        code = int8_codes(v, d);
-        if (has) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rank[k] < 0)
-                    continue;
-                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
-                                                     (size_t)rank[k] * H) + t, code);
-                if (t == 0)
-                    static_cast<float *>(expand_scales)[rank[k]] = scale;
-            }
-        }
-    } else if (MODE == 3) {
-        const int lanes = tile / kChunk;  // lanes per tile: 1 .. 64
-        // lanes past the row end hold a copy of chunk 0: keep it out of the
-        // last (partial) tile's maximum
-        uint32_t m = has ? amax_bits16(xa, xb) : 0u;
-        for (int o = 1; o < lanes; o <<= 1)
-            m = max(m, (uint32_t)__shfl_xor((int)m, o));
-        const float mf = __uint_as_float(m << 16);
-        const float d = m ? 127.0f / mf : 0.0f;
-        const float scale = m ? 1.0f / d : 0.0f;
-        code = int8_codes(v, d);
-        const int nt = (H + tile - 1) / tile;
-        const bool lead = has && (t & (lanes - 1)) == 0;
-        if (has) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rank[k] < 0)
-                    continue;
-                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(expand_x) +
-                                                     (size_t)rank[k] * H) + t, code);
-                if (lead)
-                    static_cast<float *>(expand_scales)[(size_t)rank[k] * nt +
-                                                        (t * kChunk) / tile] = scale;
-            }
-        }
-    } else {  // MODE == 4
-        uint32_t m = amax_bits16(xa, xb);
-        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-        int se = -127;
-        if (m) {
-            se = bf16_ilogb(m) - 8;
-            se = max(-127, min(127, se));
-        }
-        const float f = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, normal
-        code = e4m3_codes(v, f);
-        const int nb = H / 32;
-        const bool lead = has && (t & 1) == 0;
-        if (has) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rank[k] < 0)
-                    continue;
-                store_nt16(reinterpret_cast<uint4 *>(static_cast<uint8_t *>(expand_x) +
-                                                     (size_t)rank[k] * H) + t, code);
-                if (lead)
-                    static_cast<uint8_t *>(expand_scales)[(size_t)rank[k] * nb + t / 2] =
-                        (uint8_t)(se + 127);
-            }
-        }
-    }
+    code_store<MODE, KMAX>(a, t, has, xa, xb, rank, MODE == 2 ? s_amax : 0u);
 }
 
 template <int MODE>
-static hipError_t launch_mode(int kmax, dim3 grid, dim3 block, hipStream_t stream,
-                              const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
-                              int H, int K, int E, int tile, void *expand_x, void *expand_scales,
-                              int32_t *counts, int32_t *offsets, int32_t *expand_src,
-                              int32_t *assist_dst, int32_t *dev_err)
+static hipError_t launch_dispatch_mode(int kmax, const DispatchArgs &a, hipStream_t stream)
 {
-#define MOE_DISPATCH_LAUNCH(KM)                                                                \
-    hipLaunchKernelGGL((k_dispatch<MODE, KM>), grid, block, 0, stream, x, ids, mask, Bs, H, K, \
-                       E, tile, expand_x, expand_scales, counts, offsets, expand_src,          \
-                       assist_dst, dev_err)
+    const dim3 grid(a.Bs + 1), block(row_threads(a.H));
     switch (kmax) {
-    case 2: MOE_DISPATCH_LAUNCH(2); break;
-    case 4: MOE_DISPATCH_LAUNCH(4); break;
-    case 8: MOE_DISPATCH_LAUNCH(8); break;
-    default: MOE_DISPATCH_LAUNCH(16); break;
+    case 2: hipLaunchKernelGGL((k_dispatch<MODE, 2>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_dispatch<MODE, 4>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_dispatch<MODE, 8>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((k_dispatch<MODE, 16>), grid, block, 0, stream, a); break;
     }
-#undef MOE_DISPATCH_LAUNCH
     return hipGetLastError();
 }
 
@@ -431,25 +459,14 @@ hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t 
                            int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err,
                            hipStream_t stream)
 {
+    const DispatchArgs a{x, ids, mask, Bs, H, K, E, tile, expand_x, expand_scales,
+                         counts, offsets, expand_src, assist_dst, dev_err};
     const int kmax = K <= 2 ? 2 : K <= 4 ? 4 : K <= 8 ? 8 : 16;
-    const dim3 grid(Bs + 1), block(row_threads(H));
     switch (quant_mode) {
-    case 0:
-        return launch_mode<0>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
-                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
-                              dev_err);
-    case 2:
-        return launch_mode<2>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
-                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
-                              dev_err);
-    case 3:
-        return launch_mode<3>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
-                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
-                              dev_err);
-    default:
-        return launch_mode<4>(kmax, grid, block, stream, x, ids, mask, Bs, H, K, E, tile,
-                              expand_x, expand_scales, counts, offsets, expand_src, assist_dst,
-                              dev_err);
+    case 0: return launch_dispatch_mode<0>(kmax, a, stream);
+    case 2: return launch_dispatch_mode<2>(kmax, a, stream);
+    case 3: return launch_dispatch_mode<3>(kmax, a, stream);
+    default: return launch_dispatch_mode<4>(kmax, a, stream);
     }
 }
 

@@ -4,8 +4,12 @@
 //
 // One lane per entry f = i*K + k.  The work is a few scattered 4-byte reads
 // per entry (the table row of the logical expert), so the kernel is bound by
-// latency, not bandwidth; it is kept separate from the dispatch because the
-// pages define it as its own call in a fixed sequence before the dispatch.
+// latency, not bandwidth (about 3.3 us per launch back to back at Bs=512,
+// K=8, however the row is read).  It is kept separate from the dispatch: the
+// pages define it as its own call in a fixed sequence before the dispatch,
+// and folding the mapping into the dispatch (each of its Bs + 1 blocks maps
+// all Bs*K entries from an LDS copy of the table) measured slower than the
+// two launches, as did a routing kernel plus a row-scatter kernel.
 #include "device.h"
 #include "kernels.h"
 

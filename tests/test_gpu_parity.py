@@ -206,7 +206,7 @@ def test_device_error_bits():
 
 def test_identity_expert_round_trip_closed_form():
     # mode-0 dispatch, identity experts, residual 0, no shared expert:
-    # x_out = bf16(sum_k s_k * x_i) (spec invariant), on the GPU path only
+    # x_out = bf16(sum_k s_k * x_i) (identity experts reproduce the token), on the GPU path only
     wl = W.make_small(14, 128, 4096, 8, 4, 8, 0, shared=False)
     say("[parity] identity round trip")
     gd = gpu_dispatch(wl, cuda(wl.logical_ids), None)
@@ -215,3 +215,57 @@ def test_identity_expert_round_trip_closed_form():
     expect = (wl.scales.double().sum(1, keepdim=True) * wl.x.double())
     got = xo.double().cpu()
     assert torch.all((got - expect).abs() <= 2e-2 + 1e-2 * expect.abs())
+
+
+def wide_table(rng, n_logical, F, n_instances, bad_rows):
+    """Seeded mapping table of width F: row e holds n in [1, F-1] replicas, the
+    rest -1; bad_rows rows are made malformed (n out of range, an instance
+    out of range) so that both error kinds are exercised."""
+    table = np.full((n_logical, F), -1, dtype=np.int32)
+    for e in range(n_logical):
+        n = int(rng.integers(1, F))
+        table[e, 0] = n
+        table[e, 1:1 + n] = rng.integers(0, n_instances, n)
+    for j, e in enumerate(rng.choice(n_logical, bad_rows, replace=False)):
+        kind = j % 4
+        if kind == 0:
+            table[e, 0] = 0
+        elif kind == 1:
+            table[e, 0] = F
+        elif kind == 2:
+            table[e, 1 + int(rng.integers(0, table[e, 0]))] = n_instances
+        else:
+            table[e, 1 + int(rng.integers(0, table[e, 0]))] = -1
+    return table
+
+
+@pytest.mark.parametrize("F", [2, 3, 8, 9, 20, 65])
+def test_update_expert_wide_tables(F):
+    """Replica slots beyond the first eight words of a row take a second load
+    in the kernel; all slots, malformed rows, pruning and a prefix mask
+    against the oracle, with the error bits."""
+    m = M()
+    rng = np.random.default_rng(4000 + F)
+    Bs, K, n_logical, n_inst = 512, 8, 96, 1024
+    say(f"[parity] update_expert F={F}")
+    table = wide_table(rng, n_logical, F, n_inst, bad_rows=0 if F == 2 else 6)
+    ids = rng.integers(0, n_logical, (Bs, K)).astype(np.int32)
+    ids[7, 3] = n_logical  # a logical id out of range
+    scores = rng.random((Bs, K), dtype=np.float32)
+    thr = (rng.random(K, dtype=np.float32) * 0.3).astype(np.float32)
+    scores[7, 3] = 1.0  # the out-of-range id stays kept, so its error bit is raised
+    tmask = (np.arange(Bs) < 449).astype(np.uint8)
+    for use_prune, use_mask in ((False, False), (True, True)):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        gi, gm = m.moe_update_expert(
+            cuda(torch.from_numpy(ids)), cuda(torch.from_numpy(table)), n_inst,
+            expert_scales=cuda(torch.from_numpy(scores)) if use_prune else None,
+            prune_thr=cuda(torch.from_numpy(thr)) if use_prune else None,
+            token_mask=cuda(torch.from_numpy(tmask)) if use_mask else None, dev_err=err)
+        oi, om, oe = oracle.update_expert(ids, scores if use_prune else None, table,
+                                          thr if use_prune else None,
+                                          tmask if use_mask else None, n_inst)
+        np.testing.assert_array_equal(np_(gi), oi)
+        np.testing.assert_array_equal(np_(gm), om)
+        assert int(err.item()) == oe
+        assert oe & 1

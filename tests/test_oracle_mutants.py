@@ -26,7 +26,8 @@ MUTANTS = [
     ("scan_short_total", "offsets[e + 1] = offsets[e] + counts[e];",
      "offsets[e + 1] = offsets[e] + counts[e] - (e == E - 1 && counts[e] > 0);"),
     ("histogram_drops_first", "counts[ids[f]] += 1;", "counts[ids[f]] += (f > 0);"),
-    ("int8_truncate", "float r = nearbyintf(v);", "float r = truncf(v);"),
+    ("int8_truncate", "float r = (v != v) ? 0.0f : nearbyintf(v);",
+     "float r = (v != v) ? 0.0f : truncf(v);"),
     ("int8_scale_direction", "*scale = 1.0f / d;", "*scale = d;"),
     ("int8_no_abs", "float a = fabsf(bf16_value(x[j]));\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {",
      "float a = bf16_value(x[j]);\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {"),
