@@ -12,13 +12,17 @@
 //                K times.
 // The row of entry f with instance id e is offsets[e] plus the number of
 // active entries before f with the same id (a stable counting sort).  Each
-// token block derives it on its own from two LDS histograms of all N = Bs*K
+// token block derives it on its own from LDS histograms of all N = Bs*K
 // entries (at most 8192 four-byte ids, read with 16-byte loads from L2): one
-// over every entry, one over the entries before its token.  offsets[e] is
-// then a sum over the smaller ids, the earlier same-id count is one LDS read
-// plus the token's own duplicates.  This replaces a serial routing kernel
-// between two launches with a little redundant LDS work that overlaps the HBM
-// load of the token's row.  Nothing depends on scheduling: bitwise repeatable.
+// over every entry and one over the entries before its token, packed as the
+// low and high 16 bits of one counter (each count is at most 8192), so each
+// entry costs one LDS atomic.  An in-place exclusive scan of the low halves
+// gives offsets[e]; one lane per entry of the token then adds the high half
+// and the token's own earlier duplicates.  This replaces a serial routing
+// kernel between two launches with redundant LDS work that overlaps the HBM
+// load of the token's row.  (Two tokens per block, sharing the histograms,
+// measured slower: one block per compute unit hides less latency than two.)
+// Nothing depends on scheduling: bitwise repeatable.
 //
 // Row layout: one thread owns 16 consecutive elements (two 16-byte loads of
 // bf16), so a 32-element mxfp8 block is a lane pair and a 128-element int8
@@ -35,6 +39,7 @@
 namespace moe {
 
 constexpr int kHistSlots = 1024;  // one LDS counter per instance (E <= 1024)
+constexpr int kPreOne = 0x10001;  // packed counter increment: all (low) and before-token (high)
 
 // Where the entries come from: [Bs, K] instance ids and an optional mask.
 struct Entries {
@@ -309,20 +314,48 @@ __device__ __forceinline__ void code_store(const DispatchArgs &a, int t, bool ha
     }
 }
 
+// Exclusive scan of the low 16 bits of s[0, n) in place by the whole block,
+// keeping the high 16 bits (s_wave: one int per wave).  Each thread owns a
+// contiguous run of counters.  Ends with a barrier.
+__device__ void block_exclusive_scan_lo16(int *s, int n, int *s_wave)
+{
+    const int t = threadIdx.x, T = blockDim.x;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
+    const int per = (n + T - 1) / T;
+    const int e0 = min(t * per, n), e1 = min(e0 + per, n);
+    int local = 0;
+    for (int e = e0; e < e1; ++e)
+        local += s[e] & 0xffff;
+    const int incl = wave_incl_scan(local);
+    if (lane == kWave - 1)
+        s_wave[w] = incl;
+    lds_barrier();
+    int run = incl - local;
+    for (int j = 0; j < nw; ++j)
+        run += j < w ? s_wave[j] : 0;
+    for (int e = e0; e < e1; ++e) {
+        const int c = s[e];
+        s[e] = run | (c & ~0xffff);
+        run += c & 0xffff;
+    }
+    lds_barrier();
+}
+
 template <int MODE, int KMAX>
 __global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
 {
-    __shared__ int s_hist[kHistSlots];
-    __shared__ int s_pre[kHistSlots];
-    __shared__ int s_part[kMaxWaves][KMAX / 2 + 1];
+    // low 16 bits: active entries with id e; high: those before this token.
+    // After the scan the low half holds offsets[e].
+    __shared__ int s_cnt[kHistSlots];
+    __shared__ int s_wave[kMaxWaves];
     __shared__ int s_rank[KMAX];
-    __shared__ uint32_t s_amax;
+    __shared__ uint32_t s_wmax[kMaxWaves];
 
     const int Bs = a.Bs, H = a.H, K = a.K, E = a.E;
     const int N = Bs * K;
     const Entries s{a.ids, a.mask, E};
     if (blockIdx.x == 0) {
-        route_summary(a, s, s_hist, &s_part[0][0]);
+        route_summary(a, s, s_cnt, s_wave);
         return;
     }
     const int i = blockIdx.x - 1;
@@ -337,27 +370,18 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
     const int raw_id = a.ids[f0 + kk];
     const uint8_t *mp = a.mask ? a.mask : reinterpret_cast<const uint8_t *>(a.ids);
     const uint8_t raw_on = mp[f0 + kk];
-    for (int e = t; e < E; e += T) {
-        s_hist[e] = 0;
-        s_pre[e] = 0;
-    }
+    for (int e = t; e < E; e += T)
+        s_cnt[e] = 0;
 
-    // 2. stable rows of the token's entries.  Row of entry f with id e:
-    //    offsets[e] (active entries with a smaller id) + active entries g < f
-    //    with id e.  Both come from two LDS histograms of the active ids, one
-    //    over all entries and one over the entries before this token.  The
-    //    token's row (16 elements per thread) is loaded after the first batch
-    //    of ids, so it stays in flight while the histograms are built.
+    // 2. the packed histograms.  The token's row (16 elements per thread) is
+    //    loaded after the first batch of ids, so it stays in flight meanwhile.
     uint4 xa, xb;
     int err = 0;
     for_each_entry(
         s, N, err,
         [&](int inst, bool on, int g) {
-            if (on) {
-                atomicAdd(&s_hist[inst], 1);
-                if (g < f0)
-                    atomicAdd(&s_pre[inst], 1);
-            }
+            if (on)
+                atomicAdd(&s_cnt[inst], g < f0 ? kPreOne : 1);
         },
         [&] {
             const uint4 *src =
@@ -369,75 +393,43 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
     const bool my_on =
         lane < K && (a.mask == nullptr || raw_on != 0) && (unsigned)raw_id < (unsigned)E;
     const int my_id = my_on ? raw_id : -1;
-    int tid[KMAX];  // instance id of each of the token's entries, -1 if inactive
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        tid[k] = k < K ? __builtin_amdgcn_readlane(my_id, k) : -1;
     lds_barrier();
-    int cnt[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-        cnt[k] = 0;
-    for (int e = t; e < E; e += T) {
-        const int c = s_hist[e];
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-            cnt[k] += e < tid[k] ? c : 0;
-    }
+    block_exclusive_scan_lo16(s_cnt, E, s_wave);
 
-    // 3. block sums: two 16-bit counters per word (each sum <= 8192)
-    constexpr int P = KMAX / 2;
-    int pk[P];
+    // 3. rows of the token's entries (wave 0, lane k = entry k)
+    if (w == 0) {
+        int dup = 0;  // earlier entries of this token with the same id
 #pragma unroll
-    for (int j = 0; j < P; ++j)
-        pk[j] = wave_sum_i32(cnt[2 * j] | (cnt[2 * j + 1] << 16));
-    uint32_t amax = 0;
-    if (MODE == 2) {
-        amax = wave_max_u32(amax_bits16(xa, xb));
-    }
-    if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < P; ++j)
-            s_part[w][j] = pk[j];
-        if (MODE == 2)
-            s_part[w][P] = (int)amax;
-    }
-    lds_barrier();
-    if (t < P) {
-        int sum = 0;
-        for (int j = 0; j < nw; ++j)
-            sum += s_part[j][t];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int k = 2 * t + h;
-            int dup = 0;  // earlier entries of this token with the same id
-#pragma unroll
-            for (int q = 0; q < KMAX; ++q)
-                dup += (q < k && tid[q] == tid[k]) ? 1 : 0;
-            const int off = h ? (sum >> 16) : (sum & 0xffff);
-            s_rank[k] = tid[k] < 0 ? -1 : off + s_pre[tid[k]] + dup;
+        for (int j = 0; j < KMAX; ++j) {
+            const int v = j < K ? __builtin_amdgcn_readlane(my_id, j) : -1;
+            dup += (j < lane && v == my_id) ? 1 : 0;
+        }
+        if (lane < K) {
+            const int c = my_on ? s_cnt[my_id] : 0;
+            const int r = my_on ? (c & 0xffff) + (c >> 16) + dup : -1;
+            s_rank[lane] = r;
+            a.assist_dst[f0 + lane] = r;
+            if (r >= 0)
+                a.expand_src[r] = f0 + lane;
         }
     }
-    if (MODE == 2 && t == P) {
-        uint32_t m = 0;
-        for (int j = 0; j < nw; ++j)
-            m = max(m, (uint32_t)s_part[j][P]);
-        s_amax = m;
+    if (MODE == 2) {  // per-token maximum: wave maxima, then across the waves
+        const uint32_t m = wave_max_u32(amax_bits16(xa, xb));
+        if (lane == 0)
+            s_wmax[w] = m;
     }
     lds_barrier();
+    uint32_t amax = 0;
+    if (MODE == 2) {
+        for (int j = 0; j < nw; ++j)
+            amax = max(amax, s_wmax[j]);
+    }
     int rank[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         rank[k] = k < K ? s_rank[k] : -1;
-    if (t < K) {
-        const int f = f0 + t;
-        const int r = s_rank[t];
-        a.assist_dst[f] = r;
-        if (r >= 0)
-            a.expand_src[r] = f;
-    }
 
-    code_store<MODE, KMAX>(a, t, has, xa, xb, rank, MODE == 2 ? s_amax : 0u);
+    code_store<MODE, KMAX>(a, t, has, xa, xb, rank, amax);
 }
 
 template <int MODE>

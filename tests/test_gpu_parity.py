@@ -72,6 +72,11 @@ SMALL = [
     (111, 512, 1024, 16, 1, 16, 2, 0, False, True, 300, False),
     (112, 1, 8192, 16, 128, 8, 3, 256, True, False, None, False),
     (113, 200, 1024, 2, 8, 128, 0, 0, False, True, None, True),
+    # Bs > 256: two tokens per dispatch block; odd Bs leaves the last block one token
+    (114, 301, 1056, 5, 3, 4, 2, 0, True, True, 280, False),
+    (115, 257, 8192, 16, 64, 16, 4, 0, False, True, None, False),
+    (116, 511, 2080, 3, 2, 3, 3, 32, True, False, None, True),
+    (117, 400, 7168, 8, 32, 8, 0, 0, False, True, None, False),
 ]
 
 
