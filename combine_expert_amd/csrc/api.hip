@@ -17,6 +17,7 @@ constexpr int kMaxK = 16;         // 0 < K <= 16
 constexpr int kMinH = 1024;       // combine page: H in [1024, 8192]
 constexpr int kMaxH = 8192;
 constexpr int kMaxExperts = 1024; // update-expert page: at most 1024 instances
+constexpr int kMaxStagedTable = 8192;  // table words a fused dispatch block stages in LDS (32 KB)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -63,14 +64,17 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
                                               static_cast<hipStream_t>(stream)));
 }
 
-int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask, int Bs,
-                 int H, int K, int n_ranks, int local_experts, int quant_mode, int tile,
-                 void *expand_x, void *expand_scales, int32_t *expert_counts,
-                 int32_t *expert_offsets, int32_t *expand_src, int32_t *assist_dst,
-                 int32_t *dev_err, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Checks shared by moe_dispatch and moe_update_dispatch.
+int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int n_ranks,
+                   int local_experts, int quant_mode, int tile, const void *expand_x,
+                   const void *expand_scales, const int32_t *counts, const int32_t *offsets,
+                   const int32_t *expand_src, const int32_t *assist_dst, const int32_t *dev_err)
 {
-    if (!x || !expert_ids || !expand_x || !expert_counts || !expert_offsets || !expand_src ||
-        !assist_dst)
+    if (!x || !ids || !expand_x || !counts || !offsets || !expand_src || !assist_dst)
         return MOE_EINVAL;
     if (bad_bs_k(Bs, K) || bad_h(H) || n_ranks < 1 || local_experts < 1)
         return MOE_EINVAL;
@@ -96,17 +100,67 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active
     default:
         return MOE_EINVAL;
     }
-    if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(expert_ids, 16) ||
-        (active_mask && !aligned(active_mask, 4)) || !aligned(expert_counts, 4) ||
-        !aligned(expert_offsets, 4) || !aligned(expand_src, 4) || !aligned(assist_dst, 4) ||
+    if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(ids, 16) || !aligned(counts, 4) ||
+        !aligned(offsets, 4) || !aligned(expand_src, 4) || !aligned(assist_dst, 4) ||
         (dev_err && !aligned(dev_err, 4)) ||
         ((quant_mode == MOE_Q_INT8_TOKEN || quant_mode == MOE_Q_INT8_TILE) &&
          !aligned(expand_scales, 4)))
         return MOE_EINVAL;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask, int Bs,
+                 int H, int K, int n_ranks, int local_experts, int quant_mode, int tile,
+                 void *expand_x, void *expand_scales, int32_t *expert_counts,
+                 int32_t *expert_offsets, int32_t *expand_src, int32_t *assist_dst,
+                 int32_t *dev_err, void *stream)
+{
+    const int rc = check_dispatch(x, expert_ids, Bs, H, K, n_ranks, local_experts, quant_mode,
+                                  tile, expand_x, expand_scales, expert_counts, expert_offsets,
+                                  expand_src, assist_dst, dev_err);
+    if (rc != MOE_OK)
+        return rc;
+    if (active_mask && !aligned(active_mask, 4))
+        return MOE_EINVAL;
     return from_hip(moe::launch_dispatch(
-        static_cast<const uint16_t *>(x), expert_ids, active_mask, Bs, H, K, (int)E, quant_mode,
-        quant_mode == MOE_Q_INT8_TILE ? tile : 0, expand_x, expand_scales, expert_counts,
-        expert_offsets, expand_src, assist_dst, dev_err, static_cast<hipStream_t>(stream)));
+        static_cast<const uint16_t *>(x), expert_ids, active_mask, Bs, H, K,
+        n_ranks * local_experts, quant_mode, quant_mode == MOE_Q_INT8_TILE ? tile : 0, expand_x,
+        expand_scales, expert_counts, expert_offsets, expand_src, assist_dst, dev_err,
+        static_cast<hipStream_t>(stream)));
+}
+
+int moe_update_dispatch(const void *x, const int32_t *expert_ids, const float *expert_scales,
+                        const int32_t *table, const float *prune_thr, const uint8_t *token_mask,
+                        int Bs, int H, int K, int n_logical, int F, int n_ranks,
+                        int local_experts, int quant_mode, int tile, int32_t *balanced_ids,
+                        uint8_t *balanced_mask, void *expand_x, void *expand_scales,
+                        int32_t *expert_counts, int32_t *expert_offsets, int32_t *expand_src,
+                        int32_t *assist_dst, int32_t *dev_err, void *stream)
+{
+    const int rc = check_dispatch(x, expert_ids, Bs, H, K, n_ranks, local_experts, quant_mode,
+                                  tile, expand_x, expand_scales, expert_counts, expert_offsets,
+                                  expand_src, assist_dst, dev_err);
+    if (rc != MOE_OK)
+        return rc;
+    if (!table || n_logical <= 0 || n_logical > kMaxExperts || K > n_logical || F < 2 ||
+        F > n_logical + 1)
+        return MOE_EINVAL;
+    if ((long long)n_logical * F > kMaxStagedTable)
+        return MOE_ENOTSUP;
+    const bool prune = expert_scales && prune_thr;
+    if (!aligned(table, 4) || (prune && !aligned(expert_scales, 16)) ||
+        (prune_thr && !aligned(prune_thr, 4)) || (balanced_ids && !aligned(balanced_ids, 4)))
+        return MOE_EINVAL;
+    return from_hip(moe::launch_update_dispatch(
+        static_cast<const uint16_t *>(x), expert_ids, expert_scales, table, prune_thr,
+        token_mask, n_logical, F, Bs, H, K, n_ranks * local_experts, quant_mode,
+        quant_mode == MOE_Q_INT8_TILE ? tile : 0, balanced_ids, balanced_mask, expand_x,
+        expand_scales, expert_counts, expert_offsets, expand_src, assist_dst, dev_err,
+        static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,

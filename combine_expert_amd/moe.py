@@ -21,7 +21,8 @@ QUANT_NONE, QUANT_STATIC, QUANT_INT8_TOKEN, QUANT_INT8_TILE, QUANT_MXFP8 = 0, 1,
 SHARED_PAGE, SHARED_ADD = 0, 1
 ERR_ID, ERR_TABLE, ERR_MASK1D, ERR_ROW = 1, 2, 4, 8
 
-EXPORTS = ("moe_update_expert", "moe_dispatch", "moe_combine_add_rmsnorm", "moe_status_string")
+EXPORTS = ("moe_update_expert", "moe_dispatch", "moe_update_dispatch", "moe_combine_add_rmsnorm",
+           "moe_status_string")
 
 if not os.path.exists(_build.LIB):
     raise ImportError(f"{_build.LIB} is not built: run `python -m combine_expert_amd.build`")
@@ -31,9 +32,12 @@ _P, _I = C.c_void_p, C.c_int
 _lib.moe_update_expert.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
 _lib.moe_dispatch.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
                               _P, _P]
+_lib.moe_update_dispatch.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                                     _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_combine_add_rmsnorm.argtypes = [_P, _P, _P, _P, _P, _P, C.c_float, _I, _I, _I, _I,
                                          _P, _P, _P, _P, _P]
-for _f in (_lib.moe_update_expert, _lib.moe_dispatch, _lib.moe_combine_add_rmsnorm):
+for _f in (_lib.moe_update_expert, _lib.moe_dispatch, _lib.moe_update_dispatch,
+           _lib.moe_combine_add_rmsnorm):
     _f.restype = C.c_int
 _lib.moe_status_string.argtypes = [_I]
 _lib.moe_status_string.restype = C.c_char_p
@@ -132,6 +136,34 @@ def moe_dispatch(x, expert_ids, n_ranks: int, local_experts: int, quant_mode: in
                            _ptr(out["expert_offsets"]), _ptr(out["expand_src"]),
                            _ptr(out["assist_dst"]), _ptr(dev_err), _stream(stream))
     _check("moe_dispatch", rc)
+    return out
+
+
+def moe_update_dispatch(x, expert_ids, table, n_ranks: int, local_experts: int,
+                        quant_mode: int = 0, tile: int = 0, expert_scales=None, prune_thr=None,
+                        token_mask=None, balanced_ids=None, balanced_mask=None,
+                        out: Optional[dict] = None, dev_err=None, stream=None) -> dict:
+    """Expert mapping + dispatch in one launch; returns the dispatch outputs
+    plus 'balanced_ids' / 'balanced_mask' (allocated unless passed in)."""
+    Bs, H = x.shape
+    K = expert_ids.shape[1]
+    n_logical, F = table.shape
+    if out is None:
+        out = dispatch_buffers(Bs, H, K, n_ranks * local_experts, quant_mode, tile, x.device)
+    if balanced_ids is None:
+        balanced_ids = torch.empty((Bs, K), dtype=torch.int32, device=x.device)
+    if balanced_mask is None:
+        balanced_mask = torch.empty((Bs, K), dtype=torch.uint8, device=x.device)
+    rc = _lib.moe_update_dispatch(_ptr(x), _ptr(expert_ids), _ptr(expert_scales), _ptr(table),
+                                  _ptr(prune_thr), _ptr(token_mask), Bs, H, K, n_logical, F,
+                                  n_ranks, local_experts, quant_mode, tile, _ptr(balanced_ids),
+                                  _ptr(balanced_mask), _ptr(out["expand_x"]),
+                                  _ptr(out.get("expand_scales")), _ptr(out["expert_counts"]),
+                                  _ptr(out["expert_offsets"]), _ptr(out["expand_src"]),
+                                  _ptr(out["assist_dst"]), _ptr(dev_err), _stream(stream))
+    _check("moe_update_dispatch", rc)
+    out["balanced_ids"] = balanced_ids
+    out["balanced_mask"] = balanced_mask
     return out
 
 

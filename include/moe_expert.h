@@ -152,6 +152,35 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active
                  int32_t *dev_err, void *stream);
 
 /*
+ * moe_update_dispatch -- moe_update_expert followed by moe_dispatch in one
+ * launch (the pages' fixed calling sequence UpdateExpert -> DispatchV2).
+ *
+ * Same results as
+ *   moe_update_expert(expert_ids, expert_scales, table, prune_thr, token_mask,
+ *                     Bs, K, n_logical, F, n_ranks * local_experts, ids', mask', ...)
+ *   moe_dispatch(x, ids', mask', Bs, H, K, n_ranks, local_experts, quant_mode, tile, ...)
+ * with the intermediate ids' / mask' written to balanced_ids / balanced_mask
+ * when those are non-NULL, and dev_err collecting the bits of both calls.
+ * Every dispatch block maps the entries it counts through an LDS copy of the
+ * table, which saves the second launch.
+ *
+ *   expert_ids    int32 [Bs, K]  logical ids (16-byte aligned)
+ *   expert_scales f32   [Bs, K] or NULL (16-byte aligned when prune_thr is given)
+ *   table, prune_thr, token_mask, n_logical, F: as moe_update_expert
+ *   balanced_ids  int32 [Bs, K] or NULL (out); balanced_mask u8 [Bs, K] or NULL (out)
+ *   the rest: as moe_dispatch.
+ * Limits: those of both calls, and n_logical * F <= 8192 (the table a block
+ * stages in LDS); a larger table returns MOE_ENOTSUP (make the two calls).
+ */
+int moe_update_dispatch(const void *x, const int32_t *expert_ids, const float *expert_scales,
+                        const int32_t *table, const float *prune_thr, const uint8_t *token_mask,
+                        int Bs, int H, int K, int n_logical, int F, int n_ranks,
+                        int local_experts, int quant_mode, int tile, int32_t *balanced_ids,
+                        uint8_t *balanced_mask, void *expand_x, void *expand_scales,
+                        int32_t *expert_counts, int32_t *expert_offsets, int32_t *expand_src,
+                        int32_t *assist_dst, int32_t *dev_err, void *stream);
+
+/*
  * moe_combine_add_rmsnorm -- weighted gather of expert outputs, shared
  * expert and residual add, RMSNorm ("aclnnMoeDistributeCombineAddRmsNorm"
  * 计算公式: combineOut = Sum(expertScales*ataOut + expertScales*sharedExpertX),

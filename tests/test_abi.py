@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["moe_combine_add_rmsnorm", "moe_dispatch",
-                                    "moe_status_string", "moe_update_expert"]
+                                    "moe_status_string", "moe_update_dispatch",
+                                    "moe_update_expert"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -130,3 +131,29 @@ def test_update_expert_rejects_out_of_range_arguments():
            dict(sc=P + 1), dict(thr=P + 3)]
     for kw in bad:
         assert update(**kw) == 1, kw
+
+
+def fused(**kw):
+    from combine_expert_amd import moe
+    a = dict(x=P, ids=P, sc=None, t=P, thr=None, tm=None, Bs=512, H=8192, K=16, nl=512, F=3,
+             R=64, L=16, q=3, tile=128, bi=None, bm=None, ex=P, esc=P, cnt=P, off=P, src=P,
+             asg=P, err=None)
+    a.update(kw)
+    return moe.raw().moe_update_dispatch(a["x"], a["ids"], a["sc"], a["t"], a["thr"], a["tm"],
+                                         a["Bs"], a["H"], a["K"], a["nl"], a["F"], a["R"],
+                                         a["L"], a["q"], a["tile"], a["bi"], a["bm"], a["ex"],
+                                         a["esc"], a["cnt"], a["off"], a["src"], a["asg"],
+                                         a["err"], None)
+
+
+@pytest.mark.skipif("not _no_gpu()")
+def test_fused_update_dispatch_rejects_out_of_range_arguments():
+    bad = [dict(Bs=0), dict(K=17), dict(H=7168 + 16), dict(t=None), dict(nl=0), dict(nl=1025),
+           dict(nl=8, K=16), dict(F=1), dict(F=514), dict(R=0), dict(R=65), dict(x=None),
+           dict(ids=None), dict(ids=P + 4), dict(sc=P + 4, thr=P), dict(thr=P + 1),
+           dict(bi=P + 2), dict(q=3, tile=0), dict(q=7), dict(asg=None)]
+    for kw in bad:
+        assert fused(**kw) == 1, kw
+    # a table too large to stage in LDS, static quantisation, odd tiles: not supported
+    for kw in (dict(nl=1024, F=13, K=16), dict(q=1), dict(q=3, tile=96)):
+        assert fused(**kw) == 2, kw
