@@ -5,6 +5,13 @@ expert + residual + RMSNorm, on the DeepSeek-V3-shaped workload
 (Bs=512 tokens, H=7168, 256 expert instances = 32 ranks x 8, top-8,
 Zipf(1.2) routing, one shared expert).
 
+A step is the pages' calling sequence, three launches: moe_update_expert,
+moe_dispatch, moe_combine_add_rmsnorm.  The same step with the mapping fused
+into the dispatch (moe_update_dispatch, then the combine) is timed as well and
+reported under "step_fused"; on its own the fused launch is faster than the
+two it replaces, but back to back with the combine the three-call sequence
+measured slightly faster.
+
     python bench.py [--steps 500] [--warmup 50] [--sets 5] [--cpu-seconds 10]
     python bench.py --copy-mb 256                        # copy kernel for counter scaling
     python bench.py --summarize-trace STATS.csv --out profiles/X.md --command CMD
@@ -107,7 +114,10 @@ def algorithmic_bytes(Bs, H, K, E, rows, n_logical, F, quant_mode, n_scale, shar
     cmb = (rows * H * 2 + 2 * N * 4               # expert rows, assist, scales
            + (Bs * H * 2 if shared else 0) + Bs * H * 2 + H * 2   # shared, residual, gamma
            + 2 * Bs * H * 2 + Bs * 4)             # y, x_out, rstd
-    return dict(update_expert=upd, dispatch=dsp, combine=cmb)
+    # fused mapping + dispatch: logical ids and the table in, mapped ids and mask
+    # out, then the dispatch traffic without re-reading the mapped ids and mask
+    fused = upd + dsp - (N * 4 + N)
+    return dict(update_expert=upd, dispatch=dsp, update_dispatch=fused, combine=cmb)
 
 
 def source_digest(*names):
@@ -224,10 +234,15 @@ def step_args(wl, s, stream):
            wl.local_experts, wl.quant_mode, wl.tile, p(d["expand_x"]), p(d["expand_scales"]),
            p(d["expert_counts"]), p(d["expert_offsets"]), p(d["expand_src"]),
            p(d["assist_dst"]), None, stream)
+    fused = (p(s["x"]), p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.H, wl.K,
+             n_logical, F, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile,
+             p(s["bal_ids"]), p(s["bal_mask"]), p(d["expand_x"]), p(d["expand_scales"]),
+             p(d["expert_counts"]), p(d["expert_offsets"]), p(d["expand_src"]),
+             p(d["assist_dst"]), None, stream)
     cmb = (p(s["eout"]), p(d["assist_dst"]), p(s["scales"]), p(s["shared"]), p(s["residual"]),
            p(s["gamma"]), wl.eps, wl.Bs, wl.H, wl.K, wl.shared_mode, p(s["y"]), p(s["x_out"]),
            p(s["rstd"]), None, stream)
-    return upd, dsp, cmb
+    return upd, dsp, fused, cmb
 
 
 def check_parity(wl, s, oracle, np):
@@ -311,22 +326,36 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     lib = moe.raw()
-    f_upd, f_dsp, f_cmb = lib.moe_update_expert, lib.moe_dispatch, lib.moe_combine_add_rmsnorm
+    fns = (lib.moe_update_expert, lib.moe_dispatch, lib.moe_update_dispatch,
+           lib.moe_combine_add_rmsnorm)
+    UPD, DSP, FUSED, CMB = range(4)
+    STEP, FUSED_STEP = (UPD, DSP, CMB), (FUSED, CMB)
 
     sets = [make_set(wl, torch, moe) for _ in range(args.sets)]
     argv = [step_args(wl, s, sp) for s in sets]
     torch.cuda.synchronize()
 
-    def run_steps(n):
+    def run_steps(n, calls):
         for k in range(n):
-            a_u, a_d, a_c = argv[k % len(argv)]
-            if f_upd(*a_u) | f_dsp(*a_d) | f_cmb(*a_c):
+            a = argv[k % len(argv)]
+            rc = 0
+            for c in calls:
+                rc |= fns[c](*a[c])
+            if rc:
                 raise RuntimeError("a library call returned a non-zero status")
+
+    def timed_steps(n, calls):
+        """Exactly n steps, synchronised on both sides."""
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(n, calls)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
 
     def kernel_us(which, n):
         """Average launch duration of one kernel: HIP events on the launch stream
         bracket n back-to-back launches that rotate over the buffer sets."""
-        f = (f_upd, f_dsp, f_cmb)[which]
+        f = fns[which]
         for k in range(len(argv)):
             f(*argv[k][which])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -337,35 +366,41 @@ def main():
         e1.synchronize()
         return e0.elapsed_time(e1) * 1e3 / n
 
-    run_steps(args.warmup)
+    run_steps(args.warmup, FUSED_STEP)
+    run_steps(args.warmup, STEP)
     torch.cuda.synchronize()
     ok = True
     if not args.no_check:
         import oracle
         ok = check_parity(wl, sets[0], oracle, np)
 
-    # timed region: exactly K steps, synchronised on both sides
+    # timed region: exactly K steps (mapping, dispatch, combine)
     K = args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(K)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    t_step = timed_steps(K, STEP)
+    t_fused = timed_steps(K, FUSED_STEP)  # the same step with the fused launch
 
     # per-kernel launch durations (the dominant kernel's feeds the roofline)
     n_k = max(K, 100)
-    us_upd, us_dsp, us_cmb = (kernel_us(j, n_k) for j in range(3))
+    us = [kernel_us(j, n_k) for j in range(4)]
     rows = int(sets[0]["d"]["expert_offsets"][-1].item())
     nb = algorithmic_bytes(wl.Bs, wl.H, wl.K, wl.E, rows, wl.table.shape[0], wl.table.shape[1],
                            wl.quant_mode, moe.n_scale_entries(wl.quant_mode, wl.H, wl.tile),
                            shared=True)
-    step_bytes = sum(nb.values())
-    t_step = wall / K
+    step_bytes = nb["update_expert"] + nb["dispatch"] + nb["combine"]
     gbs = step_bytes / t_step / 1e9
-    a_cmb = nb["combine"] / (us_cmb * 1e-6) / 1e9
-    a_dsp = nb["dispatch"] / (us_dsp * 1e-6) / 1e9
-    a_upd = nb["update_expert"] / (us_upd * 1e-6) / 1e9
+    fused_bytes = nb["update_dispatch"] + nb["combine"]
+    gbs_f = fused_bytes / t_fused / 1e9
+    names = ("update_expert", "dispatch", "update_dispatch", "combine")
+    rate = {n: nb[n] / (u * 1e-6) / 1e9 for n, u in zip(names, us)}
+    us_cmb = us[CMB]
+    a_cmb = rate["combine"]
 
+    # HBM bytes per launch from the committed counter summaries (null when the
+    # kernel source changed since they were taken)
+    traffic = {"update_dispatch": counter_traffic("update_dispatch_c3_traffic.txt",
+                                                  ("dispatch.hip", "device.h")),
+               "dispatch": counter_traffic("dispatch_c3_traffic.txt", ("dispatch.hip", "device.h")),
+               "combine": counter_traffic("combine_c3_traffic.txt", ("combine.hip", "device.h"))}
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -389,20 +424,16 @@ def main():
         "roofline": {
             "kernel": "k_combine", "bound": "hbm", "achieved": round(a_cmb, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(a_cmb / HBM_PEAK_GBS, 4),
-            "traffic": counter_traffic("combine_c3_traffic.txt", ("combine.hip", "device.h")),
+            "traffic": traffic["combine"],
             "algorithmic_bytes_per_launch": nb["combine"],
             "avg_launch_us": round(us_cmb, 3),
         },
         "kernels": {
-            "update_expert": {"avg_us": round(us_upd, 3), "bytes": nb["update_expert"],
-                              "GBps": round(a_upd, 1)},
-            "dispatch": {"avg_us": round(us_dsp, 3), "bytes": nb["dispatch"],
-                         "GBps": round(a_dsp, 1), "frac": round(a_dsp / HBM_PEAK_GBS, 4),
-                         "traffic": counter_traffic("dispatch_c3_traffic.txt",
-                                                    ("dispatch.hip", "device.h"))},
-            "combine": {"avg_us": round(us_cmb, 3), "bytes": nb["combine"],
-                        "GBps": round(a_cmb, 1), "frac": round(a_cmb / HBM_PEAK_GBS, 4)},
-        },
+            n: {"avg_us": round(u, 3), "bytes": nb[n], "GBps": round(rate[n], 1),
+                "frac": round(rate[n] / HBM_PEAK_GBS, 4), "traffic": traffic.get(n)}
+            for n, u in zip(names, us)},
+        "step_fused": {"ms_per_step": round(t_fused * 1e3, 5), "GBps": round(gbs_f, 2),
+                       "tokens_per_s": round(wl.Bs / t_fused, 1), "bytes": fused_bytes},
         "step_bytes": step_bytes,
         "parity_step0": "ok" if ok else "MISMATCH",
         "cpu_baseline": None,

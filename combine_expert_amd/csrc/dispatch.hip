@@ -596,7 +596,7 @@ __device__ void block_exclusive_scan_lo16(int *s, int n, int *s_wave)
 }
 
 template <int MODE, int KMAX, typename Src>
-__global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
+__device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
 {
     // low 16 bits: active entries with id e; high: those before this token.
     // After the scan the low half holds offsets[e].
@@ -722,16 +722,39 @@ __global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
     code_store<MODE, KMAX>(a, t, has, xa, xb, rank, amax);
 }
 
+// routed entries (moe_dispatch)
+template <int MODE, int KMAX>
+__global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
+{
+    dispatch_body<MODE, KMAX, Routed>(a);
+}
+
+// mapped entries (moe_update_dispatch); KEEP: a token mask or thresholds
+template <int MODE, int KMAX, bool KEEP>
+__global__ __launch_bounds__(kMaxThreads) void k_update_dispatch(DispatchArgs a)
+{
+    dispatch_body<MODE, KMAX, Mapped<KEEP>>(a);
+}
+
+template <int MODE, int KMAX, typename Src>
+static void launch_kernel(const DispatchArgs &a, hipStream_t stream)
+{
+    const dim3 grid(a.Bs + 1), block(row_threads(a.H));
+    if constexpr (Src::kMapped)
+        hipLaunchKernelGGL((k_update_dispatch<MODE, KMAX, Src::kKeep>), grid, block,
+                           (size_t)a.n_logical * a.F * sizeof(int), stream, a);
+    else
+        hipLaunchKernelGGL((k_dispatch<MODE, KMAX>), grid, block, 0, stream, a);
+}
+
 template <int MODE, typename Src>
 static hipError_t launch_dispatch_mode(int kmax, const DispatchArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.Bs + 1), block(row_threads(a.H));
-    const size_t lds = Src::kMapped ? (size_t)a.n_logical * a.F * sizeof(int) : 0;
     switch (kmax) {
-    case 2: hipLaunchKernelGGL((k_dispatch<MODE, 2, Src>), grid, block, lds, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_dispatch<MODE, 4, Src>), grid, block, lds, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_dispatch<MODE, 8, Src>), grid, block, lds, stream, a); break;
-    default: hipLaunchKernelGGL((k_dispatch<MODE, 16, Src>), grid, block, lds, stream, a); break;
+    case 2: launch_kernel<MODE, 2, Src>(a, stream); break;
+    case 4: launch_kernel<MODE, 4, Src>(a, stream); break;
+    case 8: launch_kernel<MODE, 8, Src>(a, stream); break;
+    default: launch_kernel<MODE, 16, Src>(a, stream); break;
     }
     return hipGetLastError();
 }
