@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline (0 = skip)")
     p.add_argument("--no-check", action="store_true", help="skip the parity check of step 0")
+    p.add_argument("--no-c5", dest="c5", action="store_false",
+                   help="skip the 16-layer graph-captured stack")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the step, time a plain device copy of this many MB "
                         "(the reference kernel for counter scaling and achievable bandwidth)")
@@ -245,6 +247,112 @@ def step_args(wl, s, stream):
     return upd, dsp, fused, cmb
 
 
+# ----------------------------------------------------------------- c5: a chained stack
+
+def make_stack(wls, torch, moe):
+    """Device buffers of a chained layer stack: layer l + 1 reads y_l as its
+    x and x_out_l as its residual (layer 0 reads the first workload's x and
+    residual)."""
+    dev = torch.device("cuda")
+    c = lambda t: None if t is None else t.contiguous().to(dev)
+    layers = []
+    for wl in wls:
+        s = dict(ids=c(wl.logical_ids), scales=c(wl.scales), table=c(wl.table),
+                 eout=c(wl.expert_out), shared=c(wl.shared), gamma=c(wl.gamma))
+        s["bal_ids"] = torch.empty((wl.Bs, wl.K), dtype=torch.int32, device=dev)
+        s["bal_mask"] = torch.empty((wl.Bs, wl.K), dtype=torch.uint8, device=dev)
+        s["d"] = moe.dispatch_buffers(wl.Bs, wl.H, wl.K, wl.E, wl.quant_mode, wl.tile, dev)
+        s["y"] = torch.empty((wl.Bs, wl.H), dtype=torch.bfloat16, device=dev)
+        s["x_out"] = torch.empty((wl.Bs, wl.H), dtype=torch.bfloat16, device=dev)
+        s["rstd"] = torch.empty((wl.Bs,), dtype=torch.float32, device=dev)
+        layers.append(s)
+    return dict(x0=c(wls[0].x), r0=c(wls[0].residual), layers=layers)
+
+
+def stack_calls(wls, st, lib, stream):
+    """(function, C-ABI arguments) of every launch of one pass over the stack."""
+    p = lambda t: None if t is None else t.data_ptr()
+    calls = []
+    for l, (wl, s) in enumerate(zip(wls, st["layers"])):
+        x = st["x0"] if l == 0 else st["layers"][l - 1]["y"]
+        res = st["r0"] if l == 0 else st["layers"][l - 1]["x_out"]
+        d = s["d"]
+        n_logical, F = wl.table.shape
+        calls.append((lib.moe_update_expert,
+                      (p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.K, n_logical, F,
+                       wl.E, p(s["bal_ids"]), p(s["bal_mask"]), None, stream)))
+        calls.append((lib.moe_dispatch,
+                      (p(x), p(s["bal_ids"]), p(s["bal_mask"]), wl.Bs, wl.H, wl.K, wl.n_ranks,
+                       wl.local_experts, wl.quant_mode, wl.tile, p(d["expand_x"]),
+                       p(d["expand_scales"]), p(d["expert_counts"]), p(d["expert_offsets"]),
+                       p(d["expand_src"]), p(d["assist_dst"]), None, stream)))
+        calls.append((lib.moe_combine_add_rmsnorm,
+                      (p(s["eout"]), p(d["assist_dst"]), p(s["scales"]), p(s["shared"]), p(res),
+                       p(s["gamma"]), wl.eps, wl.Bs, wl.H, wl.K, wl.shared_mode, p(s["y"]),
+                       p(s["x_out"]), p(s["rstd"]), None, stream)))
+    return calls
+
+
+def run_calls(calls):
+    for f, a in calls:
+        if f(*a):
+            raise RuntimeError("a library call returned a non-zero status")
+
+
+def capture_stack(wls, st, lib, torch):
+    """One HIP graph holding every launch of a pass over the stack (the calls
+    only enqueue kernels: no allocation, no memset, no host synchronisation)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_calls(stack_calls(wls, st, lib, side.cuda_stream))  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_calls(stack_calls(wls, st, lib, torch.cuda.current_stream().cuda_stream))
+    return g
+
+
+def time_stack(moe, torch, n_layers, replays, warmup):
+    """The c5 stack (16 c3-shaped layers, int8 per token, chained) captured in
+    one graph: microseconds per replay, per layer, and the stack's bytes."""
+    from combine_expert_amd import workloads as W
+    wls = W.make_c5_layers(n_layers)
+    st = make_stack(wls, torch, moe)
+    lib = moe.raw()
+    g = capture_stack(wls, st, lib, torch)
+    calls = stack_calls(wls, st, lib, torch.cuda.current_stream().cuda_stream)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / replays
+
+    t = timed(g.replay)
+    t_eager = timed(lambda: run_calls(calls))
+    total = 0
+    for wl, s in zip(wls, st["layers"]):
+        rows = int(s["d"]["expert_offsets"][-1].item())
+        nb = algorithmic_bytes(wl.Bs, wl.H, wl.K, wl.E, rows, wl.table.shape[0],
+                               wl.table.shape[1], wl.quant_mode,
+                               moe.n_scale_entries(wl.quant_mode, wl.H, wl.tile), shared=True)
+        total += nb["update_expert"] + nb["dispatch"] + nb["combine"]
+    Bs = wls[0].Bs
+    return {"layers": n_layers, "graph_replays": replays, "us_per_replay": round(t * 1e6, 2),
+            "us_per_layer": round(t * 1e6 / n_layers, 3),
+            "us_per_layer_eager": round(t_eager * 1e6 / n_layers, 3), "bytes": total,
+            "GBps": round(total / t / 1e9, 2),
+            "tokens_per_s_per_layer": round(Bs * n_layers / t, 1),
+            "workload": "16 chained layers of Bs=512 H=7168 K=8 E=256 (32 x 8), Zipf(1.2), "
+                        "int8 per token, 1 shared expert; x_{l+1} = y_l, residual_{l+1} = "
+                        "x_out_l; one HIP graph per pass"}
+
+
 def check_parity(wl, s, oracle, np):
     """Step-0 outputs against the oracle: routing/codes exact, y within tolerance."""
     oi, om, _ = oracle.update_expert(wl.logical_ids.numpy(), None, wl.table.numpy(), None, None,
@@ -395,6 +503,8 @@ def main():
     us_cmb = us[CMB]
     a_cmb = rate["combine"]
 
+    c5 = time_stack(moe, torch, 16, max(10, K // 10), 3) if args.c5 else None
+
     # HBM bytes per launch from the committed counter summaries (null when the
     # kernel source changed since they were taken)
     traffic = {"update_dispatch": counter_traffic("update_dispatch_c3_traffic.txt",
@@ -434,6 +544,7 @@ def main():
             for n, u in zip(names, us)},
         "step_fused": {"ms_per_step": round(t_fused * 1e3, 5), "GBps": round(gbs_f, 2),
                        "tokens_per_s": round(wl.Bs / t_fused, 1), "bytes": fused_bytes},
+        "c5_stack": c5,
         "step_bytes": step_bytes,
         "parity_step0": "ok" if ok else "MISMATCH",
         "cpu_baseline": None,
