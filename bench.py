@@ -158,14 +158,30 @@ def _median_counter(path, kernel, counter):
 
 
 def summarize_trace(args):
+    """Per-kernel statistics from kernel_stats.csv, with p10 / p50 / p90 of the
+    per-dispatch durations from the kernel_trace.csv beside it."""
     rows = list(csv.DictReader(open(args.summarize_trace)))
+    durs = {}
+    trace = args.summarize_trace.replace("kernel_stats.csv", "kernel_trace.csv")
+    if os.path.exists(trace):
+        for r in csv.DictReader(open(trace)):
+            durs.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def pct(v, q):
+        v = sorted(v)
+        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
     lines = [f"# {args.title}", "", "Command (from the repository root, on one MI355X):", "",
              "```", *args.command, "```", "",
-             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg us | p10 us | p50 us | p90 us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
+        d = durs.get(r["Name"], [])
+        p = [f"{pct(d, q):.3f}" if d else "-" for q in (0.1, 0.5, 0.9)]
         lines.append(f"| {r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
-                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
-                     f"{float(r['Percentage']):.1f}% |")
+                     f"{p[0]} | {p[1]} | {p[2]} | {float(r['MinNs']) / 1e3:.3f} | "
+                     f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f}% |")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -395,8 +411,15 @@ def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
         if time.perf_counter() >= t_end or len(times) >= 50:
             break
     t = statistics.median(times)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
     return {"value": round(step_bytes / t / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": model, "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": f"the full step (update + dispatch + combine) on all {wl.Bs} tokens of the "
                       f"workload, {len(times)} repetitions, median {t * 1e3:.1f} ms; "
                       f"{wl.Bs / t:.0f} tokens/s",

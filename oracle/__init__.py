@@ -37,10 +37,12 @@ def lib():
         L.oracle_update_expert.argtypes = [P, P, P, P, P, i, i, i, i, i, P, P, P]
         L.oracle_route.argtypes = [P, P, i, i, P, P, P, P, P]
         L.oracle_dispatch.argtypes = [P, P, P, i, i, i, i, i, i, i, P, P, P, P, P, P, P]
+        L.oracle_dispatch_scaled.argtypes = [P, P, P, i, i, i, i, i, i, i, P, i, P, P, P, P, P,
+                                             P, P]
         L.oracle_combine_add_rmsnorm.argtypes = [P, P, P, P, P, P, C.c_float, i, i, i, i,
                                                  P, P, P]
         for f in (L.oracle_update_expert, L.oracle_route, L.oracle_dispatch,
-                  L.oracle_combine_add_rmsnorm):
+                  L.oracle_dispatch_scaled, L.oracle_combine_add_rmsnorm):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -127,13 +129,18 @@ def route(ids, mask, E: int):
 
 
 def n_scales(quant_mode: int, H: int, tile: int) -> int:
-    return {0: 0, 2: 1, 3: -(-H // tile) if tile > 0 else 0, 4: H // 32}[quant_mode]
+    return {0: 0, 1: 0, 2: 1, 3: -(-H // tile) if tile > 0 else 0, 4: H // 32}[quant_mode]
+
+
+SCALES_NONE, SCALES_ONE, SCALES_ROW, SCALES_EXPERT = 0, 1, 2, 3
 
 
 def dispatch(x_bits, ids, mask, n_ranks: int, local_experts: int, quant_mode: int,
-             tile: int = 0):
+             tile: int = 0, qscales=None, qscales_kind: int = SCALES_NONE):
     """Returns dict(expand_x, scales, counts, offsets, src, assist, err).
-    Rows past offsets[E] are zero (never written)."""
+    Rows past offsets[E] are zero (never written).  quant_mode 1 (static) and
+    the scales input (qscales_kind: 1 = [1], 2 = [H], 3 = [E, H]) go through
+    oracle_dispatch_scaled."""
     x = _c(x_bits, np.uint16)
     Bs, H = x.shape
     ids = _c(ids, np.int32)
@@ -159,9 +166,16 @@ def dispatch(x_bits, ids, mask, n_ranks: int, local_experts: int, quant_mode: in
     src = np.empty(N, dtype=np.int32)
     assist = np.empty(N, dtype=np.int32)
     err = np.zeros(1, dtype=np.int32)
-    rc = lib().oracle_dispatch(_p(x), _p(ids), _p(mask), Bs, H, K, n_ranks, local_experts,
-                               quant_mode, tile, _p(ex), _p(sc), _p(counts), _p(offsets),
-                               _p(src), _p(assist), _p(err))
+    if quant_mode == 1 or qscales_kind != SCALES_NONE:
+        qs = _c(qscales, np.float32)
+        rc = lib().oracle_dispatch_scaled(_p(x), _p(ids), _p(mask), Bs, H, K, n_ranks,
+                                          local_experts, quant_mode, tile, _p(qs), qscales_kind,
+                                          _p(ex), _p(sc), _p(counts), _p(offsets), _p(src),
+                                          _p(assist), _p(err))
+    else:
+        rc = lib().oracle_dispatch(_p(x), _p(ids), _p(mask), Bs, H, K, n_ranks, local_experts,
+                                   quant_mode, tile, _p(ex), _p(sc), _p(counts), _p(offsets),
+                                   _p(src), _p(assist), _p(err))
     if rc:
         raise ValueError(f"oracle_dispatch rc={rc}")
     return dict(expand_x=ex, scales=sc, counts=counts, offsets=offsets, src=src,

@@ -14,21 +14,26 @@
  *         threshold broadcast over the batch, and the mapping-table format
  *         (column 0 = replica count > 0, columns 1.. = instance ids).
  *   [DSP] "aclnnMoeDistributeDispatchV2", 计算公式 (formula): case 1
- *         (quantMode 0, no quantisation), case 3 (quantMode 2, per-token
+ *         (quantMode 0, no quantisation), case 2 (quantMode 1, static), the
+ *         scales factor of cases 2-4, case 3 (quantMode 2, per-token
  *         dynamic int8), case 4 (quantMode 3, per-tile dynamic int8), case 5
  *         (quantMode 4, mxfp8), and the note that emax is the exponent of
  *         the target type's largest normal number; 约束说明 (constraints) for
- *         the 1-D / 2-D active mask.
+ *         the 1-D / 2-D active mask and the quantMode-dependent shapes of
+ *         the scales input.
  *   [CMB] "aclnnMoeDistributeCombineAddRmsNorm", 计算公式 (formula): the
  *         weighted sum of expert outputs and shared-expert output, the
  *         residual add and RMSNorm.
  *
- * Readings where the pages are silent or garbled (each also listed with its
- * reason in the design notes of this repository):
+ * Readings where the pages are silent or garbled:
  *   - instance ids are global: instance = rank * local_experts + local slot;
  *   - the replica used by token i is column 1 + (i mod replica count);
  *   - pruning keeps an entry unless score < threshold[k] (NaN is kept);
  *   - rows of one instance are ordered by ascending flat index f = i*K + k;
+ *   - static int8 (quantMode 1): the cast rounds half to even and saturates
+ *     to [-128, 127]; the scales input is one coefficient, one row of H
+ *     shared by all experts, or one row per instance ([E, H], indexed by the
+ *     instance a copy is sent to);
  *   - int8: dstTypeMax = 127, round half to even, clamp to [-127, 127],
  *     scale written = 1 / dynamicScales, all-zero segment -> codes 0, scale 0;
  *     if 127 / max overflows fp32 (max below about 3.7e-38), zero elements
@@ -112,13 +117,14 @@ static uint8_t e4m3_from_float(float v)
 
 /* ---------------------------------------------------------------- quantisers */
 
-/* [DSP] cases 3/4: dynamicScales = 127 / max|x| over the segment;
- * code = CastToInt8(x * dynamicScales); the scale sent is 1 / dynamicScales. */
-static void quant_int8_segment(const uint16_t *x, int n, int8_t *q, float *scale)
+/* [DSP] cases 3/4: dynamicScales = 127 / max|v| over the segment of fp32
+ * values v (xFp32 of the formula); code = CastToInt8(v * dynamicScales); the
+ * scale sent is 1 / dynamicScales. */
+static void quant_int8_values(const float *v, int n, int8_t *q, float *scale)
 {
     float m = 0.0f;
     for (int j = 0; j < n; ++j) {
-        float a = fabsf(bf16_value(x[j]));
+        float a = fabsf(v[j]);
         if (a > m)
             m = a;
     }
@@ -130,8 +136,8 @@ static void quant_int8_segment(const uint16_t *x, int n, int8_t *q, float *scale
     }
     float d = 127.0f / m;  /* +inf when m < 127 / FLT_MAX (a tiny subnormal maximum) */
     for (int j = 0; j < n; ++j) {
-        float v = bf16_value(x[j]) * d;
-        float r = (v != v) ? 0.0f : nearbyintf(v);  /* 0 * inf: a zero element stays 0 */
+        float w = v[j] * d;
+        float r = (w != w) ? 0.0f : nearbyintf(w);  /* 0 * inf: a zero element stays 0 */
         if (r > 127.0f)
             r = 127.0f;
         if (r < -127.0f)
@@ -139,6 +145,34 @@ static void quant_int8_segment(const uint16_t *x, int n, int8_t *q, float *scale
         q[j] = (int8_t)r;
     }
     *scale = 1.0f / d;
+}
+
+/* The same on bf16 input: xFp32 = CastToFp32(X) (exact). */
+static void quant_int8_segment(const uint16_t *x, int n, int8_t *q, float *scale)
+{
+    float *v = (float *)malloc((size_t)n * sizeof(float));
+    if (!v) {
+        *scale = -1.0f;  /* never happens at the sizes tested */
+        return;
+    }
+    for (int j = 0; j < n; ++j)
+        v[j] = bf16_value(x[j]);
+    quant_int8_values(v, n, q, scale);
+    free(v);
+}
+
+/* [DSP] case 2 (static): quantOut = Cast(xFp32, int8): the nearest integer,
+ * ties to even, saturated to [-128, 127]; NaN codes to 0. */
+static int8_t int8_cast(float v)
+{
+    if (v != v)
+        return 0;
+    float r = nearbyintf(v);
+    if (r > 127.0f)
+        r = 127.0f;
+    if (r < -128.0f)
+        r = -128.0f;
+    return (int8_t)r;
 }
 
 /* [DSP] case 5: sharedExp = floor(log2(max|x|)) - emax with emax = 8;
@@ -372,6 +406,73 @@ int oracle_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, 
     free(q);
     free(fs);
     free(bs);
+    return 0;
+}
+
+/* [DSP] cases 2-4 with the scales input: xFp32 = CastToFp32(X) * scales, then
+ *   quant_mode 1 (static):     code = Cast(xFp32, int8)            (int8_cast)
+ *   quant_mode 2 (per token):  the dynamic int8 quantiser on xFp32
+ *   quant_mode 3 (per tile):   the same per tile of `tile` elements
+ * The scale applied to element j of the copy of token i sent to instance e is
+ *   qscales_kind 0: none (1)    1: qscales[0]    2: qscales[j]
+ *   qscales_kind 3: qscales[e * H + j]   (one row per instance, [E, H])
+ * each one fp32 multiply.  Every (token, instance) copy is quantised on its
+ * own (with kinds 0-2 all copies of a token are equal).  Outputs as
+ * oracle_dispatch; quant_mode 1 writes no scales (expand_scales unused).
+ * quant_mode 1 needs qscales_kind >= 1; modes 0 and 4 are oracle_dispatch's. */
+int oracle_dispatch_scaled(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
+                           int H, int K, int n_ranks, int local_experts, int quant_mode,
+                           int tile, const float *qscales, int qscales_kind, void *expand_x,
+                           void *expand_scales, int32_t *counts, int32_t *offsets,
+                           int32_t *expand_src, int32_t *assist_dst, int32_t *err)
+{
+    if (Bs <= 0 || H <= 0 || K <= 0 || n_ranks <= 0 || local_experts <= 0)
+        return -1;
+    if (quant_mode < 1 || quant_mode > 3 || qscales_kind < 0 || qscales_kind > 3)
+        return -1;
+    if ((quant_mode == 1 && qscales_kind == 0) || (qscales_kind != 0 && qscales == NULL))
+        return -1;
+    if (quant_mode == 3 && tile <= 0)
+        return -1;
+    int E = n_ranks * local_experts, N = Bs * K;
+    int rc = oracle_route(ids, mask, N, E, counts, offsets, assist_dst, expand_src, err);
+    if (rc)
+        return rc;
+    int n_sc = quant_mode == 2 ? 1 : quant_mode == 3 ? (H + tile - 1) / tile : 0;
+    float *v = (float *)malloc((size_t)H * sizeof(float));
+    if (!v)
+        return -2;
+    for (int f = 0; f < N; ++f) {
+        int r = assist_dst[f];
+        if (r < 0)
+            continue;
+        int i = f / K, e = ids[f];
+        const uint16_t *xi = x + (size_t)i * H;
+        for (int j = 0; j < H; ++j) {
+            float s = 1.0f;
+            if (qscales_kind == 1)
+                s = qscales[0];
+            else if (qscales_kind == 2)
+                s = qscales[j];
+            else if (qscales_kind == 3)
+                s = qscales[(size_t)e * H + j];
+            v[j] = qscales_kind == 0 ? bf16_value(xi[j]) : bf16_value(xi[j]) * s;
+        }
+        int8_t *q = (int8_t *)expand_x + (size_t)r * H;
+        if (quant_mode == 1) {
+            for (int j = 0; j < H; ++j)
+                q[j] = int8_cast(v[j]);
+        } else if (quant_mode == 2) {
+            quant_int8_values(v, H, q, (float *)expand_scales + r);
+        } else {
+            for (int t = 0; t < n_sc; ++t) {
+                int n = H - t * tile < tile ? H - t * tile : tile;
+                quant_int8_values(v + (size_t)t * tile, n, q + (size_t)t * tile,
+                                  (float *)expand_scales + (size_t)r * n_sc + t);
+            }
+        }
+    }
+    free(v);
     return 0;
 }
 

@@ -26,11 +26,11 @@ MUTANTS = [
     ("scan_short_total", "offsets[e + 1] = offsets[e] + counts[e];",
      "offsets[e + 1] = offsets[e] + counts[e] - (e == E - 1 && counts[e] > 0);"),
     ("histogram_drops_first", "counts[ids[f]] += 1;", "counts[ids[f]] += (f > 0);"),
-    ("int8_truncate", "float r = (v != v) ? 0.0f : nearbyintf(v);",
-     "float r = (v != v) ? 0.0f : truncf(v);"),
+    ("int8_truncate", "float r = (w != w) ? 0.0f : nearbyintf(w);",
+     "float r = (w != w) ? 0.0f : truncf(w);"),
     ("int8_scale_direction", "*scale = 1.0f / d;", "*scale = d;"),
-    ("int8_no_abs", "float a = fabsf(bf16_value(x[j]));\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {",
-     "float a = bf16_value(x[j]);\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {"),
+    ("int8_no_abs", "float a = fabsf(v[j]);\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {",
+     "float a = v[j];\n        if (a > m)\n            m = a;\n    }\n    if (m == 0.0f) {"),
     ("int8_dst_max", "float d = 127.0f / m;", "float d = 128.0f / m;"),
     ("mx_emax", "se = ilogbf(m) - 8;", "se = ilogbf(m) - 7;"),
     ("mx_scale_direction", "*scale_byte = (uint8_t)(se + 127);", "*scale_byte = (uint8_t)(127 - se);"),
@@ -44,12 +44,22 @@ MUTANTS = [
     ("rms_mean_n_minus_1", "sqrt(ss / H + (double)eps)", "sqrt(ss / (H - 1) + (double)eps)"),
     ("eps_outside_sqrt", "1.0 / sqrt(ss / H + (double)eps)", "1.0 / (sqrt(ss / H) + (double)eps)"),
     ("gamma_dropped", "xf[h] * rstd * (double)bf16_value(gamma[h])", "xf[h] * rstd"),
+    ("static_clamp_symmetric", "if (r < -128.0f)\n        r = -128.0f;",
+     "if (r < -127.0f)\n        r = -127.0f;"),
+    ("static_truncate", "    float r = nearbyintf(v);\n    if (r > 127.0f)",
+     "    float r = truncf(v);\n    if (r > 127.0f)"),
+    ("expert_row_of_column", "s = qscales[(size_t)e * H + j];",
+     "s = qscales[(size_t)(f % K) * H + j];"),
+    ("smoothing_dropped", "v[j] = qscales_kind == 0 ? bf16_value(xi[j]) : bf16_value(xi[j]) * s;",
+     "v[j] = bf16_value(xi[j]);"),
+    ("static_row_index", "s = qscales[j];", "s = qscales[H - 1 - j];"),
     ("pruned_weight_counted", "int r = assist[i * K + k];\n            if (r < 0)\n                continue;\n            double s = scales[i * K + k];\n            ws += s;",
      "int r = assist[i * K + k];\n            double s = scales[i * K + k];\n            ws += s;\n            if (r < 0)\n                continue;"),
 ]
 
 PIN_FILES = ["tests/test_oracle_numbers.py", "tests/test_oracle_route.py",
-             "tests/test_oracle_dispatch_combine.py", "tests/test_golden.py"]
+             "tests/test_oracle_dispatch_combine.py", "tests/test_oracle_scaled.py",
+             "tests/test_golden.py"]
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])

@@ -1,0 +1,167 @@
+"""Pins of the oracle's scales input and static quantisation (CPU only).
+
+Dispatch page ("aclnnMoeDistributeDispatchV2"), 计算公式 case 2 (quantMode 1,
+static: xFp32 = CastToFp32(X) * scales, quantOut = Cast(xFp32, int8)) and the
+scales factor of cases 3-4; quantMode constraints for the shapes of the
+scales input (one coefficient, one row shared by all experts, one row per
+expert).
+
+Pinned against:
+- brute force: the static code of each element is the integer in
+  [-128, 127] nearest to the fp32 product (numpy float32 multiply), ties to
+  even, found by searching all 256 codes;
+- hand-worked ties, saturation and NaN;
+- special cases that reduce to the pinned unscaled quantisers: unit scales,
+  and power-of-two scales (codes unchanged, scale output multiplied by the
+  power exactly);
+- consistency: one row for all experts equals that row repeated per expert;
+  per-expert rows follow the instance each copy is sent to.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+CODES = np.arange(-128, 128, dtype=np.float64)
+
+
+def bf16_bits_of(a):
+    return oracle.bf16_bits(torch.from_numpy(np.asarray(a, dtype=np.float32)).bfloat16())
+
+
+def bf16_vals(bits):
+    return (np.asarray(bits).astype(np.uint32) << 16).view(np.float32)
+
+
+def brute_static(v):
+    """Nearest of the 256 int8 codes to each fp32 value, ties to the even code."""
+    v = np.asarray(v, dtype=np.float64).ravel()
+    dist = np.abs(v[:, None] - CODES[None, :])
+    best = dist.min(axis=1, keepdims=True)
+    cand = dist == best
+    even = (CODES.astype(np.int64) % 2 == 0)[None, :]
+    pick = np.where(cand & even, 1, 0) + np.where(cand, 1, 0)  # prefer even among ties
+    return CODES[pick.argmax(axis=1)].astype(np.int8)
+
+
+def case(seed, Bs=13, H=96, K=3, R=2, L=3, scale=1.0):
+    rng = np.random.default_rng(seed)
+    E = R * L
+    x = bf16_bits_of(rng.normal(0.0, scale, size=(Bs, H)))
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(Bs)]).astype(np.int32)
+    return rng, x, ids, E
+
+
+def scale_of(kind, qs, e, H):
+    if kind == 1:
+        return np.full(H, qs[0], dtype=np.float32)
+    if kind == 2:
+        return qs.astype(np.float32)
+    return qs[e].astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", [1, 2, 3])
+def test_static_codes_brute_force(kind):
+    rng, x, ids, E = case(71 + kind, scale=40.0)
+    Bs, H = x.shape
+    K = ids.shape[1]
+    qs = {1: rng.uniform(0.5, 4.0, size=1), 2: rng.uniform(0.2, 4.0, size=H),
+          3: rng.uniform(0.2, 4.0, size=(E, H))}[kind].astype(np.float32)
+    o = oracle.dispatch(x, ids, None, 2, 3, 1, 0, qs, kind)
+    assert o["scales"] is None
+    xv = bf16_vals(x)
+    for f in range(Bs * K):
+        i, e, r = f // K, ids.flat[f], o["assist"][f]
+        v = xv[i] * scale_of(kind, qs, e, H)  # numpy float32 product (IEEE)
+        np.testing.assert_array_equal(o["expand_x"][r], brute_static(v))
+
+
+def test_static_hand_worked():
+    vals = [0.5, 1.5, 2.5, -0.5, -2.5, 126.5, 127.5, -127.5, 129.0, -300.0, 3.25, -3.75]
+    want = [0, 2, 2, 0, -2, 126, 127, -128, 127, -128, 3, -4]
+    x = bf16_bits_of([vals + [0.0] * (32 - len(vals))])
+    assert np.array_equal(bf16_vals(x)[0, :len(vals)], np.float32(vals))  # exact in bf16
+    o = oracle.dispatch(x, np.array([[0]], np.int32), None, 1, 1, 1, 0,
+                        np.array([1.0], np.float32), 1)
+    assert o["expand_x"][0, :len(vals)].tolist() == want
+    nan = np.full((1, 32), 0x7FC0, dtype=np.uint16)
+    o = oracle.dispatch(nan, np.array([[0]], np.int32), None, 1, 1, 1, 0,
+                        np.array([1.0], np.float32), 1)
+    assert not o["expand_x"][0].any()
+
+
+def test_static_integers_pass_through():
+    # integer-valued inputs in [-128, 127] with scale 1 are their own codes
+    x = bf16_bits_of(np.arange(-128, 128, dtype=np.float32).reshape(2, 128))
+    ids = np.array([[0], [1]], np.int32)
+    o = oracle.dispatch(x, ids, None, 1, 2, 1, 0, np.ones(128, np.float32), 2)
+    got = np.concatenate([o["expand_x"][o["assist"][0]], o["expand_x"][o["assist"][1]]])
+    np.testing.assert_array_equal(got, np.arange(-128, 128).astype(np.int8))
+
+
+@pytest.mark.parametrize("mode,tile", [(2, 0), (3, 32), (3, 40)])
+@pytest.mark.parametrize("kind", [1, 2, 3])
+def test_unit_scales_reduce_to_unscaled(mode, tile, kind):
+    rng, x, ids, E = case(90 + kind + mode)
+    H = x.shape[1]
+    qs = {1: np.ones(1), 2: np.ones(H), 3: np.ones((E, H))}[kind].astype(np.float32)
+    a = oracle.dispatch(x, ids, None, 2, 3, mode, tile, qs, kind)
+    b = oracle.dispatch(x, ids, None, 2, 3, mode, tile)
+    for key in ("expand_x", "scales", "assist", "offsets", "src"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+@pytest.mark.parametrize("mode,tile", [(2, 0), (3, 32)])
+def test_power_of_two_expert_rows(mode, tile):
+    """Row e = 2^p(e): codes equal the unscaled ones, the scale sent is the
+    unscaled scale times 2^p(e) exactly."""
+    rng, x, ids, E = case(120 + mode)
+    H = x.shape[1]
+    K = ids.shape[1]
+    p = np.array([(e % 5) - 2 for e in range(E)])
+    qs = np.repeat(np.ldexp(1.0, p)[:, None], H, axis=1).astype(np.float32)
+    a = oracle.dispatch(x, ids, None, 2, 3, mode, tile, qs, 3)
+    b = oracle.dispatch(x, ids, None, 2, 3, mode, tile)
+    np.testing.assert_array_equal(a["expand_x"], b["expand_x"])
+    for f in range(ids.size):
+        r = a["assist"][f]
+        np.testing.assert_array_equal(a["scales"][r],
+                                      np.ldexp(b["scales"][r], p[ids.flat[f]]).astype(np.float32))
+
+
+@pytest.mark.parametrize("mode,tile", [(1, 0), (2, 0), (3, 32)])
+def test_row_equals_repeated_expert_rows(mode, tile):
+    rng, x, ids, E = case(140 + mode)
+    H = x.shape[1]
+    row = rng.uniform(0.25, 3.0, size=H).astype(np.float32)
+    a = oracle.dispatch(x, ids, None, 2, 3, mode, tile, row, 2)
+    b = oracle.dispatch(x, ids, None, 2, 3, mode, tile, np.tile(row, (E, 1)), 3)
+    np.testing.assert_array_equal(a["expand_x"], b["expand_x"])
+    if mode != 1:
+        np.testing.assert_array_equal(a["scales"], b["scales"])
+
+
+def test_dynamic_smoothing_brute_force():
+    """Per-token dynamic int8 on xFp32 = x * row(e): max over the copy, IEEE
+    float32 127 / max, codes by searching the codes in [-127, 127]."""
+    rng, x, ids, E = case(160)
+    Bs, H = x.shape
+    K = ids.shape[1]
+    qs = rng.uniform(0.1, 5.0, size=(E, H)).astype(np.float32)
+    o = oracle.dispatch(x, ids, None, 2, 3, 2, 0, qs, 3)
+    xv = bf16_vals(x)
+    for f in range(Bs * K):
+        i, e, r = f // K, ids.flat[f], o["assist"][f]
+        v = xv[i] * qs[e]
+        d = np.float32(127.0) / np.abs(v).max()
+        codes = brute_static(v * d)
+        assert np.abs(codes.astype(int)).max() <= 127
+        np.testing.assert_array_equal(o["expand_x"][r], codes)
+        assert o["scales"][r, 0] == np.float32(1.0) / d
+
+
+def test_rejects_static_without_scales():
+    rng, x, ids, E = case(170)
+    with pytest.raises(ValueError):
+        oracle.dispatch(x, ids, None, 2, 3, 1, 0)
