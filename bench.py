@@ -58,8 +58,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline (0 = skip)")
     p.add_argument("--no-check", action="store_true", help="skip the parity check of step 0")
-    p.add_argument("--no-c5", dest="c5", action="store_false",
-                   help="skip the 16-layer graph-captured stack")
+    p.add_argument("--c5", action="store_true",
+                   help="also time the 16-layer graph-captured stack (c5) and the dispatch "
+                        "variants (static and per-instance scales); off by default so that a "
+                        "kernel trace of the default run covers the headline step alone")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the step, time a plain device copy of this many MB "
                         "(the reference kernel for counter scaling and achievable bandwidth)")
@@ -249,11 +251,12 @@ def step_args(wl, s, stream):
     upd = (p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.K, n_logical, F, wl.E,
            p(s["bal_ids"]), p(s["bal_mask"]), None, stream)
     dsp = (p(s["x"]), p(s["bal_ids"]), p(s["bal_mask"]), wl.Bs, wl.H, wl.K, wl.n_ranks,
-           wl.local_experts, wl.quant_mode, wl.tile, p(d["expand_x"]), p(d["expand_scales"]),
+           wl.local_experts, wl.quant_mode, wl.tile, None, 0, p(d["expand_x"]),
+           p(d["expand_scales"]),
            p(d["expert_counts"]), p(d["expert_offsets"]), p(d["expand_src"]),
            p(d["assist_dst"]), None, stream)
     fused = (p(s["x"]), p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.H, wl.K,
-             n_logical, F, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile,
+             n_logical, F, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile, None, 0,
              p(s["bal_ids"]), p(s["bal_mask"]), p(d["expand_x"]), p(d["expand_scales"]),
              p(d["expert_counts"]), p(d["expert_offsets"]), p(d["expand_src"]),
              p(d["assist_dst"]), None, stream)
@@ -299,7 +302,7 @@ def stack_calls(wls, st, lib, stream):
                        wl.E, p(s["bal_ids"]), p(s["bal_mask"]), None, stream)))
         calls.append((lib.moe_dispatch,
                       (p(x), p(s["bal_ids"]), p(s["bal_mask"]), wl.Bs, wl.H, wl.K, wl.n_ranks,
-                       wl.local_experts, wl.quant_mode, wl.tile, p(d["expand_x"]),
+                       wl.local_experts, wl.quant_mode, wl.tile, None, 0, p(d["expand_x"]),
                        p(d["expand_scales"]), p(d["expert_counts"]), p(d["expert_offsets"]),
                        p(d["expand_src"]), p(d["assist_dst"]), None, stream)))
         calls.append((lib.moe_combine_add_rmsnorm,
@@ -367,6 +370,59 @@ def time_stack(moe, torch, n_layers, replays, warmup):
             "workload": "16 chained layers of Bs=512 H=7168 K=8 E=256 (32 x 8), Zipf(1.2), "
                         "int8 per token, 1 shared expert; x_{l+1} = y_l, residual_{l+1} = "
                         "x_out_l; one HIP graph per pass"}
+
+
+# ----------------------------------------------------------------- dispatch variants
+
+VARIANTS = [  # (quant mode, scales kind, tile) at the c3 shapes
+    (1, 1, 0), (1, 2, 0), (1, 3, 0), (2, 0, 0), (2, 3, 0), (3, 0, 128), (3, 3, 128)]
+
+
+def dispatch_variant_bytes(Bs, H, K, E, rows, mode, kind, tile):
+    """Algorithmic bytes of one dispatch: the scales input read once, int8 rows."""
+    N = Bs * K
+    qs = {0: 0, 1: 4, 2: H * 4, 3: E * H * 4}[kind]
+    sc = {1: 0, 2: 4, 3: 4 * -(-H // tile) if tile else 0}[mode]
+    return (Bs * H * 2 + N * 4 + N + qs + rows * H + rows * sc + E * 4 + (E + 1) * 4 + 2 * N * 4)
+
+
+def dispatch_variants(moe, torch, n, sets=5):
+    """Per-launch duration (HIP events around n back-to-back launches over
+    rotating buffer sets) of moe_dispatch in the static and scaled modes."""
+    from combine_expert_amd import workloads as W
+    out = []
+    for mode, kind, tile in VARIANTS:
+        wl = W.make_c3(seed=3200 + mode, quant_mode=mode, with_expert_out=False)
+        wl.tile = tile
+        dev = torch.device("cuda")
+        qs = W.make_quant_scales(3300 + mode * 10 + kind, kind, wl.E, wl.H)
+        qs = None if qs is None else qs.to(dev)
+        ids = wl.logical_ids.to(dev)  # identity table: logical ids are instance ids
+        bufs = [(wl.x.to(dev), moe.dispatch_buffers(wl.Bs, wl.H, wl.K, wl.E, mode, tile, dev))
+                for _ in range(sets)]
+        stream = torch.cuda.current_stream()
+        f = moe.raw().moe_dispatch
+        p = lambda t: None if t is None else t.data_ptr()
+        argv = [(p(x), p(ids), None, wl.Bs, wl.H, wl.K, wl.n_ranks, wl.local_experts, mode, tile,
+                 p(qs), kind, p(d["expand_x"]), p(d["expand_scales"]), p(d["expert_counts"]),
+                 p(d["expert_offsets"]), p(d["expand_src"]), p(d["assist_dst"]), None,
+                 stream.cuda_stream) for x, d in bufs]
+        for a in argv:
+            if f(*a):
+                raise RuntimeError("moe_dispatch returned a non-zero status")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(n):
+            f(*argv[k % sets])
+        e1.record(stream)
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        rows = int(bufs[0][1]["expert_offsets"][-1].item())
+        nb = dispatch_variant_bytes(wl.Bs, wl.H, wl.K, wl.E, rows, mode, kind, tile)
+        out.append({"quant_mode": mode, "scales": ["none", "one", "row", "per-instance"][kind],
+                    "tile": tile, "avg_us": round(us, 3), "bytes": nb,
+                    "GBps": round(nb / (us * 1e-6) / 1e9, 1)})
+    return out
 
 
 def check_parity(wl, s, oracle, np):
@@ -527,12 +583,13 @@ def main():
     a_cmb = rate["combine"]
 
     c5 = time_stack(moe, torch, 16, max(10, K // 10), 3) if args.c5 else None
+    variants = dispatch_variants(moe, torch, max(K // 5, 50)) if args.c5 else None
 
     # HBM bytes per launch from the committed counter summaries (null when the
     # kernel source changed since they were taken)
-    traffic = {"update_dispatch": counter_traffic("update_dispatch_c3_traffic.txt",
-                                                  ("dispatch.hip", "device.h")),
-               "dispatch": counter_traffic("dispatch_c3_traffic.txt", ("dispatch.hip", "device.h")),
+    dsp_src = ("dispatch_impl.h", "dispatch.hip", "device.h")
+    traffic = {"update_dispatch": counter_traffic("update_dispatch_c3_traffic.txt", dsp_src),
+               "dispatch": counter_traffic("dispatch_c3_traffic.txt", dsp_src),
                "combine": counter_traffic("combine_c3_traffic.txt", ("combine.hip", "device.h"))}
     line = {
         "metric": METRIC,
@@ -568,6 +625,7 @@ def main():
         "step_fused": {"ms_per_step": round(t_fused * 1e3, 5), "GBps": round(gbs_f, 2),
                        "tokens_per_s": round(wl.Bs / t_fused, 1), "bytes": fused_bytes},
         "c5_stack": c5,
+        "dispatch_variants": variants,
         "step_bytes": step_bytes,
         "parity_step0": "ok" if ok else "MISMATCH",
         "cpu_baseline": None,

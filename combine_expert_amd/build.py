@@ -31,25 +31,50 @@ def headers():
     return sorted(glob.glob(os.path.join(CSRC, "*.h"))) + [os.path.join(INCLUDE, "moe_expert.h")]
 
 
-def command(out: str):
-    return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Wall", "-Wno-unused-command-line-argument",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INCLUDE, "-I", CSRC, "-o", out, *sources()]
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Wno-unused-command-line-argument", "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops"]
+OBJDIR = os.path.join(PKG, "_build")
+
+
+def _filter(text: str) -> str:
+    return "\n".join(line for line in text.splitlines()
+                     if "packed-fp32-ops" not in line and "not a recognized feature" not in line)
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    return r.returncode, _filter(r.stdout + r.stderr)
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip to an object (in parallel: the dispatch kernels
+    are split by quantisation mode across several files), then link the
+    shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = []
+    for src in sources():
+        obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
+        jobs.append((src, obj, [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        results = list(ex.map(lambda j: (j, _run(j[2])), jobs))
+    for (src, _, cmd), (rc, out) in results:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{out}")
+        if verbose and out.strip():
+            print(out)
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = command(tmp)
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+            *[j[1] for j in jobs]]
+    rc, out = _run(link)
     if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in line and "not a recognized feature" not in line)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
-    if verbose and out.strip():
-        print(out)
+        print(" ".join(link), flush=True)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{out}")
     os.replace(tmp, LIB)
     return LIB
 

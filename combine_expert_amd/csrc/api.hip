@@ -70,9 +70,10 @@ namespace {
 
 // Checks shared by moe_dispatch and moe_update_dispatch.
 int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int n_ranks,
-                   int local_experts, int quant_mode, int tile, const void *expand_x,
-                   const void *expand_scales, const int32_t *counts, const int32_t *offsets,
-                   const int32_t *expand_src, const int32_t *assist_dst, const int32_t *dev_err)
+                   int local_experts, int quant_mode, int tile, const float *qs, int qs_kind,
+                   const void *expand_x, const void *expand_scales, const int32_t *counts,
+                   const int32_t *offsets, const int32_t *expand_src,
+                   const int32_t *assist_dst, const int32_t *dev_err)
 {
     if (!x || !ids || !expand_x || !counts || !offsets || !expand_src || !assist_dst)
         return MOE_EINVAL;
@@ -81,11 +82,36 @@ int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int 
     const long long E = (long long)n_ranks * local_experts;
     if (E > kMaxExperts || K > E)
         return MOE_EINVAL;
+    // the scales input: its shape must be one the mode takes (quantMode
+    // constraints of the dispatch page), and present iff named
+    if (qs_kind < MOE_SCALES_NONE || qs_kind > MOE_SCALES_EXPERT ||
+        (qs_kind == MOE_SCALES_NONE) != (qs == nullptr))
+        return MOE_EINVAL;
+    if ((qs_kind == MOE_SCALES_ROW || qs_kind == MOE_SCALES_EXPERT) ? !aligned(qs, 16)
+                                                                     : (qs && !aligned(qs, 4)))
+        return MOE_EINVAL;
     switch (quant_mode) {
     case MOE_Q_NONE:
+    case MOE_Q_MXFP8:
+        if (qs_kind != MOE_SCALES_NONE)
+            return MOE_EINVAL;
         break;
     case MOE_Q_STATIC:
-        return MOE_ENOTSUP;
+        if (qs_kind == MOE_SCALES_NONE)
+            return MOE_EINVAL;
+        break;
+    case MOE_Q_INT8_TOKEN:
+    case MOE_Q_INT8_TILE:
+        if (qs_kind != MOE_SCALES_NONE && qs_kind != MOE_SCALES_EXPERT)
+            return MOE_EINVAL;
+        break;
+    default:
+        return MOE_EINVAL;
+    }
+    switch (quant_mode) {
+    case MOE_Q_NONE:
+    case MOE_Q_STATIC:
+        break;
     case MOE_Q_INT8_TOKEN:
     case MOE_Q_MXFP8:
         if (!expand_scales)
@@ -115,35 +141,36 @@ extern "C" {
 
 int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask, int Bs,
                  int H, int K, int n_ranks, int local_experts, int quant_mode, int tile,
-                 void *expand_x, void *expand_scales, int32_t *expert_counts,
-                 int32_t *expert_offsets, int32_t *expand_src, int32_t *assist_dst,
-                 int32_t *dev_err, void *stream)
+                 const float *quant_scales, int quant_scales_kind, void *expand_x,
+                 void *expand_scales, int32_t *expert_counts, int32_t *expert_offsets,
+                 int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err, void *stream)
 {
     const int rc = check_dispatch(x, expert_ids, Bs, H, K, n_ranks, local_experts, quant_mode,
-                                  tile, expand_x, expand_scales, expert_counts, expert_offsets,
-                                  expand_src, assist_dst, dev_err);
+                                  tile, quant_scales, quant_scales_kind, expand_x, expand_scales,
+                                  expert_counts, expert_offsets, expand_src, assist_dst, dev_err);
     if (rc != MOE_OK)
         return rc;
     if (active_mask && !aligned(active_mask, 4))
         return MOE_EINVAL;
     return from_hip(moe::launch_dispatch(
         static_cast<const uint16_t *>(x), expert_ids, active_mask, Bs, H, K,
-        n_ranks * local_experts, quant_mode, quant_mode == MOE_Q_INT8_TILE ? tile : 0, expand_x,
-        expand_scales, expert_counts, expert_offsets, expand_src, assist_dst, dev_err,
-        static_cast<hipStream_t>(stream)));
+        n_ranks * local_experts, quant_mode, quant_mode == MOE_Q_INT8_TILE ? tile : 0,
+        quant_scales, quant_scales_kind, expand_x, expand_scales, expert_counts, expert_offsets,
+        expand_src, assist_dst, dev_err, static_cast<hipStream_t>(stream)));
 }
 
 int moe_update_dispatch(const void *x, const int32_t *expert_ids, const float *expert_scales,
                         const int32_t *table, const float *prune_thr, const uint8_t *token_mask,
                         int Bs, int H, int K, int n_logical, int F, int n_ranks,
-                        int local_experts, int quant_mode, int tile, int32_t *balanced_ids,
-                        uint8_t *balanced_mask, void *expand_x, void *expand_scales,
-                        int32_t *expert_counts, int32_t *expert_offsets, int32_t *expand_src,
-                        int32_t *assist_dst, int32_t *dev_err, void *stream)
+                        int local_experts, int quant_mode, int tile, const float *quant_scales,
+                        int quant_scales_kind, int32_t *balanced_ids, uint8_t *balanced_mask,
+                        void *expand_x, void *expand_scales, int32_t *expert_counts,
+                        int32_t *expert_offsets, int32_t *expand_src, int32_t *assist_dst,
+                        int32_t *dev_err, void *stream)
 {
     const int rc = check_dispatch(x, expert_ids, Bs, H, K, n_ranks, local_experts, quant_mode,
-                                  tile, expand_x, expand_scales, expert_counts, expert_offsets,
-                                  expand_src, assist_dst, dev_err);
+                                  tile, quant_scales, quant_scales_kind, expand_x, expand_scales,
+                                  expert_counts, expert_offsets, expand_src, assist_dst, dev_err);
     if (rc != MOE_OK)
         return rc;
     if (!table || n_logical <= 0 || n_logical > kMaxExperts || K > n_logical || F < 2 ||
@@ -158,7 +185,8 @@ int moe_update_dispatch(const void *x, const int32_t *expert_ids, const float *e
     return from_hip(moe::launch_update_dispatch(
         static_cast<const uint16_t *>(x), expert_ids, expert_scales, table, prune_thr,
         token_mask, n_logical, F, Bs, H, K, n_ranks * local_experts, quant_mode,
-        quant_mode == MOE_Q_INT8_TILE ? tile : 0, balanced_ids, balanced_mask, expand_x,
+        quant_mode == MOE_Q_INT8_TILE ? tile : 0, quant_scales, quant_scales_kind,
+        balanced_ids, balanced_mask, expand_x,
         expand_scales, expert_counts, expert_offsets, expand_src, assist_dst, dev_err,
         static_cast<hipStream_t>(stream)));
 }

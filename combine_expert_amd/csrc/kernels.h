@@ -13,19 +13,19 @@ hipError_t launch_update_expert(const int32_t *ids, const float *scores, const i
                                 uint8_t *out_mask, int32_t *dev_err, hipStream_t stream);
 
 hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
-                           int H, int K, int E, int quant_mode, int tile, void *expand_x,
-                           void *expand_scales, int32_t *counts, int32_t *offsets,
-                           int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err,
-                           hipStream_t stream);
+                           int H, int K, int E, int quant_mode, int tile, const float *qs,
+                           int qs_kind, void *expand_x, void *expand_scales, int32_t *counts,
+                           int32_t *offsets, int32_t *expand_src, int32_t *assist_dst,
+                           int32_t *dev_err, hipStream_t stream);
 
 hipError_t launch_update_dispatch(const uint16_t *x, const int32_t *ids, const float *scores,
                                   const int32_t *table, const float *thr,
                                   const uint8_t *token_mask, int n_logical, int F, int Bs, int H,
-                                  int K, int E, int quant_mode, int tile,
-                                  int32_t *balanced_ids, uint8_t *balanced_mask, void *expand_x,
-                                  void *expand_scales, int32_t *counts, int32_t *offsets,
-                                  int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err,
-                                  hipStream_t stream);
+                                  int K, int E, int quant_mode, int tile, const float *qs,
+                                  int qs_kind, int32_t *balanced_ids, uint8_t *balanced_mask,
+                                  void *expand_x, void *expand_scales, int32_t *counts,
+                                  int32_t *offsets, int32_t *expand_src, int32_t *assist_dst,
+                                  int32_t *dev_err, hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t *expert_out, const int32_t *assist,
                           const float *scales, const uint16_t *shared,

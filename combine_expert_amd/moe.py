@@ -18,6 +18,7 @@ from . import build as _build
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ELAUNCH = 0, 1, 2, 3
 QUANT_NONE, QUANT_STATIC, QUANT_INT8_TOKEN, QUANT_INT8_TILE, QUANT_MXFP8 = 0, 1, 2, 3, 4
+SCALES_NONE, SCALES_ONE, SCALES_ROW, SCALES_EXPERT = 0, 1, 2, 3
 SHARED_PAGE, SHARED_ADD = 0, 1
 ERR_ID, ERR_TABLE, ERR_MASK1D, ERR_ROW = 1, 2, 4, 8
 
@@ -30,10 +31,10 @@ if not os.path.exists(_build.LIB):
 _lib = C.CDLL(_build.LIB)
 _P, _I = C.c_void_p, C.c_int
 _lib.moe_update_expert.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
-_lib.moe_dispatch.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P,
-                              _P, _P]
+_lib.moe_dispatch.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P,
+                              _P, _P, _P, _P]
 _lib.moe_update_dispatch.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
-                                     _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+                                     _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_combine_add_rmsnorm.argtypes = [_P, _P, _P, _P, _P, _P, C.c_float, _I, _I, _I, _I,
                                          _P, _P, _P, _P, _P]
 for _f in (_lib.moe_update_expert, _lib.moe_dispatch, _lib.moe_update_dispatch,
@@ -80,6 +81,8 @@ def n_scale_entries(quant_mode: int, H: int, tile: int = 0) -> int:
     """Scale entries per expand_x row for a quantisation mode."""
     if quant_mode == QUANT_INT8_TOKEN:
         return 1
+    if quant_mode == QUANT_STATIC:
+        return 0
     if quant_mode == QUANT_INT8_TILE:
         return -(-H // tile)
     if quant_mode == QUANT_MXFP8:
@@ -109,7 +112,7 @@ def dispatch_buffers(Bs: int, H: int, K: int, E: int, quant_mode: int, tile: int
                      device="cuda"):
     """Allocate the dispatch outputs for a shape (capacity Bs*K rows)."""
     N = Bs * K
-    dt = {QUANT_NONE: torch.bfloat16, QUANT_INT8_TOKEN: torch.int8,
+    dt = {QUANT_NONE: torch.bfloat16, QUANT_STATIC: torch.int8, QUANT_INT8_TOKEN: torch.int8,
           QUANT_INT8_TILE: torch.int8, QUANT_MXFP8: torch.uint8}[quant_mode]
     ns = n_scale_entries(quant_mode, H, tile)
     sdt = torch.uint8 if quant_mode == QUANT_MXFP8 else torch.float32
@@ -123,15 +126,30 @@ def dispatch_buffers(Bs: int, H: int, K: int, E: int, quant_mode: int, tile: int
     )
 
 
+def scales_kind(quant_scales, H: int, E: int) -> int:
+    """The shape name of a scales tensor: [1], [H] or [E, H]."""
+    if quant_scales is None:
+        return SCALES_NONE
+    if quant_scales.dim() == 2 and tuple(quant_scales.shape) == (E, H):
+        return SCALES_EXPERT
+    if quant_scales.dim() == 1 and quant_scales.numel() == H:
+        return SCALES_ROW
+    if quant_scales.numel() == 1:
+        return SCALES_ONE
+    raise ValueError(f"scales of shape {tuple(quant_scales.shape)}: expected [1], [H] or [E, H]")
+
+
 def moe_dispatch(x, expert_ids, n_ranks: int, local_experts: int, quant_mode: int = 0,
-                 tile: int = 0, active_mask=None, out: Optional[dict] = None, dev_err=None,
-                 stream=None) -> dict:
+                 tile: int = 0, active_mask=None, quant_scales=None,
+                 out: Optional[dict] = None, dev_err=None, stream=None) -> dict:
     Bs, H = x.shape
     K = expert_ids.shape[1]
+    E = n_ranks * local_experts
     if out is None:
-        out = dispatch_buffers(Bs, H, K, n_ranks * local_experts, quant_mode, tile, x.device)
+        out = dispatch_buffers(Bs, H, K, E, quant_mode, tile, x.device)
     rc = _lib.moe_dispatch(_ptr(x), _ptr(expert_ids), _ptr(active_mask), Bs, H, K, n_ranks,
-                           local_experts, quant_mode, tile, _ptr(out["expand_x"]),
+                           local_experts, quant_mode, tile, _ptr(quant_scales),
+                           scales_kind(quant_scales, H, E), _ptr(out["expand_x"]),
                            _ptr(out.get("expand_scales")), _ptr(out["expert_counts"]),
                            _ptr(out["expert_offsets"]), _ptr(out["expand_src"]),
                            _ptr(out["assist_dst"]), _ptr(dev_err), _stream(stream))
@@ -141,8 +159,9 @@ def moe_dispatch(x, expert_ids, n_ranks: int, local_experts: int, quant_mode: in
 
 def moe_update_dispatch(x, expert_ids, table, n_ranks: int, local_experts: int,
                         quant_mode: int = 0, tile: int = 0, expert_scales=None, prune_thr=None,
-                        token_mask=None, balanced_ids=None, balanced_mask=None,
-                        out: Optional[dict] = None, dev_err=None, stream=None) -> dict:
+                        token_mask=None, quant_scales=None, balanced_ids=None,
+                        balanced_mask=None, out: Optional[dict] = None, dev_err=None,
+                        stream=None) -> dict:
     """Expert mapping + dispatch in one launch; returns the dispatch outputs
     plus 'balanced_ids' / 'balanced_mask' (allocated unless passed in)."""
     Bs, H = x.shape
@@ -156,7 +175,9 @@ def moe_update_dispatch(x, expert_ids, table, n_ranks: int, local_experts: int,
         balanced_mask = torch.empty((Bs, K), dtype=torch.uint8, device=x.device)
     rc = _lib.moe_update_dispatch(_ptr(x), _ptr(expert_ids), _ptr(expert_scales), _ptr(table),
                                   _ptr(prune_thr), _ptr(token_mask), Bs, H, K, n_logical, F,
-                                  n_ranks, local_experts, quant_mode, tile, _ptr(balanced_ids),
+                                  n_ranks, local_experts, quant_mode, tile, _ptr(quant_scales),
+                                  scales_kind(quant_scales, H, n_ranks * local_experts),
+                                  _ptr(balanced_ids),
                                   _ptr(balanced_mask), _ptr(out["expand_x"]),
                                   _ptr(out.get("expand_scales")), _ptr(out["expert_counts"]),
                                   _ptr(out["expert_offsets"]), _ptr(out["expand_src"]),

@@ -273,3 +273,15 @@ def identity_bias_expert(expand_x: torch.Tensor, offsets: torch.Tensor,
     inst = torch.searchsorted(off[1:E + 1], r, right=True)
     out[:total] = (expand_x[:total].float().cpu() + bias[inst].float()).to(torch.bfloat16)
     return out
+
+
+def make_quant_scales(seed: int, kind: int, E: int, H: int, lo: float = 0.25,
+                      hi: float = 4.0) -> Optional[torch.Tensor]:
+    """Seeded scales input of the dispatch: kind 1 -> f32 [1], 2 -> [H] (one
+    row shared by the experts), 3 -> [E, H] (one row per instance); values
+    uniform in [lo, hi).  kind 0 -> None."""
+    if kind == 0:
+        return None
+    rng = np.random.default_rng(seed)
+    shape = {1: (1,), 2: (H,), 3: (E, H)}[kind]
+    return torch.from_numpy(rng.uniform(lo, hi, size=shape).astype(np.float32))

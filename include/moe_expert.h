@@ -48,14 +48,25 @@ typedef enum {
     MOE_ELAUNCH = 3   /* the HIP runtime rejected a kernel launch */
 } moe_status;
 
-/* Dispatch quantisation modes (dispatch page 计算公式 cases 1, 3, 4, 5). */
+/* Dispatch quantisation modes (dispatch page 计算公式 cases 1-5). */
 typedef enum {
     MOE_Q_NONE = 0,        /* expand_x rows are bit copies of x (bf16)                  */
-    MOE_Q_STATIC = 1,      /* static quantisation: not implemented -> MOE_ENOTSUP       */
+    MOE_Q_STATIC = 1,      /* static int8: code = sat(round_half_even(x * scales))     */
     MOE_Q_INT8_TOKEN = 2,  /* per-token dynamic int8                                    */
     MOE_Q_INT8_TILE = 3,   /* per-tile dynamic int8 ("pertile" / "pergroup")            */
     MOE_Q_MXFP8 = 4        /* mxfp8: E4M3 codes, one E8M0 exponent per 32 elements      */
 } moe_quant;
+
+/* Shape of the dispatch's scales input (dispatch page 计算公式: xFp32 =
+ * CastToFp32(X) * scales in cases 2-4; quantMode constraints for the shapes).
+ * A device pointer carries no shape, so the caller names it. */
+typedef enum {
+    MOE_SCALES_NONE = 0,   /* no scales input (scales pointer NULL)                     */
+    MOE_SCALES_ONE = 1,    /* f32 [1]: one coefficient (static mode only)                */
+    MOE_SCALES_ROW = 2,    /* f32 [H]: one row shared by all experts (static mode only)  */
+    MOE_SCALES_EXPERT = 3  /* f32 [E, H]: one row per instance, picked by the instance a
+                              copy is sent to; every copy is then quantised on its own */
+} moe_scales_kind;
 
 /* Weight of the shared-expert output in the combine (combine page 计算公式). */
 typedef enum {
@@ -119,9 +130,13 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *   assist_dst[f]     = row of entry f: offsets[id] + number of active g < f
  *                       with the same id (stable, ascending f); -1 if inactive
  *   expand_src[r]     = entry placed in row r; -1 for r >= offsets[E]
- *   expand_x[r]       = token i = f / K, coded once per token:
+ *   expand_x[r]       = token i = f / K sent to instance e = id of f, coded
+ *                       from v = x[i] (no scales) or v = x[i] * s (one fp32
+ *                       multiply per element; s by quant_scales_kind):
  *     MOE_Q_NONE       bf16 [N, H] bit copy of x[i]
- *     MOE_Q_INT8_TOKEN int8 [N, H]: m = max|x[i]|, d = 127/m (fp32, IEEE),
+ *     MOE_Q_STATIC     int8 [N, H]: code = clamp(round_half_even(v), -128, 127),
+ *                      NaN -> 0; no expand_scales (may be NULL)
+ *     MOE_Q_INT8_TOKEN int8 [N, H]: m = max|v|, d = 127/m (fp32, IEEE),
  *                      code = clamp(round_half_even(x*d), -127, 127);
  *                      expand_scales f32 [N] = 1/d  (m == 0: codes 0, scale 0)
  *     MOE_Q_INT8_TILE  the same per tile of `tile` elements along H (the last
@@ -137,8 +152,12 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *   x              bf16 [Bs, H]
  *   expert_ids     int32 [Bs, K]     instance ids (e.g. balanced_ids)
  *   active_mask    u8 [Bs, K] or NULL (e.g. balanced_mask)
+ *   quant_scales   f32, shape by quant_scales_kind (16-byte aligned for ROW and
+ *                  EXPERT), or NULL with MOE_SCALES_NONE.  MOE_Q_STATIC takes
+ *                  ONE, ROW or EXPERT; MOE_Q_INT8_TOKEN / _TILE take NONE or
+ *                  EXPERT; MOE_Q_NONE and MOE_Q_MXFP8 take NONE (else MOE_EINVAL).
  *   expand_x       [N, H] elements of the mode's type (out)
- *   expand_scales  see above; NULL for MOE_Q_NONE (out)
+ *   expand_scales  see above; NULL for MOE_Q_NONE and MOE_Q_STATIC (out)
  *   expert_counts  int32 [E]  (out)      expert_offsets int32 [E+1] (out)
  *   expand_src     int32 [N]  (out)      assist_dst     int32 [N]   (out)
  *   dev_err        int32 [1] or NULL
@@ -147,9 +166,9 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  */
 int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask,
                  int Bs, int H, int K, int n_ranks, int local_experts, int quant_mode,
-                 int tile, void *expand_x, void *expand_scales, int32_t *expert_counts,
-                 int32_t *expert_offsets, int32_t *expand_src, int32_t *assist_dst,
-                 int32_t *dev_err, void *stream);
+                 int tile, const float *quant_scales, int quant_scales_kind, void *expand_x,
+                 void *expand_scales, int32_t *expert_counts, int32_t *expert_offsets,
+                 int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err, void *stream);
 
 /*
  * moe_update_dispatch -- moe_update_expert followed by moe_dispatch in one
@@ -175,7 +194,8 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active
 int moe_update_dispatch(const void *x, const int32_t *expert_ids, const float *expert_scales,
                         const int32_t *table, const float *prune_thr, const uint8_t *token_mask,
                         int Bs, int H, int K, int n_logical, int F, int n_ranks,
-                        int local_experts, int quant_mode, int tile, int32_t *balanced_ids,
+                        int local_experts, int quant_mode, int tile, const float *quant_scales,
+                        int quant_scales_kind, int32_t *balanced_ids,
                         uint8_t *balanced_mask, void *expand_x, void *expand_scales,
                         int32_t *expert_counts, int32_t *expert_offsets, int32_t *expand_src,
                         int32_t *assist_dst, int32_t *dev_err, void *stream);

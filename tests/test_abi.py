@@ -60,12 +60,12 @@ P = 0x10000  # a 16-byte aligned stand-in address; never dereferenced by these c
 
 def dispatch(**kw):
     from combine_expert_amd import moe
-    a = dict(x=P, ids=P, mask=None, Bs=512, H=7168, K=8, R=32, L=8, q=4, tile=0, ex=P, sc=P,
-             cnt=P, off=P, src=P, asg=P, err=None)
+    a = dict(x=P, ids=P, mask=None, Bs=512, H=7168, K=8, R=32, L=8, q=4, tile=0, qs=None, qk=0,
+             ex=P, sc=P, cnt=P, off=P, src=P, asg=P, err=None)
     a.update(kw)
     return moe.raw().moe_dispatch(a["x"], a["ids"], a["mask"], a["Bs"], a["H"], a["K"], a["R"],
-                                  a["L"], a["q"], a["tile"], a["ex"], a["sc"], a["cnt"],
-                                  a["off"], a["src"], a["asg"], a["err"], None)
+                                  a["L"], a["q"], a["tile"], a["qs"], a["qk"], a["ex"], a["sc"],
+                                  a["cnt"], a["off"], a["src"], a["asg"], a["err"], None)
 
 
 def combine(**kw):
@@ -103,10 +103,15 @@ def test_dispatch_rejects_out_of_range_arguments():
            dict(x=None), dict(ids=None), dict(ex=None), dict(cnt=None), dict(off=None),
            dict(src=None), dict(asg=None), dict(q=2, sc=None), dict(q=4, sc=None),
            dict(q=3, tile=128, sc=None), dict(q=3, tile=0), dict(x=P + 8), dict(ex=P + 4),
-           dict(ids=P + 4), dict(q=2, sc=P + 2), dict(mask=P + 1)]
+           dict(ids=P + 4), dict(q=2, sc=P + 2), dict(mask=P + 1),
+           # the scales input: shape named iff present, a shape the mode takes, aligned
+           dict(q=1), dict(q=1, qk=1), dict(q=1, qs=P), dict(q=1, qs=P, qk=4),
+           dict(q=1, qs=P, qk=-1), dict(q=0, qs=P, qk=1), dict(q=4, qs=P, qk=3),
+           dict(q=2, qs=P, qk=1), dict(q=2, qs=P, qk=2), dict(q=3, tile=128, qs=P, qk=2),
+           dict(q=1, qs=P + 4, qk=2), dict(q=2, qs=P + 8, qk=3), dict(q=1, qs=P + 2, qk=1)]
     for kw in bad:
         assert dispatch(**kw) == 1, kw
-    for kw in (dict(q=1), dict(q=3, tile=96), dict(q=3, tile=8), dict(q=3, tile=2048)):
+    for kw in (dict(q=3, tile=96), dict(q=3, tile=8), dict(q=3, tile=2048)):
         assert dispatch(**kw) == 2, kw
 
 
@@ -136,14 +141,14 @@ def test_update_expert_rejects_out_of_range_arguments():
 def fused(**kw):
     from combine_expert_amd import moe
     a = dict(x=P, ids=P, sc=None, t=P, thr=None, tm=None, Bs=512, H=8192, K=16, nl=512, F=3,
-             R=64, L=16, q=3, tile=128, bi=None, bm=None, ex=P, esc=P, cnt=P, off=P, src=P,
-             asg=P, err=None)
+             R=64, L=16, q=3, tile=128, qs=None, qk=0, bi=None, bm=None, ex=P, esc=P, cnt=P,
+             off=P, src=P, asg=P, err=None)
     a.update(kw)
     return moe.raw().moe_update_dispatch(a["x"], a["ids"], a["sc"], a["t"], a["thr"], a["tm"],
                                          a["Bs"], a["H"], a["K"], a["nl"], a["F"], a["R"],
-                                         a["L"], a["q"], a["tile"], a["bi"], a["bm"], a["ex"],
-                                         a["esc"], a["cnt"], a["off"], a["src"], a["asg"],
-                                         a["err"], None)
+                                         a["L"], a["q"], a["tile"], a["qs"], a["qk"], a["bi"],
+                                         a["bm"], a["ex"], a["esc"], a["cnt"], a["off"],
+                                         a["src"], a["asg"], a["err"], None)
 
 
 @pytest.mark.skipif("not _no_gpu()")
@@ -151,9 +156,10 @@ def test_fused_update_dispatch_rejects_out_of_range_arguments():
     bad = [dict(Bs=0), dict(K=17), dict(H=7168 + 16), dict(t=None), dict(nl=0), dict(nl=1025),
            dict(nl=8, K=16), dict(F=1), dict(F=514), dict(R=0), dict(R=65), dict(x=None),
            dict(ids=None), dict(ids=P + 4), dict(sc=P + 4, thr=P), dict(thr=P + 1),
-           dict(bi=P + 2), dict(q=3, tile=0), dict(q=7), dict(asg=None)]
+           dict(bi=P + 2), dict(q=3, tile=0), dict(q=7), dict(asg=None), dict(q=1),
+           dict(q=3, qs=P, qk=1)]
     for kw in bad:
         assert fused(**kw) == 1, kw
-    # a table too large to stage in LDS, static quantisation, odd tiles: not supported
-    for kw in (dict(nl=1024, F=13, K=16), dict(q=1), dict(q=3, tile=96)):
+    # a table too large to stage in LDS, odd tiles: not supported
+    for kw in (dict(nl=1024, F=13, K=16), dict(q=3, tile=96)):
         assert fused(**kw) == 2, kw

@@ -1,0 +1,100 @@
+"""GPU parity of the dispatch's scales input and static quantisation against
+the oracle, bit for bit: quantMode 1 with one coefficient, one shared row and
+one row per instance; quantMode 2 and 3 with one smoothing row per instance
+(every copy quantised on its own); through moe_dispatch and through the
+fused moe_update_dispatch.  Small ragged shapes (partial tiles, K = 1 .. 16,
+inputs large enough to saturate the static cast) and the c3 shapes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_expert_amd import workloads as W
+from tests.gpu_common import (M, check_dispatch, cuda, gpu_update, np_, oracle_update, say,
+                              POISON)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_dispatch_scaled(wl, ids, mask, qs, fused=False):
+    m = M()
+    out = m.dispatch_buffers(wl.Bs, wl.H, wl.K, wl.E, wl.quant_mode, wl.tile)
+    for key in ("expand_x", "expand_scales"):
+        if out.get(key) is not None:
+            out[key].view(torch.uint8).fill_(POISON)
+    for key in ("expert_counts", "expert_offsets", "expand_src", "assist_dst"):
+        out[key].fill_(-7)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    if fused:
+        prune = wl.prune_thr is not None
+        out = m.moe_update_dispatch(
+            cuda(wl.x), cuda(wl.logical_ids), cuda(wl.table), wl.n_ranks, wl.local_experts,
+            wl.quant_mode, wl.tile, expert_scales=cuda(wl.scales) if prune else None,
+            prune_thr=cuda(wl.prune_thr) if prune else None, token_mask=cuda(wl.token_mask),
+            quant_scales=cuda(qs), out=out, dev_err=err)
+    else:
+        out = m.moe_dispatch(cuda(wl.x), ids, wl.n_ranks, wl.local_experts, wl.quant_mode,
+                             wl.tile, active_mask=mask, quant_scales=cuda(qs), out=out,
+                             dev_err=err)
+    return out, int(err.item())
+
+
+def check(wl, kind, seed, fused=False):
+    qs = W.make_quant_scales(seed, kind, wl.E, wl.H)
+    oi, om, oe = oracle_update(wl)
+    od = oracle.dispatch(oracle.bf16_bits(wl.x), oi, om, wl.n_ranks, wl.local_experts,
+                         wl.quant_mode, wl.tile, None if qs is None else qs.numpy(), kind)
+    if fused:
+        g, err = gpu_dispatch_scaled(wl, None, None, qs, fused=True)
+        np.testing.assert_array_equal(np_(g["balanced_ids"]), oi)
+        np.testing.assert_array_equal(np_(g["balanced_mask"]), om)
+    else:
+        gi, gm = gpu_update(wl)
+        g, err = gpu_dispatch_scaled(wl, gi, gm, qs)
+    total = check_dispatch(wl, g, od)
+    assert err == (oe | od["err"])
+    return total
+
+
+SMALL = [
+    # seed, Bs, H, K, ranks, local, mode, tile, kind, prune, replicas, x_scale
+    (301, 37, 1056, 5, 3, 4, 1, 0, 1, True, False, 30.0),
+    (302, 37, 1056, 5, 3, 4, 1, 0, 2, False, True, 30.0),
+    (303, 37, 1056, 5, 3, 4, 1, 0, 3, True, True, 30.0),
+    (304, 19, 2080, 3, 2, 3, 2, 0, 3, False, False, 1.0),
+    (305, 19, 2080, 3, 2, 3, 3, 32, 3, True, False, 1.0),
+    (306, 64, 4128, 7, 5, 5, 3, 64, 3, True, True, 1.0),
+    (307, 1, 8192, 16, 128, 8, 2, 0, 3, False, False, 1.0),
+    (308, 3, 1024, 1, 1, 1, 1, 0, 3, False, False, 100.0),
+    (309, 512, 1024, 16, 1, 16, 2, 0, 3, True, False, 1.0),
+    (310, 200, 1024, 2, 8, 128, 3, 1024, 3, False, True, 1.0),
+    (311, 64, 2048, 4, 4, 8, 1, 0, 2, False, False, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+def test_scales_small_and_edge_shapes(case):
+    seed, Bs, H, K, R, L, mode, tile, kind, prune, rep, xs = case
+    say(f"[scales] small {case}")
+    wl = W.make_small(seed, Bs, H, K, R, L, mode, tile, prune=prune, shared=False,
+                      replicas=rep, x_scale=xs)
+    check(wl, kind, seed)
+
+
+@pytest.mark.parametrize("mode,kind", [(1, 1), (1, 3), (2, 3), (3, 3)])
+def test_scales_c3_shapes(mode, kind):
+    say(f"[scales] c3 shapes mode {mode} kind {kind}")
+    wl = W.make_c3(seed=3100 + mode, quant_mode=mode, with_expert_out=False,
+                   name=f"c3.q{mode}")
+    if mode == 3:
+        wl.tile = 128
+    check(wl, kind, 3100 + 10 * mode + kind)
+
+
+@pytest.mark.parametrize("mode,tile,kind", [(1, 0, 2), (1, 0, 3), (2, 0, 3), (3, 128, 3)])
+def test_scales_through_the_fused_call(mode, tile, kind):
+    say(f"[scales] fused mode {mode} kind {kind}")
+    wl = W.make_small(320 + mode, 96, 2048, 6, 4, 6, mode, tile, prune=True, shared=False,
+                      token_mask_prefix=90, replicas=True, x_scale=8.0)
+    check(wl, kind, 330 + mode, fused=True)
