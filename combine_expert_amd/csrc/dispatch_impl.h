@@ -717,33 +717,6 @@ __device__ __forceinline__ void code_store(const DispatchArgs &a, int t, bool ha
     }
 }
 
-// Exclusive scan of the low 16 bits of s[0, n) in place by the whole block,
-// keeping the high 16 bits (s_wave: one int per wave).  Each thread owns a
-// contiguous run of counters.  Ends with a barrier.
-__device__ void block_exclusive_scan_lo16(int *s, int n, int *s_wave)
-{
-    const int t = threadIdx.x, T = blockDim.x;
-    const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
-    const int per = (n + T - 1) / T;
-    const int e0 = min(t * per, n), e1 = min(e0 + per, n);
-    int local = 0;
-    for (int e = e0; e < e1; ++e)
-        local += s[e] & 0xffff;
-    const int incl = wave_incl_scan(local);
-    if (lane == kWave - 1)
-        s_wave[w] = incl;
-    lds_barrier();
-    int run = incl - local;
-    for (int j = 0; j < nw; ++j)
-        run += j < w ? s_wave[j] : 0;
-    for (int e = e0; e < e1; ++e) {
-        const int c = s[e];
-        s[e] = run | (c & ~0xffff);
-        run += c & 0xffff;
-    }
-    lds_barrier();
-}
-
 template <int MODE, int KMAX, typename Src, bool PE>
 __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
 {
@@ -833,11 +806,25 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         my_id = my_on ? raw_id : -1;
     }
     const bool my_on = my_id >= 0;
-    lds_barrier();
-    block_exclusive_scan_lo16(s_cnt, E, s_wave);
+    lds_barrier();  // histograms complete
 
-    // 3. rows of the token's entries (wave 0, lane k = entry k)
+    // 3. rows of the token's entries (wave 0, lane k = entry k).  Only these K
+    //    offsets are needed, so wave 0 alone scans: lane c sums the low halves
+    //    of counters [c*per, (c+1)*per), a wave scan gives each chunk's
+    //    exclusive prefix, and lane k takes its chunk's prefix by a lane
+    //    shuffle plus the counters before its id inside the chunk.
     if (w == 0) {
+        const int per = (E + kWave - 1) / kWave;
+        const int c0 = min(lane * per, E), c1 = min(c0 + per, E);
+        int local = 0;
+        for (int e = c0; e < c1; ++e)
+            local += s_cnt[e] & 0xffff;
+        const int excl = wave_incl_scan(local) - local;
+        const int id = my_on ? my_id : 0;
+        const int chunk = id / per;
+        int off = __shfl(excl, chunk);
+        for (int e = chunk * per; e < id; ++e)
+            off += s_cnt[e] & 0xffff;
         int dup = 0;  // earlier entries of this token with the same id
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
@@ -845,8 +832,7 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
             dup += (j < lane && v == my_id) ? 1 : 0;
         }
         if (lane < K) {
-            const int c = my_on ? s_cnt[my_id] : 0;
-            const int r = my_on ? (c & 0xffff) + (c >> 16) + dup : -1;
+            const int r = my_on ? off + (s_cnt[id] >> 16) + dup : -1;
             s_rank[lane] = r;
             a.assist_dst[f0 + lane] = r;
             if (r >= 0)
