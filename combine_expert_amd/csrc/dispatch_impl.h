@@ -589,32 +589,25 @@ __device__ __forceinline__ void code_store_rows(const DispatchArgs &a, int t, bo
     }
 }
 
-// Codes a token's row once (this thread's 16 elements in xa, xb) and writes it,
-// with its scales, to each destination row rank[k] >= 0.  amax_row is the
-// token's largest |x| pattern (per-token int8 only).
-template <int MODE, int KMAX>
-__device__ __forceinline__ void code_store(const DispatchArgs &a, int t, bool has, const uint4 &xa,
-                                           const uint4 &xb, const int *rank, uint32_t amax_row)
-{
-    const int H = a.H;
-    if (MODE == 0) {
-        if (!has)
-            return;
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-            if (rank[k] < 0)
-                continue;
-            uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.expand_x) +
-                                                   (size_t)rank[k] * H) + 2 * t;
-            store_nt16(dst, xa);
-            store_nt16(dst + 1, xb);
-        }
-        return;
-    }
+// A token's coded chunk (this thread's 16 elements) and its scale.
+struct Coded {
+    uint4 code;    // modes 1-4
+    float fscale;  // modes 2 and 3: 1 / dynamicScales of the token / tile
+    int se;        // mode 4: the block's shared exponent
+};
 
+// Codes a token's row once (this thread's 16 elements in xa, xb); no memory
+// writes, so it can run before the rows are known.  amax_row is the token's
+// largest |x| pattern (per-token int8 only).
+template <int MODE>
+__device__ __forceinline__ Coded code_row(const DispatchArgs &a, int t, bool has, const uint4 &xa,
+                                          const uint4 &xb, uint32_t amax_row)
+{
+    Coded c{};
+    if (MODE == 0)
+        return c;
     float v[16];
     unpack16(xa, xb, v);
-    uint4 code;
     if (MODE == 1) {  // static: one coefficient or one row shared by all experts
         const int tc = has ? t : 0;
         float sv[16];
@@ -629,44 +622,23 @@ __device__ __forceinline__ void code_store(const DispatchArgs &a, int t, bool ha
                 sv[4 * q + 3] = f.w;
             }
         } else {
-            const float c = a.qs[0];
+            const float cst = a.qs[0];
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                sv[j] = c;
+                sv[j] = cst;
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             v[j] *= sv[j];
-        code = int8_static_codes(v);
-        if (has) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rank[k] < 0)
-                    continue;
-                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(a.expand_x) +
-                                                     (size_t)rank[k] * H) + t, code);
-            }
-        }
+        c.code = int8_static_codes(v);
     } else if (MODE == 2) {
         const uint32_t m = amax_row;
         const float mf = __uint_as_float(m << 16);
         const float d = m ? 127.0f / mf : 0.0f;
-        const float scale = m ? 1.0f / d : 0.0f;
-        code = int8_codes(v, d);
-        if (has) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rank[k] < 0)
-                    continue;
-                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(a.expand_x) +
-                                                     (size_t)rank[k] * H) + t, code);
-                if (t == 0)
-                    static_cast<float *>(a.expand_scales)[rank[k]] = scale;
-            }
-        }
+        c.fscale = m ? 1.0f / d : 0.0f;
+        c.code = int8_codes(v, d);
     } else if (MODE == 3) {
-        const int tile = a.tile;
-        const int lanes = tile / kChunk;  // lanes per tile: 1 .. 64
+        const int lanes = a.tile / kChunk;  // lanes per tile: 1 .. 64
         // lanes past the row end hold a copy of chunk 0: keep it out of the
         // last (partial) tile's maximum
         uint32_t m = has ? amax_bits16(xa, xb) : 0u;
@@ -674,22 +646,8 @@ __device__ __forceinline__ void code_store(const DispatchArgs &a, int t, bool ha
             m = max(m, (uint32_t)__shfl_xor((int)m, o));
         const float mf = __uint_as_float(m << 16);
         const float d = m ? 127.0f / mf : 0.0f;
-        const float scale = m ? 1.0f / d : 0.0f;
-        code = int8_codes(v, d);
-        const int nt = (H + tile - 1) / tile;
-        const bool lead = has && (t & (lanes - 1)) == 0;
-        if (has) {
-#pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rank[k] < 0)
-                    continue;
-                store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(a.expand_x) +
-                                                     (size_t)rank[k] * H) + t, code);
-                if (lead)
-                    static_cast<float *>(a.expand_scales)[(size_t)rank[k] * nt +
-                                                          (t * kChunk) / tile] = scale;
-            }
-        }
+        c.fscale = m ? 1.0f / d : 0.0f;
+        c.code = int8_codes(v, d);
     } else {  // MODE == 4
         uint32_t m = amax_bits16(xa, xb);
         m = max(m, (uint32_t)__shfl_xor((int)m, 1));
@@ -699,21 +657,47 @@ __device__ __forceinline__ void code_store(const DispatchArgs &a, int t, bool ha
             se = max(-127, min(127, se));
         }
         const float f = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, normal
-        code = e4m3_codes(v, f);
-        const int nb = H / 32;
-        const bool lead = has && (t & 1) == 0;
-        if (has) {
+        c.code = e4m3_codes(v, f);
+        c.se = se;
+    }
+    return c;
+}
+
+// Writes the coded chunk (mode 0: the raw bf16 chunk), with its scales, to
+// each destination row rank[k] >= 0.
+template <int MODE, int KMAX>
+__device__ __forceinline__ void store_row(const DispatchArgs &a, int t, bool has, const uint4 &xa,
+                                          const uint4 &xb, const Coded &c, const int *rank)
+{
+    const int H = a.H;
+    if (!has)
+        return;
 #pragma unroll
-            for (int k = 0; k < KMAX; ++k) {
-                if (rank[k] < 0)
-                    continue;
-                store_nt16(reinterpret_cast<uint4 *>(static_cast<uint8_t *>(a.expand_x) +
-                                                     (size_t)rank[k] * H) + t, code);
-                if (lead)
-                    static_cast<uint8_t *>(a.expand_scales)[(size_t)rank[k] * nb + t / 2] =
-                        (uint8_t)(se + 127);
+    for (int k = 0; k < KMAX; ++k) {
+        if (rank[k] < 0)
+            continue;
+        if (MODE == 0) {
+            uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.expand_x) +
+                                                   (size_t)rank[k] * H) + 2 * t;
+            store_nt16(dst, xa);
+            store_nt16(dst + 1, xb);
+            continue;
+        }
+        store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(a.expand_x) +
+                                             (size_t)rank[k] * H) + t, c.code);
+        if (MODE == 2 && t == 0)
+            static_cast<float *>(a.expand_scales)[rank[k]] = c.fscale;
+        if (MODE == 3) {
+            const int lanes = a.tile / kChunk;
+            if ((t & (lanes - 1)) == 0) {
+                const int nt = (H + a.tile - 1) / a.tile;
+                static_cast<float *>(a.expand_scales)[(size_t)rank[k] * nt +
+                                                      (t * kChunk) / a.tile] = c.fscale;
             }
         }
+        if (MODE == 4 && (t & 1) == 0)
+            static_cast<uint8_t *>(a.expand_scales)[(size_t)rank[k] * (H / 32) + t / 2] =
+                (uint8_t)(c.se + 127);
     }
 }
 
@@ -806,7 +790,28 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         my_id = my_on ? raw_id : -1;
     }
     const bool my_on = my_id >= 0;
+    // Coding needs no ranks: wave 0 codes its chunk now, while the other waves
+    // finish their histogram work; they code after the barrier, while wave 0
+    // works out the ranks.  Per-token int8 publishes its wave maxima first and
+    // codes after the barrier.
+    Coded cd{};
+    if (MODE == 2 && !PE) {
+        const uint32_t m = wave_max_u32(amax_bits16(xa, xb));
+        if (lane == 0)
+            s_wmax[w] = m;
+    }
+    if (!PE && MODE != 2 && w == 0)
+        cd = code_row<MODE>(a, t, has, xa, xb, 0u);
     lds_barrier();  // histograms complete
+    if (!PE && MODE != 2 && w != 0)
+        cd = code_row<MODE>(a, t, has, xa, xb, 0u);
+    if (!PE && MODE == 2) {
+        uint32_t amax = 0;
+        for (int j = 0; j < nw; ++j)
+            amax = max(amax, s_wmax[j]);
+        if (w != 0)
+            cd = code_row<MODE>(a, t, has, xa, xb, amax);
+    }
 
     // 3. rows of the token's entries (wave 0, lane k = entry k).  Only these K
     //    offsets are needed, so wave 0 alone scans: lane c sums the low halves
@@ -839,17 +844,13 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
                 a.expand_src[r] = f0 + lane;
         }
     }
-    if (MODE == 2) {  // per-token maximum: wave maxima, then across the waves
-        const uint32_t m = wave_max_u32(amax_bits16(xa, xb));
-        if (lane == 0)
-            s_wmax[w] = m;
-    }
-    lds_barrier();
-    uint32_t amax = 0;
-    if (MODE == 2) {
+    if (!PE && MODE == 2 && w == 0) {
+        uint32_t amax = 0;
         for (int j = 0; j < nw; ++j)
             amax = max(amax, s_wmax[j]);
+        cd = code_row<MODE>(a, t, has, xa, xb, amax);
     }
+    lds_barrier();  // rows published
     int rank[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
@@ -862,7 +863,7 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
             eid[k] = k < K ? __builtin_amdgcn_readlane(my_id, k) : -1;
         code_store_rows<MODE, KMAX>(a, t, has, xa, xb, rank, eid, s_pmax);
     } else {
-        code_store<MODE, KMAX>(a, t, has, xa, xb, rank, amax);
+        store_row<MODE, KMAX>(a, t, has, xa, xb, cd, rank);
     }
 }
 
