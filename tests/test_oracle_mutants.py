@@ -62,16 +62,37 @@ PIN_FILES = ["tests/test_oracle_numbers.py", "tests/test_oracle_route.py",
              "tests/test_golden.py"]
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_planted_mistake(name, old, new, tmp_path):
+def _run_mutant(name, old, new, workdir):
+    """Build the oracle with one planted mistake and run the pin suite on it;
+    returns (pytest return code, tail of its output)."""
     src = open(obuild.SRC).read()
-    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
-    mut_src = tmp_path / "moe_oracle_mutant.c"
-    mut_src.write_text(src.replace(old, new))
-    lib = str(tmp_path / "libmoe_oracle_mutant.so")
-    obuild.build(src=str(mut_src), lib=lib)
-    env = dict(os.environ, MOE_ORACLE_LIB=lib)
+    if src.count(old) != 1:
+        return -1, f"mutation site for {name} not unique/present"
+    mut_src = os.path.join(workdir, f"moe_oracle_{name}.c")
+    with open(mut_src, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(workdir, f"libmoe_oracle_{name}.so")
+    obuild.build(src=mut_src, lib=lib)
+    env = dict(os.environ, MOE_ORACLE_LIB=lib, OMP_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         *PIN_FILES], cwd=ROOT, env=env, capture_output=True, text=True,
                        timeout=600)
-    assert r.returncode == 1, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+    return r.returncode, r.stdout[-2000:]
+
+
+@pytest.fixture(scope="module")
+def mutant_results(tmp_path_factory):
+    """Every mutant's pin-suite run, several at a time (each is a subprocess)."""
+    from concurrent.futures import ThreadPoolExecutor
+    workdir = str(tmp_path_factory.mktemp("mutants"))
+    workers = max(1, min(6, (os.cpu_count() or 2) - 1))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = {m[0]: ex.submit(_run_mutant, *m, workdir) for m in MUTANTS}
+        return {name: f.result() for name, f in futs.items()}
+
+
+@pytest.mark.parametrize("name", [m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, mutant_results):
+    rc, out = mutant_results[name]
+    assert rc != -1, out
+    assert rc == 1, f"pins did not catch mutant {name}:\n{out}"
