@@ -16,10 +16,13 @@
 // entries (at most 8192 four-byte ids, read with 16-byte loads from L2): one
 // over every entry and one over the entries before its token, packed as the
 // low and high 16 bits of one counter (each count is at most 8192), so each
-// entry costs one LDS atomic.  Only the token's K offsets are needed, so wave
-// 0 alone scans chunk sums of the low halves; each of its first K lanes takes
-// its chunk's prefix by a lane shuffle, adds the counters before its id in
-// the chunk, the high half and the token's own earlier duplicates.  This replaces a serial routing
+// entry costs one LDS atomic.  Only the token's K offsets are needed, so one
+// wave alone scans chunk sums of the low halves; each of its first K lanes
+// takes its chunk's prefix by a lane shuffle, adds the counters before its id
+// in the chunk, the high half and the token's own earlier duplicates.  That
+// wave is an extra one holding no row data, so the row's waves code their
+// chunks (codes need no ranks) while it works out the rows; only the stores
+// wait for it.  This replaces a serial routing
 // kernel between two launches with redundant LDS work that overlaps the HBM
 // load of the token's row.  (Two tokens per block, sharing the histograms,
 // measured slower: one block per compute unit hides less latency than two.)

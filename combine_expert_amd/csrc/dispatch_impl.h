@@ -10,6 +10,7 @@ namespace moe {
 
 
 constexpr int kHistSlots = 1024;  // one LDS counter per instance (E <= 1024)
+constexpr int kDispatchWaves = kMaxWaves + 1;
 constexpr int kPreOne = 0x10001;  // packed counter increment: all (low) and before-token (high)
 constexpr int kMaxTokens = 512;   // Bs limit: staged token mask
 constexpr int kMaxTopK = 16;      // K limit: staged thresholds
@@ -498,7 +499,7 @@ __device__ __forceinline__ uint32_t absmax_bits16(const float *w)
 // Cache: the table is E * H * 4 bytes).  Per-token dynamic int8 needs each
 // copy's maximum over the whole row first: a pass computes all K maxima
 // (one barrier for all of them), a second pass codes.  s_pmax: LDS
-// [kMaxWaves][KMAX].
+// [kDispatchWaves][KMAX].
 constexpr int kPrefetch = 4;
 
 template <int MODE, int KMAX>
@@ -707,10 +708,10 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
     // low 16 bits: active entries with id e; high: those before this token.
     // After the scan the low half holds offsets[e].
     __shared__ int s_cnt[kHistSlots];
-    __shared__ int s_wave[kMaxWaves];
+    __shared__ int s_wave[kDispatchWaves];
     __shared__ int s_rank[KMAX];
-    __shared__ uint32_t s_wmax[kMaxWaves];
-    __shared__ uint32_t s_pmax[PE && MODE == 2 ? kMaxWaves * KMAX : 1];
+    __shared__ uint32_t s_wmax[kDispatchWaves];
+    __shared__ uint32_t s_pmax[PE && MODE == 2 ? kDispatchWaves * KMAX : 1];
     __shared__ uint8_t s_tok[Src::kMapped ? kMaxTokens : 1];
     __shared__ float s_thr[Src::kMapped ? kMaxTopK : 1];
     extern __shared__ int s_tab[];  // mapped: the [n_logical, F] table
@@ -790,35 +791,33 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         my_id = my_on ? raw_id : -1;
     }
     const bool my_on = my_id >= 0;
-    // Coding needs no ranks: wave 0 codes its chunk now, while the other waves
-    // finish their histogram work; they code after the barrier, while wave 0
-    // works out the ranks.  Per-token int8 publishes its wave maxima first and
-    // codes after the barrier.
+    // Coding needs no ranks: after the histogram barrier the row's waves code
+    // their chunks while the block's last wave, which holds no row data (the
+    // block has one wave more than the row needs), works out the rows.
+    // Per-token int8 publishes its wave maxima before the barrier.
     Coded cd{};
     if (MODE == 2 && !PE) {
         const uint32_t m = wave_max_u32(amax_bits16(xa, xb));
         if (lane == 0)
             s_wmax[w] = m;
     }
-    if (!PE && MODE != 2 && w == 0)
-        cd = code_row<MODE>(a, t, has, xa, xb, 0u);
+    const int rw = nw - 1;  // the rank wave: holds no row data
     lds_barrier();  // histograms complete
-    if (!PE && MODE != 2 && w != 0)
+    if (!PE && MODE != 2 && w != rw)
         cd = code_row<MODE>(a, t, has, xa, xb, 0u);
-    if (!PE && MODE == 2) {
+    if (!PE && MODE == 2 && w != rw) {
         uint32_t amax = 0;
         for (int j = 0; j < nw; ++j)
             amax = max(amax, s_wmax[j]);
-        if (w != 0)
-            cd = code_row<MODE>(a, t, has, xa, xb, amax);
+        cd = code_row<MODE>(a, t, has, xa, xb, amax);
     }
 
-    // 3. rows of the token's entries (wave 0, lane k = entry k).  Only these K
-    //    offsets are needed, so wave 0 alone scans: lane c sums the low halves
+    // 3. rows of the token's entries (the rank wave, lane k = entry k).  Only
+    //    these K offsets are needed, so that wave alone scans: lane c sums the low halves
     //    of counters [c*per, (c+1)*per), a wave scan gives each chunk's
     //    exclusive prefix, and lane k takes its chunk's prefix by a lane
     //    shuffle plus the counters before its id inside the chunk.
-    if (w == 0) {
+    if (w == rw) {
         const int per = (E + kWave - 1) / kWave;
         const int c0 = min(lane * per, E), c1 = min(c0 + per, E);
         int local = 0;
@@ -844,12 +843,6 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
                 a.expand_src[r] = f0 + lane;
         }
     }
-    if (!PE && MODE == 2 && w == 0) {
-        uint32_t amax = 0;
-        for (int j = 0; j < nw; ++j)
-            amax = max(amax, s_wmax[j]);
-        cd = code_row<MODE>(a, t, has, xa, xb, amax);
-    }
     lds_barrier();  // rows published
     int rank[KMAX];
 #pragma unroll
@@ -869,14 +862,14 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
 
 // routed entries (moe_dispatch); PE: one scales row per instance
 template <int MODE, int KMAX, bool PE>
-__global__ __launch_bounds__(kMaxThreads) void k_dispatch(DispatchArgs a)
+__global__ __launch_bounds__(kMaxThreads + kWave) void k_dispatch(DispatchArgs a)
 {
     dispatch_body<MODE, KMAX, Routed, PE>(a);
 }
 
 // mapped entries (moe_update_dispatch); KEEP: a token mask or thresholds
 template <int MODE, int KMAX, bool KEEP, bool PE>
-__global__ __launch_bounds__(kMaxThreads) void k_update_dispatch(DispatchArgs a)
+__global__ __launch_bounds__(kMaxThreads + kWave) void k_update_dispatch(DispatchArgs a)
 {
     dispatch_body<MODE, KMAX, Mapped<KEEP>, PE>(a);
 }
@@ -884,7 +877,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_update_dispatch(DispatchArgs a)
 template <int MODE, int KMAX, typename Src, bool PE>
 void launch_kernel(const DispatchArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.Bs + 1), block(row_threads(a.H));
+    const dim3 grid(a.Bs + 1), block(row_threads(a.H) + kWave);
     if constexpr (Src::kMapped)
         hipLaunchKernelGGL((k_update_dispatch<MODE, KMAX, Src::kKeep, PE>), grid, block,
                            (size_t)a.n_logical * a.F * sizeof(int), stream, a);
