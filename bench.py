@@ -230,7 +230,7 @@ def summarize_copy(args):
 
 def make_set(wl, torch, moe):
     dev = torch.device("cuda")
-    c = lambda t: t.contiguous().to(dev)
+    c = lambda t: None if t is None else t.contiguous().to(dev)
     s = dict(x=c(wl.x), ids=c(wl.logical_ids), scales=c(wl.scales), table=c(wl.table),
              eout=c(wl.expert_out), shared=c(wl.shared), residual=c(wl.residual),
              gamma=c(wl.gamma))
@@ -425,6 +425,64 @@ def dispatch_variants(moe, torch, n, sets=5):
     return out
 
 
+# ----------------------------------------------------------------- other configs
+
+def config_table(moe, torch, n, sets=3):
+    """Per-launch durations (HIP events around n back-to-back launches over
+    rotating buffer sets) of the three calls and the fused call on the other
+    workloads at full size, with their algorithmic bytes."""
+    from combine_expert_amd import workloads as W
+    rows = []
+    for name in ("c1", "c2", "c4", "c4b"):
+        wl = W.make(name)
+        if wl.expert_out is None:  # the identity + bias expert: any bf16 rows serve for timing
+            wl.expert_out = torch.randn(wl.Bs * wl.K, wl.H).bfloat16()
+        stream = torch.cuda.current_stream()
+        bufs = [make_set(wl, torch, moe) for _ in range(sets)]
+        prune = wl.prune_thr is not None
+        dev = torch.device("cuda")
+        extra = dict(sc=wl.scales.to(dev) if prune else None,
+                     thr=wl.prune_thr.to(dev) if prune else None,
+                     tm=None if wl.token_mask is None else wl.token_mask.to(dev))
+        p = lambda t: None if t is None else t.data_ptr()
+        argv = []
+        for s in bufs:
+            upd, dsp, fused, cmb = step_args(wl, s, stream.cuda_stream)
+            n_logical, F = wl.table.shape
+            upd = (upd[0], p(extra["sc"]), upd[2], p(extra["thr"]), p(extra["tm"])) + upd[5:]
+            fused = (fused[0], fused[1], p(extra["sc"]), fused[3], p(extra["thr"]),
+                     p(extra["tm"])) + fused[6:]
+            argv.append((upd, dsp, fused, cmb))
+        lib = moe.raw()
+        fns = (lib.moe_update_expert, lib.moe_dispatch, lib.moe_update_dispatch,
+               lib.moe_combine_add_rmsnorm)
+        for a in argv:  # one full step per set: the dispatch outputs feed the combine
+            for j in (0, 1, 3):
+                if fns[j](*a[j]):
+                    raise RuntimeError(f"{name}: a library call failed")
+        us = []
+        for j in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for k in range(n):
+                fns[j](*argv[k % sets][j])
+            e1.record(stream)
+            e1.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / n)
+        nrows = int(bufs[0]["d"]["expert_offsets"][-1].item())
+        nb = algorithmic_bytes(wl.Bs, wl.H, wl.K, wl.E, nrows, wl.table.shape[0],
+                               wl.table.shape[1], wl.quant_mode,
+                               moe.n_scale_entries(wl.quant_mode, wl.H, wl.tile),
+                               shared=wl.shared is not None)
+        keys = ("update_expert", "dispatch", "update_dispatch", "combine")
+        rows.append({"config": name, "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E,
+                     "quant_mode": wl.quant_mode, "rows_dispatched": nrows,
+                     **{k: {"avg_us": round(u, 3), "bytes": nb[k],
+                            "GBps": round(nb[k] / (u * 1e-6) / 1e9, 1)}
+                        for k, u in zip(keys, us)}})
+    return rows
+
+
 def check_parity(wl, s, oracle, np):
     """Step-0 outputs against the oracle: routing/codes exact, y within tolerance."""
     oi, om, _ = oracle.update_expert(wl.logical_ids.numpy(), None, wl.table.numpy(), None, None,
@@ -584,6 +642,7 @@ def main():
 
     c5 = time_stack(moe, torch, 16, max(10, K // 10), 3) if args.c5 else None
     variants = dispatch_variants(moe, torch, max(K // 5, 50)) if args.c5 else None
+    configs = config_table(moe, torch, max(K // 5, 50)) if args.c5 else None
 
     # HBM bytes per launch from the committed counter summaries (null when the
     # kernel source changed since they were taken)
@@ -626,6 +685,7 @@ def main():
                        "tokens_per_s": round(wl.Bs / t_fused, 1), "bytes": fused_bytes},
         "c5_stack": c5,
         "dispatch_variants": variants,
+        "other_configs": configs,
         "step_bytes": step_bytes,
         "parity_step0": "ok" if ok else "MISMATCH",
         "cpu_baseline": None,
