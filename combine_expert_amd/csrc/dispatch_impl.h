@@ -15,8 +15,8 @@ constexpr int kPreOne = 0x10001;  // packed counter increment: all (low) and bef
 constexpr int kMaxTokens = 512;   // Bs limit: staged token mask
 constexpr int kMaxTopK = 16;      // K limit: staged thresholds
 
-constexpr int kStageTab = 8;      // mapping-table words per thread staged through registers
-constexpr int kStageTok = 8;      // token-mask bytes per thread staged through registers
+constexpr int kStageTab = 4;      // mapping-table words per thread staged through registers
+constexpr int kStageTok = 4;      // token-mask bytes per thread staged through registers
 
 // floor(a / d) for 0 <= a < 2^23, 1 <= d <= 1024: fp32 reciprocal estimate
 // (off by far less than one unit here) and one correction step.
@@ -164,12 +164,37 @@ struct Mapped {
         const int g0 = in ? g4 * 4 : 0;
         int ii[4], at[4], hv[4];
         bool keep[4], e_ok[4];
+        if ((K & 3) == 0) {
+            // the group is one token's columns k0 .. k0 + 3: one token index,
+            // one mask byte and one 16-byte threshold read
+            const int i0 = token_of(g0);
+            const int k0 = g0 - (int)__umul24((unsigned)i0, (unsigned)K);
+            bool kp[4] = {true, true, true, true};
+            if (KEEP) {
+                const int tv = tok[i0];
+                const float4 th = *reinterpret_cast<const float4 *>(thr + k0);
+                kp[0] = (tv != 0) & !(scv[0] < th.x);
+                kp[1] = (tv != 0) & !(scv[1] < th.y);
+                kp[2] = (tv != 0) & !(scv[2] < th.z);
+                kp[3] = (tv != 0) & !(scv[3] < th.w);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                keep[j] = in && kp[j];
+                ii[j] = i0;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = token_of(g0 + j);
+                keep[j] =
+                    in && keep_of(i, g0 + j - (int)__umul24((unsigned)i, (unsigned)K), scv[j]);
+                ii[j] = i;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int i = token_of(g0 + j);
-            keep[j] = in && keep_of(i, g0 + j - (int)__umul24((unsigned)i, (unsigned)K), scv[j]);
             e_ok[j] = (unsigned)idv[j] < (unsigned)n_logical;
-            ii[j] = i;
             at[j] = (int)__umul24(e_ok[j] ? (unsigned)idv[j] : 0u, (unsigned)F);
         }
 #pragma unroll
@@ -713,7 +738,7 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
     __shared__ uint32_t s_wmax[kDispatchWaves];
     __shared__ uint32_t s_pmax[PE && MODE == 2 ? kDispatchWaves * KMAX : 1];
     __shared__ uint8_t s_tok[Src::kMapped ? kMaxTokens : 1];
-    __shared__ float s_thr[Src::kMapped ? kMaxTopK : 1];
+    __shared__ __align__(16) float s_thr[Src::kMapped ? kMaxTopK : 1];
     extern __shared__ int s_tab[];  // mapped: the [n_logical, F] table
 
     const int Bs = a.Bs, H = a.H, K = a.K, E = a.E;

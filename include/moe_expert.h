@@ -181,7 +181,10 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active
  * with the intermediate ids' / mask' written to balanced_ids / balanced_mask
  * when those are non-NULL, and dev_err collecting the bits of both calls.
  * Every dispatch block maps the entries it counts through an LDS copy of the
- * table, which saves the second launch.
+ * table, which saves the second launch but repeats the mapping in each of the
+ * Bs + 1 blocks: measured on MI355X it pays off up to about Bs*K = 4096
+ * entries (Bs=512, K=8: 10.2 us against 3.3 + 8.6 us for the two calls) and
+ * not at Bs*K = 8192 with pruning (Bs=512, K=16: 17.0 us against 3.5 + 10.9).
  *
  *   expert_ids    int32 [Bs, K]  logical ids (16-byte aligned)
  *   expert_scales f32   [Bs, K] or NULL (16-byte aligned when prune_thr is given)
