@@ -27,6 +27,20 @@ Five workloads are defined (c1..c5) plus a replica-mix variant of c4 (c4b):
       (768 instances on 64 x 12)
   c5  16 layers of c3 shapes with per-token int8, fresh Zipf routing per layer
 
+Expert-computation (grouped GEMM) operands, the step between dispatch and
+combine:
+
+  g3  one expert-parallel rank's share of a c3-shaped layer: 8 local
+      instances, Kd = H = 7168, N = 4096 output columns (a gate and an up
+      projection of width 2048 side by side), 4096 rows (the average number
+      of rows a rank receives: 32 ranks x 512 tokens x 8 / 32) split over the
+      8 instances by a multinomial draw from a Zipf(1.2) law over a seeded
+      permutation.  Operands are mxfp8: random finite E4M3 codes with the
+      exponent field uniform in [6, 15] (magnitudes 2^-1 .. 448, like the
+      codes of a block whose maximum is scaled to the top binade) and E8M0
+      block scales uniform in a narrow band (activations 2^-9 .. 2^-5,
+      weights 2^-17 .. 2^-13).
+
 N(mu, s) means mean mu and standard deviation s.  bf16 values are fp32 draws
 rounded to nearest even.  Seeds: 1000 * config number (+ layer for c5).
 """
@@ -285,3 +299,70 @@ def make_quant_scales(seed: int, kind: int, E: int, H: int, lo: float = 0.25,
     rng = np.random.default_rng(seed)
     shape = {1: (1,), 2: (H,), 3: (E, H)}[kind]
     return torch.from_numpy(rng.uniform(lo, hi, size=shape).astype(np.float32))
+
+
+def e4m3_codes(rng, shape, ef_lo: int = 6, ef_hi: int = 15) -> np.ndarray:
+    """Random finite OCP E4M3 codes: uniform sign bit, exponent field uniform
+    in [ef_lo, ef_hi], mantissa field uniform (the NaN pattern S.1111.111 is
+    replaced by S.1111.110)."""
+    u8 = np.uint8
+    sign = rng.integers(0, 2, size=shape, dtype=u8) << u8(7)
+    ef = rng.integers(ef_lo, ef_hi + 1, size=shape, dtype=u8)
+    m = rng.integers(0, 8, size=shape, dtype=u8)
+    m[(ef == 15) & (m == 7)] = 6
+    return sign | (ef << u8(3)) | m
+
+
+def e8m0_codes(rng, shape, lo: int, hi: int) -> np.ndarray:
+    """Random E8M0 scale codes uniform in [lo, hi] (2^(lo-127) .. 2^(hi-127))."""
+    return rng.integers(lo, hi + 1, size=shape, dtype=np.uint8)
+
+
+def zipf_counts(rng, total: int, E: int, s: float) -> np.ndarray:
+    """Rows per instance: a multinomial draw of `total` rows over a Zipf(s)
+    law on a seeded permutation of the E instances."""
+    perm = rng.permutation(E)
+    p = np.empty(E)
+    p[perm] = (np.arange(E) + 1.0) ** (-s)
+    return rng.multinomial(total, p / p.sum()).astype(np.int32)
+
+
+@dataclass
+class GemmCase:
+    name: str
+    E: int
+    N: int
+    Kd: int
+    rows: int                # capacity of a / y; rows past offsets[E] are not part of any instance
+    offsets: np.ndarray      # int32 [E+1], offsets[0] = 0, non-decreasing
+    a: np.ndarray            # u8 E4M3 [rows, Kd]
+    a_sc: np.ndarray         # u8 E8M0 [rows, Kd/32]
+    w: np.ndarray            # u8 E4M3 [E, N, Kd]
+    w_sc: np.ndarray         # u8 E8M0 [E, N, Kd/32]
+
+    @property
+    def counts(self) -> np.ndarray:
+        return np.diff(self.offsets).astype(np.int32)
+
+
+def make_gemm_case(seed: int, counts, N: int, Kd: int, tail: int = 0,
+                   name: str = "gemm") -> GemmCase:
+    """mxfp8 grouped-GEMM operands for the given rows per instance, plus
+    `tail` spare rows past the last instance."""
+    rng = np.random.default_rng(seed)
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.size
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    rows = int(offsets[-1]) + tail
+    a = e4m3_codes(rng, (rows, Kd))
+    a_sc = e8m0_codes(rng, (rows, Kd // 32), 118, 122)
+    w = e4m3_codes(rng, (E, N, Kd))
+    w_sc = e8m0_codes(rng, (E, N, Kd // 32), 110, 114)
+    return GemmCase(name, E, N, Kd, rows, offsets, a, a_sc, w, w_sc)
+
+
+def make_g3(seed: int = 3100) -> GemmCase:
+    rng = np.random.default_rng(seed)
+    counts = zipf_counts(rng, 4096, 8, 1.2)
+    return make_gemm_case(seed + 1, counts, 4096, 7168, name="g3")

@@ -41,8 +41,11 @@ def lib():
                                              P, P]
         L.oracle_combine_add_rmsnorm.argtypes = [P, P, P, P, P, P, C.c_float, i, i, i, i,
                                                  P, P, P]
+        L.oracle_e4m3_decode.argtypes = [P, i, P]
+        L.oracle_expert_gemm_mx.argtypes = [P, P, P, i, i, P, P, i, i, P, P, P]
         for f in (L.oracle_update_expert, L.oracle_route, L.oracle_dispatch,
-                  L.oracle_dispatch_scaled, L.oracle_combine_add_rmsnorm):
+                  L.oracle_dispatch_scaled, L.oracle_combine_add_rmsnorm,
+                  L.oracle_expert_gemm_mx):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -202,3 +205,35 @@ def combine(expert_out_bits, assist, scales, shared_bits, residual_bits, gamma_b
     if rc:
         raise ValueError(f"oracle_combine rc={rc}")
     return y, xo, rstd
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    c = _c(codes, np.uint8).reshape(-1)
+    out = np.empty(c.size, dtype=np.float64)
+    lib().oracle_e4m3_decode(_p(c), c.size, _p(out))
+    return out
+
+
+def expert_gemm_mx(a, a_sc, offsets, w, w_sc, y_init=None):
+    """Expert computation on mxfp8 operands.  a u8 [rows, Kd], a_sc u8
+    [rows, Kd/32], offsets int32 [E+1], w u8 [E, N, Kd], w_sc u8 [E, N, Kd/32].
+    Returns (y_bits uint16 [rows, N], y64, abs64); rows outside the experts'
+    ranges keep y_init (default zeros) and 0 in y64 / abs64."""
+    a = _c(a, np.uint8)
+    rows, Kd = a.shape
+    a_sc = _c(a_sc, np.uint8)
+    offsets = _c(offsets, np.int32)
+    E = offsets.size - 1
+    w = _c(w, np.uint8)
+    N = w.shape[1]
+    assert w.shape == (E, N, Kd) and a_sc.shape == (rows, Kd // 32)
+    w_sc = _c(w_sc, np.uint8)
+    assert w_sc.shape == (E, N, Kd // 32)
+    y = np.zeros((rows, N), dtype=np.uint16) if y_init is None else _c(y_init, np.uint16).copy()
+    y64 = np.zeros((rows, N), dtype=np.float64)
+    abs64 = np.zeros((rows, N), dtype=np.float64)
+    rc = lib().oracle_expert_gemm_mx(_p(a), _p(a_sc), _p(offsets), E, rows, _p(w), _p(w_sc), N,
+                                     Kd, _p(y), _p(y64), _p(abs64))
+    if rc:
+        raise ValueError(f"oracle_expert_gemm_mx rc={rc}")
+    return y, y64, abs64

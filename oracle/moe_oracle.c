@@ -24,6 +24,10 @@
  *   [CMB] "aclnnMoeDistributeCombineAddRmsNorm", 计算公式 (formula): the
  *         weighted sum of expert outputs and shared-expert output, the
  *         residual add and RMSNorm.
+ *   [SEQ] "aclnnMoeUpdateExpert", calling sequence: the expert computation
+ *         sits between dispatch and combine and consumes expandX with its
+ *         dynamicScales.  The pages do not define that computation; the
+ *         oracle takes it as one linear layer per expert instance (below).
  *
  * Readings where the pages are silent or garbled:
  *   - instance ids are global: instance = rank * local_experts + local slot;
@@ -45,7 +49,12 @@
  *     all-zero block -> exponent -127;
  *   - the shared-expert term is weighted by the sum of the token's active
  *     scales (the formula's literal reading) or by 1 (selectable);
- *   - RMS is taken over the unrounded x; y = x * (1 / RMS(x)) * gamma.
+ *   - RMS is taken over the unrounded x; y = x * (1 / RMS(x)) * gamma;
+ *   - expert computation: rows offsets[e] .. offsets[e+1]-1 of expandX belong
+ *     to instance e and are multiplied by that instance's weight matrix W[e]
+ *     ([N, H], one row per output column); for mxfp8 both operands are
+ *     dequantised as code value * 2^(scale byte - 127) per block of 32 along
+ *     H, the products are summed exactly (fp64) and rounded once to bf16.
  *
  * Precision: the quantisers work in fp32 exactly as the dispatch formula's
  * CastToFp32 prescribes (IEEE division, no contraction; build with
@@ -528,5 +537,81 @@ int oracle_combine_add_rmsnorm(const uint16_t *expert_out, const int32_t *assist
             rstd_out[i] = (float)rstd;
     }
     free(xf);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- expert GEMM */
+
+/* OCP E4M3 code -> value, from the format: sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 is the subnormal grid m * 2^-9;
+ * S.1111.111 is NaN. */
+static double e4m3_value(uint8_t c)
+{
+    int ef = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (ef == 15 && m == 7)
+        return NAN;
+    if (ef == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(8.0 + m, ef - 10);   /* (1 + m/8) * 2^(ef - 7) */
+    return (c & 0x80) ? -v : v;
+}
+
+/* OCP E8M0 scale code -> 2^(c - 127); 255 is NaN. */
+static double e8m0_value(uint8_t c)
+{
+    return c == 255 ? NAN : ldexp(1.0, (int)c - 127);
+}
+
+void oracle_e4m3_decode(const uint8_t *codes, int n, double *out)
+{
+    for (int j = 0; j < n; ++j)
+        out[j] = e4m3_value(codes[j]);
+}
+
+/* [SEQ] expert computation, mxfp8 operands (the expandX / dynamicScales
+ * layout of [DSP] case 5): for each instance e < E and each row r in
+ * [offsets[e], offsets[e+1]):
+ *   y[r][n] = bf16( sum_k  A(r, k) * W(e, n, k) ),  n < N, k < Kd
+ *   A(r, k)    = e4m3(a[r][k])    * 2^(a_sc[r][k/32] - 127)
+ *   W(e, n, k) = e4m3(w[e][n][k]) * 2^(w_sc[e][n][k/32] - 127)
+ * Every product is exact in fp64 and the sum is taken in fp64.  y64 (if
+ * given) receives the unrounded sums and abs64 (if given) the sums of the
+ * products' magnitudes, both [rows, N].  Rows outside every instance's range
+ * are left untouched.  Returns -1 for bad sizes or offsets that are not
+ * non-decreasing within [0, rows]. */
+int oracle_expert_gemm_mx(const uint8_t *a, const uint8_t *a_sc, const int32_t *offsets, int E,
+                          int rows, const uint8_t *w, const uint8_t *w_sc, int N, int Kd,
+                          uint16_t *y, double *y64, double *abs64)
+{
+    if (E <= 0 || rows < 0 || N <= 0 || Kd <= 0 || Kd % 32 != 0)
+        return -1;
+    if (offsets[0] < 0 || offsets[E] > rows)
+        return -1;
+    for (int e = 0; e < E; ++e)
+        if (offsets[e] > offsets[e + 1])
+            return -1;
+    const int nb = Kd / 32;
+    for (int e = 0; e < E; ++e) {
+        const uint8_t *we = w + (size_t)e * N * Kd;
+        const uint8_t *wse = w_sc + (size_t)e * N * nb;
+        for (int r = offsets[e]; r < offsets[e + 1]; ++r) {
+            for (int n = 0; n < N; ++n) {
+                double sum = 0.0, mag = 0.0;
+                for (int k = 0; k < Kd; ++k) {
+                    double av = e4m3_value(a[(size_t)r * Kd + k]) * e8m0_value(a_sc[(size_t)r * nb + k / 32]);
+                    double wv = e4m3_value(we[(size_t)n * Kd + k]) * e8m0_value(wse[(size_t)n * nb + k / 32]);
+                    sum += av * wv;
+                    mag += fabs(av * wv);
+                }
+                y[(size_t)r * N + n] = bf16_from_double(sum);
+                if (y64)
+                    y64[(size_t)r * N + n] = sum;
+                if (abs64)
+                    abs64[(size_t)r * N + n] = mag;
+            }
+        }
+    }
     return 0;
 }

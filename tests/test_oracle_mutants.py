@@ -55,11 +55,21 @@ MUTANTS = [
     ("static_row_index", "s = qscales[j];", "s = qscales[H - 1 - j];"),
     ("pruned_weight_counted", "int r = assist[i * K + k];\n            if (r < 0)\n                continue;\n            double s = scales[i * K + k];\n            ws += s;",
      "int r = assist[i * K + k];\n            double s = scales[i * K + k];\n            ws += s;\n            if (r < 0)\n                continue;"),
+    ("e4m3_decode_bias", "v = ldexp(8.0 + m, ef - 10);", "v = ldexp(8.0 + m, ef - 9);"),
+    ("e4m3_decode_subnormal", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    ("e8m0_bias", "ldexp(1.0, (int)c - 127)", "ldexp(1.0, (int)c - 128)"),
+    ("gemm_act_scale_block", "a_sc[(size_t)r * nb + k / 32]", "a_sc[(size_t)r * nb + (k / 32 + 1) % nb]"),
+    ("gemm_weight_scale_row", "wse[(size_t)n * nb + k / 32]", "wse[(size_t)(n / 2) * nb + k / 32]"),
+    ("gemm_wrong_instance", "const uint8_t *we = w + (size_t)e * N * Kd;",
+     "const uint8_t *we = w + (size_t)((e + 1) % E) * N * Kd;"),
+    ("gemm_transposed_weights", "we[(size_t)n * Kd + k]", "we[(size_t)k * N + n]"),
+    ("gemm_extra_row", "for (int r = offsets[e]; r < offsets[e + 1]; ++r) {",
+     "for (int r = offsets[e]; r <= offsets[e + 1] && r < rows; ++r) {"),
 ]
 
 PIN_FILES = ["tests/test_oracle_numbers.py", "tests/test_oracle_route.py",
              "tests/test_oracle_dispatch_combine.py", "tests/test_oracle_scaled.py",
-             "tests/test_golden.py"]
+             "tests/test_oracle_gemm.py", "tests/test_golden.py"]
 
 
 def _run_mutant(name, old, new, workdir):
