@@ -20,10 +20,10 @@ MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ELAUNCH = 0, 1, 2, 3
 QUANT_NONE, QUANT_STATIC, QUANT_INT8_TOKEN, QUANT_INT8_TILE, QUANT_MXFP8 = 0, 1, 2, 3, 4
 SCALES_NONE, SCALES_ONE, SCALES_ROW, SCALES_EXPERT = 0, 1, 2, 3
 SHARED_PAGE, SHARED_ADD = 0, 1
-ERR_ID, ERR_TABLE, ERR_MASK1D, ERR_ROW = 1, 2, 4, 8
+ERR_ID, ERR_TABLE, ERR_MASK1D, ERR_ROW, ERR_OFFSETS = 1, 2, 4, 8, 16
 
 EXPORTS = ("moe_update_expert", "moe_dispatch", "moe_update_dispatch", "moe_combine_add_rmsnorm",
-           "moe_status_string")
+           "moe_expert_gemm", "moe_status_string")
 
 if not os.path.exists(_build.LIB):
     raise ImportError(f"{_build.LIB} is not built: run `python -m combine_expert_amd.build`")
@@ -37,8 +37,9 @@ _lib.moe_update_dispatch.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                      _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_combine_add_rmsnorm.argtypes = [_P, _P, _P, _P, _P, _P, C.c_float, _I, _I, _I, _I,
                                          _P, _P, _P, _P, _P]
+_lib.moe_expert_gemm.argtypes = [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P]
 for _f in (_lib.moe_update_expert, _lib.moe_dispatch, _lib.moe_update_dispatch,
-           _lib.moe_combine_add_rmsnorm):
+           _lib.moe_combine_add_rmsnorm, _lib.moe_expert_gemm):
     _f.restype = C.c_int
 _lib.moe_status_string.argtypes = [_I]
 _lib.moe_status_string.restype = C.c_char_p
@@ -207,6 +208,24 @@ def moe_combine_add_rmsnorm(expert_out, assist_dst, expert_scales, residual_x, g
                                       _ptr(dev_err), _stream(stream))
     _check("moe_combine_add_rmsnorm", rc)
     return y, x_out, rstd
+
+
+def moe_expert_gemm(expand_x, expand_scales, expert_offsets, weights, weight_scales,
+                    quant_mode: int = QUANT_MXFP8, y=None, dev_err=None, stream=None):
+    """Grouped GEMM of the expert computation.  expand_x u8 [rows, H] (E4M3),
+    expand_scales u8 [rows, H/32] (E8M0), expert_offsets int32 [E+1],
+    weights u8 [E, N, H], weight_scales u8 [E, N, H/32] -> y bf16 [rows, N]
+    (rows outside every instance's range are not written)."""
+    rows, H = expand_x.shape
+    E = expert_offsets.numel() - 1
+    N = weights.shape[1]
+    if y is None:
+        y = torch.empty((rows, N), dtype=torch.bfloat16, device=expand_x.device)
+    rc = _lib.moe_expert_gemm(_ptr(expand_x), _ptr(expand_scales), _ptr(expert_offsets), E, rows,
+                              _ptr(weights), _ptr(weight_scales), N, H, quant_mode, _ptr(y),
+                              _ptr(dev_err), _stream(stream))
+    _check("moe_expert_gemm", rc)
+    return y
 
 
 def raw():

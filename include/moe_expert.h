@@ -80,6 +80,7 @@ typedef enum {
                                instance id in the table outside [0, n_instances)         */
 #define MOE_ERR_MASK1D 4    /* a 1-D token mask that is not all-true-then-all-false      */
 #define MOE_ERR_ROW 8       /* combine: an assist_dst entry >= Bs*K                      */
+#define MOE_ERR_OFFSETS 16  /* expert GEMM: offsets not non-decreasing within [0, rows]   */
 
 /*
  * moe_update_expert -- load balancing and expert pruning
@@ -237,6 +238,38 @@ int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
                             const void *residual_x, const void *gamma, float eps, int Bs,
                             int H, int K, int shared_mode, void *y, void *x_out, float *rstd,
                             int32_t *dev_err, void *stream);
+
+/*
+ * moe_expert_gemm -- the expert computation between dispatch and combine
+ * (the calling sequence of "aclnnMoeUpdateExpert" places it there; the pages
+ * do not define it).  One linear layer per instance over the rows dispatch
+ * wrote for it, reading expand_x and expand_scales as dispatch leaves them
+ * ("aclnnMoeDistributeDispatchV2", case 5: mxfp8):
+ *
+ *   for e < n_instances, r in [expert_offsets[e], expert_offsets[e+1]), n < N:
+ *     y[r][n] = bf16( sum_k  A(r, k) * W(e, n, k) )        (fp32 accumulation)
+ *     A(r, k)    = e4m3(expand_x[r][k])   * 2^(expand_scales[r][k/32] - 127)
+ *     W(e, n, k) = e4m3(weights[e][n][k]) * 2^(weight_scales[e][n][k/32] - 127)
+ *
+ *   expand_x       u8 E4M3 [rows, H]     16-byte aligned
+ *   expand_scales  u8 E8M0 [rows, H/32]  4-byte aligned
+ *   expert_offsets int32 [n_instances+1] (moe_dispatch's offsets, or a slice
+ *                  of them for a subset of instances; values are absolute rows)
+ *   weights        u8 E4M3 [n_instances, N, H]     16-byte aligned
+ *   weight_scales  u8 E8M0 [n_instances, N, H/32]  4-byte aligned
+ *   y              bf16 [rows, N] (out; rows outside every instance's range
+ *                  are not written)  16-byte aligned
+ *   dev_err        int32 [1] or NULL: MOE_ERR_OFFSETS when the offsets are not
+ *                  non-decreasing within [0, rows]; every range is then
+ *                  clamped into [0, rows] and the output is unspecified
+ *                  (but no access leaves the buffers)
+ * Limits: 1 <= n_instances <= 1024, rows >= 0, H and N multiples of 128 in
+ * [128, 16384], quant_mode = MOE_Q_MXFP8 (other modes: MOE_ENOTSUP).
+ */
+int moe_expert_gemm(const void *expand_x, const void *expand_scales,
+                    const int32_t *expert_offsets, int n_instances, int rows,
+                    const void *weights, const void *weight_scales, int N, int H,
+                    int quant_mode, void *y, int32_t *dev_err, void *stream);
 
 /* A static, human-readable name for a moe_status value. */
 const char *moe_status_string(int status);

@@ -26,8 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["moe_combine_add_rmsnorm", "moe_dispatch",
-                                    "moe_status_string", "moe_update_dispatch",
-                                    "moe_update_expert"]
+                                    "moe_expert_gemm", "moe_status_string",
+                                    "moe_update_dispatch", "moe_update_expert"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -163,3 +163,24 @@ def test_fused_update_dispatch_rejects_out_of_range_arguments():
     # a table too large to stage in LDS, odd tiles: not supported
     for kw in (dict(nl=1024, F=13, K=16), dict(q=3, tile=96)):
         assert fused(**kw) == 2, kw
+
+
+def gemm(**kw):
+    from combine_expert_amd import moe
+    a = dict(a=P, asc=P, off=P, E=8, rows=4096, w=P, wsc=P, N=4096, H=7168, q=4, y=P, err=None)
+    a.update(kw)
+    return moe.raw().moe_expert_gemm(a["a"], a["asc"], a["off"], a["E"], a["rows"], a["w"],
+                                     a["wsc"], a["N"], a["H"], a["q"], a["y"], a["err"], None)
+
+
+@pytest.mark.skipif("not _no_gpu()")
+def test_expert_gemm_rejects_out_of_range_arguments():
+    bad = [dict(a=None), dict(asc=None), dict(off=None), dict(w=None), dict(wsc=None),
+           dict(y=None), dict(E=0), dict(E=1025), dict(rows=-1), dict(H=7168 + 32), dict(H=0),
+           dict(H=16384 + 128), dict(N=100), dict(N=0), dict(N=16384 + 128), dict(q=5),
+           dict(q=-1), dict(a=P + 8), dict(w=P + 4), dict(y=P + 8), dict(asc=P + 2),
+           dict(wsc=P + 1), dict(off=P + 2), dict(err=P + 1)]
+    for kw in bad:
+        assert gemm(**kw) == 1, kw
+    for q in (0, 1, 2, 3):
+        assert gemm(q=q) == 2, q
