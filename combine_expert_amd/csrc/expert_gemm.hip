@@ -8,14 +8,27 @@
 // dequantised per block of 32 along K as E4M3 value x 2^(E8M0 code - 127) --
 // the mxfp8 expandX / dynamicScales layout of that page's case 5.
 //
-// Tiling.  A block computes a 128 x 128 output tile (128 rows of one
-// instance x 128 output columns) with four waves of 64 x 64 each.  K is
-// walked 128 at a time; both operand tiles (16 KB each) and their scale bytes
-// go through registers into a double-buffered LDS stage, so the global loads
-// of step s+1 are in flight while the MFMAs of step s run, with one LDS
-// barrier per step.  Each 128-byte LDS row keeps its eight 16-byte chunks in
-// XOR-swizzled order (chunk c at c ^ (row & 7)) so that the fragment reads of
-// sixteen consecutive rows spread over the banks.
+// Tiling.  One block per CU computes a 128 x 256 output tile (128 rows of one
+// instance x 256 output columns) with four waves of 64 x 128 each.  The tile
+// size is set by the L2 -> CU load rate (about 50 B/clk per CU measured): a
+// K step of 128 brings (128 + 256) x 128 bytes for 128 x 256 x 128 MACs,
+// which keeps the loads under that rate at full MFMA speed, where a 128 x 128
+// tile does not.
+//
+// Pipeline.  K is walked 128 at a time through a three-stage LDS ring.  The
+// operand tiles go global -> LDS with global_load_lds_dwordx4 (no register
+// staging, no LDS store instructions: those run at about a third of the LDS
+// read rate) two steps ahead of the MFMAs, so each step waits only for loads
+// issued two steps earlier.  A wave's DMA instruction fills 1 KB of LDS
+// lane-contiguously; each 128-byte LDS row keeps its eight 16-byte chunks in
+// XOR-swizzled order (slot s holds chunk s ^ (row & 7)), which the lanes
+// realise by fetching the permuted global chunk, so that the MFMA fragment
+// reads of sixteen consecutive rows spread over the banks.  The scale bytes
+// travel separately: when a row's scales for four K steps are 16 contiguous
+// bytes (K a multiple of 512) one 16-byte copy per row brings them every
+// fourth step into a two-group ring; otherwise a 4-byte copy per row each step.
+// Either way a copy touches one line per row, so the scales cost as many L2
+// line requests as the tiles they scale unless they are grouped.
 //
 // MFMA operand layout (v_mfma_scale_f32_16x16x128_f8f6f4, measured): lane l
 // holds 32 K-bytes of row l % 16 of its operand: bytes 0-15 are K offsets
@@ -32,6 +45,7 @@
 // blocks working on one weight tile run together.  Consecutive block ids are
 // spread over the eight XCDs round-robin by the hardware, so the block id is
 // remapped to give each XCD (and its L2) a contiguous range of tiles.
+#include <stddef.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -44,12 +58,26 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 128;        // rows per tile
-constexpr int kBN = 128;        // output columns per tile
+constexpr int kBN = 256;        // output columns per tile
 constexpr int kBK = 128;        // K elements (bytes) per step
-constexpr int kGemmThreads = 256;
+constexpr int kStages = 3;
+constexpr int kWavesM = 2;      // waves along the rows of a tile
+constexpr int kWavesN = 2;      // waves along the columns
+constexpr int kGemmWaves = kWavesM * kWavesN;
+constexpr int kGemmThreads = kGemmWaves * 64;
+constexpr int kFragM = kBM / kWavesM / 16;   // 16-row MFMA fragments per wave (activations)
+constexpr int kFragN = kBN / kWavesN / 16;   // 16-row MFMA fragments per wave (weights)
+// per wave and step: 1 KB DMA runs of the two tiles (8 rows x 128 bytes each)
+constexpr int kXRuns = kBM / 8 / kGemmWaves;
+constexpr int kWRuns = kBN / 8 / kGemmWaves;
+constexpr int kDataLoads = kXRuns + kWRuns;
 constexpr int kXcds = 8;
+constexpr int kCus = 256;
 constexpr int kMaxInstances = 1024;
-constexpr int kGemmGrid = 1024;  // grid-stride cap (a multiple of the XCD count)
+constexpr int kGroupM = 8;      // row tiles per patch of the tile order
+constexpr int kScaleGroup = 4;  // K steps per grouped scale copy (16 bytes per row)
+
+static_assert(kBM / 64 <= kGemmWaves && kBN / 64 == kGemmWaves, "scale runs: one per wave");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -66,10 +94,55 @@ struct GemmArgs {
 };
 
 struct Stage {
-    uint8_t x[kBM * kBK];
-    uint8_t w[kBN * kBK];
-    uint32_t sc[kBM + kBN];  // the step's four scale bytes of each row: activations, weights
+    uint8_t x[kBM * kBK];    // 16 KB: activation rows, swizzled 16-byte chunks
+    uint8_t w[kBN * kBK];    // 32 KB: weight rows
 };
+
+// Scale words of one K step (4 bytes per row) or of a group of four steps (16 bytes per row).
+template <int STEPS>
+struct Scales {
+    uint32_t x[kBM][STEPS];
+    uint32_t w[kBN][STEPS];
+};
+
+// s_waitcnt immediate (gfx9 layout): vmcnt <= n, expcnt and lgkmcnt not waited on
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// One lane's share of a wave-wide global -> LDS copy: lane i's bytes land at
+// LDS address lds + i * size, lds being the same for the whole wave (it goes
+// through M0).  Written as inline asm on purpose: the compiler would make
+// every later LDS read, and every LDS fence, wait for all such copies in
+// flight, which caps the pipeline at one step; here the waits are explicit.
+// The asm has no output registers (the data goes to LDS), and the address
+// registers are read when the instruction issues.
+__device__ __forceinline__ void dma16(const uint8_t *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ void dma4(const uint8_t *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+                 :: "v"(src), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)p);
+}
+
+// s_waitcnt needs an immediate: the few counts the kernel uses, chosen at run time by a
+// wave-uniform value
+__device__ __forceinline__ void wait_vm(int n)
+{
+    switch (n) {
+    case kDataLoads: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDataLoads)); break;
+    case kDataLoads + 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDataLoads + 1)); break;
+    case kDataLoads + 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDataLoads + 2)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    }
+}
 
 // Clamped row range of instance e: [lo, hi) within [0, rows); *bad is set
 // when the offsets are not non-decreasing within [0, rows].
@@ -83,15 +156,21 @@ __device__ __forceinline__ void instance_rows(const GemmArgs &p, int e, int &lo,
         *bad = o0 < 0 || o1 < o0 || o1 > p.rows;
 }
 
-__global__ __launch_bounds__(kGemmThreads, 2) void k_expert_gemm_mx(GemmArgs p)
+// GROUPED: scales in 16-byte groups of four K steps (needs K % 512 == 0), else per step.
+template <bool GROUPED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
 {
-    __shared__ __align__(16) Stage s_stage[2];
-    __shared__ int s_tiles[kMaxInstances + 1];  // exclusive prefix of row tiles per instance
-    __shared__ int s_wave_sum[kGemmThreads / kWave];
+    constexpr int kScaleSteps = GROUPED ? kScaleGroup : 1;
+    constexpr int kScaleBufs = GROUPED ? 2 : kStages;
+    using Sc = Scales<kScaleSteps>;
+    __shared__ __align__(16) Stage s_stage[kStages];
+    __shared__ __align__(16) Sc s_scale[kScaleBufs];
+    __shared__ uint16_t s_tiles[kMaxInstances + 1];  // exclusive prefix of row tiles per instance
+    __shared__ int s_wave_sum[kGemmWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
     // ---- row tiles per instance, prefix-summed (thread t owns instances 4t .. 4t+3)
     int c[4], tsum = 0;
@@ -122,14 +201,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_expert_gemm_mx(GemmArgs p)
     for (int q = 0; q < 4; ++q) {
         const int e = 4 * tid + q;
         if (e < p.E)
-            s_tiles[e] = excl;
+            s_tiles[e] = (uint16_t)excl;
         if (e == p.E - 1)
-            s_tiles[p.E] = excl + c[q];
+            s_tiles[p.E] = (uint16_t)(excl + c[q]);
         excl += c[q];
     }
     lds_barrier();
     const int m_tiles = s_tiles[p.E];
-    const int n_tiles = p.N / kBN;
+    const int n_tiles = (p.N + kBN - 1) / kBN;
     const int total = m_tiles * n_tiles;
 
     // ---- XCD-grouped virtual block id
@@ -141,16 +220,28 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_expert_gemm_mx(GemmArgs p)
     const int kb = p.K / 32;                  // scale bytes per row
     const int g = lane >> 4;                  // lane group: K chunk / scale block
     const int r16 = lane & 15;
-    const int wn = wave & 1, wm = wave >> 1;  // wave's 64 x 64 quadrant (columns, rows)
+    const int wn = wave % kWavesN, wm = wave / kWavesN;   // the wave's part of the tile
+    // scale runs of 64 rows: every wave one of the weights; the first kBM / 64 waves also one
+    // of the activations
+    const bool x_run = wave < kBM / 64;
+    const int n_scale = x_run ? 2 : 1;        // scale copies per issue (wave-uniform)
 
-    // global -> register staging: thread owns 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 j
-    const int ld_chunk = tid & 7;
-    const int ld_row = tid >> 3;
-    const int sw_chunk = (ld_chunk ^ (ld_row & 7)) << 4;  // swizzled LDS byte offset in the row
+    // DMA lane mapping: one instruction covers 8 rows x 128 bytes; lane -> row lane / 8, LDS
+    // slot lane % 8, global chunk slot ^ row (runs start at multiples of 8 rows, so
+    // row & 7 = lane / 8)
+    const int dma_row = lane >> 3;
+    const int dma_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
+    const int fr_c0 = ((g ^ (r16 & 7)) << 4);   // swizzled offsets of chunks g and g + 4
+    const int fr_c1 = (((g + 4) ^ (r16 & 7)) << 4);
 
     for (int t = v; t < total; t += G) {
-        const int tm = t % m_tiles;
-        const int tn = t / m_tiles;
+        // patch order: kGroupM row tiles x every column tile, row tiles fastest, so the 32
+        // blocks an XCD runs at once share about 8 row tiles and 4 column tiles
+        const int grp = t / (kGroupM * n_tiles);
+        const int tin = t - grp * kGroupM * n_tiles;
+        const int gm = min(kGroupM, m_tiles - grp * kGroupM);
+        const int tm = grp * kGroupM + tin % gm;
+        const int tn = tin / gm;
         // instance of row tile tm: the last e with s_tiles[e] <= tm
         int lo_e = 0, hi_e = p.E;
         while (hi_e - lo_e > 1) {
@@ -165,112 +256,142 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_expert_gemm_mx(GemmArgs p)
         instance_rows(p, e, row_lo, row_hi, nullptr);
         const int m0 = row_lo + (tm - s_tiles[e]) * kBM;   // first row of the tile
         const int n0 = tn * kBN;
-
-        // per-thread global sources for the step (rows past the instance are clamped to its
-        // last row: loaded, multiplied, never stored)
-        const uint8_t *xsrc[4];
-        const uint8_t *wsrc[4];
         const uint8_t *w_e = p.w + (size_t)e * p.N * p.K;
+
+        // this thread's DMA sources at K offset 0.  Rows past the instance (or past N) are
+        // clamped to its last row (column): loaded, multiplied, never stored.
+        const uint8_t *xsrc[kXRuns];
+        const uint8_t *wsrc[kWRuns];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = min(m0 + ld_row + 32 * j, row_hi - 1);
-            xsrc[j] = p.a + (size_t)r * p.K + ld_chunk * 16;
-            wsrc[j] = w_e + (size_t)(n0 + ld_row + 32 * j) * p.K + ld_chunk * 16;
+        for (int q = 0; q < kXRuns; ++q) {
+            const int r = min(m0 + (wave * kXRuns + q) * 8 + dma_row, row_hi - 1);
+            xsrc[q] = p.a + (size_t)r * p.K + dma_chunk;
         }
-        const uint8_t *scsrc;
-        if (tid < kBM)
-            scsrc = p.a_sc + (size_t)min(m0 + tid, row_hi - 1) * kb;
-        else
-            scsrc = p.w_sc + ((size_t)e * p.N + n0 + (tid - kBM)) * kb;
-
-        u32x4 rx[4], rw[4];
-        uint32_t rsc;
-#define MOE_GEMM_LOAD_STEP(s_)                                                             \
-    do {                                                                                   \
-        const int k0_ = (s_) * kBK;                                                        \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                      \
-        {                                                                                  \
-            rx[j] = *reinterpret_cast<const u32x4 *>(xsrc[j] + k0_);                       \
-            rw[j] = *reinterpret_cast<const u32x4 *>(wsrc[j] + k0_);                       \
-        }                                                                                  \
-        rsc = *reinterpret_cast<const uint32_t *>(scsrc + k0_ / 32);                       \
-    } while (0)
-#define MOE_GEMM_STORE_STEP(st_)                                                           \
-    do {                                                                                   \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                      \
-        {                                                                                  \
-            const int row_ = ld_row + 32 * j;                                              \
-            *reinterpret_cast<u32x4 *>(&(st_).x[row_ * kBK + sw_chunk]) = rx[j];           \
-            *reinterpret_cast<u32x4 *>(&(st_).w[row_ * kBK + sw_chunk]) = rw[j];           \
-        }                                                                                  \
-        (st_).sc[tid] = rsc;                                                               \
-    } while (0)
-
-        v4f acc[4][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int q = 0; q < kWRuns; ++q) {
+            const int n = min(n0 + (wave * kWRuns + q) * 8 + dma_row, p.N - 1);
+            wsrc[q] = w_e + (size_t)n * p.K + dma_chunk;
+        }
+        const uint8_t *wsc_src =
+            p.w_sc + ((size_t)e * p.N + min(n0 + wave * 64 + lane, p.N - 1)) * kb;
+        const uint8_t *xsc_src =
+            p.a_sc + (size_t)min(m0 + (x_run ? wave : 0) * 64 + lane, row_hi - 1) * kb;
+
+        // copies of K step s into stage s % kStages
+        auto issue_data = [&](int s) {
+            const int k0 = s * kBK;
+            const uint8_t *base = reinterpret_cast<const uint8_t *>(&s_stage[s % kStages]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int q = 0; q < kXRuns; ++q)
+                dma16(xsrc[q] + k0, lds_addr(base + offsetof(Stage, x) + (wave * kXRuns + q) * 1024));
+#pragma unroll
+            for (int q = 0; q < kWRuns; ++q)
+                dma16(wsrc[q] + k0, lds_addr(base + offsetof(Stage, w) + (wave * kWRuns + q) * 1024));
+        };
+        // scale copies: buffer `buf`, scale bytes from byte offset `off` of each row
+        auto issue_scales = [&](int buf, int off) {
+            Sc &sc = s_scale[buf];
+            if (GROUPED) {
+                dma16(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+                if (x_run)
+                    dma16(xsc_src + off, lds_addr(&sc.x[wave * 64][0]));
+            } else {
+                dma4(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+                if (x_run)
+                    dma4(xsc_src + off, lds_addr(&sc.x[wave * 64][0]));
+            }
+        };
+
+        v4f acc[kFragN][kFragM];
+#pragma unroll
+        for (int i = 0; i < kFragN; ++i)
+#pragma unroll
+            for (int j = 0; j < kFragM; ++j)
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-        MOE_GEMM_LOAD_STEP(0);
-        MOE_GEMM_STORE_STEP(s_stage[0]);
+        // prologue: step 0 (and its scales), then step 1; wait for the first two
+        issue_data(0);
+        issue_scales(0, 0);
+        issue_data(min(1, nk - 1));
+        if (!GROUPED)
+            issue_scales(1 % kStages, 4 * min(1, nk - 1));
+        wait_vm(GROUPED ? kDataLoads : kDataLoads + n_scale);
         lds_barrier();
 
-        const int fr_c0 = ((g ^ (r16 & 7)) << 4);   // swizzled offsets of chunks g and g + 4
-        const int fr_c1 = (((g + 4) ^ (r16 & 7)) << 4);
         for (int s = 0; s < nk; ++s) {
-            // prefetch the next step (the last step reloads itself: no branch in the body,
-            // which would let the compiler sink the MFMAs below the stores)
-            const int s_next = min(s + 1, nk - 1);
-            MOE_GEMM_LOAD_STEP(s_next);
-            __builtin_amdgcn_sched_barrier(0);   // issue the loads before the MFMAs
-            const Stage &st = s_stage[s & 1];
-            v8i xf[4];
-            int xs[4];
+            // copies two steps ahead (the last two steps reload the final K step into stages
+            // nobody reads any more: no branch in the count of copies in flight)
+            const int s2 = min(s + 2, nk - 1);
+            issue_data(s2);
+            bool grouped_issue = false;
+            if (GROUPED) {
+                // every fourth step, the next group into the other buffer (the last group
+                // reloads itself there, unused)
+                if (s % kScaleGroup == 0) {
+                    const int gi = min(s / kScaleGroup + 1, nk / kScaleGroup - 1);
+                    issue_scales((s / kScaleGroup + 1) & 1, 16 * gi);
+                    grouped_issue = true;
+                }
+            } else {
+                issue_scales((s + 2) % kStages, 4 * s2);
+            }
+
+            const Stage &st = s_stage[s % kStages];
+            const Sc &sc = s_scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
+            const int sw = GROUPED ? s % kScaleGroup : 0;
+            v8i xf[kFragM];
+            int xs[kFragM];
 #pragma unroll
-            for (int fm = 0; fm < 4; ++fm) {
-                const int row = wm * 64 + fm * 16 + r16;
+            for (int fm = 0; fm < kFragM; ++fm) {
+                const int row = wm * (kBM / kWavesM) + fm * 16 + r16;
                 const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c0]);
                 const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
                 xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                xs[fm] = (int)((st.sc[row] >> (8 * g)) & 0xffu);
+                xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
             }
 #pragma unroll
-            for (int fn = 0; fn < 4; ++fn) {
-                const int row = wn * 64 + fn * 16 + r16;
+            for (int fn = 0; fn < kFragN; ++fn) {
+                const int row = wn * (kBN / kWavesN) + fn * 16 + r16;
                 const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c0]);
                 const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
                 const v8i wf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                const int ws = (int)((st.sc[kBM + row] >> (8 * g)) & 0xffu);
+                const int ws = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
 #pragma unroll
-                for (int fm = 0; fm < 4; ++fm)
+                for (int fm = 0; fm < kFragM; ++fm)
                     acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         wf, xf[fm], acc[fn][fm], 0, 0, 0, ws, 0, xs[fm]);
             }
-            // keep the next stage's LDS stores (which wait for this step's global loads)
-            // behind the MFMAs, so the load latency hides under them
-            __builtin_amdgcn_sched_barrier(0);
-            MOE_GEMM_STORE_STEP(s_stage[(s + 1) & 1]);
+            // step s+1's copies were issued a step ago: wait for this thread's (only those of
+            // this step may stay in flight; an older scale group must have landed), then for
+            // everyone's
+            if (GROUPED)
+                wait_vm(grouped_issue ? kDataLoads + n_scale : kDataLoads);
+            else
+                wait_vm(kDataLoads + n_scale);
             lds_barrier();
         }
+        // the reloads of the last steps must land before the next tile rewrites the rings
+        wait_vm(0);
+        lds_barrier();
 
-#undef MOE_GEMM_LOAD_STEP
-#undef MOE_GEMM_STORE_STEP
-
-        // ---- epilogue: lane holds columns n0 + wn*64 + fn*16 + 4g .. +3 of row m0 + wm*64 + fm*16 + r16
+        // ---- epilogue: lane holds columns n0 + wn*(kBN/kWavesN) + fn*16 + 4g .. +3 of row
+        //      m0 + wm*(kBM/kWavesM) + fm*16 + r16
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) {
-            const int r = m0 + wm * 64 + fm * 16 + r16;
+        for (int fm = 0; fm < kFragM; ++fm) {
+            const int r = m0 + wm * (kBM / kWavesM) + fm * 16 + r16;
             if (r < row_hi) {
-                uint16_t *yrow = p.y + (size_t)r * p.N + n0 + wn * 64 + 4 * g;
+                uint16_t *yrow = p.y + (size_t)r * p.N;
 #pragma unroll
-                for (int fn = 0; fn < 4; ++fn) {
-                    const v4f d = acc[fn][fm];
-                    const uint2 o = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
-                    *reinterpret_cast<uint2 *>(yrow + fn * 16) = o;
+                for (int fn = 0; fn < kFragN; ++fn) {
+                    const int n = n0 + wn * (kBN / kWavesN) + fn * 16 + 4 * g;
+                    if (n < p.N) {
+                        const v4f d = acc[fn][fm];
+                        const uint2 o = make_uint2(pack_bf16x2(d[0], d[1]),
+                                                   pack_bf16x2(d[2], d[3]));
+                        *reinterpret_cast<uint2 *>(yrow + n) = o;
+                    }
                 }
             }
         }
@@ -286,9 +407,19 @@ hipError_t launch_expert_gemm_mx(const uint8_t *a, const uint8_t *a_sc, const in
     GemmArgs p{a, a_sc, offsets, w, w_sc, y, dev_err, E, rows, N, K};
     // Upper bound on row tiles: sum of ceil(rows_e / 128) <= ceil(rows / 128) + E.
     const long m_cap = (rows + kBM - 1) / kBM + E;
-    const long tiles_cap = m_cap * (N / kBN);
-    const int grid = (int)std::min<long>(tiles_cap, kGemmGrid);
-    hipLaunchKernelGGL(k_expert_gemm_mx, dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    const long tiles_cap = m_cap * ((N + kBN - 1) / kBN);
+    // one resident block per CU, walking the tiles grid-stride
+    const int grid = (int)std::min<long>(tiles_cap, kCus);
+    // grouped scale copies read 16 bytes per row: K a multiple of 512 (whole groups) and
+    // 16-byte aligned scale arrays (the row pitch K/32 is then a multiple of 16 as well)
+    const bool grouped = K % (kBK * kScaleGroup) == 0 &&
+                         (reinterpret_cast<uintptr_t>(a_sc) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(w_sc) & 15) == 0;
+    if (grouped)
+        hipLaunchKernelGGL(k_expert_gemm_mx<true>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(k_expert_gemm_mx<false>, dim3(grid), dim3(kGemmThreads), 0, stream,
+                           p);
     return hipGetLastError();
 }
 
