@@ -18,6 +18,7 @@ moe_dispatch, moe_combine_add_rmsnorm) is timed as well and reported under
     python bench.py --summarize-counters FETCH.csv WRITE.csv --kernel NAME \
                     --sources a.hip,b.h --out profiles/X.txt --command CMD1 --command CMD2
     python bench.py --summarize-copy FETCH.csv WRITE.csv --copy-mb 256 --out profiles/X.txt ...
+    python bench.py --gemm [--steps 50]                  # the expert GEMM row (its own line)
 
 Prints one JSON line.  `value` is whole-step throughput in GB/s of
 algorithmic bytes (each input read once, each output written once) with all
@@ -62,6 +63,8 @@ def parse():
                    help="also time the 16-layer graph-captured stack (c5) and the dispatch "
                         "variants (static and per-instance scales); off by default so that a "
                         "kernel trace of the default run covers the headline step alone")
+    p.add_argument("--gemm", action="store_true",
+                   help="time the expert computation (grouped mxfp8 GEMM) instead; one JSON line")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the step, time a plain device copy of this many MB "
                         "(the reference kernel for counter scaling and achievable bandwidth)")
@@ -78,6 +81,7 @@ def parse():
     g.add_argument("--command", action="append", default=[],
                    help="the command(s) that produced the CSV files")
     g.add_argument("--title", default="rocprofv3 kernel statistics")
+    g.add_argument("--workload-tag", default=None, help="workload named in a counter summary")
     return p.parse_args()
 
 
@@ -198,7 +202,8 @@ def summarize_counters(args):
     rd = round(fetch * 1024 * cal["fetch_scale"])
     wr = round(write * 1024 * cal["write_scale"])
     names = [n for n in args.sources.split(",") if n]
-    d = {"kernel": args.kernel, "workload": WORKLOAD_TAG, "source_digest": source_digest(*names),
+    d = {"kernel": args.kernel, "workload": args.workload_tag or WORKLOAD_TAG,
+         "source_digest": source_digest(*names),
          "source_files": names, "FETCH_SIZE_KiB_per_dispatch": fetch,
          "WRITE_SIZE_KiB_per_dispatch": write, "dispatches": [nf, nw],
          "fetch_scale": cal["fetch_scale"], "write_scale": cal["write_scale"],
@@ -542,6 +547,143 @@ def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
             "tokens_per_s": round(wl.Bs / t, 1)}
 
 
+# ----------------------------------------------------------------- expert GEMM row
+
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+GEMM_METRIC = "expert GEMM TFLOP/s (mxfp8 x mxfp8 -> bf16, fp32 accumulate)"
+GEMM_TAG = "8 instances, 4096 rows (Zipf split), H=7168 -> N=4096, mxfp8 (bench.py --gemm)"
+
+
+def gemm_sample(g, np, oracle, rows_per_instance=3, n_cols=256, seed=9):
+    """Rows (first, middle, last of each instance) and columns of a sub-problem the oracle
+    finishes quickly; returns (rows, cols, y64, abs64)."""
+    rows, inst = [], []
+    for e in range(g.E):
+        lo, hi = int(g.offsets[e]), int(g.offsets[e + 1])
+        pick = sorted({lo, (lo + hi) // 2, hi - 1})[:rows_per_instance] if hi > lo else []
+        rows += pick
+        inst += [e] * len(pick)
+    rows = np.array(rows)
+    cols = np.sort(np.random.default_rng(seed).choice(g.N, min(n_cols, g.N), replace=False))
+    off = np.zeros(g.E + 1, np.int32)
+    off[1:] = np.cumsum(np.bincount(np.array(inst), minlength=g.E))
+    _, y64, abs64 = oracle.expert_gemm_mx(g.a[rows], g.a_sc[rows], off,
+                                          np.ascontiguousarray(g.w[:, cols]),
+                                          np.ascontiguousarray(g.w_sc[:, cols]))
+    return rows, cols, y64, abs64
+
+
+def gemm_cpu_baseline(g, np, oracle, budget_s):
+    """The oracle on whole output rows (all N columns) of the workload, as many rows as fit
+    the budget after a one-row probe; TFLOP/s of that sample."""
+    e = int(np.argmax(np.diff(g.offsets)))
+    lo = int(g.offsets[e])
+
+    def run(n):
+        off = np.zeros(g.E + 1, np.int32)
+        off[e + 1:] = n
+        t0 = time.perf_counter()
+        oracle.expert_gemm_mx(g.a[lo:lo + n], g.a_sc[lo:lo + n], off, g.w, g.w_sc)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = max(1, min(int(budget_s / t1), int(g.offsets[e + 1]) - lo))
+    t = run(n) if n > 1 else t1
+    fl = 2.0 * n * g.N * g.Kd
+    return {"value": round(fl / t / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} whole output rows (all {g.N} columns, K={g.Kd}) of instance {e}, "
+                      f"{t:.1f} s",
+            "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def gemm_main(args):
+    import numpy as np
+    import torch
+
+    from combine_expert_amd import build as hip_build
+    if hip_build.stale():
+        hip_build.build()
+    from combine_expert_amd import moe
+    from combine_expert_amd import workloads as W
+
+    g = W.make_g3()
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    lib = moe.raw()
+    dev = torch.device("cuda")
+    n_sets = 2   # two weight copies (2 x 235 MB) so a launch cannot hit in the 256 MB MALL
+    a = torch.from_numpy(g.a).to(dev)
+    asc = torch.from_numpy(g.a_sc).to(dev)
+    off = torch.from_numpy(g.offsets).to(dev)
+    ws = [torch.from_numpy(g.w).to(dev) for _ in range(n_sets)]
+    wss = [torch.from_numpy(g.w_sc).to(dev) for _ in range(n_sets)]
+    ys = [torch.empty((g.rows, g.N), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    argv = [(a.data_ptr(), asc.data_ptr(), off.data_ptr(), g.E, g.rows, ws[k].data_ptr(),
+             wss[k].data_ptr(), g.N, g.Kd, moe.QUANT_MXFP8, ys[k].data_ptr(), None,
+             stream.cuda_stream) for k in range(n_sets)]
+    f = lib.moe_expert_gemm
+
+    def launches(n):
+        rc = 0
+        for k in range(n):
+            rc |= f(*argv[k % n_sets])
+        if rc:
+            raise RuntimeError("moe_expert_gemm returned a non-zero status")
+
+    launches(args.warmup)
+    torch.cuda.synchronize()
+    ok = True
+    if not args.no_check:
+        import oracle
+        rows, cols, y64, abs64 = gemm_sample(g, np, oracle)
+        got = ys[0].float().cpu().numpy()[rows][:, cols].astype(np.float64)
+        tol = 2.0 ** -8 * np.abs(y64) + (7 * 2.0 ** -13 + g.Kd * 2.0 ** -26) * abs64
+        ok = bool(np.all(np.abs(got - y64) <= tol))
+    K = args.steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    launches(K)
+    torch.cuda.synchronize()
+    t_wall = (time.perf_counter() - t0) / K
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    launches(K)
+    e1.record(stream)
+    e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / K
+    rows_total = int(g.offsets[-1])
+    flops = 2.0 * rows_total * g.N * g.Kd
+    tfs = flops / (us * 1e-6) / 1e12
+    alg_bytes = g.a.nbytes + g.a_sc.nbytes + g.w.nbytes + g.w_sc.nbytes + rows_total * g.N * 2
+    traffic = counter_traffic("expert_gemm_g3_traffic.txt", ("expert_gemm.hip", "device.h"))
+    line = {
+        "metric": GEMM_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(t_wall * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": "expert computation of one expert-parallel rank in a "
+                               "DeepSeek-V3-shaped layer: 8 instances, 4096 rows split by a "
+                               "Zipf(1.2) draw, H=7168 -> N=4096 (gate and up projections), "
+                               "mxfp8 operands with E8M0 block scales, bf16 out",
+                   "E": g.E, "rows": rows_total, "counts": g.counts.tolist(), "N": g.N,
+                   "H": g.Kd, "weight_sets": n_sets},
+        "roofline": {"kernel": "k_expert_gemm_mx", "bound": "mfma", "achieved": round(tfs, 2),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tfs / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(us, 3)},
+        "hbm_GBps_algorithmic": round(alg_bytes / (us * 1e-6) / 1e9, 1),
+        "parity_sample": "ok" if ok else "MISMATCH",
+        "cpu_baseline": None,
+    }
+    if args.cpu_seconds > 0:
+        import oracle
+        line["cpu_baseline"] = gemm_cpu_baseline(g, np, oracle, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    if not ok:
+        sys.exit(1)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -558,6 +700,8 @@ def main():
     if args.copy_mb:
         copy_calibration(args.copy_mb, args.steps, args.warmup)
         return
+    if args.gemm:
+        return gemm_main(args)
 
     import numpy as np
     import torch
