@@ -362,6 +362,44 @@ def make_gemm_case(seed: int, counts, N: int, Kd: int, tail: int = 0,
     return GemmCase(name, E, N, Kd, rows, offsets, a, a_sc, w, w_sc)
 
 
+@dataclass
+class GemmCaseI8:
+    name: str
+    E: int
+    N: int
+    Kd: int
+    rows: int
+    offsets: np.ndarray      # int32 [E+1]
+    a: np.ndarray            # int8 [rows, Kd]
+    a_sc: np.ndarray         # f32 [rows] (per token) or [rows, Kd/128] (per tile)
+    w: np.ndarray            # int8 [E, N, Kd]
+    w_sc: np.ndarray         # f32 [E, N] (one per output column)
+
+    @property
+    def counts(self) -> np.ndarray:
+        return np.diff(self.offsets).astype(np.int32)
+
+
+def make_gemm_case_i8(seed: int, counts, N: int, Kd: int, per_tile: bool, tail: int = 0,
+                      name: str = "gemm_i8") -> GemmCaseI8:
+    """int8 grouped-GEMM operands: codes uniform in [-127, 127] (the range the dynamic
+    quantisers produce), activation scales uniform in [0.002, 0.05] per row or per tile of
+    128 (1/127 of a row maximum of about 0.25 .. 6), weight scales uniform in
+    [0.0002, 0.002] per output column."""
+    rng = np.random.default_rng(seed)
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.size
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    rows = int(offsets[-1]) + tail
+    a = rng.integers(-127, 128, size=(rows, Kd), dtype=np.int8)
+    a_sc = rng.uniform(0.002, 0.05, size=(rows, Kd // 128) if per_tile else (rows,))
+    w = rng.integers(-127, 128, size=(E, N, Kd), dtype=np.int8)
+    w_sc = rng.uniform(0.0002, 0.002, size=(E, N))
+    return GemmCaseI8(name, E, N, Kd, rows, offsets, a, a_sc.astype(np.float32), w,
+                      w_sc.astype(np.float32))
+
+
 def make_g3(seed: int = 3100) -> GemmCase:
     rng = np.random.default_rng(seed)
     counts = zipf_counts(rng, 4096, 8, 1.2)

@@ -43,9 +43,10 @@ def lib():
                                                  P, P, P]
         L.oracle_e4m3_decode.argtypes = [P, i, P]
         L.oracle_expert_gemm_mx.argtypes = [P, P, P, i, i, P, P, i, i, P, P, P]
+        L.oracle_expert_gemm_i8.argtypes = [P, P, i, P, i, i, P, P, i, i, P, P, P]
         for f in (L.oracle_update_expert, L.oracle_route, L.oracle_dispatch,
                   L.oracle_dispatch_scaled, L.oracle_combine_add_rmsnorm,
-                  L.oracle_expert_gemm_mx):
+                  L.oracle_expert_gemm_mx, L.oracle_expert_gemm_i8):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -236,4 +237,30 @@ def expert_gemm_mx(a, a_sc, offsets, w, w_sc, y_init=None):
                                      Kd, _p(y), _p(y64), _p(abs64))
     if rc:
         raise ValueError(f"oracle_expert_gemm_mx rc={rc}")
+    return y, y64, abs64
+
+
+def expert_gemm_i8(a, a_sc, offsets, w, w_sc, y_init=None):
+    """Expert computation on int8 operands.  a int8 [rows, Kd]; a_sc f32 [rows] (one scale
+    per row) or [rows, Kd/128] (per tile of 128); offsets int32 [E+1]; w int8 [E, N, Kd];
+    w_sc f32 [E, N].  Returns (y_bits, y64, abs64) as expert_gemm_mx."""
+    a = _c(a, np.int8)
+    rows, Kd = a.shape
+    a_sc = _c(a_sc, np.float32)
+    n_tiles = 1 if a_sc.ndim == 1 else a_sc.shape[1]
+    assert a_sc.shape[0] == rows
+    offsets = _c(offsets, np.int32)
+    E = offsets.size - 1
+    w = _c(w, np.int8)
+    N = w.shape[1]
+    assert w.shape == (E, N, Kd)
+    w_sc = _c(w_sc, np.float32)
+    assert w_sc.shape == (E, N)
+    y = np.zeros((rows, N), dtype=np.uint16) if y_init is None else _c(y_init, np.uint16).copy()
+    y64 = np.zeros((rows, N), dtype=np.float64)
+    abs64 = np.zeros((rows, N), dtype=np.float64)
+    rc = lib().oracle_expert_gemm_i8(_p(a), _p(a_sc), n_tiles, _p(offsets), E, rows, _p(w),
+                                     _p(w_sc), N, Kd, _p(y), _p(y64), _p(abs64))
+    if rc:
+        raise ValueError(f"oracle_expert_gemm_i8 rc={rc}")
     return y, y64, abs64

@@ -54,7 +54,11 @@
  *     to instance e and are multiplied by that instance's weight matrix W[e]
  *     ([N, H], one row per output column); for mxfp8 both operands are
  *     dequantised as code value * 2^(scale byte - 127) per block of 32 along
- *     H, the products are summed exactly (fp64) and rounded once to bf16.
+ *     H, the products are summed exactly (fp64) and rounded once to bf16; for
+ *     int8 (the per-token and per-tile outputs of [DSP] cases 3 and 4) the
+ *     activations are dequantised as code * scale of their row (per token) or
+ *     of their row's tile of 128 (per tile), the weights as code * one scale
+ *     per output column, the integer products summed exactly per tile.
  *
  * Precision: the quantisers work in fp32 exactly as the dispatch formula's
  * CastToFp32 prescribes (IEEE division, no contraction; build with
@@ -604,6 +608,57 @@ int oracle_expert_gemm_mx(const uint8_t *a, const uint8_t *a_sc, const int32_t *
                     double wv = e4m3_value(we[(size_t)n * Kd + k]) * e8m0_value(wse[(size_t)n * nb + k / 32]);
                     sum += av * wv;
                     mag += fabs(av * wv);
+                }
+                y[(size_t)r * N + n] = bf16_from_double(sum);
+                if (y64)
+                    y64[(size_t)r * N + n] = sum;
+                if (abs64)
+                    abs64[(size_t)r * N + n] = mag;
+            }
+        }
+    }
+    return 0;
+}
+
+/* [SEQ] expert computation, int8 operands (the expandX / dynamicScales of
+ * [DSP] case 3, per token, or case 4 with tiles of 128, per tile): for each
+ * instance e < E and each row r in [offsets[e], offsets[e+1]), n < N:
+ *   y[r][n] = bf16( sum_t a_sc[r][t] * w_sc[e][n] * sum_{k in tile t} a[r][k] * w[e][n][k] )
+ * with n_tiles = 1 (one scale per row, the tile is all of Kd) or Kd / 128 (one
+ * scale per row and tile of 128).  The integer sums are exact (int64), the
+ * scaling and the sum over tiles are fp64, rounded once to bf16.  y64 / abs64
+ * as for mxfp8 (abs64 = sum over k of |dequantised a * dequantised w|).
+ * Returns -1 for bad sizes or offsets. */
+int oracle_expert_gemm_i8(const int8_t *a, const float *a_sc, int n_tiles, const int32_t *offsets,
+                          int E, int rows, const int8_t *w, const float *w_sc, int N, int Kd,
+                          uint16_t *y, double *y64, double *abs64)
+{
+    if (E <= 0 || rows < 0 || N <= 0 || Kd <= 0)
+        return -1;
+    if (!(n_tiles == 1 || (Kd % 128 == 0 && n_tiles == Kd / 128)))
+        return -1;
+    if (offsets[0] < 0 || offsets[E] > rows)
+        return -1;
+    for (int e = 0; e < E; ++e)
+        if (offsets[e] > offsets[e + 1])
+            return -1;
+    const int tl = Kd / n_tiles;
+    for (int e = 0; e < E; ++e) {
+        const int8_t *we = w + (size_t)e * N * Kd;
+        for (int r = offsets[e]; r < offsets[e + 1]; ++r) {
+            for (int n = 0; n < N; ++n) {
+                const double ws = (double)w_sc[(size_t)e * N + n];
+                double sum = 0.0, mag = 0.0;
+                for (int t = 0; t < n_tiles; ++t) {
+                    int64_t isum = 0, iabs = 0;
+                    for (int k = t * tl; k < (t + 1) * tl; ++k) {
+                        int64_t prod = (int64_t)a[(size_t)r * Kd + k] * (int64_t)we[(size_t)n * Kd + k];
+                        isum += prod;
+                        iabs += prod < 0 ? -prod : prod;
+                    }
+                    const double as = (double)a_sc[(size_t)r * n_tiles + t];
+                    sum += as * ws * (double)isum;
+                    mag += fabs(as * ws) * (double)iabs;
                 }
                 y[(size_t)r * N + n] = bf16_from_double(sum);
                 if (y64)

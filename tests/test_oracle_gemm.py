@@ -141,3 +141,87 @@ def test_gemm_empty_untouched_and_bad_offsets():
     for bad in ([0, 3, 2], [-1, 2, 5], [0, 2, 8]):
         with pytest.raises(ValueError):
             oracle.expert_gemm_mx(g.a, g.a_sc, np.array(bad, np.int32), g.w, g.w_sc)
+
+
+# ---------------------------------------------------------------- int8 operands
+
+def numpy_gemm_i8(g) -> np.ndarray:
+    """Per tile: exact int64 products summed, scaled in float64 (numpy einsum)."""
+    out = np.zeros((g.rows, g.N))
+    n_t = 1 if g.a_sc.ndim == 1 else g.a_sc.shape[1]
+    tl = g.Kd // n_t
+    a_sc = g.a_sc.reshape(g.rows, n_t).astype(np.float64)
+    for e in range(g.E):
+        lo, hi = g.offsets[e], g.offsets[e + 1]
+        for t in range(n_t):
+            isum = np.einsum("rk,nk->rn", g.a[lo:hi, t * tl:(t + 1) * tl].astype(np.int64),
+                             g.w[e, :, t * tl:(t + 1) * tl].astype(np.int64))
+            out[lo:hi] += a_sc[lo:hi, t:t + 1] * g.w_sc[e].astype(np.float64)[None, :] * isum
+    return out
+
+
+@pytest.mark.parametrize("per_tile", [False, True])
+@pytest.mark.parametrize("counts,N,Kd,tail", [([0, 9, 21], 24, 256, 2), ([5], 8, 128, 0),
+                                                ([3, 0, 7, 1], 16, 384, 3)])
+def test_gemm_i8_matches_numpy(per_tile, counts, N, Kd, tail):
+    g = W.make_gemm_case_i8(21 + N + Kd, counts, N, Kd, per_tile, tail=tail)
+    y, y64, abs64 = oracle.expert_gemm_i8(g.a, g.a_sc, g.offsets, g.w, g.w_sc)
+    ref = numpy_gemm_i8(g)
+    last = int(g.offsets[-1])
+    assert np.all(np.abs(y64 - ref) <= 1e-13 * abs64 + 1e-300)
+    assert np.array_equal(y[:last], oracle.bf16_round(ref[:last]).reshape(last, N))
+    assert np.all(y[last:] == 0)
+    n_t = g.a_sc.reshape(g.rows, -1).shape[1]
+    A = np.abs(g.a.astype(np.float64)) * np.repeat(g.a_sc.reshape(g.rows, n_t), Kd // n_t, axis=1)
+    for e in range(g.E):
+        lo, hi = g.offsets[e], g.offsets[e + 1]
+        Wd = np.abs(g.w[e].astype(np.float64)) * g.w_sc[e].astype(np.float64)[:, None]
+        assert np.allclose(abs64[lo:hi], A[lo:hi] @ Wd.T, rtol=1e-12, atol=0)
+
+
+def test_gemm_i8_one_hot_and_scale_steps():
+    """One-hot weights with unit scales return single dequantised activations; doubling one
+    weight scale doubles one column; doubling one tile's scale adds exactly that tile's term."""
+    rng = np.random.default_rng(8)
+    g = W.make_gemm_case_i8(31, [4, 5], 32, 256, True)
+    perms = [rng.permutation(g.Kd)[:g.N] for _ in range(g.E)]
+    w = np.zeros_like(g.w)
+    for e in range(g.E):
+        w[e, np.arange(g.N), perms[e]] = 1
+    w_sc = np.ones_like(g.w_sc)
+    _, y64, _ = oracle.expert_gemm_i8(g.a, g.a_sc, g.offsets, w, w_sc)
+    for e in range(g.E):
+        for r in range(g.offsets[e], g.offsets[e + 1]):
+            k = perms[e]
+            assert np.array_equal(y64[r], g.a[r, k].astype(np.float64) *
+                                  g.a_sc[r, k // 128].astype(np.float64))
+    _, base, _ = oracle.expert_gemm_i8(g.a, g.a_sc, g.offsets, g.w, g.w_sc)
+    w_sc2 = g.w_sc.copy()
+    w_sc2[1, 7] *= 2
+    _, dbl, _ = oracle.expert_gemm_i8(g.a, g.a_sc, g.offsets, g.w, w_sc2)
+    lo, hi = g.offsets[1], g.offsets[2]
+    assert np.array_equal(dbl[lo:hi, 7], 2 * base[lo:hi, 7])
+    mask = np.ones_like(base, dtype=bool)
+    mask[lo:hi, 7] = False
+    assert np.array_equal(dbl[mask], base[mask])
+    a_sc2 = g.a_sc.copy()
+    a_sc2[2, 1] *= 2
+    _, st, _ = oracle.expert_gemm_i8(g.a, a_sc2, g.offsets, g.w, g.w_sc)
+    tile = (g.a[2, 128:256].astype(np.int64) @ g.w[0, :, 128:256].astype(np.int64).T)
+    term = g.a_sc[2, 1].astype(np.float64) * g.w_sc[0].astype(np.float64) * tile
+    assert np.allclose(st[2] - base[2], term, rtol=1e-12, atol=1e-300)
+
+
+def test_gemm_i8_one_tile_equals_per_token():
+    """Per-tile scales that are equal along a row give the per-token result."""
+    g = W.make_gemm_case_i8(41, [6, 2], 16, 384, False)
+    _, tok, _ = oracle.expert_gemm_i8(g.a, g.a_sc, g.offsets, g.w, g.w_sc)
+    per_tile = np.repeat(g.a_sc[:, None], 3, axis=1)
+    _, til, abs64 = oracle.expert_gemm_i8(g.a, per_tile, g.offsets, g.w, g.w_sc)
+    assert np.all(np.abs(til - tok) <= 1e-15 * abs64)
+
+
+def test_gemm_i8_rejects_bad_tiles():
+    g = W.make_gemm_case_i8(51, [3], 8, 256, True)
+    with pytest.raises(ValueError):
+        oracle.expert_gemm_i8(g.a, np.ones((g.rows, 3), np.float32), g.offsets, g.w, g.w_sc)

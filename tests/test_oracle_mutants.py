@@ -62,9 +62,18 @@ MUTANTS = [
     ("gemm_weight_scale_row", "wse[(size_t)n * nb + k / 32]", "wse[(size_t)(n / 2) * nb + k / 32]"),
     ("gemm_wrong_instance", "const uint8_t *we = w + (size_t)e * N * Kd;",
      "const uint8_t *we = w + (size_t)((e + 1) % E) * N * Kd;"),
-    ("gemm_transposed_weights", "we[(size_t)n * Kd + k]", "we[(size_t)k * N + n]"),
-    ("gemm_extra_row", "for (int r = offsets[e]; r < offsets[e + 1]; ++r) {",
-     "for (int r = offsets[e]; r <= offsets[e + 1] && r < rows; ++r) {"),
+    ("gemm_transposed_weights", "e4m3_value(we[(size_t)n * Kd + k])", "e4m3_value(we[(size_t)k * N + n])"),
+    ("gemm_extra_row", "(size_t)e * N * nb;\n        for (int r = offsets[e]; r < offsets[e + 1]; ++r) {",
+     "(size_t)e * N * nb;\n        for (int r = offsets[e]; r <= offsets[e + 1] && r < rows; ++r) {"),
+    ("i8_tile_index", "a_sc[(size_t)r * n_tiles + t]", "a_sc[(size_t)r * n_tiles + (t + 1) % n_tiles]"),
+    ("i8_weight_scale_column", "w_sc[(size_t)e * N + n]", "w_sc[(size_t)e * N + (n + 1) % N]"),
+    ("i8_tile_bounds", "for (int k = t * tl; k < (t + 1) * tl; ++k)",
+     "for (int k = t * tl; k < (t + 1) * tl - 1; ++k)"),
+    ("i8_unsigned_codes", "(int64_t)a[(size_t)r * Kd + k]", "(int64_t)(uint8_t)a[(size_t)r * Kd + k]"),
+    ("i8_extra_row", "const int8_t *we = w + (size_t)e * N * Kd;\n        for (int r = offsets[e]; r < offsets[e + 1]; ++r) {",
+     "const int8_t *we = w + (size_t)e * N * Kd;\n        for (int r = offsets[e]; r <= offsets[e + 1] && r < rows; ++r) {"),
+    ("i8_wrong_instance", "const int8_t *we = w + (size_t)e * N * Kd;",
+     "const int8_t *we = w + (size_t)((e + 1) % E) * N * Kd;"),
 ]
 
 PIN_FILES = ["tests/test_oracle_numbers.py", "tests/test_oracle_route.py",
