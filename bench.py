@@ -550,6 +550,7 @@ def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
 # ----------------------------------------------------------------- expert GEMM row
 
 FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA
 GEMM_METRIC = "expert GEMM TFLOP/s (mxfp8 x mxfp8 -> bf16, fp32 accumulate)"
 GEMM_TAG = "8 instances, 4096 rows (Zipf split), H=7168 -> N=4096, mxfp8 (bench.py --gemm)"
 
@@ -651,6 +652,30 @@ def gemm_main(args):
     e1.record(stream)
     e1.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / K
+    # the int8 formats at the same shape (per token, per tile of 128): kernel time only
+    variants = {}
+    for name, mode, per_tile in (("int8_per_token", moe.QUANT_INT8_TOKEN, False),
+                                 ("int8_per_tile", moe.QUANT_INT8_TILE, True)):
+        gi = W.make_gemm_case_i8(3200 + per_tile, g.counts, g.N, g.Kd, per_tile)
+        ti = [torch.from_numpy(v).to(dev) for v in (gi.a, gi.a_sc, gi.offsets, gi.w, gi.w_sc)]
+        wi2 = ti[3].clone()
+        yi = torch.empty((gi.rows, gi.N), dtype=torch.bfloat16, device=dev)
+        av = [(ti[0].data_ptr(), ti[1].data_ptr(), ti[2].data_ptr(), gi.E, gi.rows, wt.data_ptr(),
+               ti[4].data_ptr(), gi.N, gi.Kd, mode, yi.data_ptr(), None, stream.cuda_stream)
+              for wt in (ti[3], wi2)]
+        for k in range(args.warmup):
+            f(*av[k % 2])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(K):
+            f(*av[k % 2])
+        e1.record(stream)
+        e1.synchronize()
+        ui = e0.elapsed_time(e1) * 1e3 / K
+        fi = 2.0 * int(gi.offsets[-1]) * gi.N * gi.Kd
+        variants[name] = {"avg_us": round(ui, 3), "TOPS": round(fi / (ui * 1e-6) / 1e12, 2),
+                          "frac_of_int8_peak": round(fi / (ui * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
+        del ti, wi2, yi
     rows_total = int(g.offsets[-1])
     flops = 2.0 * rows_total * g.N * g.Kd
     tfs = flops / (us * 1e-6) / 1e12
@@ -667,12 +692,13 @@ def gemm_main(args):
                                "mxfp8 operands with E8M0 block scales, bf16 out",
                    "E": g.E, "rows": rows_total, "counts": g.counts.tolist(), "N": g.N,
                    "H": g.Kd, "weight_sets": n_sets},
-        "roofline": {"kernel": "k_expert_gemm_mx", "bound": "mfma", "achieved": round(tfs, 2),
+        "roofline": {"kernel": "k_expert_gemm", "bound": "mfma", "achieved": round(tfs, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfs / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(us, 3)},
         "hbm_GBps_algorithmic": round(alg_bytes / (us * 1e-6) / 1e9, 1),
+        "other_formats": variants,
         "parity_sample": "ok" if ok else "MISMATCH",
         "cpu_baseline": None,
     }

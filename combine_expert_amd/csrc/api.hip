@@ -18,6 +18,7 @@ constexpr int kMinH = 1024;       // combine page: H in [1024, 8192]
 constexpr int kMaxH = 8192;
 constexpr int kMaxExperts = 1024; // update-expert page: at most 1024 instances
 constexpr int kMaxGemmDim = 16384; // expert GEMM: H and N (multiples of 128)
+constexpr int kMaxGemmRows = 1 << 22; // expert GEMM: row tiles counted in 16 bits on the device
 constexpr int kMaxStagedTable = 8192;  // table words a fused dispatch block stages in LDS (32 KB)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -226,24 +227,24 @@ int moe_expert_gemm(const void *expand_x, const void *expand_scales,
 {
     if (!expand_x || !expand_scales || !expert_offsets || !weights || !weight_scales || !y)
         return MOE_EINVAL;
-    if (n_instances < 1 || n_instances > kMaxExperts || rows < 0)
+    if (n_instances < 1 || n_instances > kMaxExperts || rows < 0 || rows > kMaxGemmRows)
         return MOE_EINVAL;
     if (H < 128 || H > kMaxGemmDim || H % 128 != 0 || N < 128 || N > kMaxGemmDim ||
         N % 128 != 0)
         return MOE_EINVAL;
     if (quant_mode < MOE_Q_NONE || quant_mode > MOE_Q_MXFP8)
         return MOE_EINVAL;
-    if (quant_mode != MOE_Q_MXFP8)
+    if (quant_mode != MOE_Q_MXFP8 && quant_mode != MOE_Q_INT8_TOKEN &&
+        quant_mode != MOE_Q_INT8_TILE)
         return MOE_ENOTSUP;
     if (!aligned(expand_x, 16) || !aligned(weights, 16) || !aligned(y, 16) ||
         !aligned(expand_scales, 4) || !aligned(weight_scales, 4) ||
         !aligned(expert_offsets, 4) || (dev_err && !aligned(dev_err, 4)))
         return MOE_EINVAL;
-    return from_hip(moe::launch_expert_gemm_mx(
-        static_cast<const uint8_t *>(expand_x), static_cast<const uint8_t *>(expand_scales),
-        expert_offsets, n_instances, rows, static_cast<const uint8_t *>(weights),
-        static_cast<const uint8_t *>(weight_scales), N, H, static_cast<uint16_t *>(y), dev_err,
-        static_cast<hipStream_t>(stream)));
+    return from_hip(moe::launch_expert_gemm(quant_mode, expand_x, expand_scales, expert_offsets,
+                                            n_instances, rows, weights, weight_scales, N, H,
+                                            static_cast<uint16_t *>(y), dev_err,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -49,6 +49,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device.h"
 #include "kernels.h"
@@ -80,14 +81,20 @@ constexpr int kScaleGroup = 4;  // K steps per grouped scale copy (16 bytes per 
 static_assert(kBM / 64 <= kGemmWaves && kBN / 64 == kGemmWaves, "scale runs: one per wave");
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// operand formats (the dispatch's quantisation modes)
+constexpr int kModeI8Token = 2;   // int8, one f32 scale per row; weights int8, f32 per column
+constexpr int kModeI8Tile = 3;    // int8, one f32 scale per row and 128-element tile
+constexpr int kModeMx = 4;        // E4M3 with E8M0 scales per 32 elements, both operands
+
 struct GemmArgs {
-    const uint8_t *a;        // [rows, K] E4M3
-    const uint8_t *a_sc;     // [rows, K/32] E8M0
+    const uint8_t *a;        // [rows, K] E4M3 or int8
+    const uint8_t *a_sc;     // [rows, K/32] E8M0, or f32 [rows] / [rows, K/128]
     const int32_t *offsets;  // [E+1]
-    const uint8_t *w;        // [E, N, K] E4M3
-    const uint8_t *w_sc;     // [E, N, K/32] E8M0
+    const uint8_t *w;        // [E, N, K] E4M3 or int8
+    const uint8_t *w_sc;     // [E, N, K/32] E8M0, or f32 [E, N]
     uint16_t *y;             // [rows, N] bf16
     int32_t *dev_err;
     int E, rows, N, K;
@@ -156,10 +163,16 @@ __device__ __forceinline__ void instance_rows(const GemmArgs &p, int e, int &lo,
         *bad = o0 < 0 || o1 < o0 || o1 > p.rows;
 }
 
-// GROUPED: scales in 16-byte groups of four K steps (needs K % 512 == 0), else per step.
-template <bool GROUPED>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
+// MODE: operand format (kModeMx, kModeI8Tile, kModeI8Token).  GROUPED: per-step scales in
+// 16-byte groups of four K steps (needs K % 512 == 0), else 4 bytes per step.
+template <int MODE, bool GROUPED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
 {
+    // the accumulator: fp32 (mxfp8; int8 per tile, where each step's exact int32 sum is scaled
+    // into it) or int32 (int8 per token: exact over all of K, scaled at the end)
+    using Acc = std::conditional_t<MODE == kModeI8Token, v4i, v4f>;
+    constexpr bool kStepScales = MODE != kModeI8Token;   // scale copies along K
+    constexpr bool kWeightStepScales = MODE == kModeMx;
     constexpr int kScaleSteps = GROUPED ? kScaleGroup : 1;
     constexpr int kScaleBufs = GROUPED ? 2 : kStages;
     using Sc = Scales<kScaleSteps>;
@@ -224,7 +237,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
     // scale runs of 64 rows: every wave one of the weights; the first kBM / 64 waves also one
     // of the activations
     const bool x_run = wave < kBM / 64;
-    const int n_scale = x_run ? 2 : 1;        // scale copies per issue (wave-uniform)
+    // scale copies per issue (wave-uniform)
+    const int n_scale = (kWeightStepScales ? 1 : 0) + (kStepScales && x_run ? 1 : 0);
 
     // DMA lane mapping: one instruction covers 8 rows x 128 bytes; lane -> row lane / 8, LDS
     // slot lane % 8, global chunk slot ^ row (runs start at multiples of 8 rows, so
@@ -292,39 +306,76 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
         auto issue_scales = [&](int buf, int off) {
             Sc &sc = s_scale[buf];
             if (GROUPED) {
-                dma16(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+                if (kWeightStepScales)
+                    dma16(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
                 if (x_run)
                     dma16(xsc_src + off, lds_addr(&sc.x[wave * 64][0]));
             } else {
-                dma4(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+                if (kWeightStepScales)
+                    dma4(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
                 if (x_run)
                     dma4(xsc_src + off, lds_addr(&sc.x[wave * 64][0]));
             }
         };
 
-        v4f acc[kFragN][kFragM];
+        Acc acc[kFragN][kFragM];
 #pragma unroll
         for (int i = 0; i < kFragN; ++i)
 #pragma unroll
             for (int j = 0; j < kFragM; ++j)
-                acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+                acc[i][j] = Acc{0, 0, 0, 0};
 
         // prologue: step 0 (and its scales), then step 1; wait for the first two
         issue_data(0);
-        issue_scales(0, 0);
+        if (kStepScales)
+            issue_scales(0, 0);
         issue_data(min(1, nk - 1));
-        if (!GROUPED)
+        if (kStepScales && !GROUPED)
             issue_scales(1 % kStages, 4 * min(1, nk - 1));
         wait_vm(GROUPED ? kDataLoads : kDataLoads + n_scale);
         lds_barrier();
 
         for (int s = 0; s < nk; ++s) {
+            const Stage &st = s_stage[s % kStages];
+            const Sc &sc = s_scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
+            const int sw = GROUPED ? s % kScaleGroup : 0;
+            // fragment reads: the activation fragments and the first three weight fragments
+            // go out before this step's copies are issued, the remaining weight fragments
+            // three ahead of the MFMAs that use them
+            v8i xf[kFragM], wf[kFragN];
+            int xs[kFragM], ws[kFragN];   // E8M0 scale bytes (mxfp8), f32 bits (int8 per tile)
+            auto read_w = [&](int fn) {
+                const int row = wn * (kBN / kWavesN) + fn * 16 + r16;
+                const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c0]);
+                const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
+                wf[fn] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                if (kWeightStepScales)
+                    ws[fn] = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
+            };
+#pragma unroll
+            for (int fm = 0; fm < kFragM; ++fm) {
+                const int row = wm * (kBM / kWavesM) + fm * 16 + r16;
+                const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c0]);
+                const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
+                xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                if (MODE == kModeMx)
+                    xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
+                else if (MODE == kModeI8Tile)
+                    xs[fm] = (int)sc.x[row][sw];
+            }
+            read_w(0);
+            read_w(1);
+            read_w(2);
+
             // copies two steps ahead (the last two steps reload the final K step into stages
             // nobody reads any more: no branch in the count of copies in flight)
             const int s2 = min(s + 2, nk - 1);
             issue_data(s2);
             bool grouped_issue = false;
-            if (GROUPED) {
+            if (!kStepScales) {
+            } else if (GROUPED) {
                 // every fourth step, the next group into the other buffer (the last group
                 // reloads itself there, unused)
                 if (s % kScaleGroup == 0) {
@@ -336,32 +387,38 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
                 issue_scales((s + 2) % kStages, 4 * s2);
             }
 
-            const Stage &st = s_stage[s % kStages];
-            const Sc &sc = s_scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
-            const int sw = GROUPED ? s % kScaleGroup : 0;
-            v8i xf[kFragM];
-            int xs[kFragM];
-#pragma unroll
-            for (int fm = 0; fm < kFragM; ++fm) {
-                const int row = wm * (kBM / kWavesM) + fm * 16 + r16;
-                const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c0]);
-                const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
-                xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
-            }
 #pragma unroll
             for (int fn = 0; fn < kFragN; ++fn) {
-                const int row = wn * (kBN / kWavesN) + fn * 16 + r16;
-                const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c0]);
-                const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
-                const v8i wf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                const int ws = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
+                if (fn + 3 < kFragN)
+                    read_w(fn + 3);
 #pragma unroll
-                for (int fm = 0; fm < kFragM; ++fm)
-                    acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        wf, xf[fm], acc[fn][fm], 0, 0, 0, ws, 0, xs[fm]);
+                for (int fm = 0; fm < kFragM; ++fm) {
+                    if constexpr (MODE == kModeMx) {
+                        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            wf[fn], xf[fm], acc[fn][fm], 0, 0, 0, ws[fn], 0, xs[fm]);
+                    } else {
+                        // K = 128 as two int8 MFMAs of 64: chunk g, then chunk g + 4 (both
+                        // operands packed alike, which is all the instruction needs)
+                        const v4i wlo = {wf[fn][0], wf[fn][1], wf[fn][2], wf[fn][3]};
+                        const v4i whi = {wf[fn][4], wf[fn][5], wf[fn][6], wf[fn][7]};
+                        const v4i xlo = {xf[fm][0], xf[fm][1], xf[fm][2], xf[fm][3]};
+                        const v4i xhi = {xf[fm][4], xf[fm][5], xf[fm][6], xf[fm][7]};
+                        if constexpr (MODE == kModeI8Token) {
+                            acc[fn][fm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, xlo,
+                                                                                acc[fn][fm], 0, 0, 0);
+                            acc[fn][fm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, xhi,
+                                                                                acc[fn][fm], 0, 0, 0);
+                        } else {
+                            v4i t = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, xlo, v4i{0, 0, 0, 0},
+                                                                         0, 0, 0);
+                            t = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, xhi, t, 0, 0, 0);
+                            const float as = __int_as_float(xs[fm]);   // the row's tile scale
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                acc[fn][fm][i] = __builtin_fmaf((float)t[i], as, acc[fn][fm][i]);
+                        }
+                    }
+                }
             }
             // step s+1's copies were issued a step ago: wait for this thread's (only those of
             // this step may stay in flight; an older scale group must have landed), then for
@@ -377,17 +434,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
         lds_barrier();
 
         // ---- epilogue: lane holds columns n0 + wn*(kBN/kWavesN) + fn*16 + 4g .. +3 of row
-        //      m0 + wm*(kBM/kWavesM) + fm*16 + r16
+        //      m0 + wm*(kBM/kWavesM) + fm*16 + r16.  int8: times the weight column scales
+        //      (and, per token, the row scale), in that order
+        const float *wcol = reinterpret_cast<const float *>(p.w_sc) + (size_t)e * p.N;
 #pragma unroll
         for (int fm = 0; fm < kFragM; ++fm) {
             const int r = m0 + wm * (kBM / kWavesM) + fm * 16 + r16;
             if (r < row_hi) {
                 uint16_t *yrow = p.y + (size_t)r * p.N;
+                float rs = 1.0f;
+                if (MODE == kModeI8Token)
+                    rs = reinterpret_cast<const float *>(p.a_sc)[r];
 #pragma unroll
                 for (int fn = 0; fn < kFragN; ++fn) {
                     const int n = n0 + wn * (kBN / kWavesN) + fn * 16 + 4 * g;
                     if (n < p.N) {
-                        const v4f d = acc[fn][fm];
+                        v4f d;
+                        if constexpr (MODE == kModeMx) {
+                            d = acc[fn][fm];
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                if constexpr (MODE == kModeI8Token)
+                                    d[i] = (float)acc[fn][fm][i] * rs * wcol[n + i];
+                                else
+                                    d[i] = acc[fn][fm][i] * wcol[n + i];
+                            }
+                        }
                         const uint2 o = make_uint2(pack_bf16x2(d[0], d[1]),
                                                    pack_bf16x2(d[2], d[3]));
                         *reinterpret_cast<uint2 *>(yrow + n) = o;
@@ -400,26 +473,44 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
 
 }  // namespace
 
-hipError_t launch_expert_gemm_mx(const uint8_t *a, const uint8_t *a_sc, const int32_t *offsets,
-                                 int E, int rows, const uint8_t *w, const uint8_t *w_sc, int N,
-                                 int K, uint16_t *y, int32_t *dev_err, hipStream_t stream)
+hipError_t launch_expert_gemm(int quant_mode, const void *a, const void *a_sc,
+                              const int32_t *offsets, int E, int rows, const void *w,
+                              const void *w_sc, int N, int K, uint16_t *y, int32_t *dev_err,
+                              hipStream_t stream)
 {
-    GemmArgs p{a, a_sc, offsets, w, w_sc, y, dev_err, E, rows, N, K};
+    GemmArgs p{static_cast<const uint8_t *>(a), static_cast<const uint8_t *>(a_sc), offsets,
+               static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(w_sc), y, dev_err,
+               E, rows, N, K};
     // Upper bound on row tiles: sum of ceil(rows_e / 128) <= ceil(rows / 128) + E.
     const long m_cap = (rows + kBM - 1) / kBM + E;
     const long tiles_cap = m_cap * ((N + kBN - 1) / kBN);
     // one resident block per CU, walking the tiles grid-stride
-    const int grid = (int)std::min<long>(tiles_cap, kCus);
+    const dim3 grid((unsigned)std::min<long>(tiles_cap, kCus)), block(kGemmThreads);
     // grouped scale copies read 16 bytes per row: K a multiple of 512 (whole groups) and
-    // 16-byte aligned scale arrays (the row pitch K/32 is then a multiple of 16 as well)
+    // 16-byte aligned scale arrays (the row pitch, 4 bytes per K step, is then a multiple of
+    // 16 as well)
     const bool grouped = K % (kBK * kScaleGroup) == 0 &&
                          (reinterpret_cast<uintptr_t>(a_sc) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(w_sc) & 15) == 0;
-    if (grouped)
-        hipLaunchKernelGGL(k_expert_gemm_mx<true>, dim3(grid), dim3(kGemmThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(k_expert_gemm_mx<false>, dim3(grid), dim3(kGemmThreads), 0, stream,
-                           p);
+    switch (quant_mode) {
+    case kModeMx:
+        if (grouped)
+            hipLaunchKernelGGL((k_expert_gemm<kModeMx, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((k_expert_gemm<kModeMx, false>), grid, block, 0, stream, p);
+        break;
+    case kModeI8Tile:
+        if (grouped)
+            hipLaunchKernelGGL((k_expert_gemm<kModeI8Tile, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((k_expert_gemm<kModeI8Tile, false>), grid, block, 0, stream, p);
+        break;
+    case kModeI8Token:
+        hipLaunchKernelGGL((k_expert_gemm<kModeI8Token, false>), grid, block, 0, stream, p);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -33,9 +33,10 @@ hipError_t launch_combine(const uint16_t *expert_out, const int32_t *assist,
                           int H, int K, int shared_mode, uint16_t *y, uint16_t *x_out,
                           float *rstd, int32_t *dev_err, hipStream_t stream);
 
-hipError_t launch_expert_gemm_mx(const uint8_t *a, const uint8_t *a_sc, const int32_t *offsets,
-                                 int E, int rows, const uint8_t *w, const uint8_t *w_sc, int N,
-                                 int K, uint16_t *y, int32_t *dev_err, hipStream_t stream);
+hipError_t launch_expert_gemm(int quant_mode, const void *a, const void *a_sc,
+                              const int32_t *offsets, int E, int rows, const void *w,
+                              const void *w_sc, int N, int K, uint16_t *y, int32_t *dev_err,
+                              hipStream_t stream);
 
 // Threads per row block: one thread per 16 row elements, rounded up to
 // whole waves (64 .. 512 threads for H in [1024, 8192]).

@@ -212,10 +212,12 @@ def moe_combine_add_rmsnorm(expert_out, assist_dst, expert_scales, residual_x, g
 
 def moe_expert_gemm(expand_x, expand_scales, expert_offsets, weights, weight_scales,
                     quant_mode: int = QUANT_MXFP8, y=None, dev_err=None, stream=None):
-    """Grouped GEMM of the expert computation.  expand_x u8 [rows, H] (E4M3),
-    expand_scales u8 [rows, H/32] (E8M0), expert_offsets int32 [E+1],
-    weights u8 [E, N, H], weight_scales u8 [E, N, H/32] -> y bf16 [rows, N]
-    (rows outside every instance's range are not written)."""
+    """Grouped GEMM of the expert computation -> y bf16 [rows, N] (rows outside every
+    instance's range are not written).  mxfp8: expand_x u8 [rows, H] (E4M3),
+    expand_scales u8 [rows, H/32] (E8M0), weights u8 [E, N, H], weight_scales u8
+    [E, N, H/32].  int8 (QUANT_INT8_TOKEN / QUANT_INT8_TILE): expand_x int8 [rows, H],
+    expand_scales f32 [rows] / [rows, H/128], weights int8 [E, N, H], weight_scales f32
+    [E, N].  expert_offsets int32 [E+1]."""
     rows, H = expand_x.shape
     E = expert_offsets.numel() - 1
     N = weights.shape[1]

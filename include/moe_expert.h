@@ -251,20 +251,29 @@ int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
  *     A(r, k)    = e4m3(expand_x[r][k])   * 2^(expand_scales[r][k/32] - 127)
  *     W(e, n, k) = e4m3(weights[e][n][k]) * 2^(weight_scales[e][n][k/32] - 127)
  *
- *   expand_x       u8 E4M3 [rows, H]     16-byte aligned
- *   expand_scales  u8 E8M0 [rows, H/32]  4-byte aligned
+ * or, for the int8 outputs of dispatch cases 3 (MOE_Q_INT8_TOKEN) and 4
+ * (MOE_Q_INT8_TILE, tiles of 128):
+ *     y[r][n] = bf16( ws[e][n] * sum_t as[r][t] * sum_{k in tile t} a[r][k] * w[e][n][k] )
+ * with one tile covering all of H (per token) or tiles of 128 (per tile);
+ * integer sums are exact (int32), scaling and the sum over tiles are fp32.
+ *
+ *   expand_x       E4M3 or int8 [rows, H]                    16-byte aligned
+ *   expand_scales  mxfp8: u8 E8M0 [rows, H/32]; per token: f32 [rows];
+ *                  per tile: f32 [rows, H/128]               4-byte aligned
  *   expert_offsets int32 [n_instances+1] (moe_dispatch's offsets, or a slice
  *                  of them for a subset of instances; values are absolute rows)
- *   weights        u8 E4M3 [n_instances, N, H]     16-byte aligned
- *   weight_scales  u8 E8M0 [n_instances, N, H/32]  4-byte aligned
+ *   weights        E4M3 or int8 [n_instances, N, H]          16-byte aligned
+ *   weight_scales  mxfp8: u8 E8M0 [n_instances, N, H/32]; int8: f32 [n_instances, N]
+ *                                                            4-byte aligned
  *   y              bf16 [rows, N] (out; rows outside every instance's range
  *                  are not written)  16-byte aligned
  *   dev_err        int32 [1] or NULL: MOE_ERR_OFFSETS when the offsets are not
  *                  non-decreasing within [0, rows]; every range is then
  *                  clamped into [0, rows] and the output is unspecified
  *                  (but no access leaves the buffers)
- * Limits: 1 <= n_instances <= 1024, rows >= 0, H and N multiples of 128 in
- * [128, 16384], quant_mode = MOE_Q_MXFP8 (other modes: MOE_ENOTSUP).
+ * Limits: 1 <= n_instances <= 1024, 0 <= rows <= 4194304, H and N multiples of
+ * 128 in [128, 16384], quant_mode MOE_Q_MXFP8, MOE_Q_INT8_TOKEN or
+ * MOE_Q_INT8_TILE (MOE_Q_NONE and MOE_Q_STATIC: MOE_ENOTSUP).
  */
 int moe_expert_gemm(const void *expand_x, const void *expand_scales,
                     const int32_t *expert_offsets, int n_instances, int rows,

@@ -132,3 +132,101 @@ def test_gemm_full_size_sampled():
                                           np.ascontiguousarray(g.w_sc[:, cols]))
     assert_close(y[rows][:, cols], y64, abs64, g.Kd, "g3 sample")
     assert not np.any(y[:int(g.offsets[-1])] == POISON16)
+
+
+# ---------------------------------------------------------------- int8 operands
+
+def run_gpu_i8(g, quant_mode):
+    m = M()
+    y = torch.full((g.rows, g.N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    m.moe_expert_gemm(torch.from_numpy(g.a).cuda(), torch.from_numpy(g.a_sc).cuda(),
+                      torch.from_numpy(g.offsets).cuda(), torch.from_numpy(g.w).cuda(),
+                      torch.from_numpy(g.w_sc).cuda(), quant_mode=quant_mode, y=y)
+    torch.cuda.synchronize()
+    return y.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_close_i8(y_bits, y64, abs64, Kd, per_tile, where=""):
+    """int8: the integer sums are exact; per token the fp32 conversion and two multiplies
+    add at most about 3 * 2^-24 relative; per tile each step's fused multiply-add rounds once
+    (Kd/128 of them) and the column scale once more.  Plus half a bf16 ulp."""
+    got = f32(y_bits)
+    extra = (Kd // 128 + 2) * 2.0 ** -23 if per_tile else 2.0 ** -21
+    tol = 2.0 ** -8 * np.abs(y64) + extra * abs64
+    err = np.abs(got - y64)
+    bad = ~(err <= tol)
+    assert not bad.any(), f"{where}: {bad.sum()} of {bad.size} outside tolerance"
+
+
+I8_CASES = [
+    ([0, 17, 130, 1, 255], 256, 256, 5),
+    ([128], 128, 128, 0),
+    ([1, 129, 64], 384, 384, 0),
+    ([3, 0, 0, 7, 0, 200, 0, 1], 128, 512, 2),
+    ([300, 41], 256, 1024, 0),
+]
+
+
+@pytest.mark.parametrize("per_tile", [False, True])
+@pytest.mark.parametrize("ci", range(len(I8_CASES)))
+def test_gemm_i8_parity_small(ci, per_tile):
+    counts, N, Kd, tail = I8_CASES[ci]
+    mode = M().QUANT_INT8_TILE if per_tile else M().QUANT_INT8_TOKEN
+    say(f"[gemm i8] case {ci} per_tile={per_tile}: counts={counts[:8]} N={N} Kd={Kd}")
+    g = W.make_gemm_case_i8(700 + ci, counts, N, Kd, per_tile, tail=tail)
+    y = run_gpu_i8(g, mode)
+    ref, y64, abs64 = oracle.expert_gemm_i8(g.a, g.a_sc, g.offsets, g.w, g.w_sc)
+    last = int(g.offsets[-1])
+    assert_close_i8(y[:last], y64[:last], abs64[:last], Kd, per_tile, f"case {ci}")
+    assert np.all(y[last:] == POISON16)
+    assert np.mean(y[:last] == ref[:last]) > 0.9
+
+
+@pytest.mark.parametrize("per_tile", [False, True])
+def test_gemm_i8_full_size_sampled(per_tile):
+    """8 instances, 4096 rows, Kd = 7168, N = 4096, int8; sampled rows and columns."""
+    mode = M().QUANT_INT8_TILE if per_tile else M().QUANT_INT8_TOKEN
+    rng0 = np.random.default_rng(3100)
+    counts = W.zipf_counts(rng0, 4096, 8, 1.2)
+    g = W.make_gemm_case_i8(3200 + per_tile, counts, 4096, 7168, per_tile)
+    say(f"[gemm i8] full size per_tile={per_tile}")
+    y = run_gpu_i8(g, mode)
+    rows = []
+    for e in range(g.E):
+        lo, hi = int(g.offsets[e]), int(g.offsets[e + 1])
+        rows += sorted({lo, (lo + hi) // 2, hi - 1}) if hi > lo else []
+    rows = np.array(rows)
+    cols = np.sort(np.random.default_rng(10).choice(g.N, 256, replace=False))
+    inst = np.searchsorted(g.offsets[1:], rows, side="right")
+    sub_off = np.zeros(g.E + 1, np.int32)
+    sub_off[1:] = np.cumsum(np.bincount(inst, minlength=g.E))
+    _, y64, abs64 = oracle.expert_gemm_i8(g.a[rows], g.a_sc[rows], sub_off,
+                                          np.ascontiguousarray(g.w[:, cols]),
+                                          np.ascontiguousarray(g.w_sc[:, cols]))
+    assert_close_i8(y[rows][:, cols], y64, abs64, g.Kd, per_tile, "full size")
+
+
+def test_gemm_i8_on_dispatch_output():
+    """Dispatch (per-token int8, c2 shapes but 128 tokens) then the expert GEMM on its rows,
+    against the oracle's dispatch and GEMM (the two dispatch outputs are equal bit for bit)."""
+    m = M()
+    wl = W.make_small(seed=77, Bs=128, H=1024, K=4, n_ranks=2, local_experts=4,
+                      quant_mode=W.QUANT_INT8_TOKEN)
+    say("[gemm i8] on dispatch output")
+    d = m.moe_dispatch(wl.x.cuda(), wl.logical_ids.cuda(), wl.n_ranks, wl.local_experts,
+                       wl.quant_mode)
+    od = oracle.dispatch(oracle.bf16_bits(wl.x), wl.logical_ids.numpy(), None, wl.n_ranks,
+                         wl.local_experts, wl.quant_mode)
+    total = int(od["offsets"][-1])
+    assert np.array_equal(d["expand_x"].cpu().numpy()[:total], od["expand_x"][:total])
+    rng = np.random.default_rng(5)
+    w = rng.integers(-127, 128, size=(wl.E, 256, wl.H), dtype=np.int8)
+    w_sc = rng.uniform(0.0002, 0.002, size=(wl.E, 256)).astype(np.float32)
+    y = m.moe_expert_gemm(d["expand_x"], d["expand_scales"].reshape(-1), d["expert_offsets"],
+                          torch.from_numpy(w).cuda(), torch.from_numpy(w_sc).cuda(),
+                          quant_mode=m.QUANT_INT8_TOKEN)
+    torch.cuda.synchronize()
+    _, y64, abs64 = oracle.expert_gemm_i8(od["expand_x"], od["scales"].reshape(-1),
+                                          od["offsets"], w, w_sc)
+    yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert_close_i8(yb[:total], y64[:total], abs64[:total], wl.H, False, "dispatch chain")
