@@ -18,7 +18,7 @@ moe_dispatch, moe_combine_add_rmsnorm) is timed as well and reported under
     python bench.py --summarize-counters FETCH.csv WRITE.csv --kernel NAME \
                     --sources a.hip,b.h --out profiles/X.txt --command CMD1 --command CMD2
     python bench.py --summarize-copy FETCH.csv WRITE.csv --copy-mb 256 --out profiles/X.txt ...
-    python bench.py --gemm [--steps 50]                  # the expert GEMM row (its own line)
+    python bench.py --gemm [--gemm-formats]              # the expert GEMM row (its own line)
 
 Prints one JSON line.  `value` is whole-step throughput in GB/s of
 algorithmic bytes (each input read once, each output written once) with all
@@ -65,6 +65,9 @@ def parse():
                         "kernel trace of the default run covers the headline step alone")
     p.add_argument("--gemm", action="store_true",
                    help="time the expert computation (grouped mxfp8 GEMM) instead; one JSON line")
+    p.add_argument("--gemm-formats", action="store_true",
+                   help="with --gemm: also time the int8 formats (off by default so that a "
+                        "kernel trace of --gemm covers the mxfp8 kernel alone)")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="instead of the step, time a plain device copy of this many MB "
                         "(the reference kernel for counter scaling and achievable bandwidth)")
@@ -653,9 +656,10 @@ def gemm_main(args):
     e1.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / K
     # the int8 formats at the same shape (per token, per tile of 128): kernel time only
-    variants = {}
-    for name, mode, per_tile in (("int8_per_token", moe.QUANT_INT8_TOKEN, False),
-                                 ("int8_per_tile", moe.QUANT_INT8_TILE, True)):
+    variants = {} if args.gemm_formats else None
+    for name, mode, per_tile in ((("int8_per_token", moe.QUANT_INT8_TOKEN, False),
+                                  ("int8_per_tile", moe.QUANT_INT8_TILE, True))
+                                 if args.gemm_formats else ()):
         gi = W.make_gemm_case_i8(3200 + per_tile, g.counts, g.N, g.Kd, per_tile)
         ti = [torch.from_numpy(v).to(dev) for v in (gi.a, gi.a_sc, gi.offsets, gi.w, gi.w_sc)]
         wi2 = ti[3].clone()
