@@ -64,6 +64,7 @@ constexpr int kBM = 128;        // rows per tile
 constexpr int kBN = 256;        // output columns per tile
 constexpr int kBK = 128;        // K elements (bytes) per step
 constexpr int kStages = 3;
+constexpr int kAhead = kStages - 1;   // K steps between issuing a stage's copies and using it
 constexpr int kWavesM = 2;      // waves along the rows of a tile
 constexpr int kWavesN = 4;      // waves along the columns
 constexpr int kGemmWaves = kWavesM * kWavesN;
@@ -143,16 +144,24 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
     return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)p);
 }
 
-// s_waitcnt needs an immediate: the few counts the kernel uses, chosen at run time by a
-// wave-uniform value
+// s_waitcnt needs an immediate: the count, known per wave at run time (wave-uniform),
+// picks one of the immediates (counts above 31 wait for everything)
 __device__ __forceinline__ void wait_vm(int n)
 {
+#define MOE_WAIT_CASE(c) \
+    case c: __builtin_amdgcn_s_waitcnt(vmcnt_imm(c)); break;
     switch (n) {
-    case kDataLoads: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDataLoads)); break;
-    case kDataLoads + 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDataLoads + 1)); break;
-    case kDataLoads + 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDataLoads + 2)); break;
+        MOE_WAIT_CASE(1) MOE_WAIT_CASE(2) MOE_WAIT_CASE(3) MOE_WAIT_CASE(4) MOE_WAIT_CASE(5)
+        MOE_WAIT_CASE(6) MOE_WAIT_CASE(7) MOE_WAIT_CASE(8) MOE_WAIT_CASE(9) MOE_WAIT_CASE(10)
+        MOE_WAIT_CASE(11) MOE_WAIT_CASE(12) MOE_WAIT_CASE(13) MOE_WAIT_CASE(14)
+        MOE_WAIT_CASE(15) MOE_WAIT_CASE(16) MOE_WAIT_CASE(17) MOE_WAIT_CASE(18)
+        MOE_WAIT_CASE(19) MOE_WAIT_CASE(20) MOE_WAIT_CASE(21) MOE_WAIT_CASE(22)
+        MOE_WAIT_CASE(23) MOE_WAIT_CASE(24) MOE_WAIT_CASE(25) MOE_WAIT_CASE(26)
+        MOE_WAIT_CASE(27) MOE_WAIT_CASE(28) MOE_WAIT_CASE(29) MOE_WAIT_CASE(30)
+        MOE_WAIT_CASE(31)
     default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
     }
+#undef MOE_WAIT_CASE
 }
 
 // Clamped row range of instance e: [lo, hi) within [0, rows); *bad is set
@@ -331,26 +340,33 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
             for (int j = 0; j < kFragM; ++j)
                 acc[i][j] = Acc{0, 0, 0, 0};
 
-        // prologue: step 0 (and its scales), then step 1; wait for the first two
+        // copies of one step: the tiles and, unless grouped, that step's scales
+        const int step_loads = kDataLoads + (kStepScales && !GROUPED ? n_scale : 0);
+        // prologue: steps 0 .. kAhead-1 (the first scale group right after step 0's tiles);
+        // wait for step 0
         issue_data(0);
         if (kStepScales)
             issue_scales(0, 0);
-        issue_data(min(1, nk - 1));
-        if (kStepScales && !GROUPED)
-            issue_scales(1 % kStages, 4 * min(1, nk - 1));
-        wait_vm(GROUPED ? kDataLoads : kDataLoads + n_scale);
+#pragma unroll
+        for (int i = 1; i < kAhead; ++i) {
+            issue_data(min(i, nk - 1));
+            if (kStepScales && !GROUPED)
+                issue_scales(i % kStages, 4 * min(i, nk - 1));
+        }
+        wait_vm((kAhead - 1) * step_loads);
         lds_barrier();
 
         for (int s = 0; s < nk; ++s) {
             const Stage &st = s_stage[s % kStages];
             const Sc &sc = s_scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
             const int sw = GROUPED ? s % kScaleGroup : 0;
-            // fragment reads: the activation fragments and the first three weight fragments
-            // go out before this step's copies are issued, the remaining weight fragments
-            // three ahead of the MFMAs that use them
+            // fragment reads: all weight fragments and the first two activation fragments go
+            // out before this step's copies are issued; the other activation fragments two
+            // ahead of the MFMAs that use them
             v8i xf[kFragM], wf[kFragN];
             int xs[kFragM], ws[kFragN];   // E8M0 scale bytes (mxfp8), f32 bits (int8 per tile)
-            auto read_w = [&](int fn) {
+#pragma unroll
+            for (int fn = 0; fn < kFragN; ++fn) {
                 const int row = wn * (kBN / kWavesN) + fn * 16 + r16;
                 const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c0]);
                 const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
@@ -358,9 +374,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 if (kWeightStepScales)
                     ws[fn] = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
-            };
-#pragma unroll
-            for (int fm = 0; fm < kFragM; ++fm) {
+            }
+            auto read_x = [&](int fm) {
                 const int row = wm * (kBM / kWavesM) + fm * 16 + r16;
                 const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c0]);
                 const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
@@ -370,14 +385,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
                     xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
                 else if (MODE == kModeI8Tile)
                     xs[fm] = (int)sc.x[row][sw];
-            }
-            read_w(0);
-            read_w(1);
-            read_w(2);
+            };
+            read_x(0);
+            if (kFragM > 1)
+                read_x(1);
 
-            // copies two steps ahead (the last two steps reload the final K step into stages
+            // copies kAhead steps ahead (the last steps reload the final K step into stages
             // nobody reads any more: no branch in the count of copies in flight)
-            const int s2 = min(s + 2, nk - 1);
+            const int s2 = min(s + kAhead, nk - 1);
             issue_data(s2);
             bool grouped_issue = false;
             if (!kStepScales) {
@@ -390,15 +405,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
                     grouped_issue = true;
                 }
             } else {
-                issue_scales((s + 2) % kStages, 4 * s2);
+                issue_scales((s + kAhead) % kStages, 4 * s2);
             }
 
 #pragma unroll
-            for (int fn = 0; fn < kFragN; ++fn) {
-                if (fn + 3 < kFragN)
-                    read_w(fn + 3);
+            for (int fm = 0; fm < kFragM; ++fm) {
+                if (fm + 2 < kFragM)
+                    read_x(fm + 2);
 #pragma unroll
-                for (int fm = 0; fm < kFragM; ++fm) {
+                for (int fn = 0; fn < kFragN; ++fn) {
                     if constexpr (MODE == kModeMx) {
                         acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                             wf[fn], xf[fm], acc[fn][fm], 0, 0, 0, ws[fn], 0, xs[fm]);
@@ -426,13 +441,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
                     }
                 }
             }
-            // step s+1's copies were issued a step ago: wait for this thread's (only those of
-            // this step may stay in flight; an older scale group must have landed), then for
-            // everyone's
-            if (GROUPED)
-                wait_vm(grouped_issue ? kDataLoads + n_scale : kDataLoads);
-            else
-                wait_vm(kDataLoads + n_scale);
+            // step s+1's copies went out kAhead - 1 steps ago: wait for this thread's (only the
+            // steps issued since, and a scale group issued this step, may stay in flight; an
+            // older group must have landed), then for everyone's
+            wait_vm((kAhead - 1) * step_loads + (grouped_issue ? n_scale : 0));
             lds_barrier();
         }
         // the reloads of the last steps must land before the next tile rewrites the rings
