@@ -70,11 +70,8 @@ constexpr int kWavesN = 4;      // waves along the columns
 constexpr int kGemmWaves = kWavesM * kWavesN;
 constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kFragM = kBM / kWavesM / 16;   // 16-row MFMA fragments per wave (activations)
-constexpr int kFragN = kBN / kWavesN / 16;   // 16-row MFMA fragments per wave (weights)
 // per wave and step: 1 KB DMA runs of the two tiles (8 rows x 128 bytes each)
 constexpr int kXRuns = kBM / 8 / kGemmWaves;
-constexpr int kWRuns = kBN / 8 / kGemmWaves;
-constexpr int kDataLoads = kXRuns + kWRuns;
 constexpr int kXcds = 8;
 constexpr int kCus = 256;
 constexpr int kMaxInstances = 1024;
@@ -176,24 +173,266 @@ __device__ __forceinline__ void instance_rows(const GemmArgs &p, int e, int &lo,
         *bad = o0 < 0 || o1 < o0 || o1 > p.rows;
 }
 
-// MODE: operand format (kModeMx, kModeI8Tile, kModeI8Token).  GROUPED: per-step scales in
-// 16-byte groups of four K steps (needs K % 512 == 0), else 4 bytes per step.
-template <int MODE, bool GROUPED>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
+// LDS of one block: the copy ring, the scale ring (per step, or in groups of four steps),
+// the row-tile prefix of the instances and a scan scratch
+template <bool GROUPED>
+struct GemmSmem {
+    static constexpr int kScaleSteps = GROUPED ? kScaleGroup : 1;
+    static constexpr int kScaleBufs = GROUPED ? 2 : kStages;
+    Stage stage[kStages];
+    Scales<kScaleSteps> scale[kScaleBufs];
+    uint16_t tiles[kMaxInstances + 1];   // exclusive prefix of row tiles per instance
+    int wave_sum[kGemmWaves];
+};
+
+// One output tile: rows [m0, m0 + kBM) of instance e (valid below row_hi) by columns
+// [n0, n0 + BN).  MODE: operand format (kModeMx, kModeI8Tile, kModeI8Token).  GROUPED:
+// per-step scales in 16-byte groups of four K steps (needs K % 512 == 0), else 4 bytes per
+// step.  BN: 256 for whole tiles; 128 or 64 for the pieces the last round is split into.
+template <int MODE, bool GROUPED, int BN>
+__device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &sm, int e,
+                                         int m0, int row_hi, int n0)
 {
     // the accumulator: fp32 (mxfp8; int8 per tile, where each step's exact int32 sum is scaled
     // into it) or int32 (int8 per token: exact over all of K, scaled at the end)
     using Acc = std::conditional_t<MODE == kModeI8Token, v4i, v4f>;
+    using Stg = Stage;
+    using Sc = Scales<GemmSmem<GROUPED>::kScaleSteps>;
     constexpr bool kStepScales = MODE != kModeI8Token;   // scale copies along K
     constexpr bool kWeightStepScales = MODE == kModeMx;
-    constexpr int kScaleSteps = GROUPED ? kScaleGroup : 1;
-    constexpr int kScaleBufs = GROUPED ? 2 : kStages;
-    using Sc = Scales<kScaleSteps>;
-    __shared__ __align__(16) Stage s_stage[kStages];
-    __shared__ __align__(16) Sc s_scale[kScaleBufs];
-    __shared__ uint16_t s_tiles[kMaxInstances + 1];  // exclusive prefix of row tiles per instance
-    __shared__ int s_wave_sum[kGemmWaves];
+    constexpr int kWRunsT = BN / 8 / kGemmWaves;          // weight copy runs per wave
+    constexpr int kFragNT = BN / kWavesN / 16;            // weight fragments per wave
+    constexpr int kDataLoadsT = kXRuns + kWRunsT;
+    static_assert(kWRunsT >= 1 && kFragNT >= 1 && BN <= kBN, "tile width");
 
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nk = p.K / kBK;
+    const int kb = p.K / 32;                  // scale bytes per row
+    const int g = lane >> 4;                  // lane group: K chunk / scale block
+    const int r16 = lane & 15;
+    const int wn = wave % kWavesN, wm = wave / kWavesN;   // the wave's part of the tile
+    // the wave's scale runs of 64 rows: weight run j to wave j, activation run j to wave
+    // (BN / 64 + j) mod waves
+    const bool w_run = wave < BN / 64;
+    const int x_idx = (wave - BN / 64 + kGemmWaves) % kGemmWaves;   // activation run, if any
+    const bool x_run = x_idx < kBM / 64;
+    // scale copies per issue (wave-uniform)
+    const int n_scale = (kWeightStepScales && w_run ? 1 : 0) + (kStepScales && x_run ? 1 : 0);
+    // DMA lane mapping: one instruction covers 8 rows x 128 bytes; lane -> row lane / 8, LDS
+    // slot lane % 8, global chunk slot ^ row (runs start at multiples of 8 rows, so
+    // row & 7 = lane / 8)
+    const int dma_row = lane >> 3;
+    const int dma_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
+    const int fr_c0 = ((g ^ (r16 & 7)) << 4);   // swizzled offsets of chunks g and g + 4
+    const int fr_c1 = (((g + 4) ^ (r16 & 7)) << 4);
+    const uint8_t *w_e = p.w + (size_t)e * p.N * p.K;
+
+    // this thread's DMA sources at K offset 0.  Rows past the instance (or past N) are
+    // clamped to its last row (column): loaded, multiplied, never stored.
+    const uint8_t *xsrc[kXRuns];
+    const uint8_t *wsrc[kWRunsT];
+#pragma unroll
+    for (int q = 0; q < kXRuns; ++q) {
+        const int r = min(m0 + (wave * kXRuns + q) * 8 + dma_row, row_hi - 1);
+        xsrc[q] = p.a + (size_t)r * p.K + dma_chunk;
+    }
+#pragma unroll
+    for (int q = 0; q < kWRunsT; ++q) {
+        const int n = min(n0 + (wave * kWRunsT + q) * 8 + dma_row, p.N - 1);
+        wsrc[q] = w_e + (size_t)n * p.K + dma_chunk;
+    }
+    const uint8_t *wsc_src =
+        p.w_sc + ((size_t)e * p.N + min(n0 + (w_run ? wave : 0) * 64 + lane, p.N - 1)) * kb;
+    const uint8_t *xsc_src =
+        p.a_sc + (size_t)min(m0 + (x_run ? x_idx : 0) * 64 + lane, row_hi - 1) * kb;
+
+    // copies of K step s into stage s % kStages
+    auto issue_data = [&](int s) {
+        const int k0 = s * kBK;
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(&sm.stage[s % kStages]);
+#pragma unroll
+        for (int q = 0; q < kXRuns; ++q)
+            dma16(xsrc[q] + k0, lds_addr(base + offsetof(Stg, x) + (wave * kXRuns + q) * 1024));
+#pragma unroll
+        for (int q = 0; q < kWRunsT; ++q)
+            dma16(wsrc[q] + k0, lds_addr(base + offsetof(Stg, w) + (wave * kWRunsT + q) * 1024));
+    };
+    // scale copies: buffer `buf`, scale bytes from byte offset `off` of each row
+    auto issue_scales = [&](int buf, int off) {
+        Sc &sc = sm.scale[buf];
+        if (GROUPED) {
+            if (kWeightStepScales && w_run)
+                dma16(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+            if (x_run)
+                dma16(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
+        } else {
+            if (kWeightStepScales && w_run)
+                dma4(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+            if (x_run)
+                dma4(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
+        }
+    };
+
+    Acc acc[kFragNT][kFragM];
+#pragma unroll
+    for (int i = 0; i < kFragNT; ++i)
+#pragma unroll
+        for (int j = 0; j < kFragM; ++j)
+            acc[i][j] = Acc{0, 0, 0, 0};
+
+    // copies of one step: the tiles and, unless grouped, that step's scales
+    const int step_loads = kDataLoadsT + (kStepScales && !GROUPED ? n_scale : 0);
+    // prologue: steps 0 .. kAhead-1 (the first scale group right after step 0's tiles);
+    // wait for step 0
+    issue_data(0);
+    if (kStepScales)
+        issue_scales(0, 0);
+#pragma unroll
+    for (int i = 1; i < kAhead; ++i) {
+        issue_data(min(i, nk - 1));
+        if (kStepScales && !GROUPED)
+            issue_scales(i % kStages, 4 * min(i, nk - 1));
+    }
+    wait_vm((kAhead - 1) * step_loads);
+    lds_barrier();
+
+    for (int s = 0; s < nk; ++s) {
+        const Stg &st = sm.stage[s % kStages];
+        const Sc &sc = sm.scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
+        const int sw = GROUPED ? s % kScaleGroup : 0;
+        // fragment reads: all weight fragments and the first two activation fragments go
+        // out before this step's copies are issued; the other activation fragments two
+        // ahead of the MFMAs that use them
+        v8i xf[kFragM], wf[kFragNT];
+        int xs[kFragM], ws[kFragNT];   // E8M0 scale bytes (mxfp8), f32 bits (int8 per tile)
+#pragma unroll
+        for (int fn = 0; fn < kFragNT; ++fn) {
+            const int row = wn * (BN / kWavesN) + fn * 16 + r16;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c0]);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
+            wf[fn] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            if (kWeightStepScales)
+                ws[fn] = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
+        }
+        auto read_x = [&](int fm) {
+            const int row = wm * (kBM / kWavesM) + fm * 16 + r16;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c0]);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
+            xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            if (MODE == kModeMx)
+                xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
+            else if (MODE == kModeI8Tile)
+                xs[fm] = (int)sc.x[row][sw];
+        };
+        read_x(0);
+        if (kFragM > 1)
+            read_x(1);
+
+        // copies kAhead steps ahead (the last steps reload the final K step into stages
+        // nobody reads any more: no branch in the count of copies in flight)
+        const int s2 = min(s + kAhead, nk - 1);
+        issue_data(s2);
+        bool grouped_issue = false;
+        if (!kStepScales) {
+        } else if (GROUPED) {
+            // every fourth step, the next group into the other buffer (the last group
+            // reloads itself there, unused)
+            if (s % kScaleGroup == 0) {
+                const int gi = min(s / kScaleGroup + 1, nk / kScaleGroup - 1);
+                issue_scales((s / kScaleGroup + 1) & 1, 16 * gi);
+                grouped_issue = true;
+            }
+        } else {
+            issue_scales((s + kAhead) % kStages, 4 * s2);
+        }
+
+#pragma unroll
+        for (int fm = 0; fm < kFragM; ++fm) {
+            if (fm + 2 < kFragM)
+                read_x(fm + 2);
+#pragma unroll
+            for (int fn = 0; fn < kFragNT; ++fn) {
+                if constexpr (MODE == kModeMx) {
+                    acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        wf[fn], xf[fm], acc[fn][fm], 0, 0, 0, ws[fn], 0, xs[fm]);
+                } else {
+                    // K = 128 as two int8 MFMAs of 64: chunk g, then chunk g + 4 (both
+                    // operands packed alike, which is all the instruction needs)
+                    const v4i wlo = {wf[fn][0], wf[fn][1], wf[fn][2], wf[fn][3]};
+                    const v4i whi = {wf[fn][4], wf[fn][5], wf[fn][6], wf[fn][7]};
+                    const v4i xlo = {xf[fm][0], xf[fm][1], xf[fm][2], xf[fm][3]};
+                    const v4i xhi = {xf[fm][4], xf[fm][5], xf[fm][6], xf[fm][7]};
+                    if constexpr (MODE == kModeI8Token) {
+                        acc[fn][fm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, xlo,
+                                                                            acc[fn][fm], 0, 0, 0);
+                        acc[fn][fm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, xhi,
+                                                                            acc[fn][fm], 0, 0, 0);
+                    } else {
+                        v4i t = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, xlo, v4i{0, 0, 0, 0},
+                                                                     0, 0, 0);
+                        t = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, xhi, t, 0, 0, 0);
+                        const float as = __int_as_float(xs[fm]);   // the row's tile scale
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[fn][fm][i] = __builtin_fmaf((float)t[i], as, acc[fn][fm][i]);
+                    }
+                }
+            }
+        }
+        // step s+1's copies went out kAhead - 1 steps ago: wait for this thread's (only the
+        // steps issued since, and a scale group issued this step, may stay in flight; an
+        // older group must have landed), then for everyone's
+        wait_vm((kAhead - 1) * step_loads + (grouped_issue ? n_scale : 0));
+        lds_barrier();
+    }
+    // the reloads of the last steps must land before the next tile rewrites the rings
+    wait_vm(0);
+    lds_barrier();
+
+    // ---- epilogue: lane holds columns n0 + wn*(BN/kWavesN) + fn*16 + 4g .. +3 of row
+    //      m0 + wm*(kBM/kWavesM) + fm*16 + r16.  int8: times the weight column scales
+    //      (and, per token, the row scale), in that order
+    const float *wcol = reinterpret_cast<const float *>(p.w_sc) + (size_t)e * p.N;
+#pragma unroll
+    for (int fm = 0; fm < kFragM; ++fm) {
+        const int r = m0 + wm * (kBM / kWavesM) + fm * 16 + r16;
+        if (r < row_hi) {
+            uint16_t *yrow = p.y + (size_t)r * p.N;
+            float rs = 1.0f;
+            if (MODE == kModeI8Token)
+                rs = reinterpret_cast<const float *>(p.a_sc)[r];
+#pragma unroll
+            for (int fn = 0; fn < kFragNT; ++fn) {
+                const int n = n0 + wn * (BN / kWavesN) + fn * 16 + 4 * g;
+                if (n < p.N) {
+                    v4f d;
+                    if constexpr (MODE == kModeMx) {
+                        d = acc[fn][fm];
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (MODE == kModeI8Token)
+                                d[i] = (float)acc[fn][fm][i] * rs * wcol[n + i];
+                            else
+                                d[i] = acc[fn][fm][i] * wcol[n + i];
+                        }
+                    }
+                    const uint2 o = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+                    *reinterpret_cast<uint2 *>(yrow + n) = o;
+                }
+            }
+        }
+    }
+}
+
+template <int MODE, bool GROUPED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
+{
+    __shared__ __align__(16) GemmSmem<GROUPED> sm;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -218,22 +457,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
         atomicOr(p.dev_err, MOE_ERR_OFFSETS);
     const int incl = wave_incl_scan(tsum);
     if (lane == kWave - 1)
-        s_wave_sum[wave] = incl;
+        sm.wave_sum[wave] = incl;
     lds_barrier();
     int excl = incl - tsum;
     for (int w = 0; w < wave; ++w)
-        excl += s_wave_sum[w];
+        excl += sm.wave_sum[w];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = 4 * tid + q;
         if (e < p.E)
-            s_tiles[e] = (uint16_t)excl;
+            sm.tiles[e] = (uint16_t)excl;
         if (e == p.E - 1)
-            s_tiles[p.E] = (uint16_t)(excl + c[q]);
+            sm.tiles[p.E] = (uint16_t)(excl + c[q]);
         excl += c[q];
     }
     lds_barrier();
-    const int m_tiles = s_tiles[p.E];
+    const int m_tiles = sm.tiles[p.E];
     const int n_tiles = (p.N + kBN - 1) / kBN;
     const int total = m_tiles * n_tiles;
 
@@ -242,249 +481,54 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
     const int b = blockIdx.x;
     const int v = (G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
 
-    const int nk = p.K / kBK;
-    const int kb = p.K / 32;                  // scale bytes per row
-    const int g = lane >> 4;                  // lane group: K chunk / scale block
-    const int r16 = lane & 15;
-    const int wn = wave % kWavesN, wm = wave / kWavesN;   // the wave's part of the tile
-    // the wave's scale runs (see kBN / 64 above)
-    // of the activations
-    const bool w_run = wave < kBN / 64;
-    const int x_idx = (wave - kBN / 64 + kGemmWaves) % kGemmWaves;   // activation run, if any
-    const bool x_run = x_idx < kBM / 64;
-    // scale copies per issue (wave-uniform)
-    const int n_scale = (kWeightStepScales && w_run ? 1 : 0) + (kStepScales && x_run ? 1 : 0);
-
-    // DMA lane mapping: one instruction covers 8 rows x 128 bytes; lane -> row lane / 8, LDS
-    // slot lane % 8, global chunk slot ^ row (runs start at multiples of 8 rows, so
-    // row & 7 = lane / 8)
-    const int dma_row = lane >> 3;
-    const int dma_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
-    const int fr_c0 = ((g ^ (r16 & 7)) << 4);   // swizzled offsets of chunks g and g + 4
-    const int fr_c1 = (((g + 4) ^ (r16 & 7)) << 4);
-
-    for (int t = v; t < total; t += G) {
-        // patch order: kGroupM row tiles x every column tile, row tiles fastest, so the 32
-        // blocks an XCD runs at once share about 8 row tiles and 4 column tiles
+    // tile t -> instance e, rows [m0, row_hi), columns from n0.  Patch order: kGroupM row
+    // tiles x every column tile, row tiles fastest, so the 32 blocks an XCD runs at once
+    // share about 8 row tiles and 4 column tiles
+    auto locate = [&](int t, int &e, int &m0, int &row_hi, int &n0) {
         const int grp = t / (kGroupM * n_tiles);
         const int tin = t - grp * kGroupM * n_tiles;
         const int gm = min(kGroupM, m_tiles - grp * kGroupM);
         const int tm = grp * kGroupM + tin % gm;
         const int tn = tin / gm;
-        // instance of row tile tm: the last e with s_tiles[e] <= tm
+        // instance of row tile tm: the last e with tiles[e] <= tm
         int lo_e = 0, hi_e = p.E;
         while (hi_e - lo_e > 1) {
             const int mid = (lo_e + hi_e) >> 1;
-            if (s_tiles[mid] <= tm)
+            if (sm.tiles[mid] <= tm)
                 lo_e = mid;
             else
                 hi_e = mid;
         }
-        const int e = lo_e;
-        int row_lo, row_hi;
+        e = lo_e;
+        int row_lo;
         instance_rows(p, e, row_lo, row_hi, nullptr);
-        const int m0 = row_lo + (tm - s_tiles[e]) * kBM;   // first row of the tile
-        const int n0 = tn * kBN;
-        const uint8_t *w_e = p.w + (size_t)e * p.N * p.K;
+        m0 = row_lo + (tm - sm.tiles[e]) * kBM;
+        n0 = tn * kBN;
+    };
 
-        // this thread's DMA sources at K offset 0.  Rows past the instance (or past N) are
-        // clamped to its last row (column): loaded, multiplied, never stored.
-        const uint8_t *xsrc[kXRuns];
-        const uint8_t *wsrc[kWRuns];
-#pragma unroll
-        for (int q = 0; q < kXRuns; ++q) {
-            const int r = min(m0 + (wave * kXRuns + q) * 8 + dma_row, row_hi - 1);
-            xsrc[q] = p.a + (size_t)r * p.K + dma_chunk;
-        }
-#pragma unroll
-        for (int q = 0; q < kWRuns; ++q) {
-            const int n = min(n0 + (wave * kWRuns + q) * 8 + dma_row, p.N - 1);
-            wsrc[q] = w_e + (size_t)n * p.K + dma_chunk;
-        }
-        const uint8_t *wsc_src =
-            p.w_sc + ((size_t)e * p.N + min(n0 + wave * 64 + lane, p.N - 1)) * kb;
-        const uint8_t *xsc_src =
-            p.a_sc + (size_t)min(m0 + (x_run ? x_idx : 0) * 64 + lane, row_hi - 1) * kb;
-
-        // copies of K step s into stage s % kStages
-        auto issue_data = [&](int s) {
-            const int k0 = s * kBK;
-            const uint8_t *base = reinterpret_cast<const uint8_t *>(&s_stage[s % kStages]);
-#pragma unroll
-            for (int q = 0; q < kXRuns; ++q)
-                dma16(xsrc[q] + k0, lds_addr(base + offsetof(Stage, x) + (wave * kXRuns + q) * 1024));
-#pragma unroll
-            for (int q = 0; q < kWRuns; ++q)
-                dma16(wsrc[q] + k0, lds_addr(base + offsetof(Stage, w) + (wave * kWRuns + q) * 1024));
-        };
-        // scale copies: buffer `buf`, scale bytes from byte offset `off` of each row
-        auto issue_scales = [&](int buf, int off) {
-            Sc &sc = s_scale[buf];
-            if (GROUPED) {
-                if (kWeightStepScales && w_run)
-                    dma16(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
-                if (x_run)
-                    dma16(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
-            } else {
-                if (kWeightStepScales && w_run)
-                    dma4(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
-                if (x_run)
-                    dma4(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
-            }
-        };
-
-        Acc acc[kFragN][kFragM];
-#pragma unroll
-        for (int i = 0; i < kFragN; ++i)
-#pragma unroll
-            for (int j = 0; j < kFragM; ++j)
-                acc[i][j] = Acc{0, 0, 0, 0};
-
-        // copies of one step: the tiles and, unless grouped, that step's scales
-        const int step_loads = kDataLoads + (kStepScales && !GROUPED ? n_scale : 0);
-        // prologue: steps 0 .. kAhead-1 (the first scale group right after step 0's tiles);
-        // wait for step 0
-        issue_data(0);
-        if (kStepScales)
-            issue_scales(0, 0);
-#pragma unroll
-        for (int i = 1; i < kAhead; ++i) {
-            issue_data(min(i, nk - 1));
-            if (kStepScales && !GROUPED)
-                issue_scales(i % kStages, 4 * min(i, nk - 1));
-        }
-        wait_vm((kAhead - 1) * step_loads);
-        lds_barrier();
-
-        for (int s = 0; s < nk; ++s) {
-            const Stage &st = s_stage[s % kStages];
-            const Sc &sc = s_scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
-            const int sw = GROUPED ? s % kScaleGroup : 0;
-            // fragment reads: all weight fragments and the first two activation fragments go
-            // out before this step's copies are issued; the other activation fragments two
-            // ahead of the MFMAs that use them
-            v8i xf[kFragM], wf[kFragN];
-            int xs[kFragM], ws[kFragN];   // E8M0 scale bytes (mxfp8), f32 bits (int8 per tile)
-#pragma unroll
-            for (int fn = 0; fn < kFragN; ++fn) {
-                const int row = wn * (kBN / kWavesN) + fn * 16 + r16;
-                const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c0]);
-                const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
-                wf[fn] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                if (kWeightStepScales)
-                    ws[fn] = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
-            }
-            auto read_x = [&](int fm) {
-                const int row = wm * (kBM / kWavesM) + fm * 16 + r16;
-                const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c0]);
-                const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
-                xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                             (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                if (MODE == kModeMx)
-                    xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
-                else if (MODE == kModeI8Tile)
-                    xs[fm] = (int)sc.x[row][sw];
-            };
-            read_x(0);
-            if (kFragM > 1)
-                read_x(1);
-
-            // copies kAhead steps ahead (the last steps reload the final K step into stages
-            // nobody reads any more: no branch in the count of copies in flight)
-            const int s2 = min(s + kAhead, nk - 1);
-            issue_data(s2);
-            bool grouped_issue = false;
-            if (!kStepScales) {
-            } else if (GROUPED) {
-                // every fourth step, the next group into the other buffer (the last group
-                // reloads itself there, unused)
-                if (s % kScaleGroup == 0) {
-                    const int gi = min(s / kScaleGroup + 1, nk / kScaleGroup - 1);
-                    issue_scales((s / kScaleGroup + 1) & 1, 16 * gi);
-                    grouped_issue = true;
-                }
-            } else {
-                issue_scales((s + kAhead) % kStages, 4 * s2);
-            }
-
-#pragma unroll
-            for (int fm = 0; fm < kFragM; ++fm) {
-                if (fm + 2 < kFragM)
-                    read_x(fm + 2);
-#pragma unroll
-                for (int fn = 0; fn < kFragN; ++fn) {
-                    if constexpr (MODE == kModeMx) {
-                        acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            wf[fn], xf[fm], acc[fn][fm], 0, 0, 0, ws[fn], 0, xs[fm]);
-                    } else {
-                        // K = 128 as two int8 MFMAs of 64: chunk g, then chunk g + 4 (both
-                        // operands packed alike, which is all the instruction needs)
-                        const v4i wlo = {wf[fn][0], wf[fn][1], wf[fn][2], wf[fn][3]};
-                        const v4i whi = {wf[fn][4], wf[fn][5], wf[fn][6], wf[fn][7]};
-                        const v4i xlo = {xf[fm][0], xf[fm][1], xf[fm][2], xf[fm][3]};
-                        const v4i xhi = {xf[fm][4], xf[fm][5], xf[fm][6], xf[fm][7]};
-                        if constexpr (MODE == kModeI8Token) {
-                            acc[fn][fm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, xlo,
-                                                                                acc[fn][fm], 0, 0, 0);
-                            acc[fn][fm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, xhi,
-                                                                                acc[fn][fm], 0, 0, 0);
-                        } else {
-                            v4i t = __builtin_amdgcn_mfma_i32_16x16x64_i8(wlo, xlo, v4i{0, 0, 0, 0},
-                                                                         0, 0, 0);
-                            t = __builtin_amdgcn_mfma_i32_16x16x64_i8(whi, xhi, t, 0, 0, 0);
-                            const float as = __int_as_float(xs[fm]);   // the row's tile scale
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                acc[fn][fm][i] = __builtin_fmaf((float)t[i], as, acc[fn][fm][i]);
-                        }
-                    }
-                }
-            }
-            // step s+1's copies went out kAhead - 1 steps ago: wait for this thread's (only the
-            // steps issued since, and a scale group issued this step, may stay in flight; an
-            // older group must have landed), then for everyone's
-            wait_vm((kAhead - 1) * step_loads + (grouped_issue ? n_scale : 0));
-            lds_barrier();
-        }
-        // the reloads of the last steps must land before the next tile rewrites the rings
-        wait_vm(0);
-        lds_barrier();
-
-        // ---- epilogue: lane holds columns n0 + wn*(kBN/kWavesN) + fn*16 + 4g .. +3 of row
-        //      m0 + wm*(kBM/kWavesM) + fm*16 + r16.  int8: times the weight column scales
-        //      (and, per token, the row scale), in that order
-        const float *wcol = reinterpret_cast<const float *>(p.w_sc) + (size_t)e * p.N;
-#pragma unroll
-        for (int fm = 0; fm < kFragM; ++fm) {
-            const int r = m0 + wm * (kBM / kWavesM) + fm * 16 + r16;
-            if (r < row_hi) {
-                uint16_t *yrow = p.y + (size_t)r * p.N;
-                float rs = 1.0f;
-                if (MODE == kModeI8Token)
-                    rs = reinterpret_cast<const float *>(p.a_sc)[r];
-#pragma unroll
-                for (int fn = 0; fn < kFragN; ++fn) {
-                    const int n = n0 + wn * (kBN / kWavesN) + fn * 16 + 4 * g;
-                    if (n < p.N) {
-                        v4f d;
-                        if constexpr (MODE == kModeMx) {
-                            d = acc[fn][fm];
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                if constexpr (MODE == kModeI8Token)
-                                    d[i] = (float)acc[fn][fm][i] * rs * wcol[n + i];
-                                else
-                                    d[i] = acc[fn][fm][i] * wcol[n + i];
-                            }
-                        }
-                        const uint2 o = make_uint2(pack_bf16x2(d[0], d[1]),
-                                                   pack_bf16x2(d[2], d[3]));
-                        *reinterpret_cast<uint2 *>(yrow + n) = o;
-                    }
-                }
-            }
+    // whole rounds of whole tiles; the tiles left over for a last, partial round are cut along
+    // the columns into 2 or 4 pieces so that it keeps (nearly) every CU busy, in a fraction of
+    // a round (a piece loads the same activation tile and a part of the weight tile)
+    const int rounds = total / G;
+    const int tail = total - rounds * G;
+    const int split = tail == 0 ? 1 : (G / tail >= 4 ? 4 : (G / tail >= 2 ? 2 : 1));
+    for (int r = 0; r < rounds; ++r) {
+        int e, m0, row_hi, n0;
+        locate(r * G + v, e, m0, row_hi, n0);
+        run_tile<MODE, GROUPED, kBN>(p, sm, e, m0, row_hi, n0);
+    }
+    if (v < tail * split) {
+        int e, m0, row_hi, n0;
+        locate(rounds * G + v / split, e, m0, row_hi, n0);
+        const int piece = v % split;
+        if (split == 1) {
+            run_tile<MODE, GROUPED, kBN>(p, sm, e, m0, row_hi, n0);
+        } else if (split == 2) {
+            if (n0 + piece * (kBN / 2) < p.N)
+                run_tile<MODE, GROUPED, kBN / 2>(p, sm, e, m0, row_hi, n0 + piece * (kBN / 2));
+        } else {
+            if (n0 + piece * (kBN / 4) < p.N)
+                run_tile<MODE, GROUPED, kBN / 4>(p, sm, e, m0, row_hi, n0 + piece * (kBN / 4));
         }
     }
 }
