@@ -230,3 +230,55 @@ def test_gemm_i8_on_dispatch_output():
                                           od["offsets"], w, w_sc)
     yb = y.view(torch.int16).cpu().numpy().view(np.uint16)
     assert_close_i8(yb[:total], y64[:total], abs64[:total], wl.H, False, "dispatch chain")
+
+
+# ---------------------------------------------------------------- determinism, graphs
+
+def test_gemm_deterministic_and_graph_replays():
+    """Two launches give the same bits; a captured HIP graph of the GEMM (mxfp8 and int8 per
+    tile, the split last round included) reproduces the eager output on every replay, with
+    the output poisoned before each replay and unrelated eager work between replays."""
+    m = M()
+    say("[gemm] determinism and graph replays")
+    g = W.make_gemm_case(800, [300, 41, 0, 129], 512, 1024, tail=3)
+    gi = W.make_gemm_case_i8(801, [300, 41, 0, 129], 512, 1024, True, tail=3)
+    bufs = []
+    for case, mode in ((g, m.QUANT_MXFP8), (gi, m.QUANT_INT8_TILE)):
+        t = [torch.from_numpy(np.ascontiguousarray(v)).cuda()
+             for v in (case.a, case.a_sc, case.offsets, case.w, case.w_sc)]
+        y = torch.empty((case.rows, case.N), dtype=torch.bfloat16, device="cuda")
+        bufs.append((t, y, mode))
+
+    def launch_all():
+        for t, y, mode in bufs:
+            m.moe_expert_gemm(*t, quant_mode=mode, y=y)
+
+    launch_all()
+    torch.cuda.synchronize()
+    first = [y.clone() for _, y, _ in bufs]
+    launch_all()
+    torch.cuda.synchronize()
+    for (_, y, _), f in zip(bufs, first):
+        assert torch.equal(y.view(torch.int16), f.view(torch.int16))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch_all()
+    other = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        for _, y, _ in bufs:
+            y.view(torch.int16).fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (_, y, _), f in zip(bufs, first):
+            last = y.shape[0] - 3
+            assert torch.equal(y[:last].view(torch.int16), f[:last].view(torch.int16)), rep
+        other.mul_(1.0001).add_(0.5)
+        launch_all()
+        torch.cuda.synchronize()
