@@ -389,44 +389,58 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
         wait_vm((kAhead - 1) * step_loads + (grouped_issue ? n_scale : 0));
         lds_barrier();
     }
-    // the reloads of the last steps must land before the next tile rewrites the rings
+    // the reloads of the last steps must land, and every wave be done with the rings,
+    // before the epilogue reuses them
     wait_vm(0);
     lds_barrier();
 
-    // ---- epilogue: lane holds columns n0 + wn*(BN/kWavesN) + fn*16 + 4g .. +3 of row
-    //      m0 + wm*(kBM/kWavesM) + fm*16 + r16.  int8: times the weight column scales
-    //      (and, per token, the row scale), in that order
+    // ---- epilogue: lane holds columns wn*(BN/kWavesN) + fn*16 + 4g .. +3 of tile row
+    //      wm*(kBM/kWavesM) + fm*16 + r16.  int8: times the weight column scales (and, per
+    //      token, the row scale), in that order.  The bf16 tile goes through LDS (the
+    //      rings are free now) so that the stores write whole rows: written straight from
+    //      the MFMA layout, each store instruction would touch 16 rows with 32 bytes each.
+    constexpr int kPitch = BN * 2 + 16;   // bytes per LDS row; the pad spreads the rows' banks
+    static_assert(kBM * kPitch <= (int)sizeof(sm.stage), "output tile fits the rings");
+    uint8_t *otile = reinterpret_cast<uint8_t *>(&sm.stage[0]);
     const float *wcol = reinterpret_cast<const float *>(p.w_sc) + (size_t)e * p.N;
 #pragma unroll
     for (int fm = 0; fm < kFragM; ++fm) {
-        const int r = m0 + wm * (kBM / kWavesM) + fm * 16 + r16;
-        if (r < row_hi) {
-            uint16_t *yrow = p.y + (size_t)r * p.N;
-            float rs = 1.0f;
-            if (MODE == kModeI8Token)
-                rs = reinterpret_cast<const float *>(p.a_sc)[r];
+        const int lr = wm * (kBM / kWavesM) + fm * 16 + r16;
+        float rs = 1.0f;
+        if (MODE == kModeI8Token)
+            rs = reinterpret_cast<const float *>(p.a_sc)[min(m0 + lr, row_hi - 1)];
 #pragma unroll
-            for (int fn = 0; fn < kFragNT; ++fn) {
-                const int n = n0 + wn * (BN / kWavesN) + fn * 16 + 4 * g;
-                if (n < p.N) {
-                    v4f d;
-                    if constexpr (MODE == kModeMx) {
-                        d = acc[fn][fm];
-                    } else {
+        for (int fn = 0; fn < kFragNT; ++fn) {
+            const int lc = wn * (BN / kWavesN) + fn * 16 + 4 * g;
+            const int n = min(n0 + lc, p.N - 4);   // columns past N: computed, never stored
+            v4f d;
+            if constexpr (MODE == kModeMx) {
+                d = acc[fn][fm];
+            } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            if constexpr (MODE == kModeI8Token)
-                                d[i] = (float)acc[fn][fm][i] * rs * wcol[n + i];
-                            else
-                                d[i] = acc[fn][fm][i] * wcol[n + i];
-                        }
-                    }
-                    const uint2 o = make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
-                    *reinterpret_cast<uint2 *>(yrow + n) = o;
+                for (int i = 0; i < 4; ++i) {
+                    if constexpr (MODE == kModeI8Token)
+                        d[i] = (float)acc[fn][fm][i] * rs * wcol[n + i];
+                    else
+                        d[i] = acc[fn][fm][i] * wcol[n + i];
                 }
             }
+            *reinterpret_cast<uint2 *>(otile + lr * kPitch + lc * 2) =
+                make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
         }
     }
+    lds_barrier();
+    // 16-byte chunks, row-major over the tile: a wave instruction stores whole rows
+    constexpr int kRowChunks = BN / 8;
+#pragma unroll
+    for (int c = tid; c < kBM * kRowChunks; c += kGemmThreads) {
+        const int lr = c / kRowChunks, cc = c % kRowChunks;
+        const int r = m0 + lr, n = n0 + cc * 8;
+        const uint4 v = *reinterpret_cast<const uint4 *>(otile + lr * kPitch + cc * 16);
+        if (r < row_hi && n < p.N)
+            *reinterpret_cast<uint4 *>(p.y + (size_t)r * p.N + n) = v;
+    }
+    lds_barrier();   // the next tile's copies rewrite the rings
 }
 
 template <int MODE, bool GROUPED>
