@@ -620,7 +620,7 @@ def gemm_main(args):
     asc = torch.from_numpy(g.a_sc).to(dev)
     off = torch.from_numpy(g.offsets).to(dev)
     ws = [torch.from_numpy(g.w).to(dev) for _ in range(n_sets)]
-    wss = [torch.from_numpy(g.w_sc).to(dev) for _ in range(n_sets)]
+    wss = [moe.pack_mx_weight_scales(torch.from_numpy(g.w_sc).to(dev)) for _ in range(n_sets)]
     ys = [torch.empty((g.rows, g.N), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
     argv = [(a.data_ptr(), asc.data_ptr(), off.data_ptr(), g.E, g.rows, ws[k].data_ptr(),
              wss[k].data_ptr(), g.N, g.Kd, moe.QUANT_MXFP8, ys[k].data_ptr(), None,

@@ -243,8 +243,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
         const int n = min(n0 + (wave * kWRunsT + q) * 8 + dma_row, p.N - 1);
         wsrc[q] = w_e + (size_t)n * p.K + dma_chunk;
     }
+    // mxfp8 weight scales are group-major ([E][ceil(K/512)][N][16]): a scale offset `off`
+    // along K (bytes of the row-major layout) is group off / 16, byte off % 16
+    const int n_groups = (p.K + kBK * kScaleGroup - 1) / (kBK * kScaleGroup);
     const uint8_t *wsc_src =
-        p.w_sc + ((size_t)e * p.N + min(n0 + (w_run ? wave : 0) * 64 + lane, p.N - 1)) * kb;
+        p.w_sc + ((size_t)e * n_groups * p.N + min(n0 + (w_run ? wave : 0) * 64 + lane, p.N - 1)) * 16;
+    const size_t wsc_group = (size_t)p.N * 16;   // bytes between groups
     const uint8_t *xsc_src =
         p.a_sc + (size_t)min(m0 + (x_run ? x_idx : 0) * 64 + lane, row_hi - 1) * kb;
 
@@ -264,12 +268,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
         Sc &sc = sm.scale[buf];
         if (GROUPED) {
             if (kWeightStepScales && w_run)
-                dma16(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+                dma16(wsc_src + (off >> 4) * wsc_group, lds_addr(&sc.w[wave * 64][0]));
             if (x_run)
                 dma16(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
         } else {
             if (kWeightStepScales && w_run)
-                dma4(wsc_src + off, lds_addr(&sc.w[wave * 64][0]));
+                dma4(wsc_src + (off >> 4) * wsc_group + (off & 15), lds_addr(&sc.w[wave * 64][0]));
             if (x_run)
                 dma4(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
         }

@@ -210,12 +210,24 @@ def moe_combine_add_rmsnorm(expert_out, assist_dst, expert_scales, residual_x, g
     return y, x_out, rstd
 
 
+def pack_mx_weight_scales(w_sc: torch.Tensor) -> torch.Tensor:
+    """Weight preparation for mxfp8 moe_expert_gemm, done once per weight set: the E8M0
+    weight exponents u8 [E, N, H/32] (row-major, one per 32 elements of a column) ->
+    the group-major u8 [E, ceil(H/512), N, 16] the library reads (group q holds blocks
+    16q .. 16q+15 of every column; a partial last group is zero-padded)."""
+    E, N, nb = w_sc.shape
+    groups = -(-nb // 16)
+    padded = torch.zeros((E, N, groups * 16), dtype=torch.uint8, device=w_sc.device)
+    padded[:, :, :nb] = w_sc
+    return padded.view(E, N, groups, 16).permute(0, 2, 1, 3).contiguous()
+
+
 def moe_expert_gemm(expand_x, expand_scales, expert_offsets, weights, weight_scales,
                     quant_mode: int = QUANT_MXFP8, y=None, dev_err=None, stream=None):
     """Grouped GEMM of the expert computation -> y bf16 [rows, N] (rows outside every
     instance's range are not written).  mxfp8: expand_x u8 [rows, H] (E4M3),
     expand_scales u8 [rows, H/32] (E8M0), weights u8 [E, N, H], weight_scales u8
-    [E, N, H/32].  int8 (QUANT_INT8_TOKEN / QUANT_INT8_TILE): expand_x int8 [rows, H],
+    [E, ceil(H/512), N, 16] (pack_mx_weight_scales of the [E, N, H/32] exponents).  int8 (QUANT_INT8_TOKEN / QUANT_INT8_TILE): expand_x int8 [rows, H],
     expand_scales f32 [rows] / [rows, H/128], weights int8 [E, N, H], weight_scales f32
     [E, N].  expert_offsets int32 [E+1]."""
     rows, H = expand_x.shape

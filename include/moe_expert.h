@@ -249,7 +249,8 @@ int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
  *   for e < n_instances, r in [expert_offsets[e], expert_offsets[e+1]), n < N:
  *     y[r][n] = bf16( sum_k  A(r, k) * W(e, n, k) )        (fp32 accumulation)
  *     A(r, k)    = e4m3(expand_x[r][k])   * 2^(expand_scales[r][k/32] - 127)
- *     W(e, n, k) = e4m3(weights[e][n][k]) * 2^(weight_scales[e][n][k/32] - 127)
+ *     W(e, n, k) = e4m3(weights[e][n][k]) * 2^(S(e, n, k/32) - 127)
+ *     S(e, n, b) = weight_scales[e][b/16][n][b%16]
  *
  * or, for the int8 outputs of dispatch cases 3 (MOE_Q_INT8_TOKEN) and 4
  * (MOE_Q_INT8_TILE, tiles of 128):
@@ -263,8 +264,13 @@ int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
  *   expert_offsets int32 [n_instances+1] (moe_dispatch's offsets, or a slice
  *                  of them for a subset of instances; values are absolute rows)
  *   weights        E4M3 or int8 [n_instances, N, H]          16-byte aligned
- *   weight_scales  mxfp8: u8 E8M0 [n_instances, N, H/32]; int8: f32 [n_instances, N]
- *                                                            4-byte aligned
+ *   weight_scales  mxfp8: u8 E8M0 [n_instances, ceil(H/512), N, 16], group-major:
+ *                  group q holds the exponents of K blocks 16q .. 16q+15 of every
+ *                  column, 16 bytes per column (a last, partial group is padded; the
+ *                  pad is never read), so the kernel's copies of one group for a
+ *                  run of columns are contiguous.  A weight-preparation step, done
+ *                  once per weight set: pack_mx_weight_scales in the binding.
+ *                  int8: f32 [n_instances, N].                4-byte aligned
  *   y              bf16 [rows, N] (out; rows outside every instance's range
  *                  are not written)  16-byte aligned
  *   dev_err        int32 [1] or NULL: MOE_ERR_OFFSETS when the offsets are not

@@ -36,7 +36,8 @@ def run_gpu(g: W.GemmCase, offsets=None, dev_err=None):
     y = torch.full((g.rows, g.N), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     m.moe_expert_gemm(torch.from_numpy(g.a).cuda(), torch.from_numpy(g.a_sc).cuda(),
                       torch.from_numpy(np.ascontiguousarray(off, np.int32)).cuda(),
-                      torch.from_numpy(g.w).cuda(), torch.from_numpy(g.w_sc).cuda(), y=y,
+                      torch.from_numpy(g.w).cuda(),
+                      m.pack_mx_weight_scales(torch.from_numpy(g.w_sc).cuda()), y=y,
                       dev_err=dev_err)
     torch.cuda.synchronize()
     return y.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -101,7 +102,8 @@ def test_gemm_malformed_offsets_flagged_in_bounds():
         y = guard[:g.rows].view(torch.bfloat16)
         m.moe_expert_gemm(torch.from_numpy(g.a).cuda(), torch.from_numpy(g.a_sc).cuda(),
                           torch.tensor(off, dtype=torch.int32, device="cuda"),
-                          torch.from_numpy(g.w).cuda(), torch.from_numpy(g.w_sc).cuda(), y=y,
+                          torch.from_numpy(g.w).cuda(),
+                          m.pack_mx_weight_scales(torch.from_numpy(g.w_sc).cuda()), y=y,
                           dev_err=dev_err)
         torch.cuda.synchronize()
         assert int(dev_err.item()) & m.ERR_OFFSETS, off
@@ -246,6 +248,8 @@ def test_gemm_deterministic_and_graph_replays():
     for case, mode in ((g, m.QUANT_MXFP8), (gi, m.QUANT_INT8_TILE)):
         t = [torch.from_numpy(np.ascontiguousarray(v)).cuda()
              for v in (case.a, case.a_sc, case.offsets, case.w, case.w_sc)]
+        if mode == m.QUANT_MXFP8:
+            t[4] = m.pack_mx_weight_scales(t[4])
         y = torch.empty((case.rows, case.N), dtype=torch.bfloat16, device="cuda")
         bufs.append((t, y, mode))
 
