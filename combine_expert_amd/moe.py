@@ -67,6 +67,49 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+_BYTE_TYPES = (torch.uint8, torch.int8, torch.bool)
+
+
+def _arg(t: Optional[torch.Tensor], name: str, dtypes, numel: int, required: bool = True):
+    """Checks a tensor argument before its pointer goes to the library: a CUDA tensor,
+    contiguous, of one of `dtypes`, holding at least `numel` elements.  The kernels trust
+    the sizes they are given, so an undersized or host tensor is refused here."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements; at least {numel} are needed")
+
+
+_I32, _F32, _BF16 = (torch.int32,), (torch.float32,), (torch.bfloat16,)
+
+
+def _dispatch_args(x, expert_ids, Bs, H, K, E, quant_mode, tile, quant_scales, out,
+                   dev_err, ids_name="expert_ids"):
+    _arg(x, "x", _BF16, Bs * H)
+    _arg(expert_ids, ids_name, _I32, Bs * K)
+    if quant_scales is not None:
+        _arg(quant_scales, "quant_scales", _F32, 1)
+    N = Bs * K
+    _arg(out["expand_x"], "expand_x", _BF16 if quant_mode == QUANT_NONE else _BYTE_TYPES[:2],
+         N * H)
+    ns = n_scale_entries(quant_mode, H, tile) if quant_mode != QUANT_INT8_TILE or tile > 0 else 0
+    _arg(out.get("expand_scales"), "expand_scales",
+         (torch.uint8,) if quant_mode == QUANT_MXFP8 else _F32, N * ns, required=ns > 0)
+    _arg(out["expert_counts"], "expert_counts", _I32, E)
+    _arg(out["expert_offsets"], "expert_offsets", _I32, E + 1)
+    _arg(out["expand_src"], "expand_src", _I32, N)
+    _arg(out["assist_dst"], "assist_dst", _I32, N)
+    _arg(dev_err, "dev_err", _I32, 1, required=False)
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -101,6 +144,14 @@ def moe_update_expert(expert_ids, table, n_instances: int, expert_scales=None, p
         balanced_ids = torch.empty((Bs, K), dtype=torch.int32, device=dev)
     if balanced_mask is None:
         balanced_mask = torch.empty((Bs, K), dtype=torch.uint8, device=dev)
+    _arg(expert_ids, "expert_ids", _I32, Bs * K)
+    _arg(table, "table", _I32, n_logical * F)
+    _arg(expert_scales, "expert_scales", _F32, Bs * K, required=False)
+    _arg(prune_thr, "prune_thr", _F32, K, required=False)
+    _arg(token_mask, "token_mask", _BYTE_TYPES, Bs, required=False)
+    _arg(balanced_ids, "balanced_ids", _I32, Bs * K)
+    _arg(balanced_mask, "balanced_mask", _BYTE_TYPES, Bs * K)
+    _arg(dev_err, "dev_err", _I32, 1, required=False)
     rc = _lib.moe_update_expert(_ptr(expert_ids), _ptr(expert_scales), _ptr(table),
                                 _ptr(prune_thr), _ptr(token_mask), Bs, K, n_logical, F,
                                 n_instances, _ptr(balanced_ids), _ptr(balanced_mask),
@@ -148,6 +199,8 @@ def moe_dispatch(x, expert_ids, n_ranks: int, local_experts: int, quant_mode: in
     E = n_ranks * local_experts
     if out is None:
         out = dispatch_buffers(Bs, H, K, E, quant_mode, tile, x.device)
+    _dispatch_args(x, expert_ids, Bs, H, K, E, quant_mode, tile, quant_scales, out, dev_err)
+    _arg(active_mask, "active_mask", _BYTE_TYPES, Bs * K, required=False)
     rc = _lib.moe_dispatch(_ptr(x), _ptr(expert_ids), _ptr(active_mask), Bs, H, K, n_ranks,
                            local_experts, quant_mode, tile, _ptr(quant_scales),
                            scales_kind(quant_scales, H, E), _ptr(out["expand_x"]),
@@ -174,6 +227,14 @@ def moe_update_dispatch(x, expert_ids, table, n_ranks: int, local_experts: int,
         balanced_ids = torch.empty((Bs, K), dtype=torch.int32, device=x.device)
     if balanced_mask is None:
         balanced_mask = torch.empty((Bs, K), dtype=torch.uint8, device=x.device)
+    _dispatch_args(x, expert_ids, Bs, H, K, n_ranks * local_experts, quant_mode, tile,
+                   quant_scales, out, dev_err)
+    _arg(table, "table", _I32, n_logical * F)
+    _arg(expert_scales, "expert_scales", _F32, Bs * K, required=False)
+    _arg(prune_thr, "prune_thr", _F32, K, required=False)
+    _arg(token_mask, "token_mask", _BYTE_TYPES, Bs, required=False)
+    _arg(balanced_ids, "balanced_ids", _I32, Bs * K)
+    _arg(balanced_mask, "balanced_mask", _BYTE_TYPES, Bs * K)
     rc = _lib.moe_update_dispatch(_ptr(x), _ptr(expert_ids), _ptr(expert_scales), _ptr(table),
                                   _ptr(prune_thr), _ptr(token_mask), Bs, H, K, n_logical, F,
                                   n_ranks, local_experts, quant_mode, tile, _ptr(quant_scales),
@@ -202,6 +263,16 @@ def moe_combine_add_rmsnorm(expert_out, assist_dst, expert_scales, residual_x, g
         x_out = torch.empty((Bs, H), dtype=torch.bfloat16, device=dev)
     if rstd is None and want_rstd:
         rstd = torch.empty((Bs,), dtype=torch.float32, device=dev)
+    _arg(expert_out, "expert_out", _BF16, Bs * K * H)
+    _arg(assist_dst, "assist_dst", _I32, Bs * K)
+    _arg(expert_scales, "expert_scales", _F32, Bs * K)
+    _arg(shared_x, "shared_x", _BF16, Bs * H, required=False)
+    _arg(residual_x, "residual_x", _BF16, Bs * H)
+    _arg(gamma, "gamma", _BF16, H)
+    _arg(y, "y", _BF16, Bs * H)
+    _arg(x_out, "x_out", _BF16, Bs * H, required=False)
+    _arg(rstd, "rstd", _F32, Bs, required=False)
+    _arg(dev_err, "dev_err", _I32, 1, required=False)
     rc = _lib.moe_combine_add_rmsnorm(_ptr(expert_out), _ptr(assist_dst), _ptr(expert_scales),
                                       _ptr(shared_x), _ptr(residual_x), _ptr(gamma), eps, Bs, H,
                                       K, shared_mode, _ptr(y), _ptr(x_out), _ptr(rstd),
@@ -235,6 +306,16 @@ def moe_expert_gemm(expand_x, expand_scales, expert_offsets, weights, weight_sca
     N = weights.shape[1]
     if y is None:
         y = torch.empty((rows, N), dtype=torch.bfloat16, device=expand_x.device)
+    mx = quant_mode == QUANT_MXFP8
+    _arg(expand_x, "expand_x", _BYTE_TYPES[:2], rows * H)
+    _arg(expand_scales, "expand_scales", (torch.uint8,) if mx else _F32,
+         rows * (H // 32 if mx else H // 128 if quant_mode == QUANT_INT8_TILE else 1))
+    _arg(expert_offsets, "expert_offsets", _I32, E + 1)
+    _arg(weights, "weights", _BYTE_TYPES[:2], E * N * H)
+    _arg(weight_scales, "weight_scales", (torch.uint8,) if mx else _F32,
+         E * (-(-H // 512)) * N * 16 if mx else E * N)
+    _arg(y, "y", _BF16, rows * N)
+    _arg(dev_err, "dev_err", _I32, 1, required=False)
     rc = _lib.moe_expert_gemm(_ptr(expand_x), _ptr(expand_scales), _ptr(expert_offsets), E, rows,
                               _ptr(weights), _ptr(weight_scales), N, H, quant_mode, _ptr(y),
                               _ptr(dev_err), _stream(stream))
