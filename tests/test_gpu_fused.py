@@ -99,6 +99,46 @@ def test_fused_matches_separate_calls():
         assert torch.equal(g[key].view(torch.uint8), gd[key].view(torch.uint8)), key
 
 
+@pytest.mark.parametrize("name", ["c4", "c4b"])
+def test_single_launch_at_large_sizes(name):
+    """Above 4096 entries the call runs the mapping and the dispatch as two launches when
+    the mapped ids and mask are given; with them NULL it stays one launch.  Both forms give
+    the same outputs and error bits (the two-launch form is checked against the oracle by
+    the full-size test)."""
+    m = M()
+    wl = W.make(name)
+    say(f"[fused] one launch against two, {name} (Bs*K = {wl.Bs * wl.K})")
+    err2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g2 = fused(wl, dev_err=err2)
+    out = m.dispatch_buffers(wl.Bs, wl.H, wl.K, wl.E, wl.quant_mode, wl.tile)
+    for key in ("expand_x", "expand_scales"):
+        if out.get(key) is not None:
+            out[key].view(torch.uint8).fill_(POISON)
+    err1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    prune = wl.prune_thr is not None
+    t = dict(x=cuda(wl.x), ids=cuda(wl.logical_ids), table=cuda(wl.table),
+             sc=cuda(wl.scales) if prune else None, thr=cuda(wl.prune_thr) if prune else None,
+             tm=cuda(wl.token_mask))
+    p = lambda v: None if v is None else v.data_ptr()
+    n_logical, F = wl.table.shape
+    rc = m.raw().moe_update_dispatch(
+        p(t["x"]), p(t["ids"]), p(t["sc"]), p(t["table"]), p(t["thr"]), p(t["tm"]), wl.Bs,
+        wl.H, wl.K, n_logical, F, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile, None,
+        0, None, None, p(out["expand_x"]), p(out.get("expand_scales")),
+        p(out["expert_counts"]), p(out["expert_offsets"]), p(out["expand_src"]),
+        p(out["assist_dst"]), p(err1), torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    total = int(g2["expert_offsets"][-1].item())
+    for key in ("expert_counts", "expert_offsets", "assist_dst", "expand_src"):
+        assert torch.equal(out[key], g2[key]), key
+    for key in ("expand_x", "expand_scales"):
+        if out.get(key) is not None:
+            assert torch.equal(out[key][:total].view(torch.uint8),
+                               g2[key][:total].view(torch.uint8)), key
+    assert int(err1.item()) == int(err2.item())
+
+
 def test_fused_large_table_and_long_rows():
     """A table of 512 x 16 words (the staging limit is 8192): every block
     stages it through registers and the plain loop, and replica slots reach
