@@ -136,6 +136,62 @@ def test_gemm_full_size_sampled():
     assert not np.any(y[:int(g.offsets[-1])] == POISON16)
 
 
+
+def check_sampled(g, y, cols=None, extra_rows=(), where=""):
+    """The first, middle and last row of every instance (plus extra_rows) and the given
+    columns (all by default) against the oracle on that sub-problem."""
+    rows, inst = [], []
+    for e in range(g.E):
+        lo, hi = int(g.offsets[e]), int(g.offsets[e + 1])
+        pick = {lo, (lo + hi) // 2, hi - 1} if hi > lo else set()
+        pick |= {r for r in extra_rows if lo <= r < hi}
+        for r in sorted(pick):
+            rows.append(r)
+            inst.append(e)
+    rows = np.array(rows)
+    cols = np.arange(g.N) if cols is None else np.asarray(cols)
+    sub_off = np.zeros(g.E + 1, np.int32)
+    sub_off[1:] = np.cumsum(np.bincount(np.array(inst), minlength=g.E))
+    _, y64, abs64 = oracle.expert_gemm_mx(g.a[rows], g.a_sc[rows], sub_off,
+                                          np.ascontiguousarray(g.w[:, cols]),
+                                          np.ascontiguousarray(g.w_sc[:, cols]))
+    assert_close(y[rows][:, cols], y64, abs64, g.Kd, where)
+
+
+def test_gemm_max_instances():
+    """1024 instances (the limit), most with 0-3 rows: the instance prefix and the binary
+    search over it at full length."""
+    counts = np.random.default_rng(7101).integers(0, 4, 1024)
+    g = W.make_gemm_case(7102, counts, 128, 128, tail=5)
+    say(f"[gemm] 1024 instances, {int(g.offsets[-1])} rows")
+    y = run_gpu(g)
+    check_sampled(g, y, where="1024 instances")
+    assert np.all(y[int(g.offsets[-1]):] == POISON16)
+
+
+def test_gemm_max_k_and_max_n():
+    """K = 16384 (the limit: 128 K steps, 32 scale groups) and, separately, N = 16384 (64
+    column tiles; 256 sampled columns checked)."""
+    g = W.make_gemm_case(7103, [200, 77, 129], 256, 16384)
+    say("[gemm] K = 16384")
+    check_sampled(g, run_gpu(g), where="K=16384")
+    g = W.make_gemm_case(7104, [130, 3], 16384, 128)
+    say("[gemm] N = 16384")
+    cols = np.sort(np.random.default_rng(7105).choice(g.N, 256, replace=False))
+    check_sampled(g, run_gpu(g), cols=cols, where="N=16384")
+
+
+def test_gemm_max_rows():
+    """4194304 rows (the limit; 32768 row tiles counted in 16 bits on the device, 128
+    rounds of the grid), split into two instances at a row that is not a tile boundary;
+    sampled rows checked."""
+    g = W.make_gemm_case(7106, [4194304 - 1000, 1000], 128, 128)
+    say("[gemm] 4194304 rows")
+    y = run_gpu(g)
+    extra = np.random.default_rng(7107).integers(0, g.rows, 64)
+    check_sampled(g, y, extra_rows=extra, where="4M rows")
+
+
 # ---------------------------------------------------------------- int8 operands
 
 def run_gpu_i8(g, quant_mode):
