@@ -698,7 +698,7 @@ def gemm_main(args):
                                "mxfp8 operands with E8M0 block scales, bf16 out",
                    "E": g.E, "rows": rows_total, "counts": g.counts.tolist(), "N": g.N,
                    "H": g.Kd, "weight_sets": n_sets},
-        "roofline": {"kernel": "k_expert_gemm", "bound": "mfma", "achieved": round(tfs, 2),
+        "roofline": {"kernel": "k_expert_gemm_mx", "bound": "mfma", "achieved": round(tfs, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfs / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flops_per_launch": flops,

@@ -41,6 +41,13 @@
 // transposed output tile and each lane ends with four consecutive output
 // columns of one row: one 8-byte bf16 store.
 //
+// Two tilings for mxfp8 (grouped scales).  Besides the 128 x 256 tiles described here,
+// 256 x 256 tiles (further down) need a third fewer line requests per flop and win by
+// 11-14% on shapes that fill whole rounds of them; on uneven row counts their last,
+// partial round costs more than it saves.  The launch computes both row-tile counts on
+// the device and takes the tiling a cost model of whole and partial rounds estimates
+// faster (every block decides alike).  int8 and ungrouped scales use the 128 x 256 tiles.
+//
 // Scheduling.  Each instance needs ceil(rows_e / 128) row tiles; a block
 // prefix-sums those counts into LDS once and then walks the flattened
 // (column tile, row tile) space grid-stride, row tiles fastest so that the
@@ -447,15 +454,16 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
     lds_barrier();   // the next tile's copies rewrite the rings
 }
 
-template <int MODE, bool GROUPED>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
+// Row tiles of `bm` rows per instance, prefix-summed into tiles[0 .. E] in LDS (thread t
+// owns instances 4t .. 4t+3); returns the total.  Offsets that are not non-decreasing within
+// [0, rows] raise the error bit (once, from block 0, when `report`).
+__device__ __forceinline__ int tile_prefix(const GemmArgs &p, int bm, uint16_t *tiles,
+                                           int *wave_sum, bool report)
 {
-    __shared__ __align__(16) GemmSmem<GROUPED> sm;
+    static_assert(kGemmThreads * 4 >= kMaxInstances, "prefix covers every instance");
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-
-    // ---- row tiles per instance, prefix-summed (thread t owns instances 4t .. 4t+3)
     int c[4], tsum = 0;
     bool bad_any = false;
 #pragma unroll
@@ -467,30 +475,37 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
             bool bad;
             instance_rows(p, e, lo, hi, &bad);
             bad_any |= bad;
-            c[q] = (hi - lo + kBM - 1) / kBM;
+            c[q] = (hi - lo + bm - 1) / bm;
         }
         tsum += c[q];
     }
-    if (bad_any && blockIdx.x == 0 && p.dev_err)
+    if (report && bad_any && blockIdx.x == 0 && p.dev_err)
         atomicOr(p.dev_err, MOE_ERR_OFFSETS);
     const int incl = wave_incl_scan(tsum);
     if (lane == kWave - 1)
-        sm.wave_sum[wave] = incl;
+        wave_sum[wave] = incl;
     lds_barrier();
     int excl = incl - tsum;
     for (int w = 0; w < wave; ++w)
-        excl += sm.wave_sum[w];
+        excl += wave_sum[w];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = 4 * tid + q;
         if (e < p.E)
-            sm.tiles[e] = (uint16_t)excl;
+            tiles[e] = (uint16_t)excl;
         if (e == p.E - 1)
-            sm.tiles[p.E] = (uint16_t)(excl + c[q]);
+            tiles[p.E] = (uint16_t)(excl + c[q]);
         excl += c[q];
     }
     lds_barrier();
-    const int m_tiles = sm.tiles[p.E];
+    return tiles[p.E];
+}
+
+// The tiles of 128 rows x 256 columns, walked by the grid (see the kernel below).
+template <int MODE, bool GROUPED>
+__device__ __forceinline__ void narrow_tiles(const GemmArgs &p, GemmSmem<GROUPED> &sm,
+                                             int m_tiles)
+{
     const int n_tiles = (p.N + kBN - 1) / kBN;
     const int total = m_tiles * n_tiles;
 
@@ -551,6 +566,298 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
     }
 }
 
+template <int MODE, bool GROUPED>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm(GemmArgs p)
+{
+    __shared__ __align__(16) GemmSmem<GROUPED> sm;
+    const int m_tiles = tile_prefix(p, kBM, sm.tiles, sm.wave_sum, true);
+    narrow_tiles<MODE, GROUPED>(p, sm, m_tiles);
+}
+
+// ---------------------------------------------------------------- 256 x 256 tiles (mxfp8)
+//
+// The same computation with 256 x 256 output tiles, for mxfp8 with grouped scales.  A K
+// step then brings 512 rows of 128 bytes for twice the MACs of a 128 x 256 tile: a third
+// fewer line requests per flop, which is what bounds the smaller tile (its copies cannot
+// keep its MFMAs busy).  Eight waves of 64 x 128 (two per SIMD), two LDS stages of 64 KB:
+// a step's 32 MFMAs per wave, 64 per SIMD (about 2048 cycles), cover the copies of the
+// next step, issued right after the barrier that opens the step.
+constexpr int kWBM = 256;
+constexpr int kWBN = 256;
+constexpr int kWWaves = 8;
+constexpr int kWThreads = kWWaves * 64;
+constexpr int kWWavesM = 4;                      // waves along the rows (64 rows each)
+constexpr int kWFragM = kWBM / kWWavesM / 16;    // 4 fragments of 16 rows per wave
+constexpr int kWXRuns = kWBM / 8 / kWWaves;      // 4 copy runs of 8 rows per wave and step
+constexpr int kWGroupM = 4;                      // row tiles per patch of the tile order
+
+struct WStage {
+    uint8_t x[kWBM * kBK];   // 32 KB: activation rows, swizzled 16-byte chunks
+    uint8_t w[kWBN * kBK];   // 32 KB: weight rows
+};
+
+struct WScales {
+    uint32_t x[kWBM][kScaleGroup];
+    uint32_t w[kWBN][kScaleGroup];
+};
+
+struct WSmem {
+    WStage stage[2];
+    WScales scale[2];
+    uint16_t tiles[kMaxInstances + 1];   // exclusive prefix of row tiles per instance
+    int wave_sum[kWWaves];
+};
+
+// One 256 x BN output tile (BN 256, or 128 / 64 for the pieces of the last round).
+template <int BN>
+__device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, int m0,
+                                          int row_hi, int n0)
+{
+    constexpr int kFragNT = BN / 2 / 16;          // weight fragments per wave
+    constexpr int kWRunsT = BN / 8 / kWWaves;     // weight copy runs per wave and step
+    static_assert(kFragNT >= 1 && kWRunsT >= 1, "tile width");
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int nk = p.K / kBK;
+    const int kb = p.K / 32;
+    const int n_groups = nk / kScaleGroup;       // K % 512 == 0 on this path
+    const int g = lane >> 4;
+    const int r16 = lane & 15;
+    const int wm = wave >> 1, wn = wave & 1;     // the wave's 64 x (BN / 2) part
+    const int dma_row = lane >> 3;
+    const int dma_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
+    const int fr_c0 = ((g ^ (r16 & 7)) << 4);
+    const int fr_c1 = (((g + 4) ^ (r16 & 7)) << 4);
+    const uint8_t *w_e = p.w + (size_t)e * p.N * p.K;
+
+    // copy sources are recomputed at each issue (a handful of integer operations per copy)
+    // rather than held in registers; rows past the instance / columns past N are clamped:
+    // loaded, multiplied, never stored
+    // scale runs of 64 rows / columns: activation run j to wave j (4 runs), weight run j
+    // to wave 4 + j (BN / 64 runs)
+    const bool x_run = wave < kWBM / 64;
+    const int wj = wave - kWBM / 64;
+    const bool w_run = wj >= 0 && wj < BN / 64;
+    const uint8_t *xsc_src =
+        p.a_sc + (size_t)min(m0 + (x_run ? wave : 0) * 64 + lane, row_hi - 1) * kb;
+    const uint8_t *wsc_src =
+        p.w_sc + ((size_t)e * n_groups * p.N + min(n0 + (w_run ? wj : 0) * 64 + lane, p.N - 1)) * 16;
+    const size_t wsc_group = (size_t)p.N * 16;
+
+    auto issue_data = [&](int s) {
+        const int k0 = s * kBK;
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(&sm.stage[s & 1]);
+#pragma unroll
+        for (int q = 0; q < kWXRuns; ++q) {
+            const int r = min(m0 + (wave * kWXRuns + q) * 8 + dma_row, row_hi - 1);
+            dma16(p.a + (size_t)r * p.K + k0 + dma_chunk,
+                  lds_addr(base + offsetof(WStage, x) + (wave * kWXRuns + q) * 1024));
+        }
+#pragma unroll
+        for (int q = 0; q < kWRunsT; ++q) {
+            const int n = min(n0 + (wave * kWRunsT + q) * 8 + dma_row, p.N - 1);
+            dma16(w_e + (size_t)n * p.K + k0 + dma_chunk,
+                  lds_addr(base + offsetof(WStage, w) + (wave * kWRunsT + q) * 1024));
+        }
+    };
+    auto issue_scales = [&](int gi) {
+        WScales &sc = sm.scale[gi & 1];
+        if (x_run)
+            dma16(xsc_src + 16 * gi, lds_addr(&sc.x[wave * 64][0]));
+        if (w_run)
+            dma16(wsc_src + gi * wsc_group, lds_addr(&sc.w[wj * 64][0]));
+    };
+
+    v4f acc[kFragNT][kWFragM];
+#pragma unroll
+    for (int i = 0; i < kFragNT; ++i)
+#pragma unroll
+        for (int j = 0; j < kWFragM; ++j)
+            acc[i][j] = v4f{0, 0, 0, 0};
+
+    issue_data(0);
+    issue_scales(0);
+    for (int s = 0; s < nk; ++s) {
+        // step s's copies (and its scale group) have landed for this wave, then for every
+        // wave; every wave is also past step s - 1, so its stage and, at a group start,
+        // the previous group's scale buffer are free
+        wait_vm(0);
+        lds_barrier();
+        if (s + 1 < nk)
+            issue_data(s + 1);
+        if (s % kScaleGroup == 0 && s / kScaleGroup + 1 < n_groups)
+            issue_scales(s / kScaleGroup + 1);
+
+        const WStage &st = sm.stage[s & 1];
+        const WScales &sc = sm.scale[(s / kScaleGroup) & 1];
+        const int sw = s % kScaleGroup;
+        // all activation fragments first (32 registers), then the weight fragments one
+        // ahead of the four MFMAs that use each
+        v8i xf[kWFragM];
+        int xs[kWFragM];
+#pragma unroll
+        for (int fm = 0; fm < kWFragM; ++fm) {
+            const int row = wm * (kWBM / kWWavesM) + fm * 16 + r16;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c0]);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
+            xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
+        }
+        auto read_w = [&](int fn, v8i &wf, int &ws) {
+            const int row = wn * (BN / 2) + fn * 16 + r16;
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c0]);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
+            wf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            ws = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
+        };
+        v8i wcur, wnext;
+        int scur, snext;
+        read_w(0, wcur, scur);
+#pragma unroll
+        for (int fn = 0; fn < kFragNT; ++fn) {
+            if (fn + 1 < kFragNT)
+                read_w(fn + 1, wnext, snext);
+#pragma unroll
+            for (int fm = 0; fm < kWFragM; ++fm)
+                acc[fn][fm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    wcur, xf[fm], acc[fn][fm], 0, 0, 0, scur, 0, xs[fm]);
+            wcur = wnext;
+            scur = snext;
+        }
+    }
+    // every wave is done with the rings before the epilogue reuses them
+    lds_barrier();
+
+    // epilogue through LDS (the rings and the scale buffers, contiguous): whole rows out
+    constexpr int kPitch = BN * 2 + 16;
+    static_assert(offsetof(WSmem, scale) == sizeof(WStage) * 2, "contiguous rings");
+    static_assert(kWBM * kPitch <= (int)(sizeof(WStage) * 2 + sizeof(WScales) * 2),
+                  "output tile fits the rings");
+    uint8_t *otile = reinterpret_cast<uint8_t *>(&sm.stage[0]);
+#pragma unroll
+    for (int fm = 0; fm < kWFragM; ++fm) {
+        const int lr = wm * (kWBM / kWWavesM) + fm * 16 + r16;
+#pragma unroll
+        for (int fn = 0; fn < kFragNT; ++fn) {
+            const int lc = wn * (BN / 2) + fn * 16 + 4 * g;
+            const v4f d = acc[fn][fm];
+            *reinterpret_cast<uint2 *>(otile + lr * kPitch + lc * 2) =
+                make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+        }
+    }
+    lds_barrier();
+    constexpr int kRowChunks = BN / 8;
+#pragma unroll 4
+    for (int c = tid; c < kWBM * kRowChunks; c += kWThreads) {
+        const int lr = c / kRowChunks, cc = c % kRowChunks;
+        const int r = m0 + lr, n = n0 + cc * 8;
+        const uint4 v = *reinterpret_cast<const uint4 *>(otile + lr * kPitch + cc * 16);
+        if (r < row_hi && n < p.N)
+            *reinterpret_cast<uint4 *>(p.y + (size_t)r * p.N + n) = v;
+    }
+    lds_barrier();   // the next tile's copies rewrite the rings
+}
+
+// The tiles of 256 x 256, walked by the grid like the narrow ones.
+__device__ __forceinline__ void wide_tiles(const GemmArgs &p, WSmem &sm, int m_tiles)
+{
+    const int n_tiles = (p.N + kWBN - 1) / kWBN;
+    const int total = m_tiles * n_tiles;
+
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int v = (G % kXcds == 0) ? (b % kXcds) * (G / kXcds) + b / kXcds : b;
+    auto locate = [&](int t, int &e, int &m0, int &row_hi, int &n0) {
+        const int grp = t / (kWGroupM * n_tiles);
+        const int tin = t - grp * kWGroupM * n_tiles;
+        const int gm = min(kWGroupM, m_tiles - grp * kWGroupM);
+        const int tm = grp * kWGroupM + tin % gm;
+        const int tn = tin / gm;
+        int lo_e = 0, hi_e = p.E;
+        while (hi_e - lo_e > 1) {
+            const int mid = (lo_e + hi_e) >> 1;
+            if (sm.tiles[mid] <= tm)
+                lo_e = mid;
+            else
+                hi_e = mid;
+        }
+        e = lo_e;
+        int row_lo;
+        instance_rows(p, e, row_lo, row_hi, nullptr);
+        m0 = row_lo + (tm - sm.tiles[e]) * kWBM;
+        n0 = tn * kWBN;
+    };
+    const int rounds = total / G;
+    const int tail = total - rounds * G;
+    const int split = tail == 0 ? 1 : (G / tail >= 4 ? 4 : (G / tail >= 2 ? 2 : 1));
+    for (int r = 0; r < rounds; ++r) {
+        int e, m0, row_hi, n0;
+        locate(r * G + v, e, m0, row_hi, n0);
+        run_wtile<kWBN>(p, sm, e, m0, row_hi, n0);
+    }
+    if (v < tail * split) {
+        int e, m0, row_hi, n0;
+        locate(rounds * G + v / split, e, m0, row_hi, n0);
+        const int piece = v % split;
+        if (split == 1) {
+            run_wtile<kWBN>(p, sm, e, m0, row_hi, n0);
+        } else if (split == 2) {
+            if (n0 + piece * (kWBN / 2) < p.N)
+                run_wtile<kWBN / 2>(p, sm, e, m0, row_hi, n0 + piece * (kWBN / 2));
+        } else {
+            if (n0 + piece * (kWBN / 4) < p.N)
+                run_wtile<kWBN / 4>(p, sm, e, m0, row_hi, n0 + piece * (kWBN / 4));
+        }
+    }
+}
+
+// Estimated time of a tiling, in rounds of narrow (128 x 256) tiles: its whole rounds
+// times the cost of one, plus the last partial round at the cost of its pieces (the split
+// the tile loops use).  Measured on MI355X: a round of 256 x 256 tiles costs 1.70-1.77
+// narrow rounds (dense shapes of 4096 and 8192 rows); a last round cut into pieces of a
+// quarter (half) of the columns costs about 0.5 (0.67) of a round for narrow tiles and
+// 0.65 (0.78) for wide ones, which load more rows per flop.
+__device__ __forceinline__ float tiling_cost(int tiles, int G, float round_cost, float quarter,
+                                             float half)
+{
+    const int rounds = tiles / G;
+    const int tail = tiles - rounds * G;
+    const int split = tail == 0 ? 1 : (G / tail >= 4 ? 4 : (G / tail >= 2 ? 2 : 1));
+    const float last = tail == 0 ? 0.0f : (split == 4 ? quarter : split == 2 ? half : 1.0f);
+    return round_cost * ((float)rounds + last);
+}
+
+// mxfp8 with grouped scales: both tilings' row-tile counts are prefix-summed (each block
+// alike, so every block takes the same decision), and the launch runs the one the cost
+// model estimates faster.  The two LDS layouts share the block's LDS; their prefix arrays
+// do not overlap each other, and the chosen tiling only touches its own layout.
+union MxSmem {
+    GemmSmem<true> narrow;
+    WSmem wide;
+};
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
+{
+    static_assert(kWThreads == kGemmThreads, "one block shape for both tilings");
+    static_assert(offsetof(WSmem, wave_sum) + sizeof(int) * kWWaves <=
+                      offsetof(GemmSmem<true>, tiles),
+                  "the two prefix arrays do not overlap");
+    __shared__ __align__(16) MxSmem sm;
+    const int m_narrow = tile_prefix(p, kBM, sm.narrow.tiles, sm.narrow.wave_sum, true);
+    const int m_wide = tile_prefix(p, kWBM, sm.wide.tiles, sm.wide.wave_sum, false);
+    const int G = gridDim.x;
+    const int n_narrow = m_narrow * ((p.N + kBN - 1) / kBN);
+    const int n_wide = m_wide * ((p.N + kWBN - 1) / kWBN);
+    if (tiling_cost(n_wide, G, 1.75f, 0.65f, 0.78f) < tiling_cost(n_narrow, G, 1.0f, 0.5f, 0.67f))
+        wide_tiles(p, sm.wide, m_wide);
+    else
+        narrow_tiles<kModeMx, true>(p, sm.narrow, m_narrow);
+}
+
 }  // namespace
 
 hipError_t launch_expert_gemm(int quant_mode, const void *a, const void *a_sc,
@@ -575,7 +882,7 @@ hipError_t launch_expert_gemm(int quant_mode, const void *a, const void *a_sc,
     switch (quant_mode) {
     case kModeMx:
         if (grouped)
-            hipLaunchKernelGGL((k_expert_gemm<kModeMx, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL(k_expert_gemm_mx, grid, block, 0, stream, p);
         else
             hipLaunchKernelGGL((k_expert_gemm<kModeMx, false>), grid, block, 0, stream, p);
         break;

@@ -192,6 +192,18 @@ def test_gemm_max_rows():
     check_sampled(g, y, extra_rows=extra, where="4M rows")
 
 
+
+def test_gemm_wide_tiling():
+    """Shapes whole rounds of 256 x 256 tiles fill (one and three rounds on 256 CUs), where
+    the launch takes the wide tiling: sampled rows and columns against the oracle."""
+    for seed, counts, N, Kd in ((7201, [4096], 4096, 512), (7202, [4096, 8192], 4096, 512)):
+        g = W.make_gemm_case(seed, counts, N, Kd)
+        say(f"[gemm] wide tiling: counts={counts} N={N} Kd={Kd}")
+        y = run_gpu(g)
+        cols = np.sort(np.random.default_rng(seed).choice(g.N, 256, replace=False))
+        extra = np.random.default_rng(seed + 1).integers(0, g.rows, 48)
+        check_sampled(g, y, cols=cols, extra_rows=extra, where=f"wide {counts}")
+
 # ---------------------------------------------------------------- int8 operands
 
 def run_gpu_i8(g, quant_mode):
