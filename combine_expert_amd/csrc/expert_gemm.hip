@@ -23,9 +23,11 @@
 // read rate) two steps ahead of the MFMAs, so each step waits only for loads
 // issued two steps earlier.  A wave's DMA instruction fills 1 KB of LDS
 // lane-contiguously; each 128-byte LDS row keeps its eight 16-byte chunks in
-// XOR-swizzled order (slot s holds chunk s ^ (row & 7)), which the lanes
+// XOR-swizzled order (slot s holds chunk s ^ ((row >> 1) & 7)), which the lanes
 // realise by fetching the permuted global chunk, so that the MFMA fragment
-// reads of sixteen consecutive rows spread over the banks.  The scale bytes
+// reads of sixteen consecutive rows spread over the banks: two rows share the
+// 64 banks, so the sixteen rows are eight in each half and need eight distinct
+// slots (row & 7 gives four: a two-way conflict).  The scale bytes
 // travel separately: when a row's scales for four K steps are 16 contiguous
 // bytes (K a multiple of 512) one 16-byte copy per row brings them every
 // fourth step into a two-group ring; otherwise a 4-byte copy per row each step.
@@ -143,6 +145,14 @@ __device__ __forceinline__ void dma4(const uint8_t *src, uint32_t lds)
                  :: "v"(src), "s"(lds) : "memory", "m0");
 }
 
+// Global chunk offset a DMA lane fetches for copy run `run` (8 rows starting at LDS row
+// 8 * run): lane l fills LDS row 8 * run + l / 8, slot l % 8, which holds chunk
+// slot ^ ((row >> 1) & 7) = slot ^ (4 * (run & 1) + l / 16).
+__device__ __forceinline__ int dma_chunk_of(int run, int lane)
+{
+    return ((lane & 7) ^ (((run & 1) << 2) | (lane >> 4))) << 4;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
 {
     return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)p);
@@ -228,12 +238,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
     // scale copies per issue (wave-uniform)
     const int n_scale = (kWeightStepScales && w_run ? 1 : 0) + (kStepScales && x_run ? 1 : 0);
     // DMA lane mapping: one instruction covers 8 rows x 128 bytes; lane -> row lane / 8, LDS
-    // slot lane % 8, global chunk slot ^ row (runs start at multiples of 8 rows, so
-    // row & 7 = lane / 8)
+    // slot lane % 8, global chunk per dma_chunk_of
     const int dma_row = lane >> 3;
-    const int dma_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
-    const int fr_c0 = ((g ^ (r16 & 7)) << 4);   // swizzled offsets of chunks g and g + 4
-    const int fr_c1 = (((g + 4) ^ (r16 & 7)) << 4);
+    // swizzled offsets of chunks g and g + 4 (fragments start at multiples of 16 rows, so
+    // (row >> 1) & 7 = r16 / 2)
+    const int fr_c0 = ((g ^ (r16 >> 1)) << 4);
+    const int fr_c1 = (((g + 4) ^ (r16 >> 1)) << 4);
     const uint8_t *w_e = p.w + (size_t)e * p.N * p.K;
 
     // this thread's DMA sources at K offset 0.  Rows past the instance (or past N) are
@@ -243,12 +253,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
 #pragma unroll
     for (int q = 0; q < kXRuns; ++q) {
         const int r = min(m0 + (wave * kXRuns + q) * 8 + dma_row, row_hi - 1);
-        xsrc[q] = p.a + (size_t)r * p.K + dma_chunk;
+        xsrc[q] = p.a + (size_t)r * p.K + dma_chunk_of(wave * kXRuns + q, lane);
     }
 #pragma unroll
     for (int q = 0; q < kWRunsT; ++q) {
         const int n = min(n0 + (wave * kWRunsT + q) * 8 + dma_row, p.N - 1);
-        wsrc[q] = w_e + (size_t)n * p.K + dma_chunk;
+        wsrc[q] = w_e + (size_t)n * p.K + dma_chunk_of(wave * kWRunsT + q, lane);
     }
     // mxfp8 weight scales are group-major ([E][ceil(K/512)][N][16]): a scale offset `off`
     // along K (bytes of the row-major layout) is group off / 16, byte off % 16
@@ -627,9 +637,8 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
     const int r16 = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;     // the wave's 64 x (BN / 2) part
     const int dma_row = lane >> 3;
-    const int dma_chunk = ((lane & 7) ^ (lane >> 3)) << 4;
-    const int fr_c0 = ((g ^ (r16 & 7)) << 4);
-    const int fr_c1 = (((g + 4) ^ (r16 & 7)) << 4);
+    const int fr_c0 = ((g ^ (r16 >> 1)) << 4);
+    const int fr_c1 = (((g + 4) ^ (r16 >> 1)) << 4);
     const uint8_t *w_e = p.w + (size_t)e * p.N * p.K;
 
     // copy sources are recomputed at each issue (a handful of integer operations per copy)
@@ -652,13 +661,13 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
 #pragma unroll
         for (int q = 0; q < kWXRuns; ++q) {
             const int r = min(m0 + (wave * kWXRuns + q) * 8 + dma_row, row_hi - 1);
-            dma16(p.a + (size_t)r * p.K + k0 + dma_chunk,
+            dma16(p.a + (size_t)r * p.K + k0 + dma_chunk_of(wave * kWXRuns + q, lane),
                   lds_addr(base + offsetof(WStage, x) + (wave * kWXRuns + q) * 1024));
         }
 #pragma unroll
         for (int q = 0; q < kWRunsT; ++q) {
             const int n = min(n0 + (wave * kWRunsT + q) * 8 + dma_row, p.N - 1);
-            dma16(w_e + (size_t)n * p.K + k0 + dma_chunk,
+            dma16(w_e + (size_t)n * p.K + k0 + dma_chunk_of(wave * kWRunsT + q, lane),
                   lds_addr(base + offsetof(WStage, w) + (wave * kWRunsT + q) * 1024));
         }
     };
