@@ -276,6 +276,30 @@ def test_gemm_i8_full_size_sampled(per_tile):
     assert_close_i8(y[rows][:, cols], y64, abs64, g.Kd, per_tile, "full size")
 
 
+
+@pytest.mark.parametrize("per_tile", [False, True])
+def test_gemm_i8_limits(per_tile):
+    """int8 at the size limits: K = 16384 (grouped tile scales when per tile) and 1024
+    instances of 0-3 rows; sampled rows (first, middle, last of each instance) and columns
+    against the oracle."""
+    mode = M().QUANT_INT8_TILE if per_tile else M().QUANT_INT8_TOKEN
+    cases = ((7301 + per_tile, [200, 77, 129], 256, 16384),
+             (7303 + per_tile, list(np.random.default_rng(7305).integers(0, 4, 1024)), 128, 128))
+    for seed, counts, N, Kd in cases:
+        g = W.make_gemm_case_i8(seed, counts, N, Kd, per_tile)
+        say(f"[gemm i8] limits per_tile={per_tile} E={g.E} N={N} Kd={Kd}")
+        y = run_gpu_i8(g, mode)
+        rows = []
+        for e in range(g.E):
+            lo, hi = int(g.offsets[e]), int(g.offsets[e + 1])
+            rows += sorted({lo, (lo + hi) // 2, hi - 1}) if hi > lo else []
+        rows = np.array(rows)
+        inst = np.searchsorted(g.offsets[1:], rows, side="right")
+        sub_off = np.zeros(g.E + 1, np.int32)
+        sub_off[1:] = np.cumsum(np.bincount(inst, minlength=g.E))
+        _, y64, abs64 = oracle.expert_gemm_i8(g.a[rows], g.a_sc[rows], sub_off, g.w, g.w_sc)
+        assert_close_i8(y[rows], y64, abs64, g.Kd, per_tile, f"limits E={g.E} Kd={Kd}")
+
 def test_gemm_i8_on_dispatch_output():
     """Dispatch (per-token int8, c2 shapes but 128 tokens) then the expert GEMM on its rows,
     against the oracle's dispatch and GEMM (the two dispatch outputs are equal bit for bit)."""
