@@ -68,7 +68,31 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         acc[j] = 0.0f;
-    for (int k0 = 0; k0 < K; k0 += CH) {
+    // Every one of CH == K entries dispatched (the usual case without pruning): the row
+    // loads are unconditional straight-line code, so the compiler counts them and each
+    // row's sums start as soon as that row has arrived, overlapping the arithmetic with
+    // the later rows' loads (with a branch per row it must wait for all of them first)
+    const uint64_t live = __ballot(my_r >= 0);
+    if (K == CH && live == (1ull << CH) - 1) {
+        uint4 ea[CH], eb[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const int r = __builtin_amdgcn_readlane(my_r, j);
+            const uint4 *p = reinterpret_cast<const uint4 *>(eo + (size_t)r * H) + 2 * tc;
+            ea[j] = load_nt16(p);
+            eb[j] = load_nt16(p + 1);
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const float sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
+            float v[16];
+            unpack16(ea[j], eb[j], v);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[e] = fmaf(sk, v[e], acc[e]);
+        }
+    }
+    for (int k0 = 0; k0 < K && !(K == CH && live == (1ull << CH) - 1); k0 += CH) {
         uint4 ea[CH], eb[CH];
         int rr[CH];
 #pragma unroll
