@@ -72,11 +72,15 @@ SMALL = [
     (111, 512, 1024, 16, 1, 16, 2, 0, False, True, 300, False),
     (112, 1, 8192, 16, 128, 8, 3, 256, True, False, None, False),
     (113, 200, 1024, 2, 8, 128, 0, 0, False, True, None, True),
-    # Bs > 256: two tokens per dispatch block; odd Bs leaves the last block one token
+    # Bs > 256 (more token blocks than compute units), odd Bs
     (114, 301, 1056, 5, 3, 4, 2, 0, True, True, 280, False),
     (115, 257, 8192, 16, 64, 16, 4, 0, False, True, None, False),
     (116, 511, 2080, 3, 2, 3, 3, 32, True, False, None, True),
     (117, 400, 7168, 8, 32, 8, 0, 0, False, True, None, False),
+    # K = 8 with pruning and a token mask: combine tokens with all eight entries dispatched
+    # (straight-line row loads) next to tokens with some or none (per-row branches)
+    (118, 301, 7168, 8, 32, 8, 4, 0, True, True, 280, False),
+    (119, 64, 2048, 8, 4, 8, 2, 0, True, True, None, True),
 ]
 
 
