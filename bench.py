@@ -67,6 +67,9 @@ def parse():
                         "kernel trace of the default run covers the headline step alone")
     p.add_argument("--gemm", action="store_true",
                    help="time the expert computation (grouped mxfp8 GEMM) instead; one JSON line")
+    p.add_argument("--gemm-dense", action="store_true",
+                   help="with --gemm: one instance of all 4096 rows instead of the Zipf split "
+                        "(context: a shape whose rounds of 256 x 256 tiles are whole)")
     p.add_argument("--gemm-formats", action="store_true",
                    help="with --gemm: also time the int8 formats (off by default so that a "
                         "kernel trace of --gemm covers the mxfp8 kernel alone)")
@@ -612,7 +615,7 @@ def gemm_main(args):
     from combine_expert_amd import moe
     from combine_expert_amd import workloads as W
 
-    g = W.make_g3()
+    g = W.make_gemm_case(9001, [4096], 4096, 7168, name="dense") if args.gemm_dense else W.make_g3()
     torch.cuda.init()
     stream = torch.cuda.current_stream()
     lib = moe.raw()
@@ -686,16 +689,20 @@ def gemm_main(args):
     flops = 2.0 * rows_total * g.N * g.Kd
     tfs = flops / (us * 1e-6) / 1e12
     alg_bytes = g.a.nbytes + g.a_sc.nbytes + g.w.nbytes + g.w_sc.nbytes + rows_total * g.N * 2
-    traffic = counter_traffic("expert_gemm_g3_traffic.txt", ("expert_gemm.hip", "device.h"))
+    traffic = None if args.gemm_dense else counter_traffic("expert_gemm_g3_traffic.txt",
+                                                          ("expert_gemm.hip", "device.h"))
     line = {
         "metric": GEMM_METRIC, "value": round(tfs, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": K, "warmup": args.warmup, "ms_per_step": round(t_wall * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic",
-        "config": {"workload": "expert computation of one expert-parallel rank in a "
-                               "DeepSeek-V3-shaped layer: 8 instances, 4096 rows split by a "
-                               "Zipf(1.2) draw, H=7168 -> N=4096 (gate and up projections), "
-                               "mxfp8 operands with E8M0 block scales, bf16 out",
+        "config": {"workload": ("one instance of 4096 rows (context, not the headline shape), "
+                                "H=7168 -> N=4096, mxfp8 operands with E8M0 block scales, "
+                                "bf16 out") if args.gemm_dense else
+                               ("expert computation of one expert-parallel rank in a "
+                                "DeepSeek-V3-shaped layer: 8 instances, 4096 rows split by a "
+                                "Zipf(1.2) draw, H=7168 -> N=4096 (gate and up projections), "
+                                "mxfp8 operands with E8M0 block scales, bf16 out"),
                    "E": g.E, "rows": rows_total, "counts": g.counts.tolist(), "N": g.N,
                    "H": g.Kd, "weight_sets": n_sets},
         "roofline": {"kernel": "k_expert_gemm_mx", "bound": "mfma", "achieved": round(tfs, 2),
