@@ -123,6 +123,22 @@ struct Scales {
     uint32_t w[kBN][STEPS];
 };
 
+// A grouped scale row holds four K steps, one word each, the word's byte b being the E8M0
+// exponent of 32-element block b of that step's 128 bytes.  A lane needs only block g of
+// every step: one 16-byte read per group, packed here into one word (step j in byte j).
+// Word reads per step fetch four times the bytes, and the compiler pairs two of them 256
+// bytes apart (the same bank) into one instruction: in the 256 x 256 tiles, where each
+// step reads twelve fragments' exponents, the packed reads are 2-4% faster.  The
+// 128 x 256 tiles keep the word reads: the group read's wait, at the group's first step
+// or at the end of the previous one, cost more there (3-4%) than the conflicts.
+__device__ __forceinline__ uint32_t pack_block_exponents(const uint32_t *row, int g)
+{
+    const u32x4 q = *reinterpret_cast<const u32x4 *>(row);
+    const int sh = 8 * g;
+    return ((q.x >> sh) & 0xffu) | ((q.y >> sh) & 0xffu) << 8 | ((q.z >> sh) & 0xffu) << 16 |
+           ((q.w >> sh) & 0xffu) << 24;
+}
+
 // s_waitcnt immediate (gfx9 layout): vmcnt <= n, expcnt and lgkmcnt not waited on
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
@@ -688,6 +704,18 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
 
     issue_data(0);
     issue_scales(0);
+    // the current group's block exponents (step j of the group in byte j), read at the
+    // group's first step (read at the end of the previous group instead, the registers
+    // spill)
+    uint32_t wsp[kFragNT], xsp[kWFragM];
+    auto load_group = [&](const WScales &sc) {
+#pragma unroll
+        for (int fm = 0; fm < kWFragM; ++fm)
+            xsp[fm] = pack_block_exponents(sc.x[wm * (kWBM / kWWavesM) + fm * 16 + r16], g);
+#pragma unroll
+        for (int fn = 0; fn < kFragNT; ++fn)
+            wsp[fn] = pack_block_exponents(sc.w[wn * (BN / 2) + fn * 16 + r16], g);
+    };
     for (int s = 0; s < nk; ++s) {
         // step s's copies (and its scale group) have landed for this wave, then for every
         // wave; every wave is also past step s - 1, so its stage and, at a group start,
@@ -698,6 +726,8 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
             issue_data(s + 1);
         if (s % kScaleGroup == 0 && s / kScaleGroup + 1 < n_groups)
             issue_scales(s / kScaleGroup + 1);
+        if (s % kScaleGroup == 0)
+            load_group(sm.scale[(s / kScaleGroup) & 1]);
 
         const WStage &st = sm.stage[s & 1];
         const WScales &sc = sm.scale[(s / kScaleGroup) & 1];
@@ -713,7 +743,7 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
             xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
+            xs[fm] = (int)((xsp[fm] >> (8 * sw)) & 0xffu);
         }
         auto read_w = [&](int fn, v8i &wf, int &ws) {
             const int row = wn * (BN / 2) + fn * 16 + r16;
@@ -721,7 +751,7 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
             wf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            ws = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
+            ws = (int)((wsp[fn] >> (8 * sw)) & 0xffu);
         };
         v8i wcur, wnext;
         int scur, snext;
