@@ -126,9 +126,10 @@ struct Scales {
 // A grouped scale row holds four K steps, one word each, the word's byte b being the E8M0
 // exponent of 32-element block b of that step's 128 bytes.  A lane needs only block g of
 // every step: one 16-byte read per group, packed here into one word (step j in byte j).
-// Word reads per step fetch four times the bytes, and the compiler pairs two of them 256
-// bytes apart (the same bank) into one instruction: in the 256 x 256 tiles, where each
-// step reads twelve fragments' exponents, the packed reads are 2-4% faster.  The
+// Per-step reads of one step's exponents (a word or a byte per lane) hit LDS rows 16 bytes
+// apart and show bank conflicts on the counters; 16-byte reads of whole rows do not.  In
+// the 256 x 256 tiles, where each step reads twelve fragments' exponents, the packed reads
+// are 2-4% faster.  The
 // 128 x 256 tiles keep the word reads: the group read's wait, at the group's first step
 // or at the end of the previous one, cost more there (3-4%) than the conflicts.
 __device__ __forceinline__ uint32_t pack_block_exponents(const uint32_t *row, int g)
