@@ -19,6 +19,7 @@ moe_dispatch, moe_combine_add_rmsnorm) is timed as well and reported under
                     --sources a.hip,b.h --out profiles/X.txt --command CMD1 --command CMD2
     python bench.py --summarize-copy FETCH.csv WRITE.csv --copy-mb 256 --out profiles/X.txt ...
     python bench.py --gemm [--gemm-formats]              # the expert GEMM row (its own line)
+    python bench.py --gemm --gemm-dense                  # the GEMM on one instance of 4096 rows
 
 Prints one JSON line.  `value` is whole-step throughput in GB/s of
 algorithmic bytes (each input read once, each output written once) with all
