@@ -127,17 +127,16 @@ struct Scales {
 // exponent of 32-element block b of that step's 128 bytes.  A lane needs only block g of
 // every step: one 16-byte read per group, packed here into one word (step j in byte j).
 // Per-step reads of one step's exponents (a word or a byte per lane) hit LDS rows 16 bytes
-// apart and show bank conflicts on the counters; 16-byte reads of whole rows do not.  In
-// the 256 x 256 tiles, where each step reads twelve fragments' exponents, the packed reads
-// are 2-4% faster.  The
-// 128 x 256 tiles keep the word reads: the group read's wait, at the group's first step
-// or at the end of the previous one, cost more there (3-4%) than the conflicts.
-__device__ __forceinline__ uint32_t pack_block_exponents(const uint32_t *row, int g)
+// apart and show bank conflicts on the counters; 16-byte reads of whole rows do not.
+__device__ __forceinline__ uint32_t pack_block_exponents(const u32x4 q, int g)
 {
-    const u32x4 q = *reinterpret_cast<const u32x4 *>(row);
     const int sh = 8 * g;
     return ((q.x >> sh) & 0xffu) | ((q.y >> sh) & 0xffu) << 8 | ((q.z >> sh) & 0xffu) << 16 |
            ((q.w >> sh) & 0xffu) << 24;
+}
+__device__ __forceinline__ uint32_t pack_block_exponents(const uint32_t *row, int g)
+{
+    return pack_block_exponents(*reinterpret_cast<const u32x4 *>(row), g);
 }
 
 // s_waitcnt immediate (gfx9 layout): vmcnt <= n, expcnt and lgkmcnt not waited on
@@ -336,10 +335,18 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
     wait_vm((kAhead - 1) * step_loads);
     lds_barrier();
 
-    for (int s = 0; s < nk; ++s) {
+    // mxfp8 with grouped scales: the loop runs whole groups of four steps, so the step within
+    // the group is known at compile time.  The first step reads both operands' exponents per
+    // step and the group's weight rows whole; the second reads the activation rows whole;
+    // each is packed (step j in byte j) after that step's MFMAs, and later steps read none.
+    constexpr bool kPackedScales = MODE == kModeMx && GROUPED;
+    uint32_t wsp[kFragNT], xsp[kFragM];
+    auto step = [&](const int s, const auto sw_c) {
+        constexpr int kSw = decltype(sw_c)::value;   // -1: not known at compile time
+        constexpr bool kUseW = kPackedScales && kSw >= 1, kUseX = kPackedScales && kSw >= 2;
         const Stg &st = sm.stage[s % kStages];
         const Sc &sc = sm.scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
-        const int sw = GROUPED ? s % kScaleGroup : 0;
+        const int sw = kSw >= 0 ? kSw : (GROUPED ? s % kScaleGroup : 0);
         // fragment reads: all weight fragments and the first two activation fragments go
         // out before this step's copies are issued; the other activation fragments two
         // ahead of the MFMAs that use them
@@ -352,7 +359,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
             wf[fn] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            if (kWeightStepScales)
+            if (kUseW)
+                ws[fn] = (int)((wsp[fn] >> (8 * sw)) & 0xffu);
+            else if (kWeightStepScales)
                 ws[fn] = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
         }
         auto read_x = [&](int fm) {
@@ -361,7 +370,9 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
             xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            if (MODE == kModeMx)
+            if (kUseX)
+                xs[fm] = (int)((xsp[fm] >> (8 * sw)) & 0xffu);
+            else if (MODE == kModeMx)
                 xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
             else if (MODE == kModeI8Tile)
                 xs[fm] = (int)sc.x[row][sw];
@@ -369,6 +380,16 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
         read_x(0);
         if (kFragM > 1)
             read_x(1);
+        u32x4 raw[kFragM > kFragNT ? kFragM : kFragNT];   // whole exponent rows, packed below
+        if constexpr (kPackedScales && kSw == 0) {
+#pragma unroll
+            for (int fn = 0; fn < kFragNT; ++fn)
+                raw[fn] = *reinterpret_cast<const u32x4 *>(sc.w[wn * (BN / kWavesN) + fn * 16 + r16]);
+        } else if constexpr (kPackedScales && kSw == 1) {
+#pragma unroll
+            for (int fm = 0; fm < kFragM; ++fm)
+                raw[fm] = *reinterpret_cast<const u32x4 *>(sc.x[wm * (kBM / kWavesM) + fm * 16 + r16]);
+        }
 
         // copies kAhead steps ahead (the last steps reload the final K step into stages
         // nobody reads any more: no branch in the count of copies in flight)
@@ -421,11 +442,31 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
                 }
             }
         }
+        if constexpr (kPackedScales && kSw == 0) {
+#pragma unroll
+            for (int fn = 0; fn < kFragNT; ++fn)
+                wsp[fn] = pack_block_exponents(raw[fn], g);
+        } else if constexpr (kPackedScales && kSw == 1) {
+#pragma unroll
+            for (int fm = 0; fm < kFragM; ++fm)
+                xsp[fm] = pack_block_exponents(raw[fm], g);
+        }
         // step s+1's copies went out kAhead - 1 steps ago: wait for this thread's (only the
         // steps issued since, and a scale group issued this step, may stay in flight; an
         // older group must have landed), then for everyone's
         wait_vm((kAhead - 1) * step_loads + (grouped_issue ? n_scale : 0));
         lds_barrier();
+    };
+    if constexpr (kPackedScales) {
+        for (int s = 0; s < nk; s += kScaleGroup) {   // nk is a multiple of four here
+            step(s, std::integral_constant<int, 0>{});
+            step(s + 1, std::integral_constant<int, 1>{});
+            step(s + 2, std::integral_constant<int, 2>{});
+            step(s + 3, std::integral_constant<int, 3>{});
+        }
+    } else {
+        for (int s = 0; s < nk; ++s)
+            step(s, std::integral_constant<int, -1>{});
     }
     // the reloads of the last steps must land, and every wave be done with the rings,
     // before the epilogue reuses them
