@@ -340,7 +340,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
     // step and the group's weight rows whole; the second reads the activation rows whole;
     // each is packed (step j in byte j) after that step's MFMAs, and later steps read none.
     constexpr bool kPackedScales = MODE == kModeMx && GROUPED;
+    // int8 per tile with grouped scales: each activation fragment row's four tile scales,
+    // read whole at the group's first step
+    constexpr bool kTileRows = MODE == kModeI8Tile && GROUPED;
     uint32_t wsp[kFragNT], xsp[kFragM];
+    u32x4 xrow[kFragM];
     auto step = [&](const int s, const auto sw_c) {
         constexpr int kSw = decltype(sw_c)::value;   // -1: not known at compile time
         constexpr bool kUseW = kPackedScales && kSw >= 1, kUseX = kPackedScales && kSw >= 2;
@@ -374,8 +378,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
                 xs[fm] = (int)((xsp[fm] >> (8 * sw)) & 0xffu);
             else if (MODE == kModeMx)
                 xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
-            else if (MODE == kModeI8Tile)
-                xs[fm] = (int)sc.x[row][sw];
+            else if (MODE == kModeI8Tile) {
+                if constexpr (kTileRows && kSw >= 0) {
+                    if constexpr (kSw == 0)
+                        xrow[fm] = *reinterpret_cast<const u32x4 *>(sc.x[row]);
+                    xs[fm] = (int)xrow[fm][kSw];
+                } else {
+                    xs[fm] = (int)sc.x[row][sw];
+                }
+            }
         };
         read_x(0);
         if (kFragM > 1)
@@ -457,7 +468,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
         wait_vm((kAhead - 1) * step_loads + (grouped_issue ? n_scale : 0));
         lds_barrier();
     };
-    if constexpr (kPackedScales) {
+    if constexpr (kPackedScales || kTileRows) {
         for (int s = 0; s < nk; s += kScaleGroup) {   // nk is a multiple of four here
             step(s, std::integral_constant<int, 0>{});
             step(s + 1, std::integral_constant<int, 1>{});
