@@ -63,6 +63,7 @@ CASES = [
     ([128], 128, 128, 0),                     # exactly one tile
     ([1, 129, 64], 384, 384, 0),
     ([3, 0, 0, 7, 0, 200, 0, 1], 128, 512, 2),
+    ([5, 260, 0, 131], 256, 1536, 1),         # three scale groups: an odd count of groups
     (list(np.random.default_rng(77).integers(0, 21, 64)), 128, 128, 3),  # many small instances
     ([300, 41], 256, 1024, 0),
 ]
@@ -234,6 +235,7 @@ I8_CASES = [
     ([1, 129, 64], 384, 384, 0),
     ([3, 0, 0, 7, 0, 200, 0, 1], 128, 512, 2),
     ([300, 41], 256, 1024, 0),
+    ([5, 260, 0, 131], 256, 1536, 1),
 ]
 
 
