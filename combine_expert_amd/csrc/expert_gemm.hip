@@ -336,9 +336,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
     lds_barrier();
 
     // mxfp8 with grouped scales: the loop runs whole groups of four steps, so the step within
-    // the group is known at compile time.  The first step reads both operands' exponents per
-    // step and the group's weight rows whole; the second reads the activation rows whole;
-    // each is packed (step j in byte j) after that step's MFMAs, and later steps read none.
+    // the group is known at compile time.  The group's first step reads each fragment row's
+    // exponents whole, where a per-step read would sit, and packs them (step j in byte j);
+    // the other three steps read none.  (With a run-time test of the step in the step's
+    // body instead, the same reads were slower than per-step reads.)
     constexpr bool kPackedScales = MODE == kModeMx && GROUPED;
     // int8 per tile with grouped scales: each activation fragment row's four tile scales,
     // read whole at the group's first step
@@ -347,7 +348,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
     u32x4 xrow[kFragM];
     auto step = [&](const int s, const auto sw_c) {
         constexpr int kSw = decltype(sw_c)::value;   // -1: not known at compile time
-        constexpr bool kUseW = kPackedScales && kSw >= 1, kUseX = kPackedScales && kSw >= 2;
+        constexpr bool kUseW = kPackedScales, kUseX = kPackedScales;
         const Stg &st = sm.stage[s % kStages];
         const Sc &sc = sm.scale[GROUPED ? (s / kScaleGroup) & 1 : s % kStages];
         const int sw = kSw >= 0 ? kSw : (GROUPED ? s % kScaleGroup : 0);
@@ -363,8 +364,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.w[row * kBK + fr_c1]);
             wf[fn] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            if (kUseW)
+            if constexpr (kUseW) {
+                if constexpr (kSw == 0)
+                    wsp[fn] = pack_block_exponents(sc.w[row], g);
                 ws[fn] = (int)((wsp[fn] >> (8 * sw)) & 0xffu);
+            }
             else if (kWeightStepScales)
                 ws[fn] = (int)((sc.w[row][sw] >> (8 * g)) & 0xffu);
         }
@@ -374,8 +378,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
             const u32x4 hi = *reinterpret_cast<const u32x4 *>(&st.x[row * kBK + fr_c1]);
             xf[fm] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            if (kUseX)
+            if constexpr (kUseX) {
+                if constexpr (kSw == 0)
+                    xsp[fm] = pack_block_exponents(sc.x[row], g);
                 xs[fm] = (int)((xsp[fm] >> (8 * sw)) & 0xffu);
+            }
             else if (MODE == kModeMx)
                 xs[fm] = (int)((sc.x[row][sw] >> (8 * g)) & 0xffu);
             else if (MODE == kModeI8Tile) {
@@ -391,16 +398,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
         read_x(0);
         if (kFragM > 1)
             read_x(1);
-        u32x4 raw[kFragM > kFragNT ? kFragM : kFragNT];   // whole exponent rows, packed below
-        if constexpr (kPackedScales && kSw == 0) {
-#pragma unroll
-            for (int fn = 0; fn < kFragNT; ++fn)
-                raw[fn] = *reinterpret_cast<const u32x4 *>(sc.w[wn * (BN / kWavesN) + fn * 16 + r16]);
-        } else if constexpr (kPackedScales && kSw == 1) {
-#pragma unroll
-            for (int fm = 0; fm < kFragM; ++fm)
-                raw[fm] = *reinterpret_cast<const u32x4 *>(sc.x[wm * (kBM / kWavesM) + fm * 16 + r16]);
-        }
 
         // copies kAhead steps ahead (the last steps reload the final K step into stages
         // nobody reads any more: no branch in the count of copies in flight)
@@ -452,15 +449,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
                     }
                 }
             }
-        }
-        if constexpr (kPackedScales && kSw == 0) {
-#pragma unroll
-            for (int fn = 0; fn < kFragNT; ++fn)
-                wsp[fn] = pack_block_exponents(raw[fn], g);
-        } else if constexpr (kPackedScales && kSw == 1) {
-#pragma unroll
-            for (int fm = 0; fm < kFragM; ++fm)
-                xsp[fm] = pack_block_exponents(raw[fm], g);
         }
         // step s+1's copies went out kAhead - 1 steps ago: wait for this thread's (only the
         // steps issued since, and a scale group issued this step, may stay in flight; an
