@@ -897,11 +897,12 @@ __device__ __forceinline__ void wide_tiles(const GemmArgs &p, WSmem &sm, int m_t
 
 // Estimated time of a tiling, in rounds of narrow (128 x 256) tiles: its whole rounds
 // times the cost of one, plus the last partial round at the cost of its pieces (the split
-// the tile loops use).  Measured on MI355X (H = 7168 -> N = 4096): a round of 256 x 256
-// tiles costs 1.77-1.85 narrow rounds (one instance of 4096 or 8192 rows, four of 2048,
-// sixteen of 512); a last round cut into pieces of a quarter (half) of the columns costs
-// about 0.5 (0.67) of a round for narrow tiles and 0.5 (0.6) for wide ones (Zipf split of
-// 4096 rows over 8 instances, six of 1500 rows, two of 3072).
+// the tile loops use).  Measured on MI355X (H = 7168 -> N = 4096), each tiling forced at
+// run time: a round of 256 x 256 tiles costs 1.83-1.93 narrow rounds (one instance of
+// 4096 or 8192 rows, four of 2048, sixteen of 512); a last round cut into pieces of a
+// quarter (half) of the columns costs about 0.5 (0.67) of a round for narrow tiles and
+// 0.5 (0.6) for wide ones (Zipf split of 4096 rows over 8 instances, six of 1500 rows, two
+// of 3072).
 __device__ __forceinline__ float tiling_cost(int tiles, int G, float round_cost, float quarter,
                                              float half)
 {
@@ -933,7 +934,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_expert_gemm_mx(GemmArgs p)
     const int G = gridDim.x;
     const int n_narrow = m_narrow * ((p.N + kBN - 1) / kBN);
     const int n_wide = m_wide * ((p.N + kWBN - 1) / kWBN);
-    if (tiling_cost(n_wide, G, 1.8f, 0.5f, 0.6f) < tiling_cost(n_narrow, G, 1.0f, 0.5f, 0.67f))
+    if (tiling_cost(n_wide, G, 1.9f, 0.5f, 0.6f) < tiling_cost(n_narrow, G, 1.0f, 0.5f, 0.67f))
         wide_tiles(p, sm.wide, m_wide);
     else
         narrow_tiles<kModeMx, true>(p, sm.narrow, m_narrow);
