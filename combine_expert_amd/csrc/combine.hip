@@ -4,22 +4,29 @@
 // x = combineOut + residualX, y = x / RMS(x) * gamma with
 // RMS(x) = sqrt(mean(x^2) + normEps)).
 //
-// One block per token, one thread per 16 elements of the row: every input
-// row is read once with 16-byte loads, the fp32 sum stays in registers, the
-// sum of squares is a wave butterfly plus one LDS step, and y / x_out are
-// written once.  The kernel is bound by HBM bandwidth: per token it moves
-// (n_dispatched + 2 or 3) rows in and 2 rows out.
+// One block per token in the row layout of device.h (a wave per 1024
+// elements, two 8-element parts per lane, so every 16-byte access of a wave
+// covers one contiguous kilobyte).  Every input row is read once, the fp32
+// sum stays in registers, the sum of squares is a wave butterfly plus one LDS
+// step, and y / x_out are written once.  The kernel is bound by HBM
+// bandwidth: per token it moves (n_dispatched + 2 or 3) rows in and 2 rows
+// out.
 //
 // Every wave reads the token's K (row, weight) pairs itself, one per lane,
-// and broadcasts them with readlane, so the only block barrier is the one of
-// the sum of squares.  Row loads are issued back to back, CH rows at a time,
-// with no loads for entries that were not dispatched.
+// so the only block barrier is the one of the sum of squares.  The
+// dispatched entries are taken in order of k, eight at a time: each group of
+// eight is straight-line code (a missing entry loads at an offset past the
+// buffer, which reads zeros with no memory traffic), so the compiler counts
+// the loads and each row's sums start as soon as that row has arrived.
+// Expert rows are read once and marked non-temporal; residual, shared and
+// gamma rows use the default policy (measured faster for them).
 #include "device.h"
 #include "kernels.h"
 
 namespace moe {
 
-template <int CH>
+constexpr int kGroup = 8;  // expert rows loaded together
+
 __global__ __launch_bounds__(kMaxThreads) void k_combine(
     const uint16_t *__restrict__ eo, const int32_t *__restrict__ assist,
     const float *__restrict__ scales, const uint16_t *__restrict__ shared,
@@ -30,102 +37,83 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
     __shared__ float s_part[kMaxWaves];
 
     const int i = blockIdx.x;
-    const int t = threadIdx.x, T = blockDim.x;
-    const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
-    const bool has = t * kChunk < H;
-    const size_t rowoff = (size_t)i * H;
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = blockDim.x / kWave;
+    const uint32_t rowb = (uint32_t)H * 2;
+    // byte offsets of this lane's two parts in a row; a part past the row end
+    // reads at kNoPart (zeros) and is not stored
+    const int e0 = part_elem(t, 0), e1 = part_elem(t, 1);
+    const bool v0 = e0 < H, v1 = e1 < H;
+    const uint32_t o0 = v0 ? (uint32_t)e0 * 2 : kNoPart, o1 = v1 ? (uint32_t)e1 * 2 : kNoPart;
+    const rsrc_t r_eo = buffer_rsrc(eo, (uint32_t)(Bs * K) * rowb);
+    const rsrc_t r_tok = buffer_rsrc(residual, (uint32_t)Bs * rowb);
+    const rsrc_t r_sh = buffer_rsrc(shared ? shared : residual, shared ? (uint32_t)Bs * rowb : 0u);
+    const rsrc_t r_g = buffer_rsrc(gamma, rowb);
+    const uint32_t tok = (uint32_t)i * rowb;
 
     // 1. the token's K entries, one per lane, loaded first: the expert-row
     //    loads depend on them, and wait counters retire in issue order
-    //    (all loads here are unconditional -- lanes past K or past the row end
-    //    re-read a valid address -- so that waiting for one load never has to
-    //    assume a shorter queue on some other path and wait for later ones)
     const int kk = min(lane, K - 1);
     int my_r = assist[i * K + kk];
-    float my_s = scales[i * K + kk];
+    const float my_s = scales[i * K + kk];
     if (lane >= K)
         my_r = -1;
 
-    // 2. residual, shared and gamma do not depend on the routing
-    const int tc = has ? t : 0;
-    const uint16_t *shp = shared ? shared : residual;
-    const uint4 *pr = reinterpret_cast<const uint4 *>(residual + rowoff) + 2 * tc;
-    const uint4 *pg = reinterpret_cast<const uint4 *>(gamma) + 2 * tc;
-    const uint4 *ps = reinterpret_cast<const uint4 *>(shp + rowoff) + 2 * tc;
-    const uint4 ra = pr[0], rb = pr[1];
-    const uint4 ga = pg[0], gb = pg[1];
-    const uint4 sa = ps[0], sb = ps[1];
+    // 2. residual, shared (zeros without one) and gamma do not depend on the routing
+    const uint4 ra = buf_load16<kPlain>(r_tok, tok + o0), rb = buf_load16<kPlain>(r_tok, tok + o1);
+    const uint4 sa = buf_load16<kPlain>(r_sh, tok + o0), sb = buf_load16<kPlain>(r_sh, tok + o1);
+    const uint4 ga = buf_load16<kPlain>(r_g, o0), gb = buf_load16<kPlain>(r_g, o1);
 
-    // 3. the dispatched entries' rows, CH at a time; entries that were not
-    //    dispatched (row -1) or point outside the buffer load nothing
+    // 3. the dispatched entries' rows in groups of kGroup; entries that were
+    //    not dispatched (row -1) or point outside the buffer are skipped
     if (my_r >= Bs * K) {
         if (w == 0 && dev_err)
             atomicOr(dev_err, 8);
         my_r = -1;
     }
     const float ws = wave_sum_f32(my_r >= 0 ? my_s : 0.0f);
+    uint64_t live = __ballot(my_r >= 0);
     float acc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         acc[j] = 0.0f;
-    // Every one of CH == K entries dispatched (the usual case without pruning): the row
-    // loads are unconditional straight-line code, so the compiler counts them and each
-    // row's sums start as soon as that row has arrived, overlapping the arithmetic with
-    // the later rows' loads (with a branch per row it must wait for all of them first)
-    const uint64_t live = __ballot(my_r >= 0);
-    if (K == CH && live == (1ull << CH) - 1) {
-        uint4 ea[CH], eb[CH];
+    while (live) {
+        uint4 ea[kGroup], eb[kGroup];
+        float sk[kGroup];
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const int r = __builtin_amdgcn_readlane(my_r, j);
-            const uint4 *p = reinterpret_cast<const uint4 *>(eo + (size_t)r * H) + 2 * tc;
-            ea[j] = load_nt16(p);
-            eb[j] = load_nt16(p + 1);
+        for (int j = 0; j < kGroup; ++j) {
+            uint32_t base = kNoRow;
+            sk[j] = 0.0f;
+            if (live) {
+                const int k = __builtin_ctzll(live);
+                live &= live - 1;
+                base = (uint32_t)__builtin_amdgcn_readlane(my_r, k) * rowb;
+                sk[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+            }
+            ea[j] = buf_load16<kStream>(r_eo, base + o0);
+            eb[j] = buf_load16<kStream>(r_eo, base + o1);
         }
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            const float sk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), j));
+        for (int j = 0; j < kGroup; ++j) {
             float v[16];
-            unpack16(ea[j], eb[j], v);
+            unpack8(ea[j], v);
+            unpack8(eb[j], v + 8);
 #pragma unroll
             for (int e = 0; e < 16; ++e)
-                acc[e] = fmaf(sk, v[e], acc[e]);
-        }
-    }
-    for (int k0 = 0; k0 < K && !(K == CH && live == (1ull << CH) - 1); k0 += CH) {
-        uint4 ea[CH], eb[CH];
-        int rr[CH];
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            rr[j] = k0 + j < K ? __builtin_amdgcn_readlane(my_r, k0 + j) : -1;
-            if (rr[j] >= 0) {
-                const uint4 *p = reinterpret_cast<const uint4 *>(eo + (size_t)rr[j] * H) + 2 * tc;
-                ea[j] = load_nt16(p);
-                eb[j] = load_nt16(p + 1);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-            if (rr[j] >= 0) {
-                const float sk =
-                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k0 + j));
-                float v[16];
-                unpack16(ea[j], eb[j], v);
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    acc[e] = fmaf(sk, v[e], acc[e]);
-            }
+                acc[e] = fmaf(sk[j], v[e], acc[e]);
         }
     }
 
     float xf[16];
     {
         float rv[16];
-        unpack16(ra, rb, rv);
+        unpack8(ra, rv);
+        unpack8(rb, rv + 8);
         if (shared) {
             const float wsh = shared_mode == 0 ? ws : 1.0f;
             float sv[16];
-            unpack16(sa, sb, sv);
+            unpack8(sa, sv);
+            unpack8(sb, sv + 8);
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 acc[e] = fmaf(wsh, sv[e], acc[e]);
@@ -135,23 +123,21 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
             xf[e] = acc[e] + rv[e];
     }
 
-    // lanes past the row end loaded nothing: they add nothing to the sum of squares
+    // parts past the row end add nothing to the sum of squares
     float ss = 0.0f;
-    if (has) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            ss = fmaf(xf[e], xf[e], ss);
+    for (int e = 0; e < 8; ++e) {
+        ss = fmaf(v0 ? xf[e] : 0.0f, v0 ? xf[e] : 0.0f, ss);
+        ss = fmaf(v1 ? xf[8 + e] : 0.0f, v1 ? xf[8 + e] : 0.0f, ss);
     }
     ss = wave_sum_f32(ss);
     if (lane == 0)
         s_part[w] = ss;
 
-    if (has && x_out) {
-        uint4 *p = reinterpret_cast<uint4 *>(x_out + rowoff) + 2 * t;
-        p[0] = make_uint4(pack_bf16x2(xf[0], xf[1]), pack_bf16x2(xf[2], xf[3]),
-                          pack_bf16x2(xf[4], xf[5]), pack_bf16x2(xf[6], xf[7]));
-        p[1] = make_uint4(pack_bf16x2(xf[8], xf[9]), pack_bf16x2(xf[10], xf[11]),
-                          pack_bf16x2(xf[12], xf[13]), pack_bf16x2(xf[14], xf[15]));
+    if (x_out) {
+        const rsrc_t r_xo = buffer_rsrc(x_out, (uint32_t)Bs * rowb);
+        buf_store16<kPlain>(r_xo, tok + o0, pack8_bf16(xf));
+        buf_store16<kPlain>(r_xo, tok + o1, pack8_bf16(xf + 8));
     }
     lds_barrier();
     float tot = 0.0f;
@@ -160,18 +146,15 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
     const float rstd = 1.0f / __builtin_sqrtf(tot / (float)H + eps);
     if (t == 0 && rstd_out)
         rstd_out[i] = rstd;
-    if (!has)
-        return;
     float g[16], o[16];
-    unpack16(ga, gb, g);
+    unpack8(ga, g);
+    unpack8(gb, g + 8);
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         o[e] = xf[e] * rstd * g[e];
-    uint4 *p = reinterpret_cast<uint4 *>(y + rowoff) + 2 * t;
-    p[0] = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                      pack_bf16x2(o[6], o[7]));
-    p[1] = make_uint4(pack_bf16x2(o[8], o[9]), pack_bf16x2(o[10], o[11]),
-                      pack_bf16x2(o[12], o[13]), pack_bf16x2(o[14], o[15]));
+    const rsrc_t r_y = buffer_rsrc(y, (uint32_t)Bs * rowb);
+    buf_store16<kPlain>(r_y, tok + o0, pack8_bf16(o));
+    buf_store16<kPlain>(r_y, tok + o1, pack8_bf16(o + 8));
 }
 
 hipError_t launch_combine(const uint16_t *expert_out, const int32_t *assist,
@@ -180,9 +163,9 @@ hipError_t launch_combine(const uint16_t *expert_out, const int32_t *assist,
                           int H, int K, int shared_mode, uint16_t *y, uint16_t *x_out,
                           float *rstd, int32_t *dev_err, hipStream_t stream)
 {
-    hipLaunchKernelGGL((k_combine<8>), dim3(Bs), dim3(row_threads(H)), 0, stream, expert_out,
-                       assist, scales, shared, residual, gamma, eps, Bs, H, K, shared_mode, y,
-                       x_out, rstd, dev_err);
+    hipLaunchKernelGGL(k_combine, dim3(Bs), dim3(row_threads(H)), 0, stream, expert_out, assist,
+                       scales, shared, residual, gamma, eps, Bs, H, K, shared_mode, y, x_out,
+                       rstd, dev_err);
     return hipGetLastError();
 }
 

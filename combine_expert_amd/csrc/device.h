@@ -27,6 +27,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
            ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+__device__ __forceinline__ uint4 pack8_bf16(const float *f)
+{
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
+}
+
 // 16 bf16 (two uint4) -> 16 fp32
 __device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float *v)
 {
@@ -69,6 +75,81 @@ __device__ __forceinline__ void store_nt16(void *p, const uint4 &v)
 {
     const u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+}
+
+// ---------------------------------------------------------------- buffer access
+
+// Raw buffer loads and stores with an explicit cache policy.  The address is
+// a 32-bit byte offset from a base (every buffer here is below 2 GB), and an
+// access at an offset at or past the buffer's size reads zeros and writes
+// nothing, with no memory traffic: a load of a row that does not exist
+// (kNoRow) is still issued, so straight-line load sequences keep a fixed
+// count for the wait counters.  Every buffer passed here is below 256 MB, so
+// a row base below 256 MB plus kNoPart, or kNoRow plus any in-row offset or
+// kNoPart, is past the end without wrapping around 2^32.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+constexpr int kPlain = 0;      // default policy
+constexpr int kStream = 2;     // non-temporal: read or written once
+constexpr int kDevice = 16;    // device scope: stores write through to memory
+constexpr uint32_t kNoRow = 0x80000000u;   // row base of a row that does not exist
+constexpr uint32_t kNoPart = 0x40000000u;  // in-row offset of a part past the row end
+
+__device__ __forceinline__ rsrc_t buffer_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+template <int POL>
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off)
+{
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <int POL>
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, const uint4 &v)
+{
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, POL);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int POL>
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, uint32_t lo, uint32_t hi)
+{
+    const u32x2 w = {lo, hi};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, POL);
+}
+
+// ---------------------------------------------------------------- row layout
+
+// Row layout of the dispatch and combine kernels: wave w of a row block owns
+// elements [1024 w, 1024 w + 1024) of the row, and lane l holds two chunks of
+// eight, part 0 at 1024 w + 8 l and part 1 at 1024 w + 512 + 8 l.  A wave's
+// 16-byte accesses to a bf16 row then each cover one contiguous kilobyte
+// (eight whole cache lines); with each lane's 16 elements consecutive, every
+// access instruction would touch 16 half-used lines, which measured about 12%
+// slower for the same bytes.  A 32-element block is 4 lanes of one part and a
+// power-of-two tile of up to 512 elements is tile/8 lanes of one part.
+constexpr int kPartElems = 8;
+constexpr int kWaveElems = 1024;
+
+__device__ __forceinline__ int part_elem(int t, int p)
+{
+    return (t >> 6) * kWaveElems + p * (kWaveElems / 2) + (t & (kWave - 1)) * kPartElems;
+}
+
+// 8 bf16 (one uint4) -> 8 fp32
+__device__ __forceinline__ void unpack8(const uint4 &a, float *v)
+{
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = __uint_as_float(w[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
 }
 
 // ---------------------------------------------------------------- block barrier
