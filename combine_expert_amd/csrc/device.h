@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int kWave = 64;
@@ -167,42 +169,90 @@ __device__ __forceinline__ void lds_barrier()
 
 // ---------------------------------------------------------------- wave ops
 
+// Wave-wide reductions and scans use DPP lane moves (VALU operands, a few
+// cycles each) rather than LDS-path lane shuffles.  DPP controls: row_shr:n
+// 0x110 + n, row_mirror 0x140, row_half_mirror 0x141, row_bcast:15 0x142,
+// row_bcast:31 0x143, quad_perm 0x00-0xff.  A row is 16 lanes.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, true);
+}
+
+constexpr int kQuadXor1 = 0xb1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4e;  // quad_perm [2,3,0,1]
+
+// Reduces v over the wave into lane 63 with op (commutative, associative on
+// the values used), then returns lane 63's value in every lane: the same
+// bits everywhere, and the same order of operations on every run.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op)
+{
+    auto mv = [](T x, auto ctrl) {
+        return __builtin_bit_cast(T, dpp<decltype(ctrl)::value>(__builtin_bit_cast(int, x)));
+    };
+    v = op(v, mv(v, std::integral_constant<int, kQuadXor1>{}));
+    v = op(v, mv(v, std::integral_constant<int, kQuadXor2>{}));
+    v = op(v, mv(v, std::integral_constant<int, 0x141>{}));  // half-row mirror: 8 lanes
+    v = op(v, mv(v, std::integral_constant<int, 0x140>{}));  // row mirror: 16 lanes
+    // rows 1 and 3 add the last lane of rows 0 and 2, then rows 2 and 3 add lane 31
+    const T b15 = __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+    v = op(v, b15);
+    const T b31 = __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+    v = op(v, b31);
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, o));
-    return v;
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
 __device__ __forceinline__ int wave_sum_i32(int v)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce(v, [](int a, int b) { return a + b; });
 }
 
-// Every lane gets the same bits: the butterfly adds the same pairs in every lane.
+// Every lane gets the same bits (the total is read from one lane).
 __device__ __forceinline__ float wave_sum_f32(float v)
 {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
+    return wave_reduce(v, [](float a, float b) { return a + b; });
+}
+
+// Inclusive prefix sum over the wave: Hillis-Steele steps inside each row of
+// 16 lanes (row_shr 1, 2, 4, 8; lanes shifted in from outside the row read
+// 0), then the row broadcasts carry rows 0 and 2 into rows 1 and 3 and the
+// first half into the second.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    v += dpp<0x111>(v);
+    v += dpp<0x112>(v);
+    v += dpp<0x114>(v);
+    v += dpp<0x118>(v);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
     return v;
 }
 
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ int wave_incl_scan(int v)
+// Maximum over aligned groups of n lanes (n = 1, 2, 4, 8, 16 or 32), the
+// group's maximum in each of its lanes: quad permutes, then the half-row and
+// row mirrors (lane i and its mirror lie in different halves of the group),
+// then, for 32, a lane shuffle.
+__device__ __forceinline__ uint32_t group_max_u32(uint32_t m, int n)
 {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int t = __shfl_up(v, o);
-        if (lane >= o)
-            v += t;
-    }
-    return v;
+    if (n >= 2)
+        m = max(m, (uint32_t)dpp<kQuadXor1>((int)m));
+    if (n >= 4)
+        m = max(m, (uint32_t)dpp<kQuadXor2>((int)m));
+    if (n >= 8)
+        m = max(m, (uint32_t)dpp<0x141>((int)m));
+    if (n >= 16)
+        m = max(m, (uint32_t)dpp<0x140>((int)m));
+    if (n >= 32)
+        m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+    return m;
 }
 
 }  // namespace moe
