@@ -13,6 +13,7 @@ moe_dispatch, moe_combine_add_rmsnorm) is timed as well and reported under
 "step_three_calls".
 
     python bench.py [--steps 500] [--warmup 50] [--sets 5] [--cpu-seconds 10]
+    python bench.py --headline-only                      # the c3 step alone (for traces)
     python bench.py --copy-mb 256                        # copy kernel for counter scaling
     python bench.py --summarize-trace STATS.csv --out profiles/X.md --command CMD
     python bench.py --summarize-counters FETCH.csv WRITE.csv --kernel NAME \
@@ -20,6 +21,14 @@ moe_dispatch, moe_combine_add_rmsnorm) is timed as well and reported under
     python bench.py --summarize-copy FETCH.csv WRITE.csv --copy-mb 256 --out profiles/X.txt ...
     python bench.py --gemm [--gemm-formats]              # the expert GEMM row (its own line)
     python bench.py --gemm --gemm-dense                  # the GEMM on one instance of 4096 rows
+
+By default the same line also carries, after the headline has been timed:
+the step replayed from a captured HIP graph (the host's share of the eager
+step), every other workload (c1, c2, c4, c4b) kernel by kernel, the
+16-layer c5 stack captured in one graph, and the ceilings measured on the
+same device with the measurement kernels of libmoe_calib.so (a streaming
+copy, streams with each kernel's read/write mix, and each kernel's access
+shape with its arithmetic taken out).  --headline-only leaves them out.
 
 Prints one JSON line.  `value` is whole-step throughput in GB/s of
 algorithmic bytes (each input read once, each output written once) with all
@@ -60,12 +69,13 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline (0 = skip)")
     p.add_argument("--no-check", action="store_true", help="skip the parity check of step 0")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time the c3 step and its kernels only (no other configs, c5 stack, "
+                        "graph replay or ceilings): the command kernel traces are taken on")
     p.add_argument("--hot", action="store_true",
                    help="also time each kernel on one reused buffer set (hot Infinity Cache)")
-    p.add_argument("--c5", action="store_true",
-                   help="also time the 16-layer graph-captured stack (c5) and the dispatch "
-                        "variants (static and per-instance scales); off by default so that a "
-                        "kernel trace of the default run covers the headline step alone")
+    p.add_argument("--variants", action="store_true",
+                   help="also time the dispatch variants (static and per-instance scales)")
     p.add_argument("--gemm", action="store_true",
                    help="time the expert computation (grouped mxfp8 GEMM) instead; one JSON line")
     p.add_argument("--gemm-dense", action="store_true",
@@ -84,6 +94,9 @@ def parse():
                    help="counter_collection.csv of a FETCH_SIZE run and of a WRITE_SIZE run")
     g.add_argument("--summarize-copy", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="the same for the --copy-mb kernel: derives the counter scales")
+    g.add_argument("--headline-of", metavar="BENCH_JSON",
+                   help="summarise only the headline part of the traced run (the first "
+                        "headline_launches dispatches of each kernel in that bench line)")
     g.add_argument("--kernel", help="kernel name (prefix) to summarise")
     g.add_argument("--sources", default="", help="comma-separated csrc files of that kernel")
     g.add_argument("--out", help="summary file to write")
@@ -178,10 +191,28 @@ def summarize_trace(args):
     rows = list(csv.DictReader(open(args.summarize_trace)))
     durs = {}
     trace = args.summarize_trace.replace("kernel_stats.csv", "kernel_trace.csv")
+    recs = []
     if os.path.exists(trace):
-        for r in csv.DictReader(open(trace)):
-            durs.setdefault(r["Kernel_Name"], []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        recs = sorted(csv.DictReader(open(trace)), key=lambda r: int(r["Start_Timestamp"]))
+    if args.headline_of and recs:
+        # the headline part of the run: every dispatch up to the last combine of the
+        # headline (the bench line's headline_launches counts them); later dispatches
+        # belong to the other workloads the same command times
+        with open(args.headline_of) as f:
+            line = json.loads(next(ln for ln in f if ln.startswith("{")))
+        n_cmb = line["headline_launches"]["k_combine"]
+        cmb = [r for r in recs if "k_combine" in r["Kernel_Name"]]
+        cut = int(cmb[n_cmb - 1]["End_Timestamp"])
+        recs = [r for r in recs if int(r["Start_Timestamp"]) <= cut]
+    for r in recs:
+        durs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if args.headline_of and recs:
+        tot = sum(sum(d) for d in durs.values())
+        rows = sorted(({"Name": n, "Calls": len(d), "AverageNs": 1e3 * sum(d) / len(d),
+                        "MinNs": 1e3 * min(d), "MaxNs": 1e3 * max(d),
+                        "Percentage": 100.0 * sum(d) / tot} for n, d in durs.items()),
+                      key=lambda r: -r["Percentage"])
 
     def pct(v, q):
         v = sorted(v)
@@ -303,7 +334,8 @@ def make_stack(wls, torch, moe):
 
 
 def stack_calls(wls, st, lib, stream):
-    """(function, C-ABI arguments) of every launch of one pass over the stack."""
+    """(function, C-ABI arguments) of every call of one pass over the stack:
+    per layer the mapping fused into the dispatch, then the combine."""
     p = lambda t: None if t is None else t.data_ptr()
     calls = []
     for l, (wl, s) in enumerate(zip(wls, st["layers"])):
@@ -311,12 +343,10 @@ def stack_calls(wls, st, lib, stream):
         res = st["r0"] if l == 0 else st["layers"][l - 1]["x_out"]
         d = s["d"]
         n_logical, F = wl.table.shape
-        calls.append((lib.moe_update_expert,
-                      (p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.K, n_logical, F,
-                       wl.E, p(s["bal_ids"]), p(s["bal_mask"]), None, stream)))
-        calls.append((lib.moe_dispatch,
-                      (p(x), p(s["bal_ids"]), p(s["bal_mask"]), wl.Bs, wl.H, wl.K, wl.n_ranks,
-                       wl.local_experts, wl.quant_mode, wl.tile, None, 0, p(d["expand_x"]),
+        calls.append((lib.moe_update_dispatch,
+                      (p(x), p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.H, wl.K,
+                       n_logical, F, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile, None,
+                       0, p(s["bal_ids"]), p(s["bal_mask"]), p(d["expand_x"]),
                        p(d["expand_scales"]), p(d["expert_counts"]), p(d["expert_offsets"]),
                        p(d["expand_src"]), p(d["assist_dst"]), None, stream)))
         calls.append((lib.moe_combine_add_rmsnorm,
@@ -374,16 +404,18 @@ def time_stack(moe, torch, n_layers, replays, warmup):
         nb = algorithmic_bytes(wl.Bs, wl.H, wl.K, wl.E, rows, wl.table.shape[0],
                                wl.table.shape[1], wl.quant_mode,
                                moe.n_scale_entries(wl.quant_mode, wl.H, wl.tile), shared=True)
-        total += nb["update_expert"] + nb["dispatch"] + nb["combine"]
+        total += nb["update_dispatch"] + nb["combine"]
     Bs = wls[0].Bs
     return {"layers": n_layers, "graph_replays": replays, "us_per_replay": round(t * 1e6, 2),
             "us_per_layer": round(t * 1e6 / n_layers, 3),
             "us_per_layer_eager": round(t_eager * 1e6 / n_layers, 3), "bytes": total,
             "GBps": round(total / t / 1e9, 2),
+            "frac_of_hbm_peak": round(total / t / 1e9 / HBM_PEAK_GBS, 4),
             "tokens_per_s_per_layer": round(Bs * n_layers / t, 1),
             "workload": "16 chained layers of Bs=512 H=7168 K=8 E=256 (32 x 8), Zipf(1.2), "
                         "int8 per token, 1 shared expert; x_{l+1} = y_l, residual_{l+1} = "
-                        "x_out_l; one HIP graph per pass"}
+                        "x_out_l; per layer the fused mapping + dispatch and the combine; "
+                        "one HIP graph per pass"}
 
 
 # ----------------------------------------------------------------- dispatch variants
@@ -492,9 +524,123 @@ def config_table(moe, torch, n, sets=3):
         rows.append({"config": name, "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E,
                      "quant_mode": wl.quant_mode, "rows_dispatched": nrows,
                      **{k: {"avg_us": round(u, 3), "bytes": nb[k],
-                            "GBps": round(nb[k] / (u * 1e-6) / 1e9, 1)}
+                            "GBps": round(nb[k] / (u * 1e-6) / 1e9, 1),
+                            "frac": round(nb[k] / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
                         for k, u in zip(keys, us)}})
     return rows
+
+
+# ----------------------------------------------------------------- ceilings
+
+def _events_us(torch, fn, n, warm=10):
+    """Average duration of fn(k), k = 0 .. n-1, enqueued back to back between two
+    HIP events on the current stream."""
+    stream = torch.cuda.current_stream()
+    for k in range(warm):
+        fn(k)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(n):
+        fn(k)
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def ceilings(torch, n, wl, step_set, nb, rows):
+    """What this device sustains for the same traffic, from the measurement
+    kernels of libmoe_calib.so, each over buffers rotating past the Infinity
+    Cache: a plain streaming copy, streams with the combine's and the
+    dispatch's read/write mix at the c3 sizes, and the two kernels' access
+    shapes (the c3 routing of the headline step) with their arithmetic taken
+    out."""
+    from combine_expert_amd import calib
+    dev = torch.device("cuda")
+    out = {"note": "measurement kernels of libmoe_calib.so (include/moe_calib.h); GB/s of the "
+                   "bytes each moves, HIP events over back-to-back launches"}
+
+    def stream_case(name, rbytes, wbytes, nsets):
+        src = [torch.empty(rbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        dst = [torch.empty(wbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
+        for t in src:
+            t.fill_(3)
+        us = _events_us(torch, lambda k: calib.stream(src[k % nsets], rbytes, dst[k % nsets],
+                                                       wbytes), n)
+        out[name] = {"read_bytes": rbytes, "write_bytes": wbytes, "avg_us": round(us, 3),
+                     "GBps": round((rbytes + wbytes) / us / 1e3, 1),
+                     "frac": round((rbytes + wbytes) / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del src, dst
+
+    stream_case("copy_256MB", 256 << 20, 256 << 20, 2)
+    cr = nb["combine"] - 2 * wl.Bs * wl.H * 2 - wl.Bs * 4
+    stream_case("stream_combine_mix", cr // 16 * 16, (nb["combine"] - cr) // 16 * 16, 8)
+    dr = wl.Bs * wl.H * 2 + wl.Bs * wl.K * 5
+    stream_case("stream_dispatch_mix", dr // 16 * 16, (nb["dispatch"] - dr) // 16 * 16, 8)
+
+    # the kernels' access shapes on the headline's routing (c3)
+    assist = step_set["d"]["assist_dst"]
+    nsets = 6
+    Bs, H, K = wl.Bs, wl.H, wl.K
+    xs = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
+    outs = [torch.empty((rows, H), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    us = _events_us(torch, lambda k: calib.scatter_shape(xs[k % nsets], assist, rows,
+                                                         outs[k % nsets]), n)
+    sb = Bs * H * 2 + Bs * K * 4 + rows * H
+    out["dispatch_shape"] = {"bytes": sb, "avg_us": round(us, 3),
+                             "GBps": round(sb / us / 1e3, 1),
+                             "frac": round(sb / us / 1e3 / HBM_PEAK_GBS, 4),
+                             "what": "block per token: its row read, one byte per element "
+                                     "written to each of its K rows (no routing, no coding)"}
+    del xs, outs
+    eo = [torch.empty((rows, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
+    aa = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
+    bb = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
+    o1 = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    o2 = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    g = torch.ones(H, dtype=torch.bfloat16, device=dev)
+    us = _events_us(torch, lambda k: calib.gather_shape(eo[k % nsets], assist, aa[k % nsets],
+                                                        bb[k % nsets], g, rows, o1[k % nsets],
+                                                        o2[k % nsets]), n)
+    gb = rows * H * 2 + 2 * Bs * H * 2 + H * 2 + Bs * K * 4 + 2 * Bs * H * 2
+    out["combine_shape"] = {"bytes": gb, "avg_us": round(us, 3),
+                            "GBps": round(gb / us / 1e3, 1),
+                            "frac": round(gb / us / 1e3 / HBM_PEAK_GBS, 4),
+                            "what": "block per token: its K expert rows, two token rows and "
+                                    "gamma read, two rows written, one block barrier (no "
+                                    "arithmetic)"}
+    return out
+
+
+def step_graph(torch, fns, argv, calls, n, t_eager, step_bytes, Bs):
+    """The headline step replayed from a captured HIP graph holding one step
+    per buffer set (the same launches, no host issue between them): the
+    per-step time next to the eager one shows how much of the eager step is
+    host issue."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        sp = side.cuda_stream
+        for a in argv:
+            for c in calls:
+                a2 = a[c][:-1] + (sp,)
+                if fns[c](*a2):
+                    raise RuntimeError("a library call failed under capture")
+    torch.cuda.current_stream().wait_stream(side)
+    reps = max(1, n // len(argv))
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / (reps * len(argv))
+    return {"steps": reps * len(argv), "ms_per_step": round(t * 1e3, 5),
+            "GBps": round(step_bytes / t / 1e9, 2), "tokens_per_s": round(Bs / t, 1),
+            "frac_of_hbm_peak": round(step_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+            "host_issue_share_of_eager_step": round(max(0.0, 1.0 - t / t_eager), 4),
+            "note": f"one HIP graph of {len(argv)} steps (one per buffer set), replayed"}
 
 
 def check_parity(wl, s, oracle, np):
@@ -522,7 +668,9 @@ def check_parity(wl, s, oracle, np):
 
 
 def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
-    """The oracle as it stands: single-threaded C, whole step on the same inputs."""
+    """The oracle as it stands (plain C), the whole step on the same inputs:
+    first on one core, then with its per-token loops on every core the process
+    may use (the routing stays sequential).  Each for about budget_s / 2."""
     ids = wl.logical_ids.numpy()
     table = wl.table.numpy()
     xb = oracle.bf16_bits(wl.x)
@@ -530,17 +678,24 @@ def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
     shb, rsb, gmb = (oracle.bf16_bits(wl.shared), oracle.bf16_bits(wl.residual),
                      oracle.bf16_bits(wl.gamma))
     sc = wl.scales.numpy()
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while True:
-        t0 = time.perf_counter()
-        oi, om, _ = oracle.update_expert(ids, None, table, None, None, wl.E)
-        od = oracle.dispatch(xb, oi, om, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile)
-        oracle.combine(eob, od["assist"], sc, shb, rsb, gmb, wl.eps, wl.shared_mode)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() >= t_end or len(times) >= 50:
-            break
-    t = statistics.median(times)
+    cores = len(os.sched_getaffinity(0))
+
+    def run(threads, seconds):
+        used = oracle.set_threads(threads)
+        times = []
+        t_end = time.perf_counter() + seconds
+        while True:
+            t0 = time.perf_counter()
+            oi, om, _ = oracle.update_expert(ids, None, table, None, None, wl.E)
+            od = oracle.dispatch(xb, oi, om, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile)
+            oracle.combine(eob, od["assist"], sc, shb, rsb, gmb, wl.eps, wl.shared_mode)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() >= t_end or len(times) >= 50:
+                break
+        return used, statistics.median(times), len(times)
+
+    one, t1, n1 = run(1, budget_s / 2)
+    many, tm, nm = run(cores, budget_s / 2)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -548,12 +703,15 @@ def cpu_baseline(wl, oracle, np, budget_s, step_bytes):
                          "")
     except OSError:
         pass
-    return {"value": round(step_bytes / t / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "host_cpu": model, "host_cores_available": len(os.sched_getaffinity(0)),
+    return {"value": round(step_bytes / tm / 1e9, 3), "unit": "GB/s", "cores": many,
+            "kind": "oracle", "host_cpu": model, "host_cores_available": cores,
             "sample": f"the full step (update + dispatch + combine) on all {wl.Bs} tokens of the "
-                      f"workload, {len(times)} repetitions, median {t * 1e3:.1f} ms; "
-                      f"{wl.Bs / t:.0f} tokens/s",
-            "tokens_per_s": round(wl.Bs / t, 1)}
+                      f"workload, repeated for about {budget_s / 2:.0f} s per thread count, "
+                      f"median: {many} threads {tm * 1e3:.1f} ms ({nm} runs), 1 thread "
+                      f"{t1 * 1e3:.1f} ms ({n1} runs)",
+            "tokens_per_s": round(wl.Bs / tm, 1),
+            "single_core": {"value": round(step_bytes / t1 / 1e9, 3), "unit": "GB/s",
+                            "cores": one, "tokens_per_s": round(wl.Bs / t1, 1)}}
 
 
 # ----------------------------------------------------------------- expert GEMM row
@@ -828,17 +986,25 @@ def main():
     us_cmb = us[CMB]
     a_cmb = rate["combine"]
 
-    # hot-cache figures (opt-in, so that a trace of the default run holds only the
-    # rotating-set launches): the same launches on one buffer set, which the 256 MB
+    # launches of each kernel so far: the headline part of a kernel trace of this
+    # command is the first this many dispatches of each kernel
+    W_, S_ = args.warmup, len(argv)
+    launches = {"k_update_expert": W_ + K + S_ + n_k, "k_dispatch": W_ + K + S_ + n_k,
+                "k_update_dispatch": W_ + K + S_ + n_k, "k_combine": 2 * W_ + 2 * K + S_ + n_k}
+
+    # hot-cache figures (opt-in): the same launches on one buffer set, which the 256 MB
     # Infinity Cache then serves in part
     hot = None
     if args.hot:
         hot = {"note": "one buffer set reused back to back: inputs partly served from the "
                        "Infinity Cache; not the headline figure",
                **{f"{n}_us": round(kernel_us(j, n_k, 1), 3) for j, n in enumerate(names)}}
-    c5 = time_stack(moe, torch, 16, max(10, K // 10), 3) if args.c5 else None
-    variants = dispatch_variants(moe, torch, max(K // 5, 50)) if args.c5 else None
-    configs = config_table(moe, torch, max(K // 5, 50)) if args.c5 else None
+    extras = not args.headline_only
+    graph = step_graph(torch, fns, argv, STEP, K, t_step, step_bytes, wl.Bs) if extras else None
+    configs = config_table(moe, torch, max(K // 5, 50)) if extras else None
+    c5 = time_stack(moe, torch, 16, max(10, K // 10), 3) if extras else None
+    ceil = ceilings(torch, max(K // 5, 50), wl, sets[0], nb, rows) if extras else None
+    variants = dispatch_variants(moe, torch, max(K // 5, 50)) if args.variants else None
 
     # HBM bytes per launch from the committed counter summaries (null when the
     # kernel source changed since they were taken)
@@ -857,12 +1023,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "DeepSeek-V3-shaped MoE layer: Bs=512, H=7168, 256 instances "
                                "(32 ranks x 8), K=8, Zipf(1.2) routing, mxfp8 dispatch, "
                                "1 shared expert, combine + residual + RMSNorm (bf16 in/out)",
                    "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E, "quant": "mxfp8",
+                   "arithmetic": "bf16 rows in and out, mxfp8 (E4M3 + E8M0) codes, fp32 sums",
                    "rows_dispatched": rows, "buffer_sets": args.sets},
         "tokens_per_s": round(wl.Bs / t_step, 1),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
@@ -879,10 +1046,13 @@ def main():
             for n, u in zip(names, us)},
         "step_three_calls": {"ms_per_step": round(t_three * 1e3, 5), "GBps": round(gbs_3, 2),
                              "tokens_per_s": round(wl.Bs / t_three, 1), "bytes": three_bytes},
+        "step_graph": graph,
         "hot_cache": hot,
         "c5_stack": c5,
         "dispatch_variants": variants,
         "other_configs": configs,
+        "ceilings": ceil,
+        "headline_launches": launches,
         "step_bytes": step_bytes,
         "parity_step0": "ok" if ok else "MISMATCH",
         "cpu_baseline": None,

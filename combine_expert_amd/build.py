@@ -1,4 +1,6 @@
-"""Build libmoe_expert.so: the HIP kernels and the C ABI, for gfx950 only.
+"""Build libmoe_expert.so (the HIP kernels and the C ABI of the MoE path) and
+libmoe_calib.so (the measurement kernels of include/moe_calib.h), for gfx950
+only.
 
     python -m combine_expert_amd.build
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe_expert.so")
+CALIB_DIR = os.path.join(PKG, "calib")
+CALIB_LIB = os.path.join(PKG, "libmoe_calib.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -27,8 +31,13 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def calib_sources():
+    return sorted(glob.glob(os.path.join(CALIB_DIR, "*.hip")))
+
+
 def headers():
-    return sorted(glob.glob(os.path.join(CSRC, "*.h"))) + [os.path.join(INCLUDE, "moe_expert.h")]
+    return sorted(glob.glob(os.path.join(CSRC, "*.h"))) + [os.path.join(INCLUDE, "moe_expert.h"),
+                                                           os.path.join(INCLUDE, "moe_calib.h")]
 
 
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -47,14 +56,12 @@ def _run(cmd):
     return r.returncode, _filter(r.stdout + r.stderr)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip to an object (in parallel: the dispatch kernels
-    are split by quantisation mode across several files), then link the
-    shared library."""
+def _compile_link(srcs, lib, verbose):
+    """Compile sources to objects in parallel, then link the shared library."""
     from concurrent.futures import ThreadPoolExecutor
     os.makedirs(OBJDIR, exist_ok=True)
     jobs = []
-    for src in sources():
+    for src in srcs:
         obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
         jobs.append((src, obj, [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", "-o", obj, src]))
     workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
@@ -67,7 +74,7 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{out}")
         if verbose and out.strip():
             print(out)
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
             *[j[1] for j in jobs]]
     rc, out = _run(link)
@@ -75,15 +82,24 @@ def build(verbose: bool = False) -> str:
         print(" ".join(link), flush=True)
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{out}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every csrc/*.hip to an object (in parallel: the dispatch kernels
+    are split by quantisation mode across several files) and link the library;
+    then the same for the measurement kernels in calib/."""
+    _compile_link(sources(), LIB, verbose)
+    _compile_link(calib_sources(), CALIB_LIB, verbose)
     return LIB
 
 
 def stale() -> bool:
-    if not os.path.exists(LIB):
+    if not os.path.exists(LIB) or not os.path.exists(CALIB_LIB):
         return True
-    t = os.path.getmtime(LIB)
-    return any(os.path.getmtime(p) > t for p in sources() + headers())
+    t = min(os.path.getmtime(LIB), os.path.getmtime(CALIB_LIB))
+    return any(os.path.getmtime(p) > t for p in sources() + calib_sources() + headers())
 
 
 if __name__ == "__main__":

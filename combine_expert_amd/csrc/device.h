@@ -11,9 +11,8 @@
 namespace moe {
 
 constexpr int kWave = 64;
-constexpr int kMaxThreads = 512;        // H <= 8192 elements / 16 per thread
+constexpr int kMaxThreads = 512;        // a row of H <= 8192 elements: 16 per thread
 constexpr int kMaxWaves = kMaxThreads / kWave;
-constexpr int kChunk = 16;              // row elements owned by one thread
 
 // ---------------------------------------------------------------- bf16
 

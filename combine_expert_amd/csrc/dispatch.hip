@@ -16,26 +16,22 @@
 // entries (at most 8192 four-byte ids, read with 16-byte loads from L2): one
 // over every entry and one over the entries before its token, packed as the
 // low and high 16 bits of one counter (each count is at most 8192), so each
-// entry costs one LDS atomic.  After the one barrier that completes the
-// histograms, every wave codes its parts of the row (codes need no rows) and
-// works out the token's K rows itself: chunk sums of the counters read as
-// 16-byte LDS words, a DPP scan, one lane shuffle, then the counters before
-// the id inside its chunk, its high half and the token's own earlier
-// duplicates.  The rows are known without a second barrier, so each wave
-// stores as soon as its parts are coded.  (A single wave working out the rows
-// for the block, behind a second barrier, measured about 1.8 us per block on
-// the critical path: a chain of dependent LDS reads and lane shuffles.  Two
-// tokens per block, sharing the histograms, measured slower: one block per
-// compute unit hides less latency than two.)
+// entry costs one LDS atomic.  Only the token's K offsets are needed, so one
+// wave alone scans chunk sums of the low halves; each of its first K lanes
+// takes its chunk's prefix by a lane shuffle, adds the counters before its id
+// in the chunk, the high half and the token's own earlier duplicates.  That
+// wave is an extra one holding no row data, so the row's waves code their
+// chunks (codes need no ranks) while it works out the rows; only the stores
+// wait for it.  This replaces a serial routing
+// kernel between two launches with redundant LDS work that overlaps the HBM
+// load of the token's row.  (Two tokens per block, sharing the histograms,
+// measured slower: one block per compute unit hides less latency than two.)
 // Nothing depends on scheduling: bitwise repeatable.
 //
-// Row layout (device.h): a wave per 1024 elements, lane l holding the parts
-// at 8 l and 512 + 8 l of its wave's span, so every load and store
-// instruction of a wave covers one contiguous run of the row.  A 32-element
-// mxfp8 block is 4 lanes and a 128-element int8 tile 16 lanes of one part;
-// per-block maxima are lane shuffles, the per-token maximum is a wave
-// reduction plus one LDS step.  Coded rows and scales are stored with the
-// device-scope policy (written through to memory).
+// Row layout: one thread owns 16 consecutive elements (two 16-byte loads of
+// bf16), so a 32-element mxfp8 block is a lane pair and a 128-element int8
+// tile is 8 lanes; per-block maxima are lane shuffles, the per-token maximum
+// is a wave reduction plus one LDS step.
 //
 // Load order matters: wait counters retire in issue order, so the loads a
 // phase waits for are issued before the ones it does not (the token's row),

@@ -8,17 +8,10 @@
 
 namespace moe {
 
+constexpr int kChunk = 16;        // row elements owned by one thread (16 consecutive)
 
 constexpr int kHistSlots = 1024;  // one LDS counter per instance (E <= 1024)
-// Tokens (rows) per token block.  Two would halve the per-row routing work
-// (the loads of every id, the histogram, the table lookups) but measured
-// slower (c3: 9.2 against 7.8 us; fused mapping 12.3 against 9.5): with one
-// block per compute unit, each block's barrier holds all of its rows.  The
-// body works for any count; the per-instance scales variant would not fit
-// its registers in 1024 threads.
-template <bool PE>
-constexpr int tokens_per_block() { return 1; }
-constexpr int kDispatchWaves = kMaxWaves * 2;
+constexpr int kDispatchWaves = kMaxWaves + 1;
 constexpr int kPreOne = 0x10001;  // packed counter increment: all (low) and before-token (high)
 constexpr int kMaxTokens = 512;   // Bs limit: staged token mask
 constexpr int kMaxTopK = 16;      // K limit: staged thresholds
@@ -430,92 +423,37 @@ __device__ void route_summary(const DispatchArgs &a, const Src &s, int *s_hist, 
 
 // ------------------------------------------------------------------ token blocks
 
-// Token blocks use the row layout of device.h: lane l of wave w holds part 0
-// (elements e0 = 1024 w + 8 l .. + 7) and part 1 (e1 = e0 + 512 .. + 7) of
-// the token's row, and writes the codes of each part as 8 bytes (16 for bf16
-// rows), so every store instruction of a wave covers 512 contiguous bytes of
-// codes (1 KB of bf16).  A part past the row end reads zeros and its stores
-// go to an offset past the buffer (dropped).  Coded rows are stored with the
-// device-scope policy, which writes them through to memory: for these
-// scattered rows it measured faster than non-temporal or default stores
-// (c3: 5.5 against 6.3-6.5 us for the bare scatter), and it leaves no dirty
-// lines for the end of the kernel to write back.  Scales (a few bytes per
-// lane, partial lines) keep the default policy, so that L2 merges the pieces
-// of a line: written through, they cost 0.3 us more at c3.
-struct Lane {
-    int e0, e1;    // first element of each part
-    bool v0, v1;   // part inside the row
-};
-
-__device__ __forceinline__ Lane lane_parts(int t, int H)
-{
-    Lane L;
-    L.e0 = part_elem(t, 0);
-    L.e1 = part_elem(t, 1);
-    L.v0 = L.e0 < H;
-    L.v1 = L.e1 < H;
-    return L;
-}
-
 __device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d)
 {
     return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
            ((uint32_t)d << 24);
 }
 
-// Largest |x| bit pattern among 8 bf16 (sign cleared).  For non-negative
-// values the integer order of bf16 patterns is the numeric order.
-__device__ __forceinline__ uint32_t amax_bits8(const uint4 &a)
-{
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        m = max(m, w[j] & 0x7fffu);
-        m = max(m, (w[j] >> 16) & 0x7fffu);
-    }
-    return m;
-}
-
-// int8 codes of 8 values with multiplier d: clamp(rint(v * d), -127, 127).
+// int8 codes of 16 values with multiplier d: clamp(rint(v * d), -127, 127).
 // d is +inf when 127 / max overflows (a tiny subnormal maximum): zeros then
 // give 0 * inf = NaN and are coded 0, the rest saturate.
-__device__ __forceinline__ uint2 int8_codes8(const float *v, float d)
+__device__ __forceinline__ uint4 int8_codes(const float *v, float d)
 {
-    int q[8];
+    int q[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 16; ++j) {
         float r = __builtin_rintf(v[j] * d);
         r = r != r ? 0.0f : r;
         r = fminf(fmaxf(r, -127.0f), 127.0f);
         q[j] = (int)r;
     }
-    return make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
+    return make_uint4(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]),
+                      pack_i8x4(q[8], q[9], q[10], q[11]), pack_i8x4(q[12], q[13], q[14], q[15]));
 }
 
-// int8 codes of 8 fp32 values for the static mode: the nearest integer, ties
-// to even, saturated to [-128, 127]; NaN codes to 0.
-__device__ __forceinline__ uint2 int8_static_codes8(const float *v)
-{
-    int q[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        float r = __builtin_rintf(v[j]);
-        r = r != r ? 0.0f : r;
-        r = fminf(fmaxf(r, -128.0f), 127.0f);
-        q[j] = (int)r;
-    }
-    return make_uint2(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]));
-}
-
-// E4M3 codes of 8 values multiplied by the power of two f (an exact product):
+// E4M3 codes of 16 values multiplied by the power of two f (an exact product):
 // clamp to +-448 (saturation), then the gfx950 packed conversion, which
 // rounds to nearest even and keeps the sign of zero.
-__device__ __forceinline__ uint2 e4m3_codes8(const float *v, float f)
+__device__ __forceinline__ uint4 e4m3_codes(const float *v, float f)
 {
-    uint32_t w[2];
+    uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 4; ++q) {
         const float a = fminf(fmaxf(v[4 * q] * f, -448.0f), 448.0f);
         const float b = fminf(fmaxf(v[4 * q + 1] * f, -448.0f), 448.0f);
         const float c = fminf(fmaxf(v[4 * q + 2] * f, -448.0f), 448.0f);
@@ -524,7 +462,7 @@ __device__ __forceinline__ uint2 e4m3_codes8(const float *v, float f)
         p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
         w[q] = (uint32_t)p;
     }
-    return make_uint2(w[0], w[1]);
+    return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // floor(log2(m)) of a positive bf16 magnitude pattern (normal or subnormal)
@@ -534,97 +472,51 @@ __device__ __forceinline__ int bf16_ilogb(uint32_t m)
     return ex ? ex - 127 : (31 - __clz((int)(m & 0x7f))) - 133;
 }
 
-// mxfp8 shared exponent of a block whose largest |x| pattern is m
-__device__ __forceinline__ int mx_exponent(uint32_t m)
+// int8 codes of 16 fp32 values for the static mode: the nearest integer, ties
+// to even, saturated to [-128, 127]; NaN codes to 0.
+__device__ __forceinline__ uint4 int8_static_codes(const float *v)
 {
-    int se = -127;
-    if (m) {
-        se = bf16_ilogb(m) - 8;
-        se = max(-127, min(127, se));
+    int q[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        float r = __builtin_rintf(v[j]);
+        r = r != r ? 0.0f : r;
+        r = fminf(fmaxf(r, -128.0f), 127.0f);
+        q[j] = (int)r;
     }
-    return se;
+    return make_uint4(pack_i8x4(q[0], q[1], q[2], q[3]), pack_i8x4(q[4], q[5], q[6], q[7]),
+                      pack_i8x4(q[8], q[9], q[10], q[11]), pack_i8x4(q[12], q[13], q[14], q[15]));
 }
 
-// Maximum over the lanes of one tile of a part (tile / 8 lanes, tile <= 512),
-// in each of them: DPP steps up to 16 lanes, then lane shuffles.
-__device__ __forceinline__ uint32_t tile_max(uint32_t m, int lanes)
+// this thread's 16 values of scales row e ([E, H]); lanes past the row end
+// (tc = 0) read the row's first chunk
+__device__ __forceinline__ void scale_row16(const float *qs, int e, int H, int tc, float4 (&s)[4])
 {
-    m = group_max_u32(m, lanes < 32 ? lanes : 32);
-    if (lanes >= 64)
-        m = max(m, (uint32_t)__shfl_xor((int)m, 32));
-    return m;
+    const float4 *p = reinterpret_cast<const float4 *>(qs + (size_t)e * H) + 4 * tc;
+    s[0] = p[0];
+    s[1] = p[1];
+    s[2] = p[2];
+    s[3] = p[3];
 }
 
-// this thread's 8 + 8 values of scales row e ([E, H] or [H]); a part past the
-// row end reads the row's first chunk (its values are not used)
-__device__ __forceinline__ void scale_row_parts(const float *qs, int e, int H, const Lane &L,
-                                                float4 (&s)[4])
-{
-    const float *row = qs + (size_t)e * H;
-    const float4 *p0 = reinterpret_cast<const float4 *>(row + (L.v0 ? L.e0 : 0));
-    const float4 *p1 = reinterpret_cast<const float4 *>(row + (L.v1 ? L.e1 : 0));
-    s[0] = p0[0];
-    s[1] = p0[1];
-    s[2] = p1[0];
-    s[3] = p1[1];
-}
-
-// w = v * s for the lane's 16 values; a part past the row end gives zeros
-__device__ __forceinline__ void scaled16(const float *v, const float4 (&s)[4], const Lane &L,
-                                         float *w)
+__device__ __forceinline__ void scaled16(const float *v, const float4 (&s)[4], float *w)
 {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const bool ok = q < 2 ? L.v0 : L.v1;
-        w[4 * q] = ok ? v[4 * q] * s[q].x : 0.0f;
-        w[4 * q + 1] = ok ? v[4 * q + 1] * s[q].y : 0.0f;
-        w[4 * q + 2] = ok ? v[4 * q + 2] * s[q].z : 0.0f;
-        w[4 * q + 3] = ok ? v[4 * q + 3] * s[q].w : 0.0f;
+        w[4 * q] = v[4 * q] * s[q].x;
+        w[4 * q + 1] = v[4 * q + 1] * s[q].y;
+        w[4 * q + 2] = v[4 * q + 2] * s[q].z;
+        w[4 * q + 3] = v[4 * q + 3] * s[q].w;
     }
 }
 
-__device__ __forceinline__ uint32_t absmax_bits_f(const float *w, int n)
+__device__ __forceinline__ uint32_t absmax_bits16(const float *w)
 {
     float m = 0.0f;
-    for (int j = 0; j < n; ++j)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
         m = fmaxf(m, fabsf(w[j]));
     return __float_as_uint(m);  // non-negative floats order like their bit patterns
-}
-
-// Output buffers of one dispatch launch.
-struct Out {
-    rsrc_t x, sc;
-    uint32_t row_bytes;   // bytes of one expand_x row
-    uint32_t sc_row;      // scale entries per row (modes 2-4)
-};
-
-__device__ __forceinline__ Out out_buffers(const DispatchArgs &a, int MODE)
-{
-    const int N = a.Bs * a.K;
-    const int elt = MODE == 0 ? 2 : 1;
-    Out o;
-    o.row_bytes = (uint32_t)a.H * elt;
-    o.x = buffer_rsrc(a.expand_x, (uint32_t)N * o.row_bytes);
-    o.sc_row = MODE == 2 ? 1u : MODE == 3 ? (uint32_t)((a.H + a.tile - 1) / a.tile)
-                                          : MODE == 4 ? (uint32_t)(a.H / 32) : 0u;
-    const uint32_t sc_bytes = MODE == 4 ? 1u : 4u;
-    o.sc = buffer_rsrc(a.expand_scales ? a.expand_scales : a.expand_x,
-                       a.expand_scales ? (uint32_t)N * o.sc_row * sc_bytes : 0u);
-    return o;
-}
-
-// Writes one tile scale of part p of a per-tile int8 row: the tile's first
-// lane in the part stores it (tiles of 1024 span both parts of a wave: lane 0
-// of part 0 stores it).
-__device__ __forceinline__ void store_tile_scale(const Out &o, uint32_t row, int tile, int lane,
-                                                 int e, bool ok, int p, float f)
-{
-    const int lanes = tile >= kWaveElems ? 2 * kWave : tile / kPartElems;
-    const bool first = tile >= kWaveElems ? (lane == 0 && p == 0) : (lane & (lanes - 1)) == 0;
-    if (ok && first)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(f), o.sc,
-                                              (row * o.sc_row + (uint32_t)(e / tile)) * 4u, 0,
-                                              kPlain);
 }
 
 // One scales row per instance (the scales input of shape [E, H]): every copy
@@ -633,23 +525,21 @@ __device__ __forceinline__ void store_tile_scale(const Out &o, uint32_t row, int
 // Cache: the table is E * H * 4 bytes).  Per-token dynamic int8 needs each
 // copy's maximum over the whole row first: a pass computes all K maxima
 // (one barrier for all of them), a second pass codes.  s_pmax: LDS
-// [kDispatchWaves][KMAX]; tr is the thread's index in its token's row, w its
-// wave in the block, waves [w0, w0 + rw) the token's.
+// [kDispatchWaves][KMAX].
 constexpr int kPrefetch = 4;
 
 template <int MODE, int KMAX>
-__device__ __forceinline__ void code_store_rows(const DispatchArgs &a, int tr, int w, int w0,
-                                                int rw, const Lane &L, const uint4 &xa,
-                                                const uint4 &xb, const int *rank,
-                                                const int *eid, uint32_t *s_pmax)
+__device__ __forceinline__ void code_store_rows(const DispatchArgs &a, int t, bool has,
+                                                const uint4 &xa, const uint4 &xb,
+                                                const int *rank, const int *eid,
+                                                uint32_t *s_pmax)
 {
     constexpr int D = KMAX < kPrefetch ? KMAX : kPrefetch;
     const int H = a.H;
-    const int lane = tr & (kWave - 1);
-    const Out o = out_buffers(a, MODE);
+    const int tc = has ? t : 0;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = blockDim.x / kWave;
     float v[16];
-    unpack8(xa, v);
-    unpack8(xb, v + 8);
+    unpack16(xa, xb, v);
     int ek[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
@@ -660,22 +550,22 @@ __device__ __forceinline__ void code_store_rows(const DispatchArgs &a, int tr, i
     if (MODE == 2) {
 #pragma unroll
         for (int p = 0; p < D; ++p)
-            scale_row_parts(a.qs, ek[p], H, L, ring[p]);
+            scale_row16(a.qs, ek[p], H, tc, ring[p]);
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             float x16[16];
-            scaled16(v, ring[k % D], L, x16);
-            const uint32_t m = wave_max_u32(absmax_bits_f(x16, 16));
+            scaled16(v, ring[k % D], x16);
+            const uint32_t m = wave_max_u32(has ? absmax_bits16(x16) : 0u);
             if (lane == 0)
                 s_pmax[w * KMAX + k] = m;
             if (k + D < KMAX)
-                scale_row_parts(a.qs, ek[k + D], H, L, ring[k % D]);
+                scale_row16(a.qs, ek[k + D], H, tc, ring[k % D]);
         }
         lds_barrier();
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
             uint32_t m = 0;
-            for (int j = w0; j < w0 + rw; ++j)  // the token's waves
+            for (int j = 0; j < nw; ++j)
                 m = max(m, s_pmax[j * KMAX + k]);
             amax[k] = __uint_as_float(m);
         }
@@ -683,82 +573,80 @@ __device__ __forceinline__ void code_store_rows(const DispatchArgs &a, int tr, i
 
 #pragma unroll
     for (int p = 0; p < D; ++p)
-        scale_row_parts(a.qs, ek[p], H, L, ring[p]);
+        scale_row16(a.qs, ek[p], H, tc, ring[p]);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         float x16[16];
-        scaled16(v, ring[k % D], L, x16);
+        scaled16(v, ring[k % D], x16);
         if (k + D < KMAX)
-            scale_row_parts(a.qs, ek[k + D], H, L, ring[k % D]);
-        const uint32_t row = rank[k] >= 0 ? (uint32_t)rank[k] : 0u;
-        const uint32_t base = rank[k] >= 0 ? row * o.row_bytes : kNoRow;
-        const uint32_t p0 = L.v0 ? (uint32_t)L.e0 : kNoPart, p1 = L.v1 ? (uint32_t)L.e1 : kNoPart;
-        uint2 c0, c1;
+            scale_row16(a.qs, ek[k + D], H, tc, ring[k % D]);
+        const bool put = has && rank[k] >= 0;
+        int8_t *dst = static_cast<int8_t *>(a.expand_x) + (size_t)(rank[k] >= 0 ? rank[k] : 0) * H;
         if (MODE == 1) {
-            c0 = int8_static_codes8(x16);
-            c1 = int8_static_codes8(x16 + 8);
+            const uint4 code = int8_static_codes(x16);
+            if (put)
+                store_nt16(reinterpret_cast<uint4 *>(dst) + t, code);
         } else if (MODE == 2) {
             const float m = amax[k];
             const float d = m != 0.0f ? 127.0f / m : 0.0f;
-            c0 = int8_codes8(x16, d);
-            c1 = int8_codes8(x16 + 8, d);
-            if (tr == 0 && rank[k] >= 0)
-                __builtin_amdgcn_raw_buffer_store_b32(
-                    __float_as_uint(m != 0.0f ? 1.0f / d : 0.0f), o.sc, row * 4u, 0, kPlain);
+            const uint4 code = int8_codes(x16, d);
+            if (put) {
+                store_nt16(reinterpret_cast<uint4 *>(dst) + t, code);
+                if (t == 0)
+                    static_cast<float *>(a.expand_scales)[rank[k]] = m != 0.0f ? 1.0f / d : 0.0f;
+            }
         } else {  // MODE == 3
             const int tile = a.tile;
-            uint32_t m0 = absmax_bits_f(x16, 8), m1 = absmax_bits_f(x16 + 8, 8);
-            if (tile >= kWaveElems) {
-                m0 = m1 = wave_max_u32(max(m0, m1));
-            } else {
-                m0 = tile_max(m0, tile / kPartElems);
-                m1 = tile_max(m1, tile / kPartElems);
-            }
-            const float mf0 = __uint_as_float(m0), mf1 = __uint_as_float(m1);
-            const float d0 = m0 ? 127.0f / mf0 : 0.0f, d1 = m1 ? 127.0f / mf1 : 0.0f;
-            c0 = int8_codes8(x16, d0);
-            c1 = int8_codes8(x16 + 8, d1);
-            if (rank[k] >= 0) {
-                store_tile_scale(o, row, tile, lane, L.e0, L.v0, 0, m0 ? 1.0f / d0 : 0.0f);
-                store_tile_scale(o, row, tile, lane, L.e1, L.v1, 1, m1 ? 1.0f / d1 : 0.0f);
+            const int lanes = tile / kChunk;
+            uint32_t m = has ? absmax_bits16(x16) : 0u;
+            for (int o = 1; o < lanes; o <<= 1)
+                m = max(m, (uint32_t)__shfl_xor((int)m, o));
+            const float mf = __uint_as_float(m);
+            const float d = m ? 127.0f / mf : 0.0f;
+            const uint4 code = int8_codes(x16, d);
+            if (put) {
+                store_nt16(reinterpret_cast<uint4 *>(dst) + t, code);
+                if ((t & (lanes - 1)) == 0) {
+                    const int nt = (H + tile - 1) / tile;
+                    static_cast<float *>(a.expand_scales)[(size_t)rank[k] * nt +
+                                                          (t * kChunk) / tile] = m ? 1.0f / d : 0.0f;
+                }
             }
         }
-        buf_store8<kDevice>(o.x, base + p0, c0.x, c0.y);
-        buf_store8<kDevice>(o.x, base + p1, c1.x, c1.y);
     }
 }
 
-// A token's coded parts (this lane's 8 + 8 elements) and their scales.
+// A token's coded chunk (this thread's 16 elements) and its scale.
 struct Coded {
-    uint2 c0, c1;  // modes 1-4: codes of part 0 and part 1
-    float f0, f1;  // mode 2: the token's 1 / dynamicScales (f0); mode 3: each part's tile's
-    int se0, se1;  // mode 4: each part's block exponent
+    uint4 code;    // modes 1-4
+    float fscale;  // modes 2 and 3: 1 / dynamicScales of the token / tile
+    int se;        // mode 4: the block's shared exponent
 };
 
-// Codes a token's row once (this lane's parts in xa, xb; zeros past the row
-// end); no memory writes, so it can run before the rows are known.  amax_row
-// is the token's largest |x| pattern (per-token int8 only).
+// Codes a token's row once (this thread's 16 elements in xa, xb); no memory
+// writes, so it can run before the rows are known.  amax_row is the token's
+// largest |x| pattern (per-token int8 only).
 template <int MODE>
-__device__ __forceinline__ Coded code_row(const DispatchArgs &a, const Lane &L, const uint4 &xa,
+__device__ __forceinline__ Coded code_row(const DispatchArgs &a, int t, bool has, const uint4 &xa,
                                           const uint4 &xb, uint32_t amax_row)
 {
     Coded c{};
     if (MODE == 0)
         return c;
     float v[16];
-    unpack8(xa, v);
-    unpack8(xb, v + 8);
+    unpack16(xa, xb, v);
     if (MODE == 1) {  // static: one coefficient or one row shared by all experts
+        const int tc = has ? t : 0;
         float sv[16];
         if (a.qs_kind == 2) {
-            float4 s[4];
-            scale_row_parts(a.qs, 0, a.H, L, s);
+            const float4 *p = reinterpret_cast<const float4 *>(a.qs) + 4 * tc;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                sv[4 * q] = s[q].x;
-                sv[4 * q + 1] = s[q].y;
-                sv[4 * q + 2] = s[q].z;
-                sv[4 * q + 3] = s[q].w;
+                const float4 f = p[q];
+                sv[4 * q] = f.x;
+                sv[4 * q + 1] = f.y;
+                sv[4 * q + 2] = f.z;
+                sv[4 * q + 3] = f.w;
             }
         } else {
             const float cst = a.qs[0];
@@ -769,147 +657,90 @@ __device__ __forceinline__ Coded code_row(const DispatchArgs &a, const Lane &L, 
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             v[j] *= sv[j];
-        c.c0 = int8_static_codes8(v);
-        c.c1 = int8_static_codes8(v + 8);
+        c.code = int8_static_codes(v);
     } else if (MODE == 2) {
         const uint32_t m = amax_row;
         const float mf = __uint_as_float(m << 16);
         const float d = m ? 127.0f / mf : 0.0f;
-        c.f0 = m ? 1.0f / d : 0.0f;
-        c.c0 = int8_codes8(v, d);
-        c.c1 = int8_codes8(v + 8, d);
+        c.fscale = m ? 1.0f / d : 0.0f;
+        c.code = int8_codes(v, d);
     } else if (MODE == 3) {
-        const int tile = a.tile;
-        uint32_t m0 = amax_bits8(xa), m1 = amax_bits8(xb);
-        if (tile >= kWaveElems) {
-            m0 = m1 = wave_max_u32(max(m0, m1));
-        } else {
-            m0 = tile_max(m0, tile / kPartElems);
-            m1 = tile_max(m1, tile / kPartElems);
+        const int lanes = a.tile / kChunk;  // lanes per tile: 1 .. 64
+        // lanes past the row end hold a copy of chunk 0: keep it out of the
+        // last (partial) tile's maximum
+        uint32_t m = has ? amax_bits16(xa, xb) : 0u;
+        for (int o = 1; o < lanes; o <<= 1)
+            m = max(m, (uint32_t)__shfl_xor((int)m, o));
+        const float mf = __uint_as_float(m << 16);
+        const float d = m ? 127.0f / mf : 0.0f;
+        c.fscale = m ? 1.0f / d : 0.0f;
+        c.code = int8_codes(v, d);
+    } else {  // MODE == 4
+        uint32_t m = amax_bits16(xa, xb);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        int se = -127;
+        if (m) {
+            se = bf16_ilogb(m) - 8;
+            se = max(-127, min(127, se));
         }
-        const float mf0 = __uint_as_float(m0 << 16), mf1 = __uint_as_float(m1 << 16);
-        const float d0 = m0 ? 127.0f / mf0 : 0.0f, d1 = m1 ? 127.0f / mf1 : 0.0f;
-        c.f0 = m0 ? 1.0f / d0 : 0.0f;
-        c.f1 = m1 ? 1.0f / d1 : 0.0f;
-        c.c0 = int8_codes8(v, d0);
-        c.c1 = int8_codes8(v + 8, d1);
-    } else {  // MODE == 4: blocks of 32 are 4 lanes of one part
-        const uint32_t m0 = tile_max(amax_bits8(xa), 4), m1 = tile_max(amax_bits8(xb), 4);
-        c.se0 = mx_exponent(m0);
-        c.se1 = mx_exponent(m1);
-        const float f0 = __uint_as_float((uint32_t)(127 - c.se0) << 23);  // 2^-se, normal
-        const float f1 = __uint_as_float((uint32_t)(127 - c.se1) << 23);
-        c.c0 = e4m3_codes8(v, f0);
-        c.c1 = e4m3_codes8(v + 8, f1);
+        const float f = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, normal
+        c.code = e4m3_codes(v, f);
+        c.se = se;
     }
     return c;
 }
 
-// Writes the coded parts (mode 0: the raw bf16 parts), with their scales, to
+// Writes the coded chunk (mode 0: the raw bf16 chunk), with its scales, to
 // each destination row rank[k] >= 0.
 template <int MODE, int KMAX>
-__device__ __forceinline__ void store_row(const DispatchArgs &a, int tr, const Lane &L,
-                                          const uint4 &xa, const uint4 &xb, const Coded &c,
-                                          const int *rank)
+__device__ __forceinline__ void store_row(const DispatchArgs &a, int t, bool has, const uint4 &xa,
+                                          const uint4 &xb, const Coded &c, const int *rank)
 {
-    if (!L.v0 && !L.v1)
-        return;  // a wave past the row end
-    const Out o = out_buffers(a, MODE);
-    const int lane = tr & (kWave - 1);
-    const int elt = MODE == 0 ? 2 : 1;
-    const uint32_t p0 = L.v0 ? (uint32_t)(L.e0 * elt) : kNoPart;
-    const uint32_t p1 = L.v1 ? (uint32_t)(L.e1 * elt) : kNoPart;
+    const int H = a.H;
+    if (!has)
+        return;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
         if (rank[k] < 0)
             continue;
-        const uint32_t row = (uint32_t)rank[k];
-        const uint32_t base = row * o.row_bytes;
         if (MODE == 0) {
-            buf_store16<kDevice>(o.x, base + p0, xa);
-            buf_store16<kDevice>(o.x, base + p1, xb);
+            uint4 *dst = reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.expand_x) +
+                                                   (size_t)rank[k] * H) + 2 * t;
+            store_nt16(dst, xa);
+            store_nt16(dst + 1, xb);
             continue;
         }
-        buf_store8<kDevice>(o.x, base + p0, c.c0.x, c.c0.y);
-        buf_store8<kDevice>(o.x, base + p1, c.c1.x, c.c1.y);
-        if (MODE == 2 && tr == 0)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(c.f0), o.sc, row * 4u, 0,
-                                                  kPlain);
+        store_nt16(reinterpret_cast<uint4 *>(static_cast<int8_t *>(a.expand_x) +
+                                             (size_t)rank[k] * H) + t, c.code);
+        if (MODE == 2 && t == 0)
+            static_cast<float *>(a.expand_scales)[rank[k]] = c.fscale;
         if (MODE == 3) {
-            store_tile_scale(o, row, a.tile, lane, L.e0, L.v0, 0, c.f0);
-            store_tile_scale(o, row, a.tile, lane, L.e1, L.v1, 1, c.f1);
-        }
-        if (MODE == 4 && (lane & 3) == 0) {
-            if (L.v0)
-                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(c.se0 + 127), o.sc,
-                                                     row * o.sc_row + (uint32_t)(L.e0 / 32), 0,
-                                                     kPlain);
-            if (L.v1)
-                __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(c.se1 + 127), o.sc,
-                                                     row * o.sc_row + (uint32_t)(L.e1 / 32), 0,
-                                                     kPlain);
-        }
-    }
-}
-
-// Destination row of this lane's entry (lanes k < K hold entry k of the
-// token, id my_id >= 0 if active; other lanes -1) from the packed histograms
-// (low 16 bits: active entries of each instance; high 16 bits: those before
-// this token).  Every wave works the rows out on its own, so no barrier
-// follows: lane c sums the low halves of counters [c*per, (c+1)*per) (per a
-// multiple of 4 with 64 * per >= E, read as 16-byte words), a DPP scan gives
-// each chunk's exclusive prefix, and lane k adds its chunk's prefix (one lane
-// shuffle), the low halves before its id in the chunk, the high half of its
-// own counter and the token's earlier entries with the same id.
-template <int KMAX>
-__device__ __forceinline__ int entry_row(const int *s_cnt, int E, int K, int lane, int my_id)
-{
-    const int per = ((E + kWave - 1) / kWave + 3) & ~3;  // 4, 8, 12 or 16
-    const int q = per >> 2;
-    const int4 *c4 = reinterpret_cast<const int4 *>(s_cnt);
-    const bool on = my_id >= 0;
-    const int id = on ? my_id : 0;
-    const int chunk = small_div(id, per);
-    const int within = id - chunk * per;
-    int local = 0, part = 0, high = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if (j < q) {
-            const int4 v = c4[lane * q + j];
-            const int4 u = c4[chunk * q + j];
-            local += (v.x & 0xffff) + (v.y & 0xffff) + (v.z & 0xffff) + (v.w & 0xffff);
-            const int uv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                part += 4 * j + b < within ? (uv[b] & 0xffff) : 0;
-                high += 4 * j + b == within ? (uv[b] >> 16) : 0;
+            const int lanes = a.tile / kChunk;
+            if ((t & (lanes - 1)) == 0) {
+                const int nt = (H + a.tile - 1) / a.tile;
+                static_cast<float *>(a.expand_scales)[(size_t)rank[k] * nt +
+                                                      (t * kChunk) / a.tile] = c.fscale;
             }
         }
+        if (MODE == 4 && (t & 1) == 0)
+            static_cast<uint8_t *>(a.expand_scales)[(size_t)rank[k] * (H / 32) + t / 2] =
+                (uint8_t)(c.se + 127);
     }
-    const int excl = wave_incl_scan(local) - local;
-    const int off = __shfl(excl, chunk);
-    int dup = 0;  // earlier entries of this token with the same id
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        const int v = j < K ? __builtin_amdgcn_readlane(my_id, j) : -1;
-        dup += (j < lane && v == my_id) ? 1 : 0;
-    }
-    return on ? off + part + high + dup : -1;
 }
 
 template <int MODE, int KMAX, typename Src, bool PE>
 __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
 {
-    // low 16 bits: active entries with id e; high: those before this block's
-    // tokens
-    __shared__ __align__(16) int s_cnt[kHistSlots];
+    // low 16 bits: active entries with id e; high: those before this token.
+    // After the scan the low half holds offsets[e].
+    __shared__ int s_cnt[kHistSlots];
     __shared__ int s_wave[kDispatchWaves];
+    __shared__ int s_rank[KMAX];
     __shared__ uint32_t s_wmax[kDispatchWaves];
     __shared__ uint32_t s_pmax[PE && MODE == 2 ? kDispatchWaves * KMAX : 1];
     __shared__ uint8_t s_tok[Src::kMapped ? kMaxTokens : 1];
     __shared__ __align__(16) float s_thr[Src::kMapped ? kMaxTopK : 1];
     extern __shared__ int s_tab[];  // mapped: the [n_logical, F] table
-    constexpr int kTPB = tokens_per_block<PE>();
 
     const int Bs = a.Bs, H = a.H, K = a.K, E = a.E;
     const int N = Bs * K;
@@ -923,45 +754,35 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         route_summary(a, s, s_cnt, s_wave, s_tab, s_tok, s_thr);
         return;
     }
-    // Block 1 + b holds tokens kTPB * b + j, one row of waves each
-    // (rw waves per row); lanes below KB = kTPB * K carry the
-    // block's entries g0 + lane in order.
+    const int i = blockIdx.x - 1;
     const int t = threadIdx.x, T = blockDim.x;
     const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
-    const int rw = kTPB == 1 ? nw : nw / kTPB;
-    const int tk = kTPB == 1 ? 0 : w / rw;  // this wave's token in the block (wave-uniform)
-    const int i = (blockIdx.x - 1) * kTPB + tk;
-    const int tr = t - tk * rw * kWave;  // thread index in the token's row
-    const Lane L = lane_parts(tr, H);
-    const rsrc_t r_x = buffer_rsrc(a.x, (uint32_t)Bs * H * 2);
-    const int KB = kTPB * K;
-    const int g0 = (blockIdx.x - 1) * KB;
+    const bool has = t * kChunk < H;
 
-    // 1. the block's own entries, one per lane: the first loads issued are
+    // 1. the token's own K entries, one per lane: the first loads issued are
     //    the first ones waited for (after the rare large-table staging)
     if (Src::kMapped)
         Stage<Src::kKeep>::rest(a, s_tab, s_tok);
-    const bool mine = lane < KB && g0 + lane < N;
-    const int gm = min(g0 + min(lane, KB - 1), N - 1);
-    const int raw_id = a.ids[gm];
+    const int f0 = i * K;
+    const int kk = min(lane, K - 1);
+    const int raw_id = a.ids[f0 + kk];
     const uint8_t *mp =
         !Src::kMapped && a.mask ? a.mask : reinterpret_cast<const uint8_t *>(a.ids);
-    const uint8_t raw_on = Src::kMapped ? 1 : mp[gm];
+    const uint8_t raw_on = Src::kMapped ? 1 : mp[f0 + kk];
     const float *sp = Src::kMapped && a.scores ? a.scores : reinterpret_cast<const float *>(a.ids);
-    const float raw_sc = Src::kMapped ? sp[gm] : 0.0f;
-    for (int e = t; e < kHistSlots; e += T)  // entry_row reads whole 16-byte groups
+    const float raw_sc = Src::kMapped ? sp[f0 + kk] : 0.0f;
+    for (int e = t; e < E; e += T)
         s_cnt[e] = 0;
 
-    // 2. the packed histograms.  The tokens' rows (two 8-element parts per
-    //    lane) are loaded after the first batch of ids, so they stay in flight
-    //    meanwhile.
+    // 2. the packed histograms.  The token's row (16 elements per thread) is
+    //    loaded after the first batch of ids, so it stays in flight meanwhile.
     uint4 xa, xb;
     int err = 0;
     for_each_entry(
         s, N, err,
         [&](int inst, bool on, int g) {
             if (on)
-                atomicAdd(&s_cnt[inst], g < g0 ? kPreOne : 1);
+                atomicAdd(&s_cnt[inst], g < f0 ? kPreOne : 1);
         },
         [&] {
             // mapped source: the staging loads go out with the first ids and
@@ -970,9 +791,10 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
             Stage<Src::kKeep> st;
             if (Src::kMapped)
                 st.issue(a);
-            const uint32_t tok = i < Bs ? (uint32_t)i * H * 2 : kNoRow;
-            xa = buf_load16<kPlain>(r_x, tok + (L.v0 ? (uint32_t)L.e0 * 2 : kNoPart));
-            xb = buf_load16<kPlain>(r_x, tok + (L.v1 ? (uint32_t)L.e1 * 2 : kNoPart));
+            const uint4 *src =
+                reinterpret_cast<const uint4 *>(a.x + (size_t)i * H) + 2 * (has ? t : 0);
+            xa = src[0];
+            xb = src[1];
             if (Src::kMapped)
                 st.store(a, s_tab, s_tok, s_thr);
             lds_barrier();  // histograms zeroed (and mapping data staged) before use
@@ -981,73 +803,99 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
     if constexpr (Src::kMapped) {
         bool on;
         int e2 = 0;  // block 0 reports the errors
-        const int ie = s.token_of(gm);
-        const int inst = s.map(raw_id, ie, gm - ie * K, raw_sc, true, on, e2);
-        if (w == 0 && mine) {  // the update-expert outputs of the block's entries
+        const int inst = s.map(raw_id, i, kk, raw_sc, true, on, e2);
+        if (t < K) {  // the update-expert outputs of this token
             if (a.balanced_ids)
-                a.balanced_ids[g0 + lane] = inst;
+                a.balanced_ids[f0 + t] = inst;
             if (a.balanced_mask)
-                a.balanced_mask[g0 + lane] = on ? 1 : 0;
+                a.balanced_mask[f0 + t] = on ? 1 : 0;
         }
-        my_id = mine && on ? inst : -1;
+        my_id = lane < K && on ? inst : -1;
     } else {
         const bool my_on =
-            mine && (a.mask == nullptr || raw_on != 0) && (unsigned)raw_id < (unsigned)E;
+            lane < K && (a.mask == nullptr || raw_on != 0) && (unsigned)raw_id < (unsigned)E;
         my_id = my_on ? raw_id : -1;
     }
-    // After the histogram barrier each wave works out the block's rows itself
-    // (entry_row) and codes its parts, then stores: no further barrier.
+    const bool my_on = my_id >= 0;
+    // Coding needs no ranks: after the histogram barrier the row's waves code
+    // their chunks while the block's last wave, which holds no row data (the
+    // block has one wave more than the row needs), works out the rows.
     // Per-token int8 publishes its wave maxima before the barrier.
     Coded cd{};
     if (MODE == 2 && !PE) {
-        const uint32_t m = wave_max_u32(max(amax_bits8(xa), amax_bits8(xb)));
+        const uint32_t m = wave_max_u32(amax_bits16(xa, xb));
         if (lane == 0)
             s_wmax[w] = m;
     }
+    const int rw = nw - 1;  // the rank wave: holds no row data
     lds_barrier();  // histograms complete
-
-    // 3. rows of the block's entries (lane j = entry g0 + j), in every wave,
-    //    before the coding: their LDS reads then overlap the row's HBM load
-    const int my_row = entry_row<KMAX * kTPB>(s_cnt, E, KB, lane, my_id);
-    if (!PE && MODE != 2)
-        cd = code_row<MODE>(a, L, xa, xb, 0u);
-    if (!PE && MODE == 2) {
+    if (!PE && MODE != 2 && w != rw)
+        cd = code_row<MODE>(a, t, has, xa, xb, 0u);
+    if (!PE && MODE == 2 && w != rw) {
         uint32_t amax = 0;
-        for (int j = tk * rw; j < (tk + 1) * rw; ++j)  // the token's waves
+        for (int j = 0; j < nw; ++j)
             amax = max(amax, s_wmax[j]);
-        cd = code_row<MODE>(a, L, xa, xb, amax);
+        cd = code_row<MODE>(a, t, has, xa, xb, amax);
     }
-    if (w == 0 && mine) {
-        a.assist_dst[g0 + lane] = my_row;
-        if (my_row >= 0)
-            a.expand_src[my_row] = g0 + lane;
+
+    // 3. rows of the token's entries (the rank wave, lane k = entry k).  Only
+    //    these K offsets are needed, so that wave alone scans: lane c sums the low halves
+    //    of counters [c*per, (c+1)*per), a wave scan gives each chunk's
+    //    exclusive prefix, and lane k takes its chunk's prefix by a lane
+    //    shuffle plus the counters before its id inside the chunk.
+    if (w == rw) {
+        const int per = (E + kWave - 1) / kWave;
+        const int c0 = min(lane * per, E), c1 = min(c0 + per, E);
+        int local = 0;
+        for (int e = c0; e < c1; ++e)
+            local += s_cnt[e] & 0xffff;
+        const int excl = wave_incl_scan(local) - local;
+        const int id = my_on ? my_id : 0;
+        const int chunk = id / per;
+        int off = __shfl(excl, chunk);
+        for (int e = chunk * per; e < id; ++e)
+            off += s_cnt[e] & 0xffff;
+        int dup = 0;  // earlier entries of this token with the same id
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int v = j < K ? __builtin_amdgcn_readlane(my_id, j) : -1;
+            dup += (j < lane && v == my_id) ? 1 : 0;
+        }
+        if (lane < K) {
+            const int r = my_on ? off + (s_cnt[id] >> 16) + dup : -1;
+            s_rank[lane] = r;
+            a.assist_dst[f0 + lane] = r;
+            if (r >= 0)
+                a.expand_src[r] = f0 + lane;
+        }
     }
-    int rank[KMAX];  // rows of this wave's token's entries
+    lds_barrier();  // rows published
+    int rank[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-        rank[k] = k < K ? __builtin_amdgcn_readlane(my_row, tk * K + k) : -1;
+        rank[k] = k < K ? s_rank[k] : -1;
 
     if constexpr (PE) {
         int eid[KMAX];  // instance of each copy
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-            eid[k] = k < K ? __builtin_amdgcn_readlane(my_id, tk * K + k) : -1;
-        code_store_rows<MODE, KMAX>(a, tr, w, tk * rw, rw, L, xa, xb, rank, eid, s_pmax);
+            eid[k] = k < K ? __builtin_amdgcn_readlane(my_id, k) : -1;
+        code_store_rows<MODE, KMAX>(a, t, has, xa, xb, rank, eid, s_pmax);
     } else {
-        store_row<MODE, KMAX>(a, tr, L, xa, xb, cd, rank);
+        store_row<MODE, KMAX>(a, t, has, xa, xb, cd, rank);
     }
 }
 
 // routed entries (moe_dispatch); PE: one scales row per instance
 template <int MODE, int KMAX, bool PE>
-__global__ __launch_bounds__(kMaxThreads * tokens_per_block<PE>()) void k_dispatch(DispatchArgs a)
+__global__ __launch_bounds__(kMaxThreads + kWave) void k_dispatch(DispatchArgs a)
 {
     dispatch_body<MODE, KMAX, Routed, PE>(a);
 }
 
 // mapped entries (moe_update_dispatch); KEEP: a token mask or thresholds
 template <int MODE, int KMAX, bool KEEP, bool PE>
-__global__ __launch_bounds__(kMaxThreads * tokens_per_block<PE>()) void k_update_dispatch(DispatchArgs a)
+__global__ __launch_bounds__(kMaxThreads + kWave) void k_update_dispatch(DispatchArgs a)
 {
     dispatch_body<MODE, KMAX, Mapped<KEEP>, PE>(a);
 }
@@ -1055,8 +903,7 @@ __global__ __launch_bounds__(kMaxThreads * tokens_per_block<PE>()) void k_update
 template <int MODE, int KMAX, typename Src, bool PE>
 void launch_kernel(const DispatchArgs &a, hipStream_t stream)
 {
-    constexpr int kTPB = tokens_per_block<PE>();
-    const dim3 grid(1 + (a.Bs + kTPB - 1) / kTPB), block(row_threads(a.H) * kTPB);
+    const dim3 grid(a.Bs + 1), block(row_threads(a.H) + kWave);
     if constexpr (Src::kMapped)
         hipLaunchKernelGGL((k_update_dispatch<MODE, KMAX, Src::kKeep, PE>), grid, block,
                            (size_t)a.n_logical * a.F * sizeof(int), stream, a);

@@ -42,6 +42,8 @@ def lib():
         L.oracle_combine_add_rmsnorm.argtypes = [P, P, P, P, P, P, C.c_float, i, i, i, i,
                                                  P, P, P]
         L.oracle_e4m3_decode.argtypes = [P, i, P]
+        L.oracle_set_threads.argtypes = [i]
+        L.oracle_set_threads.restype = i
         L.oracle_expert_gemm_mx.argtypes = [P, P, P, i, i, P, P, i, i, P, P, P]
         L.oracle_expert_gemm_i8.argtypes = [P, P, i, P, i, i, P, P, i, i, P, P, P]
         for f in (L.oracle_update_expert, L.oracle_route, L.oracle_dispatch,
@@ -50,6 +52,12 @@ def lib():
             f.restype = C.c_int
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> int:
+    """Threads of the per-token loops (dispatch quantise-and-copy, combine);
+    n <= 0 means every core.  Returns the count in effect."""
+    return int(lib().oracle_set_threads(n))
 
 
 def _p(a: Optional[np.ndarray]):

@@ -2,7 +2,7 @@
 
 Test infrastructure only: the oracle is the checker, never part of the
 product path.  Flags keep IEEE fp32/fp64 semantics: no fast-math, no
-fused multiply-add contraction.
+fused multiply-add contraction; OpenMP runs the per-token loops on threads.
 """
 from __future__ import annotations
 
@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libmoe_oracle.so")
 
 def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
     tmp = lib + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+    cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
            "-shared", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))

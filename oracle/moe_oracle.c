@@ -67,11 +67,25 @@
  *
  * Parity pins: every exported function is pinned by CPU tests against brute
  * force, library routines, closed forms and invariants (tests/test_oracle_*.py).
+ *
+ * Threads: the per-token loops of the quantise-and-copy step and of the
+ * combine run their tokens on OpenMP threads (each token's arithmetic is
+ * unchanged and touches only its own rows); the routing (histogram, scan,
+ * stable rank) stays sequential.  oracle_set_threads picks the count.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads for the per-token loops (n <= 0: all available); returns the count
+ * now in effect. */
+int oracle_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+    return omp_get_max_threads();
+}
 
 enum { ORC_ERR_ID = 1, ORC_ERR_TABLE = 2, ORC_ERR_MASK1D = 4 };
 
@@ -378,48 +392,54 @@ int oracle_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, 
     else if (quant_mode == 4)
         n_sc = H / 32;
 
-    int8_t *q = (int8_t *)malloc((size_t)H);
-    float *fs = (float *)malloc((size_t)(n_sc > 0 ? n_sc : 1) * sizeof(float));
-    uint8_t *bs = (uint8_t *)malloc((size_t)(n_sc > 0 ? n_sc : 1));
-    if (!q || !fs || !bs) {
+    int fail = 0;
+#pragma omp parallel
+    {
+        int8_t *q = (int8_t *)malloc((size_t)H);
+        float *fs = (float *)malloc((size_t)(n_sc > 0 ? n_sc : 1) * sizeof(float));
+        uint8_t *bs = (uint8_t *)malloc((size_t)(n_sc > 0 ? n_sc : 1));
+        if (!q || !fs || !bs) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(static)
+        for (int i = 0; i < Bs; ++i) {
+            if (!q || !fs || !bs)
+                continue;
+            const uint16_t *xi = x + (size_t)i * H;
+            if (quant_mode == 2) {
+                quant_int8_segment(xi, H, q, &fs[0]);
+            } else if (quant_mode == 3) {
+                for (int t = 0; t < n_sc; ++t) {
+                    int n = H - t * tile < tile ? H - t * tile : tile;
+                    quant_int8_segment(xi + (size_t)t * tile, n, q + (size_t)t * tile, &fs[t]);
+                }
+            } else if (quant_mode == 4) {
+                for (int b = 0; b < n_sc; ++b)
+                    quant_mxfp8_block(xi + (size_t)b * 32, 32, (uint8_t *)q + (size_t)b * 32,
+                                      &bs[b]);
+            }
+            for (int k = 0; k < K; ++k) {
+                int r = assist_dst[i * K + k];
+                if (r < 0)
+                    continue;
+                if (quant_mode == 0) {
+                    memcpy((uint16_t *)expand_x + (size_t)r * H, xi, (size_t)H * sizeof(uint16_t));
+                } else {
+                    memcpy((int8_t *)expand_x + (size_t)r * H, q, (size_t)H);
+                    if (quant_mode == 4)
+                        memcpy((uint8_t *)expand_scales + (size_t)r * n_sc, bs, (size_t)n_sc);
+                    else
+                        memcpy((float *)expand_scales + (size_t)r * n_sc, fs,
+                               (size_t)n_sc * sizeof(float));
+                }
+            }
+        }
         free(q);
         free(fs);
         free(bs);
-        return -2;
     }
-    for (int i = 0; i < Bs; ++i) {
-        const uint16_t *xi = x + (size_t)i * H;
-        if (quant_mode == 2) {
-            quant_int8_segment(xi, H, q, &fs[0]);
-        } else if (quant_mode == 3) {
-            for (int t = 0; t < n_sc; ++t) {
-                int n = H - t * tile < tile ? H - t * tile : tile;
-                quant_int8_segment(xi + (size_t)t * tile, n, q + (size_t)t * tile, &fs[t]);
-            }
-        } else if (quant_mode == 4) {
-            for (int b = 0; b < n_sc; ++b)
-                quant_mxfp8_block(xi + (size_t)b * 32, 32, (uint8_t *)q + (size_t)b * 32, &bs[b]);
-        }
-        for (int k = 0; k < K; ++k) {
-            int r = assist_dst[i * K + k];
-            if (r < 0)
-                continue;
-            if (quant_mode == 0) {
-                memcpy((uint16_t *)expand_x + (size_t)r * H, xi, (size_t)H * sizeof(uint16_t));
-            } else {
-                memcpy((int8_t *)expand_x + (size_t)r * H, q, (size_t)H);
-                if (quant_mode == 4)
-                    memcpy((uint8_t *)expand_scales + (size_t)r * n_sc, bs, (size_t)n_sc);
-                else
-                    memcpy((float *)expand_scales + (size_t)r * n_sc, fs,
-                           (size_t)n_sc * sizeof(float));
-            }
-        }
-    }
-    free(q);
-    free(fs);
-    free(bs);
-    return 0;
+    return fail ? -2 : 0;
 }
 
 /* [DSP] cases 2-4 with the scales input: xFp32 = CastToFp32(X) * scales, then
@@ -504,44 +524,54 @@ int oracle_combine_add_rmsnorm(const uint16_t *expert_out, const int32_t *assist
 {
     if (Bs <= 0 || H <= 0 || K <= 0 || (shared_mode != 0 && shared_mode != 1))
         return -1;
-    double *xf = (double *)malloc((size_t)H * sizeof(double));
-    if (!xf)
-        return -2;
-    for (int i = 0; i < Bs; ++i) {
-        double ws = 0.0;
-        for (int h = 0; h < H; ++h)
-            xf[h] = 0.0;
-        for (int k = 0; k < K; ++k) {
-            int r = assist[i * K + k];
-            if (r < 0)
+    int fail = 0;
+#pragma omp parallel
+    {
+        double *xf = (double *)malloc((size_t)H * sizeof(double));
+        if (!xf) {
+#pragma omp atomic write
+            fail = 1;
+        }
+#pragma omp for schedule(static)
+        for (int i = 0; i < Bs; ++i) {
+            if (!xf)
                 continue;
-            double s = scales[i * K + k];
-            ws += s;
-            const uint16_t *row = expert_out + (size_t)r * H;
+            double ws = 0.0;
             for (int h = 0; h < H; ++h)
-                xf[h] += s * (double)bf16_value(row[h]);
+                xf[h] = 0.0;
+            for (int k = 0; k < K; ++k) {
+                int r = assist[i * K + k];
+                if (r < 0)
+                    continue;
+                double s = scales[i * K + k];
+                ws += s;
+                const uint16_t *row = expert_out + (size_t)r * H;
+                for (int h = 0; h < H; ++h)
+                    xf[h] += s * (double)bf16_value(row[h]);
+            }
+            if (shared) {
+                double w = shared_mode == 0 ? ws : 1.0;
+                for (int h = 0; h < H; ++h)
+                    xf[h] += w * (double)bf16_value(shared[(size_t)i * H + h]);
+            }
+            double ss = 0.0;
+            for (int h = 0; h < H; ++h) {
+                xf[h] += (double)bf16_value(residual[(size_t)i * H + h]);
+                ss += xf[h] * xf[h];
+            }
+            double rstd = 1.0 / sqrt(ss / H + (double)eps);
+            for (int h = 0; h < H; ++h) {
+                if (x_out)
+                    x_out[(size_t)i * H + h] = bf16_from_double(xf[h]);
+                y[(size_t)i * H + h] =
+                    bf16_from_double(xf[h] * rstd * (double)bf16_value(gamma[h]));
+            }
+            if (rstd_out)
+                rstd_out[i] = (float)rstd;
         }
-        if (shared) {
-            double w = shared_mode == 0 ? ws : 1.0;
-            for (int h = 0; h < H; ++h)
-                xf[h] += w * (double)bf16_value(shared[(size_t)i * H + h]);
-        }
-        double ss = 0.0;
-        for (int h = 0; h < H; ++h) {
-            xf[h] += (double)bf16_value(residual[(size_t)i * H + h]);
-            ss += xf[h] * xf[h];
-        }
-        double rstd = 1.0 / sqrt(ss / H + (double)eps);
-        for (int h = 0; h < H; ++h) {
-            if (x_out)
-                x_out[(size_t)i * H + h] = bf16_from_double(xf[h]);
-            y[(size_t)i * H + h] = bf16_from_double(xf[h] * rstd * (double)bf16_value(gamma[h]));
-        }
-        if (rstd_out)
-            rstd_out[i] = (float)rstd;
+        free(xf);
     }
-    free(xf);
-    return 0;
+    return fail ? -2 : 0;
 }
 
 /* ---------------------------------------------------------------- expert GEMM */

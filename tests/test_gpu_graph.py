@@ -1,10 +1,12 @@
-"""A chained stack of c5-shaped layers (update -> dispatch -> combine per
-layer; layer l + 1 reads y_l as x and x_out_l as residual) captured in one
-HIP graph.  Every replay must reproduce the eager pass bit for bit: the
-outputs are poisoned before each replay, other GPU work and host
-synchronisation run between replays, and several replays are checked.  The
-first two layers are also checked against the oracle, layer 1 fed with the
-GPU's layer-0 outputs.
+"""The c5 stack at its full depth: 16 chained c3-shaped layers (per layer
+the mapping fused into the dispatch, int8 per token, then the combine; layer
+l + 1 reads y_l as x and x_out_l as residual) captured in one HIP graph.
+Every layer is checked against the oracle -- mapped ids, routing, codes and
+scales bit for bit, y / x_out / rstd within tolerance -- with the oracle fed
+the GPU's outputs of the layer before.  Every replay must reproduce the eager
+pass bit for bit: the outputs are poisoned before each replay, other GPU work
+and host synchronisation run between replays, and several replays are
+checked.
 """
 import numpy as np
 import pytest
@@ -17,7 +19,7 @@ from tests.gpu_common import M, check_combine, np_, oracle_combine, say
 
 pytestmark = pytest.mark.gpu
 
-N_LAYERS = 4
+N_LAYERS = 16  # the c5 workload's depth
 KEYS = ("y", "x_out", "rstd")
 DKEYS = ("expand_x", "expand_scales", "expert_offsets", "assist_dst", "expand_src")
 
@@ -57,7 +59,8 @@ def test_stack_eager_against_oracle(stack):
     torch.cuda.synchronize()
     x_bits = oracle.bf16_bits(wls[0].x)
     res = wls[0].residual
-    for l in range(2):
+    for l in range(N_LAYERS):
+        say(f"[graph] layer {l}")
         wl, s = wls[l], st["layers"][l]
         oi, om, _ = oracle.update_expert(wl.logical_ids.numpy(), None, wl.table.numpy(), None,
                                          None, wl.E)
@@ -66,8 +69,12 @@ def test_stack_eager_against_oracle(stack):
                              wl.tile)
         np.testing.assert_array_equal(np_(s["d"]["assist_dst"]), od["assist"])
         total = int(od["offsets"][-1])
+        np.testing.assert_array_equal(np_(s["d"]["expert_offsets"]), od["offsets"])
+        np.testing.assert_array_equal(np_(s["d"]["expand_src"]), od["src"])
         gx = s["d"]["expand_x"].view(torch.uint8).cpu().numpy()[:total]
         np.testing.assert_array_equal(gx, od["expand_x"].view(np.uint8)[:total])
+        gs = s["d"]["expand_scales"].cpu().numpy()[:total].reshape(-1).view(np.uint32)
+        np.testing.assert_array_equal(gs, od["scales"][:total].reshape(-1).view(np.uint32))
         o = oracle_combine(wl, od["assist"], wl.expert_out, residual=res)
         check_combine((s["y"], s["x_out"], s["rstd"]), o)
         # the next layer reads this layer's GPU outputs

@@ -53,8 +53,8 @@ MUTANTS = [
     ("smoothing_dropped", "v[j] = qscales_kind == 0 ? bf16_value(xi[j]) : bf16_value(xi[j]) * s;",
      "v[j] = bf16_value(xi[j]);"),
     ("static_row_index", "s = qscales[j];", "s = qscales[H - 1 - j];"),
-    ("pruned_weight_counted", "int r = assist[i * K + k];\n            if (r < 0)\n                continue;\n            double s = scales[i * K + k];\n            ws += s;",
-     "int r = assist[i * K + k];\n            double s = scales[i * K + k];\n            ws += s;\n            if (r < 0)\n                continue;"),
+    ("pruned_weight_counted", "int r = assist[i * K + k];\n                if (r < 0)\n                    continue;\n                double s = scales[i * K + k];\n                ws += s;",
+     "int r = assist[i * K + k];\n                double s = scales[i * K + k];\n                ws += s;\n                if (r < 0)\n                    continue;"),
     ("e4m3_decode_bias", "v = ldexp(8.0 + m, ef - 10);", "v = ldexp(8.0 + m, ef - 9);"),
     ("e4m3_decode_subnormal", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     ("e8m0_bias", "ldexp(1.0, (int)c - 127)", "ldexp(1.0, (int)c - 128)"),
