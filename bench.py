@@ -32,14 +32,13 @@ shape with its arithmetic taken out).  --headline-only leaves them out.
 
 Prints one JSON line.  `value` is whole-step throughput in GB/s of
 algorithmic bytes (each input read once, each output written once) with all
-inputs resident in HBM; input and output buffers rotate over --sets copies
-(about 125 MB each) so that the 256 MB Infinity Cache cannot serve a step from
-the previous use of its buffers.  The combine kernel dominates the step; its
-per-launch duration is taken with HIP events on the stream it runs on,
-bracketing a run of back-to-back launches over the rotating
-buffer sets (events between the kernels of a step would add their own
-packets to the step).  The CPU oracle runs the same step on the host cores as
-a reference point.
+inputs resident in HBM: every timed loop rotates over enough buffer sets
+(about 4 GB of its own traffic; COLD_BYTES) that the 256 MB Infinity Cache
+serves little of it.  Per-kernel durations are taken with HIP events on the
+stream the kernels run on, bracketing a run of back-to-back launches over the
+rotating sets (events between the kernels of a step would add their own
+packets to the step).  The CPU oracle runs the same step on the host cores,
+on one core and on all of them, as a reference point.
 """
 from __future__ import annotations
 
@@ -56,6 +55,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "dispatch+combine HBM GB/s (% of peak) and tokens/s, Bs=512 H=7168 K=8"
+# Timed loops rotate over buffer sets covering at least this many bytes of each loop's own
+# traffic.  The 256 MB Infinity Cache does not replace least-recently-used lines only:
+# with 440 MB of rotating sets it still served part of each launch (the c3 combine ran
+# 3 us faster than its cold time); past about 2-4 GB the times stop falling.
+COLD_BYTES = 4 << 30
+
+
+def cold_sets(set_bytes, lo=2, hi=96):
+    """Buffer sets a timed loop rotates over: COLD_BYTES of traffic in all."""
+    return max(lo, min(hi, -(-COLD_BYTES // max(1, set_bytes))))
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -65,7 +74,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--sets", type=int, default=5, help="rotating buffer sets")
+    p.add_argument("--sets", type=int, default=0,
+                   help="rotating buffer sets of the headline step (0: enough for about "
+                        "4 GB of traffic per kernel loop, so the Infinity Cache serves little)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="time budget of the CPU oracle baseline (0 = skip)")
     p.add_argument("--no-check", action="store_true", help="skip the parity check of step 0")
@@ -295,7 +306,7 @@ def step_args(wl, s, stream):
     n_logical, F = wl.table.shape
     upd = (p(s["ids"]), None, p(s["table"]), None, None, wl.Bs, wl.K, n_logical, F, wl.E,
            p(s["bal_ids"]), p(s["bal_mask"]), None, stream)
-    dsp = (p(s["x"]), p(s["bal_ids"]), p(s["bal_mask"]), wl.Bs, wl.H, wl.K, wl.n_ranks,
+    dsp = (p(s["x"]), p(s["bal_ids"]), p(s["bal_mask"]), None, wl.Bs, wl.H, wl.K, wl.n_ranks,
            wl.local_experts, wl.quant_mode, wl.tile, None, 0, p(d["expand_x"]),
            p(d["expand_scales"]),
            p(d["expert_counts"]), p(d["expert_offsets"]), p(d["expand_src"]),
@@ -449,7 +460,8 @@ def dispatch_variants(moe, torch, n, sets=5):
         stream = torch.cuda.current_stream()
         f = moe.raw().moe_dispatch
         p = lambda t: None if t is None else t.data_ptr()
-        argv = [(p(x), p(ids), None, wl.Bs, wl.H, wl.K, wl.n_ranks, wl.local_experts, mode, tile,
+        argv = [(p(x), p(ids), None, None, wl.Bs, wl.H, wl.K, wl.n_ranks, wl.local_experts, mode,
+                 tile,
                  p(qs), kind, p(d["expand_x"]), p(d["expand_scales"]), p(d["expert_counts"]),
                  p(d["expert_offsets"]), p(d["expand_src"]), p(d["assist_dst"]), None,
                  stream.cuda_stream) for x, d in bufs]
@@ -473,7 +485,7 @@ def dispatch_variants(moe, torch, n, sets=5):
 
 # ----------------------------------------------------------------- other configs
 
-def config_table(moe, torch, n, sets=3):
+def config_table(moe, torch, n):
     """Per-launch durations (HIP events around n back-to-back launches over
     rotating buffer sets) of the three calls and the fused call on the other
     workloads at full size, with their algorithmic bytes."""
@@ -484,6 +496,9 @@ def config_table(moe, torch, n, sets=3):
         if wl.expert_out is None:  # the identity + bias expert: any bf16 rows serve for timing
             wl.expert_out = torch.randn(wl.Bs * wl.K, wl.H).bfloat16()
         stream = torch.cuda.current_stream()
+        # the dispatch is the smallest loop: rotate enough sets for its traffic
+        est = wl.Bs * wl.H * 2 + wl.Bs * wl.K * wl.H
+        sets = cold_sets(est, hi=64)
         bufs = [make_set(wl, torch, moe) for _ in range(sets)]
         prune = wl.prune_thr is not None
         dev = torch.device("cuda")
@@ -523,6 +538,7 @@ def config_table(moe, torch, n, sets=3):
         keys = ("update_expert", "dispatch", "update_dispatch", "combine")
         rows.append({"config": name, "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E,
                      "quant_mode": wl.quant_mode, "rows_dispatched": nrows,
+                     "buffer_sets": sets,
                      **{k: {"avg_us": round(u, 3), "bytes": nb[k],
                             "GBps": round(nb[k] / (u * 1e-6) / 1e9, 1),
                             "frac": round(nb[k] / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -571,15 +587,17 @@ def ceilings(torch, n, wl, step_set, nb, rows):
                      "frac": round((rbytes + wbytes) / us / 1e3 / HBM_PEAK_GBS, 4)}
         del src, dst
 
-    stream_case("copy_256MB", 256 << 20, 256 << 20, 2)
+    stream_case("copy_256MB", 256 << 20, 256 << 20, cold_sets(512 << 20))
     cr = nb["combine"] - 2 * wl.Bs * wl.H * 2 - wl.Bs * 4
-    stream_case("stream_combine_mix", cr // 16 * 16, (nb["combine"] - cr) // 16 * 16, 8)
+    stream_case("stream_combine_mix", cr // 16 * 16, (nb["combine"] - cr) // 16 * 16,
+                cold_sets(nb["combine"]))
     dr = wl.Bs * wl.H * 2 + wl.Bs * wl.K * 5
-    stream_case("stream_dispatch_mix", dr // 16 * 16, (nb["dispatch"] - dr) // 16 * 16, 8)
+    stream_case("stream_dispatch_mix", dr // 16 * 16, (nb["dispatch"] - dr) // 16 * 16,
+                cold_sets(nb["dispatch"]))
 
     # the kernels' access shapes on the headline's routing (c3)
     assist = step_set["d"]["assist_dst"]
-    nsets = 6
+    nsets = cold_sets(nb["dispatch"], hi=64)
     Bs, H, K = wl.Bs, wl.H, wl.K
     xs = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
     outs = [torch.empty((rows, H), dtype=torch.uint8, device=dev) for _ in range(nsets)]
@@ -592,6 +610,7 @@ def ceilings(torch, n, wl, step_set, nb, rows):
                              "what": "block per token: its row read, one byte per element "
                                      "written to each of its K rows (no routing, no coding)"}
     del xs, outs
+    nsets = cold_sets(nb["combine"], hi=64)
     eo = [torch.empty((rows, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
     aa = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
     bb = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
@@ -920,7 +939,8 @@ def main():
     UPD, DSP, FUSED, CMB = range(4)
     STEP, THREE = (FUSED, CMB), (UPD, DSP, CMB)
 
-    sets = [make_set(wl, torch, moe) for _ in range(args.sets)]
+    n_sets = args.sets or cold_sets(min(38 << 20, 126 << 20))  # the dispatch's own traffic
+    sets = [make_set(wl, torch, moe) for _ in range(n_sets)]
     argv = [step_args(wl, s, sp) for s in sets]
     torch.cuda.synchronize()
 
@@ -1030,7 +1050,7 @@ def main():
                                "1 shared expert, combine + residual + RMSNorm (bf16 in/out)",
                    "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E, "quant": "mxfp8",
                    "arithmetic": "bf16 rows in and out, mxfp8 (E4M3 + E8M0) codes, fp32 sums",
-                   "rows_dispatched": rows, "buffer_sets": args.sets},
+                   "rows_dispatched": rows, "buffer_sets": n_sets},
         "tokens_per_s": round(wl.Bs / t_step, 1),
         "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "roofline": {

@@ -142,7 +142,8 @@ int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int 
 
 extern "C" {
 
-int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask, int Bs,
+int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask,
+                 const uint8_t *token_mask, int Bs,
                  int H, int K, int n_ranks, int local_experts, int quant_mode, int tile,
                  const float *quant_scales, int quant_scales_kind, void *expand_x,
                  void *expand_scales, int32_t *expert_counts, int32_t *expert_offsets,
@@ -156,7 +157,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active
     if (active_mask && !aligned(active_mask, 4))
         return MOE_EINVAL;
     return from_hip(moe::launch_dispatch(
-        static_cast<const uint16_t *>(x), expert_ids, active_mask, Bs, H, K,
+        static_cast<const uint16_t *>(x), expert_ids, active_mask, token_mask, Bs, H, K,
         n_ranks * local_experts, quant_mode, quant_mode == MOE_Q_INT8_TILE ? tile : 0,
         quant_scales, quant_scales_kind, expand_x, expand_scales, expert_counts, expert_offsets,
         expand_src, assist_dst, dev_err, static_cast<hipStream_t>(stream)));
@@ -199,7 +200,7 @@ int moe_update_dispatch(const void *x, const int32_t *expert_ids, const float *e
         if (e != hipSuccess)
             return from_hip(e);
         return from_hip(moe::launch_dispatch(
-            static_cast<const uint16_t *>(x), balanced_ids, balanced_mask, Bs, H, K,
+            static_cast<const uint16_t *>(x), balanced_ids, balanced_mask, nullptr, Bs, H, K,
             n_ranks * local_experts, quant_mode, quant_mode == MOE_Q_INT8_TILE ? tile : 0,
             quant_scales, quant_scales_kind, expand_x, expand_scales, expert_counts,
             expert_offsets, expand_src, assist_dst, dev_err, static_cast<hipStream_t>(stream)));

@@ -60,8 +60,9 @@ static hipError_t launch_any(int quant_mode, const DispatchArgs &a, int src, hip
     }
 }
 
-hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
-                           int H, int K, int E, int quant_mode, int tile, const float *qs,
+hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask,
+                           const uint8_t *token_mask, int Bs, int H, int K, int E,
+                           int quant_mode, int tile, const float *qs,
                            int qs_kind, void *expand_x, void *expand_scales, int32_t *counts,
                            int32_t *offsets, int32_t *expand_src, int32_t *assist_dst,
                            int32_t *dev_err, hipStream_t stream)
@@ -70,6 +71,7 @@ hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t 
     a.x = x;
     a.ids = ids;
     a.mask = mask;
+    a.token_mask = token_mask;
     a.Bs = Bs;
     a.H = H;
     a.K = K;

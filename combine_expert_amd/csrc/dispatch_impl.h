@@ -56,16 +56,20 @@ __device__ __forceinline__ int replica_slot(int head, int i)
 // per-group side word (mask bytes or scores) and turn each entry into
 // (instance id or -1, active), raising device error bits.
 
-// Routed: instance ids and an optional [Bs, K] mask.  Ids outside [0, E) of
-// active entries raise bit 1.
+// Routed: instance ids, an optional [Bs, K] mask and an optional [Bs] token
+// mask (staged in LDS; an entry is active only if both allow it).  Ids
+// outside [0, E) of active entries raise bit 1.
 struct Routed {
     static constexpr bool kMapped = false;
     static constexpr bool kKeep = false;
     using Side = uint32_t;
     const int32_t *ids;
     const uint8_t *mask;  // null: every entry is active
-    int E;
+    const uint8_t *tok;   // LDS [Bs], or null: every token is active
+    int E, K;
+    unsigned mK;          // ceil(2^17 / K): g / K = (g * mK) >> 17 for g < 8192
 
+    __device__ int token_of(int g) const { return (int)(__umul24((unsigned)g, mK) >> 17); }
     __device__ Side side4(int g4) const
     {
         return mask ? reinterpret_cast<const uint32_t *>(mask)[g4] : 0x01010101u;
@@ -75,6 +79,18 @@ struct Routed {
     __device__ void group(const int4 &v, Side m, int g4, bool in, int &err, Fn &&f) const
     {
         const int idv[4] = {v.x, v.y, v.z, v.w};
+        if (tok) {  // clear the mask bytes of entries whose token is off
+            const int g0 = in ? g4 * 4 : 0;
+            uint32_t keep = 0;
+            if ((K & 3) == 0) {
+                keep = tok[token_of(g0)] ? 0xffffffffu : 0u;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    keep |= tok[token_of(g0 + j)] ? 0xffu << (8 * j) : 0u;
+            }
+            m &= keep;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bool act = in && ((m >> (8 * j)) & 0xffu) != 0;
@@ -87,7 +103,7 @@ struct Routed {
     __device__ int entry1(int g, bool &on, int &err) const
     {
         const int id = ids[g];
-        const bool act = mask == nullptr || mask[g] != 0;
+        const bool act = (mask == nullptr || mask[g] != 0) && (tok == nullptr || tok[g / K] != 0);
         const bool ok = (unsigned)id < (unsigned)E;
         err |= act && !ok ? 1 : 0;
         on = act && ok;
@@ -384,7 +400,7 @@ __device__ void route_summary(const DispatchArgs &a, const Src &s, int *s_hist, 
             }
             lds_barrier();
         });
-    if (Src::kKeep) {  // a 1-D token mask is all true, then all false
+    if (Src::kKeep || (!Src::kMapped && a.token_mask)) {  // a 1-D token mask is all true, then all false
         for (int i = 1 + t; i < a.Bs; i += T)
             err |= s_tok[i] && !s_tok[i - 1] ? 4 : 0;
     }
@@ -738,7 +754,7 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
     __shared__ int s_rank[KMAX];
     __shared__ uint32_t s_wmax[kDispatchWaves];
     __shared__ uint32_t s_pmax[PE && MODE == 2 ? kDispatchWaves * KMAX : 1];
-    __shared__ uint8_t s_tok[Src::kMapped ? kMaxTokens : 1];
+    __shared__ uint8_t s_tok[kMaxTokens];
     __shared__ __align__(16) float s_thr[Src::kMapped ? kMaxTopK : 1];
     extern __shared__ int s_tab[];  // mapped: the [n_logical, F] table
 
@@ -749,7 +765,12 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         s = Src{a.ids, a.scores ? a.scores : reinterpret_cast<const float *>(a.ids), s_tab,
                 s_tok, s_thr, a.n_logical, a.F, E, K, (unsigned)(((1 << 17) + K - 1) / K)};
     else
-        s = Routed{a.ids, a.mask, E};
+        s = Routed{a.ids, a.mask, a.token_mask ? s_tok : nullptr, E, K,
+                   (unsigned)(((1 << 17) + K - 1) / K)};
+    if (!Src::kMapped && a.token_mask) {  // staged before the first use (a barrier follows)
+        for (int j = threadIdx.x; j < Bs; j += blockDim.x)
+            s_tok[j] = a.token_mask[j];
+    }
     if (blockIdx.x == 0) {
         route_summary(a, s, s_cnt, s_wave, s_tab, s_tok, s_thr);
         return;
@@ -812,8 +833,9 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         }
         my_id = lane < K && on ? inst : -1;
     } else {
-        const bool my_on =
-            lane < K && (a.mask == nullptr || raw_on != 0) && (unsigned)raw_id < (unsigned)E;
+        const bool my_on = lane < K && (a.mask == nullptr || raw_on != 0) &&
+                           (a.token_mask == nullptr || a.token_mask[i] != 0) &&
+                           (unsigned)raw_id < (unsigned)E;
         my_id = my_on ? raw_id : -1;
     }
     const bool my_on = my_id >= 0;

@@ -12,8 +12,9 @@ hipError_t launch_update_expert(const int32_t *ids, const float *scores, const i
                                 int n_logical, int F, int n_instances, int32_t *out_ids,
                                 uint8_t *out_mask, int32_t *dev_err, hipStream_t stream);
 
-hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
-                           int H, int K, int E, int quant_mode, int tile, const float *qs,
+hipError_t launch_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask,
+                           const uint8_t *token_mask, int Bs, int H, int K, int E,
+                           int quant_mode, int tile, const float *qs,
                            int qs_kind, void *expand_x, void *expand_scales, int32_t *counts,
                            int32_t *offsets, int32_t *expand_src, int32_t *assist_dst,
                            int32_t *dev_err, hipStream_t stream);

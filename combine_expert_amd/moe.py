@@ -31,8 +31,8 @@ if not os.path.exists(_build.LIB):
 _lib = C.CDLL(_build.LIB)
 _P, _I = C.c_void_p, C.c_int
 _lib.moe_update_expert.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
-_lib.moe_dispatch.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P,
-                              _P, _P, _P, _P]
+_lib.moe_dispatch.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P,
+                              _P, _P, _P, _P, _P]
 _lib.moe_update_dispatch.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                                      _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_combine_add_rmsnorm.argtypes = [_P, _P, _P, _P, _P, _P, C.c_float, _I, _I, _I, _I,
@@ -193,7 +193,8 @@ def scales_kind(quant_scales, H: int, E: int) -> int:
 
 def moe_dispatch(x, expert_ids, n_ranks: int, local_experts: int, quant_mode: int = 0,
                  tile: int = 0, active_mask=None, quant_scales=None,
-                 out: Optional[dict] = None, dev_err=None, stream=None) -> dict:
+                 out: Optional[dict] = None, dev_err=None, stream=None,
+                 token_mask=None) -> dict:
     Bs, H = x.shape
     K = expert_ids.shape[1]
     E = n_ranks * local_experts
@@ -201,7 +202,9 @@ def moe_dispatch(x, expert_ids, n_ranks: int, local_experts: int, quant_mode: in
         out = dispatch_buffers(Bs, H, K, E, quant_mode, tile, x.device)
     _dispatch_args(x, expert_ids, Bs, H, K, E, quant_mode, tile, quant_scales, out, dev_err)
     _arg(active_mask, "active_mask", _BYTE_TYPES, Bs * K, required=False)
-    rc = _lib.moe_dispatch(_ptr(x), _ptr(expert_ids), _ptr(active_mask), Bs, H, K, n_ranks,
+    _arg(token_mask, "token_mask", _BYTE_TYPES, Bs, required=False)
+    rc = _lib.moe_dispatch(_ptr(x), _ptr(expert_ids), _ptr(active_mask), _ptr(token_mask), Bs,
+                           H, K, n_ranks,
                            local_experts, quant_mode, tile, _ptr(quant_scales),
                            scales_kind(quant_scales, H, E), _ptr(out["expand_x"]),
                            _ptr(out.get("expand_scales")), _ptr(out["expert_counts"]),

@@ -124,8 +124,12 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  * [rank][local expert][token] as the all-to-all delivers them).
  *
  * E = n_ranks * local_experts instances; N = Bs*K entries f = i*K + k.
- * Entry f is active if active_mask is NULL or active_mask[f] != 0, and its
- * id is in [0, E) (else MOE_ERR_ID and it is dropped).
+ * Entry f is active if active_mask is NULL or active_mask[f] != 0, and
+ * token_mask is NULL or token_mask[i] != 0, and its id is in [0, E) (else
+ * MOE_ERR_ID and it is dropped).  The two masks are the 2-D (Bs, K) and 1-D
+ * (Bs,) forms of the page's active mask (参数说明 of the dispatch page); a
+ * 1-D mask must be all true, then all false: otherwise MOE_ERR_MASK1D is set
+ * and the mask is applied as given.
  *   expert_counts[e]  = number of active entries with id e
  *   expert_offsets    = exclusive prefix sum of counts; offsets[E] = rows written
  *   assist_dst[f]     = row of entry f: offsets[id] + number of active g < f
@@ -153,6 +157,7 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *   x              bf16 [Bs, H]
  *   expert_ids     int32 [Bs, K]     instance ids (e.g. balanced_ids)
  *   active_mask    u8 [Bs, K] or NULL (e.g. balanced_mask)
+ *   token_mask     u8 [Bs] or NULL
  *   quant_scales   f32, shape by quant_scales_kind (16-byte aligned for ROW and
  *                  EXPERT), or NULL with MOE_SCALES_NONE.  MOE_Q_STATIC takes
  *                  ONE, ROW or EXPERT; MOE_Q_INT8_TOKEN / _TILE take NONE or
@@ -166,7 +171,8 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *         H % 32 == 0, n_ranks >= 1, local_experts >= 1.
  */
 int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active_mask,
-                 int Bs, int H, int K, int n_ranks, int local_experts, int quant_mode,
+                 const uint8_t *token_mask, int Bs, int H, int K, int n_ranks,
+                 int local_experts, int quant_mode,
                  int tile, const float *quant_scales, int quant_scales_kind, void *expand_x,
                  void *expand_scales, int32_t *expert_counts, int32_t *expert_offsets,
                  int32_t *expand_src, int32_t *assist_dst, int32_t *dev_err, void *stream);

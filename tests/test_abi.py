@@ -63,7 +63,8 @@ def dispatch(**kw):
     a = dict(x=P, ids=P, mask=None, Bs=512, H=7168, K=8, R=32, L=8, q=4, tile=0, qs=None, qk=0,
              ex=P, sc=P, cnt=P, off=P, src=P, asg=P, err=None)
     a.update(kw)
-    return moe.raw().moe_dispatch(a["x"], a["ids"], a["mask"], a["Bs"], a["H"], a["K"], a["R"],
+    return moe.raw().moe_dispatch(a["x"], a["ids"], a["mask"], None, a["Bs"], a["H"], a["K"],
+                                  a["R"],
                                   a["L"], a["q"], a["tile"], a["qs"], a["qk"], a["ex"], a["sc"],
                                   a["cnt"], a["off"], a["src"], a["asg"], a["err"], None)
 
