@@ -85,6 +85,9 @@ def parse():
                         "graph replay or ceilings): the command kernel traces are taken on")
     p.add_argument("--hot", action="store_true",
                    help="also time each kernel on one reused buffer set (hot Infinity Cache)")
+    p.add_argument("--only-config", metavar="NAME", choices=("c1", "c2", "c4", "c4b"),
+                   help="time one other workload's kernels only (its own JSON line): the "
+                        "command its counter passes are taken on")
     p.add_argument("--variants", action="store_true",
                    help="also time the dispatch variants (static and per-instance scales)")
     p.add_argument("--gemm", action="store_true",
@@ -103,6 +106,8 @@ def parse():
                    help="kernel_stats.csv of a --kernel-trace --stats run")
     g.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="counter_collection.csv of a FETCH_SIZE run and of a WRITE_SIZE run")
+    g.add_argument("--summarize-stalls", nargs="+", metavar="PMC_CSV",
+                   help="per-dispatch counter means of --kernel over the given counter CSVs")
     g.add_argument("--summarize-copy", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="the same for the --copy-mb kernel: derives the counter scales")
     g.add_argument("--headline-of", metavar="BENCH_JSON",
@@ -119,26 +124,24 @@ def parse():
 
 
 def copy_calibration(mb, steps, warmup):
-    """Plain bf16 device-to-device copy of a known size: read mb MB, write mb MB."""
+    """A plain streaming copy of known size (libmoe_calib.so's stream kernel,
+    non-temporal loads and stores): read mb MB, write mb MB, buffers rotating
+    through COLD_BYTES.  The counter runs of this command calibrate the
+    FETCH_SIZE / WRITE_SIZE scales."""
     import torch
-    n = mb * (1 << 20) // 2
-    nset = max(2, -(-1024 // (2 * mb)))  # rotate so the set pair exceeds the Infinity Cache
-    src = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(nset)]
-    dst = [torch.empty_like(s) for s in src]
+    from combine_expert_amd import calib
+    n = mb << 20
+    nset = cold_sets(2 * n)
+    src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7) for _ in range(nset)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(nset)]
     for k in range(warmup):
-        dst[k % nset].copy_(src[k % nset])
+        calib.stream(src[k % nset], n, dst[k % nset], n)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
-    for k in range(steps):
-        ev[2 * k].record()
-        dst[k % nset].copy_(src[k % nset])
-        ev[2 * k + 1].record()
-    torch.cuda.synchronize()
-    t = statistics.mean(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(steps)) * 1e-3
-    nbytes = 2 * n * 2
-    print(json.dumps({"copy_mb": mb, "bytes_per_launch": nbytes, "read_bytes": n * 2,
-                      "write_bytes": n * 2, "avg_us": round(t * 1e6, 3),
-                      "GBps": round(nbytes / t / 1e9, 1)}), flush=True)
+    us = _events_us(torch, lambda k: calib.stream(src[k % nset], n, dst[k % nset], n), steps, 0)
+    print(json.dumps({"copy_mb": mb, "kernel": "k_stream (libmoe_calib.so, non-temporal)",
+                      "bytes_per_launch": 2 * n, "read_bytes": n, "write_bytes": n,
+                      "avg_us": round(us, 3), "GBps": round(2 * n / us / 1e3, 1),
+                      "buffer_sets": nset}), flush=True)
 
 
 # ----------------------------------------------------------------- bytes
@@ -266,12 +269,65 @@ def summarize_counters(args):
         f.write("\n")
 
 
+STALL_RATIOS = [
+    # (name, numerator, denominator, scale, unit)
+    ("shader clock", "GRBM_GUI_ACTIVE", "_duration_8", 1e-3, "GHz"),
+    ("waves waiting on anything / wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", 1.0, ""),
+    ("waves waiting to issue / wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", 1.0, ""),
+    ("LDS waits / all waits", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", 1.0, ""),
+    ("vector-memory instruction issue / busy CU cycles", "SQ_ACTIVE_INST_VMEM", "SQ_BUSY_CU_CYCLES", 1.0, ""),
+    ("L2 hit rate", "TCC_HIT_sum", "_tcc_req", 1.0, ""),
+    ("mean L2 read latency seen by the vector cache", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", 1.0, "cycles"),
+    ("vector cache stalled on pending requests / cycles", "TCP_PENDING_STALL_CYCLES_sum", "_tcp_cycles", 1.0, ""),
+    ("address unit stalled by the vector cache / TA busy", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA_BUSY_sum_est", 1.0, ""),
+]
+
+
+def summarize_stalls(args):
+    """Per-dispatch averages of rocprofv3 --pmc counters for one kernel, over
+    several CSV files (one pass each), with ratios drawn from them."""
+    vals, durs = {}, []
+    for path in args.summarize_stalls:
+        for r in csv.DictReader(open(path)):
+            if not r["Kernel_Name"].split("(")[0].split("<")[0].endswith(args.kernel):
+                continue
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            if "End_Timestamp" in r and "Start_Timestamp" in r:
+                durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if not vals:
+        raise SystemExit(f"no counter rows for a kernel named {args.kernel}")
+    avg = {k: statistics.mean(v) for k, v in vals.items()}
+    dur = statistics.median(durs) if durs else None
+    if dur:
+        avg["_duration_8"] = dur * 8  # GRBM_GUI_ACTIVE sums 8 XCDs; us -> kHz-us
+    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
+        avg["_tcc_req"] = avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"]
+    if "GRBM_GUI_ACTIVE" in avg:
+        avg["_tcp_cycles"] = avg["GRBM_GUI_ACTIVE"] / 8 * 256  # one vector cache per CU
+    if "TA_BUSY_avr" in avg and "GRBM_GUI_ACTIVE" in avg:
+        avg["TA_BUSY_sum_est"] = avg["TA_BUSY_avr"] * 256
+    lines = [f"# {args.title}", "", "Commands (from the repository root, on one MI355X; one "
+             "counter group per run):", "", "```", *args.command, "```", "",
+             f"Kernel `{args.kernel}`; values are means per dispatch"
+             + (f", median dispatch duration under counters {dur:.2f} us" if dur else "") + ".",
+             "", "| counter | per dispatch |", "|---|---|"]
+    for k in sorted(k for k in avg if not k.startswith("_") and k != "TA_BUSY_sum_est"):
+        lines.append(f"| {k} | {avg[k]:.4g} |")
+    lines += ["", "| ratio | value |", "|---|---|"]
+    for name, num, den, scale, unit in STALL_RATIOS:
+        if num in avg and den in avg and avg[den]:
+            v = avg[num] / avg[den] * scale
+            lines.append(f"| {name} | {v:.3g} {unit} |" if unit else f"| {name} | {v:.3f} |")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize_copy(args):
-    kernel = args.kernel or "__amd_rocclr_copyBuffer"
+    kernel = args.kernel or "k_stream"
     fetch, _ = _median_counter(args.summarize_copy[0], kernel, "FETCH_SIZE")
     write, _ = _median_counter(args.summarize_copy[1], kernel, "WRITE_SIZE")
     nbytes = args.copy_mb * (1 << 20)
-    d = {"kernel": f"{kernel} (torch device-to-device copy of a bf16 tensor)",
+    d = {"kernel": f"{kernel} (plain streaming copy, libmoe_calib.so)",
          "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
          "FETCH_SIZE_KiB_per_dispatch": fetch, "WRITE_SIZE_KiB_per_dispatch": write,
          "fetch_scale": round(nbytes / (fetch * 1024), 4),
@@ -485,13 +541,13 @@ def dispatch_variants(moe, torch, n, sets=5):
 
 # ----------------------------------------------------------------- other configs
 
-def config_table(moe, torch, n):
+def config_table(moe, torch, n, only=None):
     """Per-launch durations (HIP events around n back-to-back launches over
     rotating buffer sets) of the three calls and the fused call on the other
     workloads at full size, with their algorithmic bytes."""
     from combine_expert_amd import workloads as W
     rows = []
-    for name in ("c1", "c2", "c4", "c4b"):
+    for name in ("c1", "c2", "c4", "c4b") if only is None else (only,):
         wl = W.make(name)
         if wl.expert_out is None:  # the identity + bias expert: any bf16 rows serve for timing
             wl.expert_out = torch.randn(wl.Bs * wl.K, wl.H).bfloat16()
@@ -565,50 +621,58 @@ def _events_us(torch, fn, n, warm=10):
 
 def ceilings(torch, n, wl, step_set, nb, rows):
     """What this device sustains for the same traffic, from the measurement
-    kernels of libmoe_calib.so, each over buffers rotating past the Infinity
-    Cache: a plain streaming copy, streams with the combine's and the
-    dispatch's read/write mix at the c3 sizes, and the two kernels' access
-    shapes (the c3 routing of the headline step) with their arithmetic taken
-    out."""
+    kernels of libmoe_calib.so, each over buffers rotating through COLD_BYTES:
+    a plain streaming copy, streams with the combine's and the dispatch's
+    read/write mix at the c3 sizes, and the two kernels' access shapes (the
+    c3 routing of the headline step) with their arithmetic taken out; each
+    with its stores in every cache policy (the best is the ceiling)."""
     from combine_expert_amd import calib
     dev = torch.device("cuda")
     out = {"note": "measurement kernels of libmoe_calib.so (include/moe_calib.h); GB/s of the "
-                   "bytes each moves, HIP events over back-to-back launches"}
+                   "bytes each moves, HIP events over back-to-back launches, buffers rotating "
+                   "through about 4 GB; per store policy, best first"}
 
-    def stream_case(name, rbytes, wbytes, nsets):
+    def entry(bytes_, times):
+        res = {"bytes": bytes_}
+        for pol, us in sorted(times.items(), key=lambda kv: kv[1]):
+            res[pol] = {"avg_us": round(us, 3), "GBps": round(bytes_ / us / 1e3, 1),
+                        "frac": round(bytes_ / us / 1e3 / HBM_PEAK_GBS, 4)}
+        best = min(times, key=times.get)
+        res["best"] = best
+        res["frac"] = res[best]["frac"]
+        return res
+
+    def stream_case(name, rbytes, wbytes):
+        nsets = cold_sets(rbytes + wbytes)
         src = [torch.empty(rbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
         dst = [torch.empty(wbytes, dtype=torch.uint8, device=dev) for _ in range(nsets)]
         for t in src:
             t.fill_(3)
-        us = _events_us(torch, lambda k: calib.stream(src[k % nsets], rbytes, dst[k % nsets],
-                                                       wbytes), n)
-        out[name] = {"read_bytes": rbytes, "write_bytes": wbytes, "avg_us": round(us, 3),
-                     "GBps": round((rbytes + wbytes) / us / 1e3, 1),
-                     "frac": round((rbytes + wbytes) / us / 1e3 / HBM_PEAK_GBS, 4)}
+        times = {pol: _events_us(torch, lambda k: calib.stream(src[k % nsets], rbytes,
+                                                               dst[k % nsets], wbytes, code), n)
+                 for pol, code in calib.POLICIES.items()}
+        out[name] = entry(rbytes + wbytes, times)
+        out[name].update(read_bytes=rbytes, write_bytes=wbytes)
         del src, dst
 
-    stream_case("copy_256MB", 256 << 20, 256 << 20, cold_sets(512 << 20))
+    stream_case("copy_256MB", 256 << 20, 256 << 20)
     cr = nb["combine"] - 2 * wl.Bs * wl.H * 2 - wl.Bs * 4
-    stream_case("stream_combine_mix", cr // 16 * 16, (nb["combine"] - cr) // 16 * 16,
-                cold_sets(nb["combine"]))
+    stream_case("stream_combine_mix", cr // 16 * 16, (nb["combine"] - cr) // 16 * 16)
     dr = wl.Bs * wl.H * 2 + wl.Bs * wl.K * 5
-    stream_case("stream_dispatch_mix", dr // 16 * 16, (nb["dispatch"] - dr) // 16 * 16,
-                cold_sets(nb["dispatch"]))
+    stream_case("stream_dispatch_mix", dr // 16 * 16, (nb["dispatch"] - dr) // 16 * 16)
 
     # the kernels' access shapes on the headline's routing (c3)
     assist = step_set["d"]["assist_dst"]
-    nsets = cold_sets(nb["dispatch"], hi=64)
     Bs, H, K = wl.Bs, wl.H, wl.K
+    nsets = cold_sets(nb["dispatch"], hi=64)
     xs = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
     outs = [torch.empty((rows, H), dtype=torch.uint8, device=dev) for _ in range(nsets)]
-    us = _events_us(torch, lambda k: calib.scatter_shape(xs[k % nsets], assist, rows,
-                                                         outs[k % nsets]), n)
-    sb = Bs * H * 2 + Bs * K * 4 + rows * H
-    out["dispatch_shape"] = {"bytes": sb, "avg_us": round(us, 3),
-                             "GBps": round(sb / us / 1e3, 1),
-                             "frac": round(sb / us / 1e3 / HBM_PEAK_GBS, 4),
-                             "what": "block per token: its row read, one byte per element "
-                                     "written to each of its K rows (no routing, no coding)"}
+    times = {pol: _events_us(torch, lambda k: calib.scatter_shape(xs[k % nsets], assist, rows,
+                                                                  outs[k % nsets], code), n)
+             for pol, code in calib.POLICIES.items()}
+    out["dispatch_shape"] = entry(Bs * H * 2 + Bs * K * 4 + rows * H, times)
+    out["dispatch_shape"]["what"] = ("block per token: its row read, one byte per element "
+                                     "written to each of its K rows (no routing, no coding)")
     del xs, outs
     nsets = cold_sets(nb["combine"], hi=64)
     eo = [torch.empty((rows, H), dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(nsets)]
@@ -617,16 +681,14 @@ def ceilings(torch, n, wl, step_set, nb, rows):
     o1 = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
     o2 = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
     g = torch.ones(H, dtype=torch.bfloat16, device=dev)
-    us = _events_us(torch, lambda k: calib.gather_shape(eo[k % nsets], assist, aa[k % nsets],
-                                                        bb[k % nsets], g, rows, o1[k % nsets],
-                                                        o2[k % nsets]), n)
-    gb = rows * H * 2 + 2 * Bs * H * 2 + H * 2 + Bs * K * 4 + 2 * Bs * H * 2
-    out["combine_shape"] = {"bytes": gb, "avg_us": round(us, 3),
-                            "GBps": round(gb / us / 1e3, 1),
-                            "frac": round(gb / us / 1e3 / HBM_PEAK_GBS, 4),
-                            "what": "block per token: its K expert rows, two token rows and "
+    times = {pol: _events_us(torch, lambda k: calib.gather_shape(
+        eo[k % nsets], assist, aa[k % nsets], bb[k % nsets], g, rows, o1[k % nsets],
+        o2[k % nsets], code), n) for pol, code in calib.POLICIES.items()}
+    out["combine_shape"] = entry(rows * H * 2 + 2 * Bs * H * 2 + H * 2 + Bs * K * 4
+                                 + 2 * Bs * H * 2, times)
+    out["combine_shape"]["what"] = ("block per token: its K expert rows, two token rows and "
                                     "gamma read, two rows written, one block barrier (no "
-                                    "arithmetic)"}
+                                    "arithmetic)")
     return out
 
 
@@ -909,6 +971,8 @@ def main():
         return summarize_counters(args)
     if args.summarize_copy:
         return summarize_copy(args)
+    if args.summarize_stalls:
+        return summarize_stalls(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py times the single-GPU share of the MoE layer and runs on one GPU only; "
               "--gpus above 1 is not supported.", file=sys.stderr)
@@ -916,6 +980,13 @@ def main():
 
     if args.copy_mb:
         copy_calibration(args.copy_mb, args.steps, args.warmup)
+        return
+    if args.only_config:
+        import torch
+        from combine_expert_amd import moe
+        torch.cuda.init()
+        print(json.dumps({"config_table": config_table(moe, torch, max(args.steps // 5, 50),
+                                                       only=args.only_config)}), flush=True)
         return
     if args.gemm:
         return gemm_main(args)

@@ -20,6 +20,7 @@ constexpr int kMaxReads = 8;                      // read chunks a block takes a
 // Block b reads chunks [b*CR/nb, (b+1)*CR/nb) of src and writes chunks
 // [b*CW/nb, (b+1)*CW/nb) of dst: every block moves reads and writes in the
 // whole kernel's proportion, so the two interleave over time.
+template <int SP>
 __global__ __launch_bounds__(kStreamThreads) void k_stream(const void *src, uint32_t rbytes,
                                                            void *dst, uint32_t wbytes,
                                                            uint32_t cr, uint32_t cw)
@@ -41,11 +42,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_stream(const void *src, uint
         acc.w ^= v[j].w;
     }
     for (uint32_t c = w0; c < w1; ++c)
-        buf_store16<kDevice>(rd, c * kStreamChunk + t * 16, make_uint4(acc.x ^ c, acc.y, acc.z, acc.w));
+        buf_store16<SP>(rd, c * kStreamChunk + t * 16, make_uint4(acc.x ^ c, acc.y, acc.z, acc.w));
     // a block with no chunk to write still needs its loads: a store the data
     // decides (practically never taken) keeps them from being dropped
     if (w0 == w1 && acc.x == 0x9e3779b9u && acc.y == acc.z)
-        buf_store16<kDevice>(rd, t * 16, acc);
+        buf_store16<SP>(rd, t * 16, acc);
 }
 
 // high byte of each of the 8 bf16 in a
@@ -60,6 +61,7 @@ __device__ __forceinline__ uint2 high_bytes(const uint4 &a)
     return make_uint2(o[0], o[1]);
 }
 
+template <int SP>
 __global__ __launch_bounds__(kMaxThreads) void k_scatter_shape(const uint16_t *x,
                                                                const int32_t *assist, int Bs,
                                                                int H, int K, int n_rows,
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_scatter_shape(const uint16_t *x
         if (r < 0)
             continue;
         const uint32_t base = (uint32_t)r * H;
-        buf_store8<kDevice>(ro, base + p0, c0.x, c0.y);
-        buf_store8<kDevice>(ro, base + p1, c1.x, c1.y);
+        buf_store8<SP>(ro, base + p0, c0.x, c0.y);
+        buf_store8<SP>(ro, base + p1, c1.x, c1.y);
     }
 }
 
@@ -96,6 +98,7 @@ __device__ __forceinline__ void add_words(uint4 &acc, const uint4 &v)
 
 constexpr int kGroup = 8;
 
+template <int SP>
 __global__ __launch_bounds__(kMaxThreads) void k_gather_shape(
     const uint16_t *rows, const int32_t *assist, const uint16_t *a, const uint16_t *b,
     const uint16_t *gamma, int Bs, int H, int K, int n_rows, uint16_t *out1, uint16_t *out2)
@@ -138,8 +141,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_gather_shape(
         }
     }
     const rsrc_t r1 = buffer_rsrc(out1, (uint32_t)Bs * rowb), r2 = buffer_rsrc(out2, (uint32_t)Bs * rowb);
-    buf_store16<kPlain>(r1, tok + o0, s0);
-    buf_store16<kPlain>(r1, tok + o1, s1);
+    buf_store16<SP>(r1, tok + o0, s0);
+    buf_store16<SP>(r1, tok + o1, s1);
     const uint32_t part = wave_max_u32(s0.x ^ s1.y);
     if (lane == 0)
         s_part[w] = part;
@@ -150,8 +153,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_gather_shape(
     add_words(s0, g0);
     add_words(s1, g1);
     s0.x ^= m;
-    buf_store16<kPlain>(r2, tok + o0, s0);
-    buf_store16<kPlain>(r2, tok + o1, s1);
+    buf_store16<SP>(r2, tok + o0, s0);
+    buf_store16<SP>(r2, tok + o1, s1);
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -164,58 +167,100 @@ bool bad_shape(int Bs, int H, int K, int n_rows)
 
 int status(hipError_t e) { return e == hipSuccess ? MOE_CALIB_OK : MOE_CALIB_ELAUNCH; }
 
+bool bad_policy(int p) { return p < MOE_CALIB_STORE_PLAIN || p > MOE_CALIB_STORE_DEVICE; }
+
+// a kernel template's instance for a store policy
+template <template <int> class F, typename... A>
+hipError_t by_policy(int policy, A... args)
+{
+    switch (policy) {
+    case MOE_CALIB_STORE_PLAIN: return F<kPlain>::run(args...);
+    case MOE_CALIB_STORE_STREAM: return F<kStream>::run(args...);
+    default: return F<kDevice>::run(args...);
+    }
+}
+
+template <int SP> struct StreamK {
+    static hipError_t run(dim3 g, hipStream_t st, const void *src, uint32_t rb, void *dst,
+                          uint32_t wb, uint32_t cr, uint32_t cw)
+    {
+        hipLaunchKernelGGL(k_stream<SP>, g, dim3(kStreamThreads), 0, st, src, rb, dst, wb, cr, cw);
+        return hipGetLastError();
+    }
+};
+template <int SP> struct ScatterK {
+    static hipError_t run(dim3 g, dim3 b, hipStream_t st, const uint16_t *x, const int32_t *assist,
+                          int Bs, int H, int K, int n_rows, uint8_t *out)
+    {
+        hipLaunchKernelGGL(k_scatter_shape<SP>, g, b, 0, st, x, assist, Bs, H, K, n_rows, out);
+        return hipGetLastError();
+    }
+};
+template <int SP> struct GatherK {
+    static hipError_t run(dim3 g, dim3 b, hipStream_t st, const uint16_t *rows,
+                          const int32_t *assist, const uint16_t *a, const uint16_t *bb,
+                          const uint16_t *gamma, int Bs, int H, int K, int n_rows, uint16_t *o1,
+                          uint16_t *o2)
+    {
+        hipLaunchKernelGGL(k_gather_shape<SP>, g, b, 0, st, rows, assist, a, bb, gamma, Bs, H, K,
+                           n_rows, o1, o2);
+        return hipGetLastError();
+    }
+};
+
 }  // namespace
 }  // namespace moe
 
 extern "C" {
 
 int moe_calib_stream(const void *src, size_t read_bytes, void *dst, size_t write_bytes,
-                     void *stream)
+                     int store_policy, void *stream)
 {
     using namespace moe;
     const size_t lim = (size_t)1 << 31;
     if (!src || !dst || !aligned16(src) || !aligned16(dst) || read_bytes % 16 ||
-        write_bytes % 16 || read_bytes > lim || write_bytes > lim || read_bytes + write_bytes == 0)
+        write_bytes % 16 || read_bytes > lim || write_bytes > lim ||
+        read_bytes + write_bytes == 0 || bad_policy(store_policy))
         return MOE_CALIB_EINVAL;
     const uint32_t cr = (uint32_t)((read_bytes + kStreamChunk - 1) / kStreamChunk);
     const uint32_t cw = (uint32_t)((write_bytes + kStreamChunk - 1) / kStreamChunk);
     uint32_t nb = (cr + cw + kChunksPerBlock - 1) / kChunksPerBlock;
     // at most kMaxReads read chunks per block
     nb = nb > (cr + kMaxReads - 1) / kMaxReads ? nb : (cr + kMaxReads - 1) / kMaxReads;
-    hipLaunchKernelGGL(k_stream, dim3(nb), dim3(kStreamThreads), 0,
-                       static_cast<hipStream_t>(stream), src, (uint32_t)read_bytes, dst,
-                       (uint32_t)write_bytes, cr, cw);
-    return status(hipGetLastError());
+    return status(by_policy<StreamK>(store_policy, dim3(nb), static_cast<hipStream_t>(stream),
+                                     src, (uint32_t)read_bytes, dst, (uint32_t)write_bytes, cr,
+                                     cw));
 }
 
 int moe_calib_scatter_shape(const void *x, const int32_t *assist, int Bs, int H, int K,
-                            int n_rows, void *out, void *stream)
+                            int n_rows, void *out, int store_policy, void *stream)
 {
     using namespace moe;
-    if (!x || !assist || !out || !aligned16(x) || !aligned16(out) || bad_shape(Bs, H, K, n_rows))
+    if (!x || !assist || !out || !aligned16(x) || !aligned16(out) ||
+        bad_shape(Bs, H, K, n_rows) || bad_policy(store_policy))
         return MOE_CALIB_EINVAL;
-    hipLaunchKernelGGL(k_scatter_shape, dim3(Bs), dim3(row_threads(H)), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(x),
-                       assist, Bs, H, K, n_rows, static_cast<uint8_t *>(out));
-    return status(hipGetLastError());
+    return status(by_policy<ScatterK>(store_policy, dim3(Bs), dim3(row_threads(H)),
+                                      static_cast<hipStream_t>(stream),
+                                      static_cast<const uint16_t *>(x), assist, Bs, H, K, n_rows,
+                                      static_cast<uint8_t *>(out)));
 }
 
 int moe_calib_gather_shape(const void *rows, const int32_t *assist, const void *a,
                            const void *b, const void *gamma, int Bs, int H, int K, int n_rows,
-                           void *out1, void *out2, void *stream)
+                           void *out1, void *out2, int store_policy, void *stream)
 {
     using namespace moe;
     if (!rows || !assist || !a || !b || !gamma || !out1 || !out2 || !aligned16(rows) ||
         !aligned16(a) || !aligned16(b) || !aligned16(gamma) || !aligned16(out1) ||
-        !aligned16(out2) || bad_shape(Bs, H, K, n_rows))
+        !aligned16(out2) || bad_shape(Bs, H, K, n_rows) || bad_policy(store_policy))
         return MOE_CALIB_EINVAL;
-    hipLaunchKernelGGL(k_gather_shape, dim3(Bs), dim3(row_threads(H)), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const uint16_t *>(rows),
-                       assist, static_cast<const uint16_t *>(a),
-                       static_cast<const uint16_t *>(b), static_cast<const uint16_t *>(gamma),
-                       Bs, H, K, n_rows, static_cast<uint16_t *>(out1),
-                       static_cast<uint16_t *>(out2));
-    return status(hipGetLastError());
+    return status(by_policy<GatherK>(store_policy, dim3(Bs), dim3(row_threads(H)),
+                                     static_cast<hipStream_t>(stream),
+                                     static_cast<const uint16_t *>(rows), assist,
+                                     static_cast<const uint16_t *>(a),
+                                     static_cast<const uint16_t *>(b),
+                                     static_cast<const uint16_t *>(gamma), Bs, H, K, n_rows,
+                                     static_cast<uint16_t *>(out1), static_cast<uint16_t *>(out2)));
 }
 
 }  // extern "C"

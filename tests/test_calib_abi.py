@@ -41,13 +41,15 @@ def _no_gpu():
 def test_bad_arguments_are_rejected_before_launch():
     from combine_expert_amd import calib
     L = calib.raw()
-    assert L.moe_calib_stream(None, 16, P, 16, None) == 1
-    assert L.moe_calib_stream(P + 8, 16, P, 16, None) == 1          # misaligned
-    assert L.moe_calib_stream(P, 15, P, 16, None) == 1              # not a multiple of 16
-    assert L.moe_calib_stream(P, 0, P, 0, None) == 1                # nothing to move
-    assert L.moe_calib_stream(P, (1 << 31) + 16, P, 16, None) == 1  # too large
-    assert L.moe_calib_scatter_shape(P, P, 512, 7168, 8, 4096 + 1, P, None) == 1  # rows > Bs*K
-    assert L.moe_calib_scatter_shape(P, P, 513, 7168, 8, 4096, P, None) == 1
-    assert L.moe_calib_scatter_shape(P, P, 512, 7200 + 16, 8, 4096, P, None) == 1  # H % 32
-    assert L.moe_calib_gather_shape(P, P, P, P, P, 512, 7168, 17, 4096, P, P, None) == 1
-    assert L.moe_calib_gather_shape(P, P, P, P, None, 512, 7168, 8, 4096, P, P, None) == 1
+    assert L.moe_calib_stream(None, 16, P, 16, 1, None) == 1
+    assert L.moe_calib_stream(P + 8, 16, P, 16, 1, None) == 1          # misaligned
+    assert L.moe_calib_stream(P, 15, P, 16, 1, None) == 1              # not a multiple of 16
+    assert L.moe_calib_stream(P, 0, P, 0, 1, None) == 1                # nothing to move
+    assert L.moe_calib_stream(P, (1 << 31) + 16, P, 16, 1, None) == 1  # too large
+    assert L.moe_calib_stream(P, 16, P, 16, 3, None) == 1              # no such policy
+    assert L.moe_calib_scatter_shape(P, P, 512, 7168, 8, 4096 + 1, P, 1, None) == 1  # rows > Bs*K
+    assert L.moe_calib_scatter_shape(P, P, 513, 7168, 8, 4096, P, 1, None) == 1
+    assert L.moe_calib_scatter_shape(P, P, 512, 7200 + 16, 8, 4096, P, 1, None) == 1  # H % 32
+    assert L.moe_calib_scatter_shape(P, P, 512, 7168, 8, 4096, P, -1, None) == 1
+    assert L.moe_calib_gather_shape(P, P, P, P, P, 512, 7168, 17, 4096, P, P, 1, None) == 1
+    assert L.moe_calib_gather_shape(P, P, P, P, None, 512, 7168, 8, 4096, P, P, 1, None) == 1
