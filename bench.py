@@ -191,9 +191,16 @@ WORKLOAD_TAG = "Bs=512 H=7168 K=8 E=256 mxfp8 (bench.py)"
 COPY_CAL = "copy_calibration.txt"
 
 
+def short_name(kernel_name):
+    """A kernel's name without namespaces, template arguments or parameters."""
+    n = kernel_name.replace("(anonymous namespace)::", "")
+    n = n.split("(")[0].split("<")[0].strip()
+    return n.split("::")[-1].split(" ")[-1]
+
+
 def _median_counter(path, kernel, counter):
     vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
-            if r["Counter_Name"] == counter and r["Kernel_Name"].startswith(kernel)]
+            if r["Counter_Name"] == counter and short_name(r["Kernel_Name"]) == kernel]
     if not vals:
         raise SystemExit(f"{path}: no {counter} rows for a kernel named {kernel}*")
     return statistics.median(vals), len(vals)
@@ -270,16 +277,18 @@ def summarize_counters(args):
 
 
 STALL_RATIOS = [
-    # (name, numerator, denominator, scale, unit)
-    ("shader clock", "GRBM_GUI_ACTIVE", "_duration_8", 1e-3, "GHz"),
-    ("waves waiting on anything / wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", 1.0, ""),
-    ("waves waiting to issue / wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", 1.0, ""),
-    ("LDS waits / all waits", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", 1.0, ""),
-    ("vector-memory instruction issue / busy CU cycles", "SQ_ACTIVE_INST_VMEM", "SQ_BUSY_CU_CYCLES", 1.0, ""),
-    ("L2 hit rate", "TCC_HIT_sum", "_tcc_req", 1.0, ""),
-    ("mean L2 read latency seen by the vector cache", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", 1.0, "cycles"),
-    ("vector cache stalled on pending requests / cycles", "TCP_PENDING_STALL_CYCLES_sum", "_tcp_cycles", 1.0, ""),
-    ("address unit stalled by the vector cache / TA busy", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "TA_BUSY_sum_est", 1.0, ""),
+    # (name, numerator, denominator, unit); GRBM_GUI_ACTIVE is not used as a cycle base:
+    # for kernels of tens of microseconds it also counts time outside the dispatch
+    ("waves waiting on a wait counter / wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", ""),
+    ("waves waiting to issue an instruction / wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", ""),
+    ("LDS waits / all waits", "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", ""),
+    ("vector cache stalled on pending L2 data / CU busy cycles", "TCP_PENDING_STALL_CYCLES_sum",
+     "SQ_BUSY_CU_CYCLES", ""),
+    ("address unit stalled by the vector cache / address-unit busy", "TA_ADDR_STALLED_BY_TC_CYCLES_sum",
+     "TA_BUSY_sum_est", ""),
+    ("L2 hit rate", "TCC_HIT_sum", "_tcc_req", ""),
+    ("mean L2 read latency seen by the vector cache", "TCP_TCC_READ_REQ_LATENCY_sum",
+     "TCP_TCC_READ_REQ_sum", "cycles"),
 ]
 
 
@@ -289,7 +298,7 @@ def summarize_stalls(args):
     vals, durs = {}, []
     for path in args.summarize_stalls:
         for r in csv.DictReader(open(path)):
-            if not r["Kernel_Name"].split("(")[0].split("<")[0].endswith(args.kernel):
+            if short_name(r["Kernel_Name"]) != args.kernel:
                 continue
             vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             if "End_Timestamp" in r and "Start_Timestamp" in r:
@@ -298,14 +307,10 @@ def summarize_stalls(args):
         raise SystemExit(f"no counter rows for a kernel named {args.kernel}")
     avg = {k: statistics.mean(v) for k, v in vals.items()}
     dur = statistics.median(durs) if durs else None
-    if dur:
-        avg["_duration_8"] = dur * 8  # GRBM_GUI_ACTIVE sums 8 XCDs; us -> kHz-us
     if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg:
         avg["_tcc_req"] = avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"]
-    if "GRBM_GUI_ACTIVE" in avg:
-        avg["_tcp_cycles"] = avg["GRBM_GUI_ACTIVE"] / 8 * 256  # one vector cache per CU
-    if "TA_BUSY_avr" in avg and "GRBM_GUI_ACTIVE" in avg:
-        avg["TA_BUSY_sum_est"] = avg["TA_BUSY_avr"] * 256
+    if "TA_BUSY_avr" in avg:
+        avg["TA_BUSY_sum_est"] = avg["TA_BUSY_avr"] * 256  # one address unit per CU
     lines = [f"# {args.title}", "", "Commands (from the repository root, on one MI355X; one "
              "counter group per run):", "", "```", *args.command, "```", "",
              f"Kernel `{args.kernel}`; values are means per dispatch"
@@ -314,9 +319,9 @@ def summarize_stalls(args):
     for k in sorted(k for k in avg if not k.startswith("_") and k != "TA_BUSY_sum_est"):
         lines.append(f"| {k} | {avg[k]:.4g} |")
     lines += ["", "| ratio | value |", "|---|---|"]
-    for name, num, den, scale, unit in STALL_RATIOS:
+    for name, num, den, unit in STALL_RATIOS:
         if num in avg and den in avg and avg[den]:
-            v = avg[num] / avg[den] * scale
+            v = avg[num] / avg[den]
             lines.append(f"| {name} | {v:.3g} {unit} |" if unit else f"| {name} | {v:.3f} |")
     with open(args.out, "w") as f:
         f.write("\n".join(lines) + "\n")
