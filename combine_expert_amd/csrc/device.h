@@ -45,18 +45,31 @@ __device__ __forceinline__ void unpack16(const uint4 &a, const uint4 &b, float *
     }
 }
 
-// Largest |x| bit pattern among 16 bf16 (sign cleared).  For non-negative
-// values the integer order of bf16 patterns is the numeric order.
-__device__ __forceinline__ uint32_t amax_bits16(const uint4 &a, const uint4 &b)
+// Largest |x| among 16 bf16 as a magnitude pattern (sign cleared), NaN
+// skipped and infinity included; *nan tells whether a NaN was seen.  For
+// non-negative values the integer order of bf16 patterns is the numeric order.
+// With p the 15-bit magnitude, (p + 0x7f) mod 2^15 keeps the order of every
+// non-NaN pattern (0 .. 0x7f80 map to 0x7f .. 0x7fff) and sends the NaN
+// patterns (0x7f81 .. 0x7fff) below zero's image; bit 15 of p + 0x7f marks a
+// NaN.  Both halves of a word are handled at once with packed 16-bit integer
+// arithmetic.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t amax_bits16(const uint4 &a, const uint4 &b, bool *nan = nullptr)
 {
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t m = 0;
+    const u16x2 bias = {0x7f, 0x7f}, mag = {0x7fff, 0x7fff};
+    u16x2 m = {0, 0}, seen = {0, 0};
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        m = max(m, w[j] & 0x7fffu);
-        m = max(m, (w[j] >> 16) & 0x7fffu);
+        const u16x2 p = (__builtin_bit_cast(u16x2, w[j]) & mag) + bias;
+        seen |= p;
+        m = __builtin_elementwise_max(m, p & mag);
     }
-    return m;
+    if (nan)
+        *nan = ((seen.x | seen.y) & 0x8000u) != 0;
+    const uint32_t mm = max((uint32_t)m.x, (uint32_t)m.y);
+    return mm > 0x7fu ? mm - 0x7fu : 0u;
 }
 
 // ---------------------------------------------------------------- streaming access

@@ -445,9 +445,11 @@ __device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d)
            ((uint32_t)d << 24);
 }
 
-// int8 codes of 16 values with multiplier d: clamp(rint(v * d), -127, 127).
-// d is +inf when 127 / max overflows (a tiny subnormal maximum): zeros then
-// give 0 * inf = NaN and are coded 0, the rest saturate.
+// int8 codes of 16 values with multiplier d: clamp(rint(v * d), -127, 127),
+// NaN products coded 0.  d is +inf when 127 / max overflows (a tiny subnormal
+// maximum): zeros then give 0 * inf = NaN and are coded 0, the rest saturate.
+// d is 0 when the maximum is infinite: every value then codes 0 (an infinity
+// through inf * 0 = NaN).  NaN inputs code 0; the maxima skip them.
 __device__ __forceinline__ uint4 int8_codes(const float *v, float d)
 {
     int q[16];
@@ -479,6 +481,24 @@ __device__ __forceinline__ uint4 e4m3_codes(const float *v, float f)
         w[q] = (uint32_t)p;
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// The E4M3 NaN code (sign of the input, all other bits set) in place of the
+// code of each NaN among the 16 bf16 inputs: the clamp in e4m3_codes has
+// turned a NaN into -448.
+__device__ __forceinline__ uint4 e4m3_nan_codes(uint4 code, const uint4 &xa, const uint4 &xb)
+{
+    const uint32_t w[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+    uint32_t c[4] = {code.x, code.y, code.z, code.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+        if ((h & 0x7fffu) > 0x7f80u) {
+            const int sh = 8 * (e & 3);
+            c[e >> 2] = (c[e >> 2] & ~(0xffu << sh)) | ((((h >> 8) & 0x80u) | 0x7fu) << sh);
+        }
+    }
+    return make_uint4(c[0], c[1], c[2], c[3]);
 }
 
 // floor(log2(m)) of a positive bf16 magnitude pattern (normal or subnormal)
@@ -692,15 +712,25 @@ __device__ __forceinline__ Coded code_row(const DispatchArgs &a, int t, bool has
         c.fscale = m ? 1.0f / d : 0.0f;
         c.code = int8_codes(v, d);
     } else {  // MODE == 4
-        uint32_t m = amax_bits16(xa, xb);
+        bool nan;
+        uint32_t m = amax_bits16(xa, xb, &nan);
         m = max(m, (uint32_t)__shfl_xor((int)m, 1));
         int se = -127;
-        if (m) {
-            se = bf16_ilogb(m) - 8;
-            se = max(-127, min(127, se));
+        if (m) {  // an infinite maximum takes the largest exponent, 127
+            se = m >= 0x7f80u ? 127 : max(-127, bf16_ilogb(m) - 8);
         }
-        const float f = __uint_as_float((uint32_t)(127 - se) << 23);  // 2^-se, normal
+        // 2^-se is a normal float except at se = 127 (only an infinite
+        // maximum gives it): the scaling then takes two exact steps
+        float f = __uint_as_float((uint32_t)(127 - se) << 23);
+        if (se == 127) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                v[j] *= 0x1p-64f;
+            f = 0x1p-63f;
+        }
         c.code = e4m3_codes(v, f);
+        if (nan)
+            c.code = e4m3_nan_codes(c.code, xa, xb);
         c.se = se;
     }
     return c;

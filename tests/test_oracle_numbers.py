@@ -259,3 +259,47 @@ def test_mxfp8_zero_block_and_worked_values():
     assert sbyte == 120
     assert list(codes[:3]) == [0x7C, 0x70, 0xE8]
     assert not codes[3:].any()
+
+
+# ---------------------------------------------------------------- non-finite inputs
+# The pages do not say how an infinity or a NaN in x is coded.  The reading
+# taken: a maximum skips NaN; an infinite maximum gives sharedExp =
+# floor(log2 inf) clamped to 127, or the int8 multiplier 127 / inf = 0 with
+# scale 1 / 0 = inf; E4M3 codes a NaN as its sign with every other bit set
+# and an infinity as +-448 (saturation); int8 codes NaN (and inf * 0) as 0.
+
+def test_mxfp8_nonfinite_worked_values():
+    # a block holding +-inf: sharedExp 127 (byte 254), every finite value
+    # scaled by 2^-127: 1 -> 2^-127 and -2 -> -2^-126 code +0 / -0;
+    # 2^117 -> 2^-10, half the smallest subnormal step, ties to even 0;
+    # 2^118 -> 2^-9 = code 1; the largest finite bf16 (2 - 2^-7) * 2^127 ->
+    # 1.9921875, which rounds to 2.0 = 0x40; NaN keeps its sign, inf saturates
+    x = np.zeros(32, dtype=np.uint16)
+    x[:9] = [0x7F80, 0x3F80, 0xC000, 0x7FC0, 0xFFC0, 0x7A00, 0x7A80, 0xFF80, 0x7F7F]
+    codes, sbyte = oracle.quant_mxfp8(x)
+    assert sbyte == 254
+    assert list(codes[:9]) == [0x7E, 0x00, 0x80, 0x7F, 0xFF, 0x00, 0x01, 0xFE, 0x40]
+    assert not codes[9:].any()
+    # a NaN does not set the maximum: max |x| = 3 as in the finite block
+    x = np.zeros(32, dtype=np.uint16)
+    x[:4] = [0x7FC0, 0x4040, 0x3F00, 0xFFFF]  # NaN, 3, 0.5, -NaN
+    codes, sbyte = oracle.quant_mxfp8(x)
+    assert sbyte == 120
+    assert list(codes[:4]) == [0x7F, 0x7C, 0x68, 0xFF]
+    assert not codes[4:].any()
+    # a block of NaN only: maximum 0, sharedExp -127 (byte 0)
+    codes, sbyte = oracle.quant_mxfp8(np.full(32, 0x7FC1, dtype=np.uint16))
+    assert sbyte == 0 and np.all(codes == 0x7F)
+
+
+def test_int8_nonfinite_worked_values():
+    # [inf, 5, NaN, -3]: m = inf, d = 127 / inf = 0: 5 * 0 = 0, inf * 0 = NaN -> 0
+    q, s = oracle.quant_int8(np.array([0x7F80, 0x40A0, 0x7FC0, 0xC040], np.uint16))
+    assert list(q) == [0, 0, 0, 0] and s == float("inf")
+    # [NaN, 4, -2]: m = 4, d = 31.75: [NaN -> 0, 127, -63.5 -> -64]
+    q, s = oracle.quant_int8(np.array([0x7FC0, 0x4080, 0xC000], np.uint16))
+    assert list(q) == [0, 127, -64]
+    assert np.float32(s) == np.float32(1.0) / np.float32(31.75)
+    # NaN only: maximum 0, codes 0, scale 0
+    q, s = oracle.quant_int8(np.full(8, 0xFFC0, dtype=np.uint16))
+    assert not q.any() and s == 0.0
