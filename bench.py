@@ -12,7 +12,7 @@ this workload.  The pages' three-call sequence (moe_update_expert,
 moe_dispatch, moe_combine_add_rmsnorm) is timed as well and reported under
 "step_three_calls".
 
-    python bench.py [--steps 500] [--warmup 50] [--sets 5] [--cpu-seconds 10]
+    python bench.py [--steps 500] [--warmup 50] [--sets 0] [--cpu-seconds 10]
     python bench.py --headline-only                      # the c3 step alone (for traces)
     python bench.py --copy-mb 256                        # copy kernel for counter scaling
     python bench.py --summarize-trace STATS.csv --out profiles/X.md --command CMD
@@ -65,6 +65,8 @@ COLD_BYTES = 4 << 30
 def cold_sets(set_bytes, lo=2, hi=96):
     """Buffer sets a timed loop rotates over: COLD_BYTES of traffic in all."""
     return max(lo, min(hi, -(-COLD_BYTES // max(1, set_bytes))))
+
+
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
