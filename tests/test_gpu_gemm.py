@@ -205,6 +205,56 @@ def test_gemm_wide_tiling():
         extra = np.random.default_rng(seed + 1).integers(0, g.rows, 48)
         check_sampled(g, y, cols=cols, extra_rows=extra, where=f"wide {counts}")
 
+
+def mx_tiling(counts, rows, N, cus=256):
+    """The mxfp8 launch's choice (with grouped scales) restated on the host: 'narrow' or
+    ('wide', split of the last round's tiles), from the row tiles of both tilings and the
+    cost model the kernel applies."""
+    def cost(tiles, G, round_cost, quarter, half):
+        r, tail = divmod(tiles, G)
+        split = 1 if tail == 0 else (4 if G // tail >= 4 else (2 if G // tail >= 2 else 1))
+        last = 0.0 if tail == 0 else (quarter if split == 4 else half if split == 2 else 1.0)
+        return np.float32(round_cost) * np.float32(r + last), split
+    col_tiles = -(-N // 256)
+    m_narrow = sum(-(-c // 128) for c in counts)
+    m_wide = sum(-(-c // 256) for c in counts)
+    G = min((-(-rows // 128) + len(counts)) * col_tiles, cus)
+    cw, split = cost(m_wide * col_tiles, G, 1.9, 0.5, 0.6)
+    cn, _ = cost(m_narrow * col_tiles, G, 1.0, 0.5, 0.67)
+    return ("wide", split) if cw < cn else ("narrow", None)
+
+
+WIDE_RAGGED = [
+    # (seed, counts per instance, N, Kd, spare rows, the branch the launch takes)
+    (7211, [6176], 2048, 512, 40, ("wide", 1)),                  # a ragged last row tile
+    (7212, [3000, 1500, 2600, 700], 2048, 512, 17, ("wide", 1)),  # boundaries inside tiles
+    (7213, [36928], 1024, 512, 8, ("wide", 2)),                  # last round in half tiles
+    (7214, [20000, 16928], 1024, 512, 3, ("wide", 2)),
+    (7215, [51264], 1024, 512, 64, ("wide", 4)),                 # last round in quarter tiles
+]
+
+
+@pytest.mark.parametrize("case", WIDE_RAGGED, ids=[f"w{c[0]}" for c in WIDE_RAGGED])
+def test_gemm_wide_tiling_ragged_and_split(case):
+    """Shapes on which the launch takes the 256 x 256 tiling with a ragged last row tile,
+    instance boundaries inside the walk, and a last round cut into half or quarter pieces:
+    rows at every instance's ends and around each 256-row tile boundary near them, plus
+    random rows, all columns, against the oracle; spare rows past the last instance stay
+    untouched."""
+    seed, counts, N, Kd, tail, branch = case
+    g = W.make_gemm_case(seed, counts, N, Kd, tail=tail)
+    assert mx_tiling(counts, g.rows, N) == branch
+    say(f"[gemm] wide tiling {branch}: counts={counts} N={N} Kd={Kd} spare={tail}")
+    y = run_gpu(g)
+    extra = set(np.random.default_rng(seed + 1).integers(0, g.rows - tail, 48).tolist())
+    for e in range(g.E):
+        lo, hi = int(g.offsets[e]), int(g.offsets[e + 1])
+        last_tile = lo + (hi - lo - 1) // 256 * 256  # first row of the instance's last tile
+        extra |= {lo + 1, last_tile - 1, last_tile, last_tile + 1, hi - 2}
+    check_sampled(g, y, extra_rows=sorted(extra), where=f"wide {counts}")
+    assert np.all(y[g.rows - tail:] == POISON16), "spare rows were written"
+
+
 # ---------------------------------------------------------------- int8 operands
 
 def run_gpu_i8(g, quant_mode):
