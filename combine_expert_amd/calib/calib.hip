@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_gather_shape(
 {
     __shared__ uint32_t s_part[kMaxWaves];
     const int i = blockIdx.x, t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-    const int nw = blockDim.x / kWave;
+    const int nw = row_threads(H) / kWave;
     int my = assist[i * K + min(lane, K - 1)];
     if (lane >= K || my >= n_rows)
         my = -1;

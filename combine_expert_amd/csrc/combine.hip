@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
 
     const int i = blockIdx.x;
     const int t = threadIdx.x;
-    const int lane = t & (kWave - 1), w = t / kWave, nw = blockDim.x / kWave;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = row_threads(H) / kWave;
     const uint32_t rowb = (uint32_t)H * 2;
     // byte offsets of this lane's two parts in a row; a part past the row end
     // reads at kNoPart (zeros) and is not stored

@@ -74,7 +74,7 @@ struct Routed {
     {
         return mask ? reinterpret_cast<const uint32_t *>(mask)[g4] : 0x01010101u;
     }
-    // the four entries of group g4 as f(inst, on, g)
+    // the four entries of group g4 as f(inst, on, g, inst)
     template <typename Fn>
     __device__ void group(const int4 &v, Side m, int g4, bool in, int &err, Fn &&f) const
     {
@@ -97,7 +97,7 @@ struct Routed {
             const bool ok = (unsigned)idv[j] < (unsigned)E;
             err |= act && !ok ? 1 : 0;
             const bool on = act && ok;
-            f(on ? idv[j] : -1, on, g4 * 4 + j);
+            f(on ? idv[j] : -1, on, g4 * 4 + j, on ? idv[j] : -1);
         }
     }
     __device__ int entry1(int g, bool &on, int &err) const
@@ -170,7 +170,9 @@ struct Mapped {
     }
     // The four entries of group g4, mapped phase by phase -- row heads (and
     // token / threshold reads), then instance slots -- so that each phase's
-    // LDS reads are in flight together, then visited as f(inst, on, g).
+    // LDS reads are in flight together, then visited as f(inst, on, g, mapped)
+    // (mapped: the instance looked up, -1 if the lookup failed, whether or
+    // not the entry is kept).
     // (Entry by entry, the LDS reads would queue behind the previous
     // counter update.)
     template <typename Fn>
@@ -226,7 +228,7 @@ struct Mapped {
             const int fail = !e_ok[j] ? 1 : (hv[j] < 0 || inst[j] < 0) ? 2 : 0;
             err |= keep[j] ? fail : 0;
             const bool on = keep[j] && fail == 0;
-            f(on ? inst[j] : -1, on, g4 * 4 + j);
+            f(on ? inst[j] : -1, on, g4 * 4 + j, fail ? -1 : inst[j]);
         }
     }
     __device__ int entry1(int g, bool &on, int &err) const
@@ -237,16 +239,17 @@ struct Mapped {
 };
 
 // Visits every entry g this thread owns -- int4 groups g4 = t, t + T, ...,
-// then the scalar tail -- as f(inst, on, g) with inst = -1 unless on.  Each
+// then the scalar tail -- as f(inst, on, g, mapped) with inst = -1 unless on
+// (mapped: the source's instance before the keep test, -1 if none).  Each
 // batch issues four 16-byte id loads (and side words) before using any;
 // indices past the end are clamped and visited as inactive.
 // after_first_issue() runs once, right after the first batch is issued:
 // loads placed there stay in flight while the batch is consumed.
 template <typename Src, typename Fn, typename G>
-__device__ __forceinline__ void for_each_entry(const Src &s, int N, int &err, Fn &&f,
+__device__ __forceinline__ void for_each_entry(const Src &s, int N, int T, int &err, Fn &&f,
                                                G &&after_first_issue)
 {
-    const int t = threadIdx.x, T = blockDim.x;
+    const int t = threadIdx.x;
     const int N4 = N >> 2;
     const int4 *ids4 = reinterpret_cast<const int4 *>(s.ids);
     bool first = true;
@@ -278,8 +281,8 @@ __device__ __forceinline__ void for_each_entry(const Src &s, int N, int &err, Fn
     }
     for (int g = N4 * 4 + t; g < N; g += T) {
         bool on;
-        const int inst = s.entry1(g, on, err);
-        f(inst, on, g);
+        const int m = s.entry1(g, on, err);
+        f(on ? m : -1, on, g, m);
     }
 }
 
@@ -320,7 +323,7 @@ struct Stage {
 
     __device__ __forceinline__ void issue(const DispatchArgs &a)
     {
-        const int t = threadIdx.x, T = blockDim.x;
+        const int t = threadIdx.x, T = dispatch_threads(a.H);
         const int tabsz = a.n_logical * a.F;
 #pragma unroll
         for (int u = 0; u < kStageTab; ++u)
@@ -340,7 +343,7 @@ struct Stage {
     __device__ __forceinline__ void store(const DispatchArgs &a, int *s_tab, uint8_t *s_tok,
                                           float *s_thr)
     {
-        const int t = threadIdx.x, T = blockDim.x;
+        const int t = threadIdx.x, T = dispatch_threads(a.H);
         const int tabsz = a.n_logical * a.F;
 #pragma unroll
         for (int u = 0; u < kStageTab; ++u) {
@@ -359,7 +362,7 @@ struct Stage {
     static __device__ __forceinline__ void rest(const DispatchArgs &a, int *s_tab,
                                                 uint8_t *s_tok)
     {
-        const int t = threadIdx.x, T = blockDim.x;
+        const int t = threadIdx.x, T = dispatch_threads(a.H);
         const int tabsz = a.n_logical * a.F;
         if (tabsz > kStageTab * T) {
             for (int j = t + kStageTab * T; j < tabsz; j += T)
@@ -378,7 +381,7 @@ template <typename Src>
 __device__ void route_summary(const DispatchArgs &a, const Src &s, int *s_hist, int *s_wave,
                               int *s_tab, uint8_t *s_tok, float *s_thr)
 {
-    const int t = threadIdx.x, T = blockDim.x;
+    const int t = threadIdx.x, T = dispatch_threads(a.H);
     const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
     const int N = a.Bs * a.K, E = a.E;
     if (Src::kMapped)
@@ -387,8 +390,8 @@ __device__ void route_summary(const DispatchArgs &a, const Src &s, int *s_hist, 
         s_hist[e] = 0;
     int err = 0;
     for_each_entry(
-        s, N, err,
-        [&](int inst, bool on, int) {
+        s, N, T, err,
+        [&](int inst, bool on, int, int) {
             if (on)
                 atomicAdd(&s_hist[inst], 1);
         },
@@ -573,7 +576,7 @@ __device__ __forceinline__ void code_store_rows(const DispatchArgs &a, int t, bo
     constexpr int D = KMAX < kPrefetch ? KMAX : kPrefetch;
     const int H = a.H;
     const int tc = has ? t : 0;
-    const int lane = t & (kWave - 1), w = t / kWave, nw = blockDim.x / kWave;
+    const int lane = t & (kWave - 1), w = t / kWave, nw = dispatch_threads(a.H) / kWave;
     float v[16];
     unpack16(xa, xb, v);
     int ek[KMAX];
@@ -779,9 +782,10 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
 {
     // low 16 bits: active entries with id e; high: those before this token.
     // After the scan the low half holds offsets[e].
-    __shared__ int s_cnt[kHistSlots];
+    __shared__ __align__(16) int s_cnt[kHistSlots];
     __shared__ int s_wave[kDispatchWaves];
     __shared__ int s_rank[KMAX];
+    __shared__ int s_my[KMAX];
     __shared__ uint32_t s_wmax[kDispatchWaves];
     __shared__ uint32_t s_pmax[PE && MODE == 2 ? kDispatchWaves * KMAX : 1];
     __shared__ uint8_t s_tok[kMaxTokens];
@@ -798,7 +802,7 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         s = Routed{a.ids, a.mask, a.token_mask ? s_tok : nullptr, E, K,
                    (unsigned)(((1 << 17) + K - 1) / K)};
     if (!Src::kMapped && a.token_mask) {  // staged before the first use (a barrier follows)
-        for (int j = threadIdx.x; j < Bs; j += blockDim.x)
+        for (int j = threadIdx.x; j < Bs; j += dispatch_threads(H))
             s_tok[j] = a.token_mask[j];
     }
     if (blockIdx.x == 0) {
@@ -806,34 +810,51 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         return;
     }
     const int i = blockIdx.x - 1;
-    const int t = threadIdx.x, T = blockDim.x;
+    const int t = threadIdx.x, T = dispatch_threads(a.H);
     const int lane = t & (kWave - 1), w = t / kWave, nw = T / kWave;
     const bool has = t * kChunk < H;
 
-    // 1. the token's own K entries, one per lane: the first loads issued are
-    //    the first ones waited for (after the rare large-table staging)
+    // 1. routed source: the token's own K entries, one per lane, are the first
+    //    loads issued and the first waited for.  (With the mapping fused in
+    //    they are picked up in step 2 instead, already mapped.)  The
+    //    histograms of step 2 are zeroed, all of them: the rank wave reads
+    //    whole runs.
     if (Src::kMapped)
         Stage<Src::kKeep>::rest(a, s_tab, s_tok);
     const int f0 = i * K;
-    const int kk = min(lane, K - 1);
-    const int raw_id = a.ids[f0 + kk];
-    const uint8_t *mp =
-        !Src::kMapped && a.mask ? a.mask : reinterpret_cast<const uint8_t *>(a.ids);
-    const uint8_t raw_on = Src::kMapped ? 1 : mp[f0 + kk];
-    const float *sp = Src::kMapped && a.scores ? a.scores : reinterpret_cast<const float *>(a.ids);
-    const float raw_sc = Src::kMapped ? sp[f0 + kk] : 0.0f;
-    for (int e = t; e < E; e += T)
+    int raw_id = -1;
+    uint8_t raw_m = 1;
+    if constexpr (!Src::kMapped) {  // both loads unconditional: no wait before the ids go out
+        const int kk = min(lane, K - 1);
+        raw_id = a.ids[f0 + kk];
+        const uint8_t *mp = a.mask ? a.mask : reinterpret_cast<const uint8_t *>(a.ids);
+        raw_m = mp[f0 + kk];  // without a mask: a byte of the ids, not used
+    }
+    for (int e = t; e < kHistSlots; e += T)
         s_cnt[e] = 0;
 
     // 2. the packed histograms.  The token's row (16 elements per thread) is
     //    loaded after the first batch of ids, so it stays in flight meanwhile.
+    //    With the mapping fused in, the token's own entries are picked up on
+    //    the way (s_my: instance or -1) and their update-expert outputs
+    //    written there, which saves mapping them again after the loop.
     uint4 xa, xb;
     int err = 0;
     for_each_entry(
-        s, N, err,
-        [&](int inst, bool on, int g) {
+        s, N, T, err,
+        [&](int inst, bool on, int g, int mapped) {
             if (on)
                 atomicAdd(&s_cnt[inst], g < f0 ? kPreOne : 1);
+            if constexpr (Src::kMapped) {
+                const unsigned k = (unsigned)(g - f0);
+                if (k < (unsigned)K) {
+                    s_my[k] = inst;
+                    if (a.balanced_ids)
+                        a.balanced_ids[g] = mapped;
+                    if (a.balanced_mask)
+                        a.balanced_mask[g] = on ? 1 : 0;
+                }
+            }
         },
         [&] {
             // mapped source: the staging loads go out with the first ids and
@@ -850,25 +871,12 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
                 st.store(a, s_tab, s_tok, s_thr);
             lds_barrier();  // histograms zeroed (and mapping data staged) before use
         });
-    int my_id;
-    if constexpr (Src::kMapped) {
-        bool on;
-        int e2 = 0;  // block 0 reports the errors
-        const int inst = s.map(raw_id, i, kk, raw_sc, true, on, e2);
-        if (t < K) {  // the update-expert outputs of this token
-            if (a.balanced_ids)
-                a.balanced_ids[f0 + t] = inst;
-            if (a.balanced_mask)
-                a.balanced_mask[f0 + t] = on ? 1 : 0;
-        }
-        my_id = lane < K && on ? inst : -1;
-    } else {
-        const bool my_on = lane < K && (a.mask == nullptr || raw_on != 0) &&
-                           (a.token_mask == nullptr || a.token_mask[i] != 0) &&
-                           (unsigned)raw_id < (unsigned)E;
-        my_id = my_on ? raw_id : -1;
+    int my_id = -1;  // lane k: entry k's instance, -1 if not dispatched
+    if constexpr (!Src::kMapped) {  // the token mask, when given, is staged in LDS
+        const bool on = lane < K && (a.mask == nullptr || raw_m != 0) &&
+                        (a.token_mask == nullptr || s_tok[i] != 0);
+        my_id = on && (unsigned)raw_id < (unsigned)E ? raw_id : -1;
     }
-    const bool my_on = my_id >= 0;
     // Coding needs no ranks: after the histogram barrier the row's waves code
     // their chunks while the block's last wave, which holds no row data (the
     // block has one wave more than the row needs), works out the rows.
@@ -881,6 +889,9 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
     }
     const int rw = nw - 1;  // the rank wave: holds no row data
     lds_barrier();  // histograms complete
+    if constexpr (Src::kMapped)
+        my_id = lane < K ? s_my[lane < KMAX ? lane : 0] : -1;
+    const bool my_on = my_id >= 0;
     if (!PE && MODE != 2 && w != rw)
         cd = code_row<MODE>(a, t, has, xa, xb, 0u);
     if (!PE && MODE == 2 && w != rw) {
@@ -890,42 +901,68 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         cd = code_row<MODE>(a, t, has, xa, xb, amax);
     }
 
-    // 3. rows of the token's entries (the rank wave, lane k = entry k).  Only
-    //    these K offsets are needed, so that wave alone scans: lane c sums the low halves
-    //    of counters [c*per, (c+1)*per), a wave scan gives each chunk's
-    //    exclusive prefix, and lane k takes its chunk's prefix by a lane
-    //    shuffle plus the counters before its id inside the chunk.
+    // 3. rows of the token's entries (the rank wave, lane k = entry k).  Lane c
+    //    owns counters [16c, 16c + 16) (four 16-byte LDS reads; the array is
+    //    zeroed to its end): the low halves are prefix-summed in registers and
+    //    across the wave, and each counter is rewritten in place with its
+    //    exclusive prefix (offsets[e]) plus its high half (the active entries
+    //    with that id before this token).  An entry's row is then that word
+    //    plus the token's earlier entries with the same id.
+    int my_row = -1;
     if (w == rw) {
-        const int per = (E + kWave - 1) / kWave;
-        const int c0 = min(lane * per, E), c1 = min(c0 + per, E);
-        int local = 0;
-        for (int e = c0; e < c1; ++e)
-            local += s_cnt[e] & 0xffff;
-        const int excl = wave_incl_scan(local) - local;
-        const int id = my_on ? my_id : 0;
-        const int chunk = id / per;
-        int off = __shfl(excl, chunk);
-        for (int e = chunk * per; e < id; ++e)
-            off += s_cnt[e] & 0xffff;
+        // raised issue priority: the row's waves are coding on the same SIMDs
+        __builtin_amdgcn_s_setprio(3);
+        static_assert(kHistSlots == 16 * kWave, "16 counters per lane");
+        int4 *run4 = reinterpret_cast<int4 *>(s_cnt) + 4 * lane;
+        int4 c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            c[q] = run4[q];
+        int v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            v[4 * q] = c[q].x;
+            v[4 * q + 1] = c[q].y;
+            v[4 * q + 2] = c[q].z;
+            v[4 * q + 3] = c[q].w;
+        }
+        int tot = 0, ex[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            ex[j] = tot;
+            tot += v[j] & 0xffff;
+        }
+        const int base = wave_incl_scan(tot) - tot;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            ex[j] += base + (int)((unsigned)v[j] >> 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            run4[q] = make_int4(ex[4 * q], ex[4 * q + 1], ex[4 * q + 2], ex[4 * q + 3]);
         int dup = 0;  // earlier entries of this token with the same id
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
-            const int v = j < K ? __builtin_amdgcn_readlane(my_id, j) : -1;
-            dup += (j < lane && v == my_id) ? 1 : 0;
+            const int u = j < K ? __builtin_amdgcn_readlane(my_id, j) : -1;
+            dup += (j < lane && u == my_id) ? 1 : 0;
         }
-        if (lane < K) {
-            const int r = my_on ? off + (s_cnt[id] >> 16) + dup : -1;
-            s_rank[lane] = r;
-            a.assist_dst[f0 + lane] = r;
-            if (r >= 0)
-                a.expand_src[r] = f0 + lane;
-        }
+        my_row = my_on ? s_cnt[my_id] + dup : -1;
+        if (lane < K)
+            s_rank[lane] = my_row;
+        __builtin_amdgcn_s_setprio(0);
     }
     lds_barrier();  // rows published
     int rank[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
         rank[k] = k < K ? s_rank[k] : -1;
+    // the routing outputs go out after the barrier: issued before it, they
+    // would wait for room in the CU's memory pipeline behind the row stores
+    // of other blocks, and hold up the barrier with them
+    if (w == rw && lane < K) {
+        a.assist_dst[f0 + lane] = my_row;
+        if (my_row >= 0)
+            a.expand_src[my_row] = f0 + lane;
+    }
 
     if constexpr (PE) {
         int eid[KMAX];  // instance of each copy
@@ -955,7 +992,7 @@ __global__ __launch_bounds__(kMaxThreads + kWave) void k_update_dispatch(Dispatc
 template <int MODE, int KMAX, typename Src, bool PE>
 void launch_kernel(const DispatchArgs &a, hipStream_t stream)
 {
-    const dim3 grid(a.Bs + 1), block(row_threads(a.H) + kWave);
+    const dim3 grid(a.Bs + 1), block(dispatch_threads(a.H));
     if constexpr (Src::kMapped)
         hipLaunchKernelGGL((k_update_dispatch<MODE, KMAX, Src::kKeep, PE>), grid, block,
                            (size_t)a.n_logical * a.F * sizeof(int), stream, a);

@@ -40,7 +40,12 @@ hipError_t launch_expert_gemm(int quant_mode, const void *a, const void *a_sc,
                               hipStream_t stream);
 
 // Threads per row block: one thread per 16 row elements, rounded up to
-// whole waves (64 .. 512 threads for H in [1024, 8192]).
-inline int row_threads(int H) { return ((H / 16 + 63) / 64) * 64; }
+// whole waves (64 .. 512 threads for H in [1024, 8192]).  Kernels derive
+// their block size from H with these functions instead of reading blockDim,
+// whose value is fetched through a chain of dependent loads.
+__host__ __device__ inline int row_threads(int H) { return ((H / 16 + 63) / 64) * 64; }
+
+// Threads per dispatch block: the row's threads and one more wave.
+__host__ __device__ inline int dispatch_threads(int H) { return row_threads(H) + 64; }
 
 }  // namespace moe

@@ -15,13 +15,15 @@
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void k_update_expert(
+constexpr int kUpdateThreads = 256;
+
+__global__ __launch_bounds__(kUpdateThreads) void k_update_expert(
     const int32_t *__restrict__ ids, const float *__restrict__ scores,
     const int32_t *__restrict__ table, const float *__restrict__ thr,
     const uint8_t *__restrict__ token_mask, int Bs, int K, int n_logical, int F, int n_instances,
     int32_t *__restrict__ out_ids, uint8_t *__restrict__ out_mask, int32_t *__restrict__ dev_err)
 {
-    const int f = blockIdx.x * blockDim.x + threadIdx.x;
+    const int f = blockIdx.x * kUpdateThreads + threadIdx.x;
     if (f >= Bs * K)
         return;
     const int i = f / K;
@@ -67,7 +69,7 @@ hipError_t launch_update_expert(const int32_t *ids, const float *scores, const i
                                 uint8_t *out_mask, int32_t *dev_err, hipStream_t stream)
 {
     const int N = Bs * K;
-    const int threads = 256;
+    const int threads = kUpdateThreads;
     hipLaunchKernelGGL(k_update_expert, dim3((N + threads - 1) / threads), dim3(threads), 0,
                        stream, ids, scores, table, thr, token_mask, Bs, K, n_logical, F,
                        n_instances, out_ids, out_mask, dev_err);
