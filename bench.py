@@ -166,6 +166,11 @@ def algorithmic_bytes(Bs, H, K, E, rows, n_logical, F, quant_mode, n_scale, shar
     return dict(update_expert=upd, dispatch=dsp, update_dispatch=fused, combine=cmb)
 
 
+# the csrc files each kernel's counter summaries are keyed to
+DISPATCH_SRC = ("dispatch_impl.h", "dispatch.hip", "device.h", "kernels.h")
+COMBINE_SRC = ("combine.hip", "device.h", "kernels.h")
+
+
 def source_digest(*names):
     h = hashlib.sha256()
     for n in names:
@@ -1106,10 +1111,9 @@ def main():
 
     # HBM bytes per launch from the committed counter summaries (null when the
     # kernel source changed since they were taken)
-    dsp_src = ("dispatch_impl.h", "dispatch.hip", "device.h")
-    traffic = {"update_dispatch": counter_traffic("update_dispatch_c3_traffic.txt", dsp_src),
-               "dispatch": counter_traffic("dispatch_c3_traffic.txt", dsp_src),
-               "combine": counter_traffic("combine_c3_traffic.txt", ("combine.hip", "device.h"))}
+    traffic = {"update_dispatch": counter_traffic("update_dispatch_c3_traffic.txt", DISPATCH_SRC),
+               "dispatch": counter_traffic("dispatch_c3_traffic.txt", DISPATCH_SRC),
+               "combine": counter_traffic("combine_c3_traffic.txt", COMBINE_SRC)}
     line = {
         "metric": METRIC,
         "value": round(gbs, 2),
