@@ -28,6 +28,11 @@ from gpu_common import M, say
 
 pytestmark = pytest.mark.gpu
 POISON16 = 0xFFFF  # a bf16 NaN pattern: any row written by mistake shows
+# Share of sampled outputs that must equal the oracle's bf16 bit for bit.  Measured on
+# MI355X: 0.966-0.973 on every sampled case (Kd from 512 to 16384, the bench shape, 1024
+# instances, 4M rows, both tilings); a structural mistake (a wrong block, chunk, scale or
+# row) leaves almost none equal, and an accuracy loss in the accumulation far fewer.
+BIT_EQUAL_MIN = 0.9
 
 
 def run_gpu(g: W.GemmCase, offsets=None, dev_err=None):
@@ -81,7 +86,7 @@ def test_gemm_parity_small(ci):
     assert np.all(y[last:] == POISON16)
     # most outputs are the oracle's bf16 bit for bit (measured: about 97%); a structural
     # mistake (a wrong block, chunk or scale) leaves far fewer
-    assert np.mean(y[:last] == ref[:last]) > 0.9 if last else True
+    assert np.mean(y[:last] == ref[:last]) > BIT_EQUAL_MIN if last else True
 
 
 def test_gemm_all_instances_empty():
@@ -130,17 +135,23 @@ def test_gemm_full_size_sampled():
     sub_counts = np.bincount(np.array(inst), minlength=g.E)
     sub_off = np.zeros(g.E + 1, np.int32)
     sub_off[1:] = np.cumsum(sub_counts)
-    _, y64, abs64 = oracle.expert_gemm_mx(g.a[rows], g.a_sc[rows], sub_off,
-                                          np.ascontiguousarray(g.w[:, cols]),
-                                          np.ascontiguousarray(g.w_sc[:, cols]))
-    assert_close(y[rows][:, cols], y64, abs64, g.Kd, "g3 sample")
+    ref, y64, abs64 = oracle.expert_gemm_mx(g.a[rows], g.a_sc[rows], sub_off,
+                                            np.ascontiguousarray(g.w[:, cols]),
+                                            np.ascontiguousarray(g.w_sc[:, cols]))
+    got = y[rows][:, cols]
+    assert_close(got, y64, abs64, g.Kd, "g3 sample")
+    equal = float(np.mean(got == ref))
+    say(f"[gemm] g3 sample: {equal:.3f} of sampled outputs bit-equal to the oracle")
+    assert equal > BIT_EQUAL_MIN, equal
     assert not np.any(y[:int(g.offsets[-1])] == POISON16)
+
 
 
 
 def check_sampled(g, y, cols=None, extra_rows=(), where=""):
     """The first, middle and last row of every instance (plus extra_rows) and the given
-    columns (all by default) against the oracle on that sub-problem."""
+    columns (all by default) against the oracle on that sub-problem: within the tolerance,
+    and mostly equal to the oracle's bf16 bit for bit."""
     rows, inst = [], []
     for e in range(g.E):
         lo, hi = int(g.offsets[e]), int(g.offsets[e + 1])
@@ -153,10 +164,14 @@ def check_sampled(g, y, cols=None, extra_rows=(), where=""):
     cols = np.arange(g.N) if cols is None else np.asarray(cols)
     sub_off = np.zeros(g.E + 1, np.int32)
     sub_off[1:] = np.cumsum(np.bincount(np.array(inst), minlength=g.E))
-    _, y64, abs64 = oracle.expert_gemm_mx(g.a[rows], g.a_sc[rows], sub_off,
-                                          np.ascontiguousarray(g.w[:, cols]),
-                                          np.ascontiguousarray(g.w_sc[:, cols]))
-    assert_close(y[rows][:, cols], y64, abs64, g.Kd, where)
+    ref, y64, abs64 = oracle.expert_gemm_mx(g.a[rows], g.a_sc[rows], sub_off,
+                                            np.ascontiguousarray(g.w[:, cols]),
+                                            np.ascontiguousarray(g.w_sc[:, cols]))
+    got = y[rows][:, cols]
+    assert_close(got, y64, abs64, g.Kd, where)
+    equal = float(np.mean(got == ref))
+    say(f"[gemm] {where}: {equal:.3f} of sampled outputs bit-equal to the oracle")
+    assert equal > BIT_EQUAL_MIN, (where, equal)
 
 
 def test_gemm_max_instances():
