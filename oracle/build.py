@@ -14,10 +14,11 @@ SRC = os.path.join(HERE, "moe_oracle.c")
 LIB = os.path.join(HERE, "libmoe_oracle.so")
 
 
-def build(verbose: bool = False, src: str = SRC, lib: str = LIB) -> str:
+def build(verbose: bool = False, src: str = SRC, lib: str = LIB, extra=()) -> str:
+    """extra: additional compiler flags (the sanitizer build of the tests)."""
     tmp = lib + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+           "-shared", "-Wall", "-Wextra", *extra, "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
