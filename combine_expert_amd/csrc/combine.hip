@@ -14,10 +14,11 @@
 //
 // Every wave reads the token's K (row, weight) pairs itself, one per lane,
 // so the only block barrier is the one of the sum of squares.  The
-// dispatched entries are taken in order of k, eight at a time: each group of
-// eight is straight-line code (a missing entry loads at an offset past the
-// buffer, which reads zeros with no memory traffic), so the compiler counts
-// the loads and each row's sums start as soon as that row has arrived.
+// dispatched entries are taken in order of k into eight register slots:
+// straight-line code (a missing entry loads at an offset past the buffer,
+// which reads zeros with no memory traffic), so the compiler counts the loads
+// and each row's sums start as soon as that row has arrived.  A token with
+// more than eight rows refills each slot as soon as its row is summed.
 // Expert rows are read once and marked non-temporal; residual, shared and
 // gamma rows use the default policy; y and x_out are stored non-temporal,
 // which streams them out instead of leaving them dirty in L2 for the end of
@@ -67,8 +68,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
     const uint4 sa = buf_load16<kPlain>(r_sh, tok + o0), sb = buf_load16<kPlain>(r_sh, tok + o1);
     const uint4 ga = buf_load16<kPlain>(r_g, o0), gb = buf_load16<kPlain>(r_g, o1);
 
-    // 3. the dispatched entries' rows in groups of kGroup; entries that were
-    //    not dispatched (row -1) or point outside the buffer are skipped
+    // 3. the dispatched entries' rows through kGroup register slots; entries
+    //    that were not dispatched (row -1) or point outside the buffer are skipped
     if (my_r >= Bs * K) {
         if (w == 0 && dev_err)
             atomicOr(dev_err, 8);
@@ -80,31 +81,61 @@ __global__ __launch_bounds__(kMaxThreads) void k_combine(
 #pragma unroll
     for (int j = 0; j < 16; ++j)
         acc[j] = 0.0f;
-    while (live) {
-        uint4 ea[kGroup], eb[kGroup];
-        float sk[kGroup];
+    uint4 ea[kGroup], eb[kGroup];
+    float sk[kGroup];
+    // the next dispatched entry in order of k into slot j (a far offset, weight 0, when
+    // none is left): its row's two parts and its weight
+    auto issue = [&](int j) {
+        uint32_t base = kNoRow;
+        sk[j] = 0.0f;
+        if (live) {
+            const int k = __builtin_ctzll(live);
+            live &= live - 1;
+            base = (uint32_t)__builtin_amdgcn_readlane(my_r, k) * rowb;
+            sk[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+        }
+        ea[j] = buf_load16<kStream>(r_eo, base + o0);
+        eb[j] = buf_load16<kStream>(r_eo, base + o1);
+    };
+    auto sum = [&](int j) {
+        float v[16];
+        unpack8(ea[j], v);
+        unpack8(eb[j], v + 8);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            acc[e] = fmaf(sk[j], v[e], acc[e]);
+    };
+    const bool two_groups = __popcll(live) > kGroup;  // the same in every wave of the block
+    if (!two_groups) {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+            issue(j);
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+            sum(j);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j)
+            issue(j);
+        // up to 2 * kGroup rows (K <= 16): each slot is refilled with the row kGroup
+        // entries later as soon as its row is summed, so the second group's loads go out
+        // while the first group is still arriving.  Rows are summed in the same order as
+        // with one group after the other.
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) {
-            uint32_t base = kNoRow;
-            sk[j] = 0.0f;
-            if (live) {
-                const int k = __builtin_ctzll(live);
-                live &= live - 1;
-                base = (uint32_t)__builtin_amdgcn_readlane(my_r, k) * rowb;
-                sk[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
-            }
-            ea[j] = buf_load16<kStream>(r_eo, base + o0);
-            eb[j] = buf_load16<kStream>(r_eo, base + o1);
+            sum(j);
+            // the sums are done and the slot is free before its next load goes out:
+            // without this the compiler hoists the second group's loads above the
+            // sums and keeps both groups in registers (216 instead of 120 VGPRs)
+#pragma unroll
+            for (int e = 0; e < 16; e += 4)
+                asm volatile("" : "+v"(acc[e]), "+v"(acc[e + 1]), "+v"(acc[e + 2]),
+                             "+v"(acc[e + 3])::"memory");
+            issue(j);
         }
 #pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-            float v[16];
-            unpack8(ea[j], v);
-            unpack8(eb[j], v + 8);
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[e] = fmaf(sk[j], v[e], acc[e]);
-        }
+        for (int j = 0; j < kGroup; ++j)
+            sum(j);
     }
 
     float xf[16];
