@@ -178,6 +178,11 @@ struct Mapped {
     template <typename Fn>
     __device__ void group(const int4 &v, Side sc, int g4, bool in, int &err, Fn &&f) const
     {
+        // a group past the end shares its first indices with the scalar tail's
+        // entries when N % 4 != 0: it visits nothing, since the token blocks'
+        // visitor also records the token's own entries and their outputs
+        if (!in)
+            return;
         const int idv[4] = {v.x, v.y, v.z, v.w};
         const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
         const int g0 = in ? g4 * 4 : 0;
