@@ -152,6 +152,10 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *                      code = E4M3(x / 2^se) rounded to nearest even and
  *                      saturated at +-448; expand_scales u8 [N, H/32] = se + 127
  *                      (E8M0 code of the dequantisation multiplier 2^se)
+ * Infinities and NaNs in x (the page defines no rule): every maximum skips
+ * NaN; an infinite maximum gives se = 127, or d = 127/inf = 0 with scale +inf
+ * (every int8 code 0); E4M3 codes NaN as 0x7F with its sign and +-inf as
+ * +-448; int8 codes NaN as 0; the static cast takes +-inf to 127 / -128.
  * Rows at or past offsets[E] of expand_x / expand_scales are not written.
  *
  *   x              bf16 [Bs, H]
