@@ -604,14 +604,53 @@ def config_table(moe, torch, n, only=None):
                                moe.n_scale_entries(wl.quant_mode, wl.H, wl.tile),
                                shared=wl.shared is not None)
         keys = ("update_expert", "dispatch", "update_dispatch", "combine")
-        rows.append({"config": name, "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E,
-                     "quant_mode": wl.quant_mode, "rows_dispatched": nrows,
-                     "buffer_sets": sets,
-                     **{k: {"avg_us": round(u, 3), "bytes": nb[k],
-                            "GBps": round(nb[k] / (u * 1e-6) / 1e9, 1),
-                            "frac": round(nb[k] / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-                        for k, u in zip(keys, us)}})
+        row = {"config": name, "Bs": wl.Bs, "H": wl.H, "K": wl.K, "E": wl.E,
+               "quant_mode": wl.quant_mode, "rows_dispatched": nrows, "buffer_sets": sets,
+               **{k: {"avg_us": round(u, 3), "bytes": nb[k],
+                      "GBps": round(nb[k] / (u * 1e-6) / 1e9, 1),
+                      "frac": round(nb[k] / (u * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                  for k, u in zip(keys, us)}}
+        if wl.quant_mode != 0:  # the measurement kernels move 8-bit dispatch rows
+            row["shape_ceilings"] = shape_ceilings(torch, wl, bufs[0]["d"]["assist_dst"], nrows, n)
+        del bufs, argv
+        rows.append(row)
     return rows
+
+
+def shape_ceilings(torch, wl, assist, nrows, n):
+    """The dispatch's and the combine's access shapes on this workload's own routing
+    (the measurement kernels of libmoe_calib.so, stores non-temporal as in the library,
+    buffers rotating through COLD_BYTES): what the part sustains for each kernel's
+    traffic in its block-per-token shape."""
+    from combine_expert_amd import calib
+    dev = torch.device("cuda")
+    Bs, H, K = wl.Bs, wl.H, wl.K
+    shared = wl.shared is not None
+    res = {}
+    db = Bs * H * 2 + Bs * K * 4 + nrows * H
+    nsets = cold_sets(db, hi=64)
+    xs = [torch.ones((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    outs = [torch.empty((nrows, H), dtype=torch.uint8, device=dev) for _ in range(nsets)]
+    us = _events_us(torch, lambda k: calib.scatter_shape(xs[k % nsets], assist, nrows,
+                                                         outs[k % nsets], calib.STORE_STREAM), n)
+    res["dispatch_shape"] = {"avg_us": round(us, 3), "bytes": db,
+                             "frac": round(db / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del xs, outs
+    cb = nrows * H * 2 + (2 if shared else 1) * Bs * H * 2 + H * 2 + Bs * K * 4 + 2 * Bs * H * 2
+    nsets = cold_sets(cb, hi=64)
+    eo = [torch.ones((nrows, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    aa = [torch.ones((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    bb = [torch.ones((Bs, H), dtype=torch.bfloat16, device=dev) if shared else None
+          for _ in range(nsets)]
+    o1 = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    o2 = [torch.empty((Bs, H), dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    g = torch.ones(H, dtype=torch.bfloat16, device=dev)
+    us = _events_us(torch, lambda k: calib.gather_shape(
+        eo[k % nsets], assist, aa[k % nsets], bb[k % nsets], g, nrows, o1[k % nsets],
+        o2[k % nsets], calib.STORE_STREAM), n)
+    res["combine_shape"] = {"avg_us": round(us, 3), "bytes": cb,
+                            "frac": round(cb / us / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 # ----------------------------------------------------------------- ceilings

@@ -67,15 +67,16 @@ def scatter_shape(x: torch.Tensor, assist: torch.Tensor, n_rows: int, out: torch
                                         out.data_ptr(), policy, _stream()))
 
 
-def gather_shape(rows: torch.Tensor, assist: torch.Tensor, a: torch.Tensor, b: torch.Tensor,
-                 gamma: torch.Tensor, n_rows: int, out1: torch.Tensor, out2: torch.Tensor,
-                 policy: int = STORE_STREAM):
+def gather_shape(rows: torch.Tensor, assist: torch.Tensor, a: torch.Tensor, b, gamma: torch.Tensor,
+                 n_rows: int, out1: torch.Tensor, out2: torch.Tensor, policy: int = STORE_STREAM):
+    """b may be None: the combine's shape without a shared expert."""
     Bs, H = a.shape
     K = assist.numel() // Bs
     for t in (rows, a, b, gamma, out1, out2):
-        assert t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous()
+        assert t is None or (t.dtype == torch.bfloat16 and t.is_cuda and t.is_contiguous())
     assert rows.numel() >= n_rows * H and assist.numel() == Bs * K
     _check("moe_calib_gather_shape",
            _lib.moe_calib_gather_shape(rows.data_ptr(), assist.data_ptr(), a.data_ptr(),
-                                       b.data_ptr(), gamma.data_ptr(), Bs, H, K, n_rows,
-                                       out1.data_ptr(), out2.data_ptr(), policy, _stream()))
+                                       None if b is None else b.data_ptr(), gamma.data_ptr(),
+                                       Bs, H, K, n_rows, out1.data_ptr(), out2.data_ptr(),
+                                       policy, _stream()))

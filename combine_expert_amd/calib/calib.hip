@@ -113,7 +113,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_gather_shape(
     const int e0 = part_elem(t, 0), e1 = part_elem(t, 1);
     const uint32_t o0 = e0 < H ? (uint32_t)e0 * 2 : kNoPart, o1 = e1 < H ? (uint32_t)e1 * 2 : kNoPart;
     const rsrc_t rr = buffer_rsrc(rows, (uint32_t)n_rows * rowb);
-    const rsrc_t ra = buffer_rsrc(a, (uint32_t)Bs * rowb), rb = buffer_rsrc(b, (uint32_t)Bs * rowb);
+    const rsrc_t ra = buffer_rsrc(a, (uint32_t)Bs * rowb);
+    const rsrc_t rb = buffer_rsrc(b ? b : a, b ? (uint32_t)Bs * rowb : 0u);  // no b: reads zeros
     const rsrc_t rg = buffer_rsrc(gamma, rowb);
     const uint32_t tok = (uint32_t)i * rowb;
     uint4 s0 = buf_load16<kPlain>(ra, tok + o0), s1 = buf_load16<kPlain>(ra, tok + o1);
@@ -250,8 +251,8 @@ int moe_calib_gather_shape(const void *rows, const int32_t *assist, const void *
                            void *out1, void *out2, int store_policy, void *stream)
 {
     using namespace moe;
-    if (!rows || !assist || !a || !b || !gamma || !out1 || !out2 || !aligned16(rows) ||
-        !aligned16(a) || !aligned16(b) || !aligned16(gamma) || !aligned16(out1) ||
+    if (!rows || !assist || !a || !gamma || !out1 || !out2 || !aligned16(rows) ||
+        !aligned16(a) || (b && !aligned16(b)) || !aligned16(gamma) || !aligned16(out1) ||
         !aligned16(out2) || bad_shape(Bs, H, K, n_rows) || bad_policy(store_policy))
         return MOE_CALIB_EINVAL;
     return status(by_policy<GatherK>(store_policy, dim3(Bs), dim3(row_threads(H)),

@@ -56,7 +56,8 @@ int moe_calib_scatter_shape(const void *x, const int32_t *assist, int Bs, int H,
 /*
  * The combine's access shape without its arithmetic: block i reads the rows
  * rows[assist[i*K + k]] (bf16 [n_rows, H]; -1 = skip), row i of a and of b
- * (bf16 [Bs, H]) and gamma (bf16 [H]), adds them as integers, and writes two
+ * (bf16 [Bs, H]; b may be NULL: the combine without a shared expert) and
+ * gamma (bf16 [H]), adds them as integers, and writes two
  * rows (out1[i], out2[i], bf16 [Bs, H]) -- the bytes the combine moves, in
  * its order, with one block barrier like the RMSNorm's.  Limits as
  * moe_calib_scatter_shape; stores take store_policy.

@@ -37,10 +37,11 @@ def test_scatter_shape(Bs, H, K):
     assert np.all(got[rows:] == 0xAB)
 
 
-@pytest.mark.parametrize("Bs,H,K", [(16, 1024, 4), (9, 7168, 8), (4, 8192, 16)])
-def test_gather_shape(Bs, H, K):
+@pytest.mark.parametrize("Bs,H,K,with_b", [(16, 1024, 4, True), (9, 7168, 8, True),
+                                            (4, 8192, 16, True), (5, 8192, 16, False)])
+def test_gather_shape(Bs, H, K, with_b):
     from combine_expert_amd import calib
-    say(f"[calib] gather shape Bs={Bs} H={H} K={K}")
+    say(f"[calib] gather shape Bs={Bs} H={H} K={K} second row={with_b}")
     rows_n = Bs * K - 2
     rng = np.random.default_rng(H + K)
     r = torch.from_numpy(rng.integers(0, 1 << 15, (rows_n, H), dtype=np.int16)).view(torch.bfloat16)
@@ -50,11 +51,11 @@ def test_gather_shape(Bs, H, K):
     asg = _assist(Bs, K, rows_n, K)
     o1 = torch.empty(Bs, H, dtype=torch.bfloat16, device="cuda")
     o2 = torch.empty(Bs, H, dtype=torch.bfloat16, device="cuda")
-    calib.gather_shape(r.cuda(), torch.from_numpy(asg).cuda(), a.cuda(), b.cuda(), g.cuda(),
-                       rows_n, o1, o2)
+    calib.gather_shape(r.cuda(), torch.from_numpy(asg).cuda(), a.cuda(),
+                       b.cuda() if with_b else None, g.cuda(), rows_n, o1, o2)
     w = lambda t: t.view(torch.int16).numpy().view(np.uint32).reshape(t.shape[0] if t.dim() > 1 else 1, -1).astype(np.uint64)
     rw, aw, bw = w(r), w(a), w(b)
-    exp1 = (aw + bw)
+    exp1 = (aw + bw) if with_b else aw.copy()  # without b its reads return zeros
     for f, rr in enumerate(asg):
         if rr >= 0:
             exp1[f // K] += rw[rr]
