@@ -97,6 +97,10 @@ def parse():
     p.add_argument("--gemm-dense", action="store_true",
                    help="with --gemm: one instance of all 4096 rows instead of the Zipf split "
                         "(context: a shape whose rounds of 256 x 256 tiles are whole)")
+    p.add_argument("--gemm-exponents", choices=("group-major", "row-major"),
+                   default="group-major",
+                   help="with --gemm: the activation exponents' layout (group-major: the "
+                        "dispatch's MOE_Q_MXFP8_GM output; row-major: its MOE_Q_MXFP8 output)")
     p.add_argument("--gemm-formats", action="store_true",
                    help="with --gemm: also time the int8 formats (off by default so that a "
                         "kernel trace of --gemm covers the mxfp8 kernel alone)")
@@ -913,13 +917,17 @@ def gemm_main(args):
     dev = torch.device("cuda")
     n_sets = 2   # two weight copies (2 x 235 MB) so a launch cannot hit in the 256 MB MALL
     a = torch.from_numpy(g.a).to(dev)
+    gm = args.gemm_exponents == "group-major"
+    mx_mode = moe.QUANT_MXFP8_GM if gm else moe.QUANT_MXFP8
     asc = torch.from_numpy(g.a_sc).to(dev)
+    if gm:   # [rows, H/32] -> [H/512, rows, 16] (H = 7168: whole groups, no pad)
+        asc = asc.view(g.rows, g.Kd // 512, 16).permute(1, 0, 2).contiguous()
     off = torch.from_numpy(g.offsets).to(dev)
     ws = [torch.from_numpy(g.w).to(dev) for _ in range(n_sets)]
     wss = [moe.pack_mx_weight_scales(torch.from_numpy(g.w_sc).to(dev)) for _ in range(n_sets)]
     ys = [torch.empty((g.rows, g.N), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
     argv = [(a.data_ptr(), asc.data_ptr(), off.data_ptr(), g.E, g.rows, ws[k].data_ptr(),
-             wss[k].data_ptr(), g.N, g.Kd, moe.QUANT_MXFP8, ys[k].data_ptr(), None,
+             wss[k].data_ptr(), g.N, g.Kd, mx_mode, ys[k].data_ptr(), None,
              stream.cuda_stream) for k in range(n_sets)]
     f = lib.moe_expert_gemm
 
@@ -995,7 +1003,8 @@ def gemm_main(args):
                                 "Zipf(1.2) draw, H=7168 -> N=4096 (gate and up projections), "
                                 "mxfp8 operands with E8M0 block scales, bf16 out"),
                    "E": g.E, "rows": rows_total, "counts": g.counts.tolist(), "N": g.N,
-                   "H": g.Kd, "weight_sets": n_sets},
+                   "H": g.Kd, "weight_sets": n_sets,
+                   "activation_exponents": args.gemm_exponents},
         "roofline": {"kernel": "k_expert_gemm_mx", "bound": "mfma", "achieved": round(tfs, 2),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tfs / FP8_PEAK_TFLOPS, 4), "traffic": traffic,

@@ -96,6 +96,7 @@ int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int 
     switch (quant_mode) {
     case MOE_Q_NONE:
     case MOE_Q_MXFP8:
+    case MOE_Q_MXFP8_GM:
         if (qs_kind != MOE_SCALES_NONE)
             return MOE_EINVAL;
         break;
@@ -117,6 +118,7 @@ int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int 
         break;
     case MOE_Q_INT8_TOKEN:
     case MOE_Q_MXFP8:
+    case MOE_Q_MXFP8_GM:
         if (!expand_scales)
             return MOE_EINVAL;
         break;
@@ -253,10 +255,10 @@ int moe_expert_gemm(const void *expand_x, const void *expand_scales,
     if (H < 128 || H > kMaxGemmDim || H % 128 != 0 || N < 128 || N > kMaxGemmDim ||
         N % 128 != 0)
         return MOE_EINVAL;
-    if (quant_mode < MOE_Q_NONE || quant_mode > MOE_Q_MXFP8)
+    if (quant_mode < MOE_Q_NONE || quant_mode > MOE_Q_MXFP8_GM)
         return MOE_EINVAL;
-    if (quant_mode != MOE_Q_MXFP8 && quant_mode != MOE_Q_INT8_TOKEN &&
-        quant_mode != MOE_Q_INT8_TILE)
+    if (quant_mode != MOE_Q_MXFP8 && quant_mode != MOE_Q_MXFP8_GM &&
+        quant_mode != MOE_Q_INT8_TOKEN && quant_mode != MOE_Q_INT8_TILE)
         return MOE_ENOTSUP;
     if (!aligned(expand_x, 16) || !aligned(weights, 16) || !aligned(y, 16) ||
         !aligned(expand_scales, 4) || !aligned(weight_scales, 4) ||

@@ -45,11 +45,17 @@
 
 namespace moe {
 
-// The host has checked the (mode, scales) pairing: modes 0 and 4 take no
+// The host has checked the (mode, scales) pairing: modes 0, 4 and 5 take no
 // scales, mode 1 takes one coefficient, one row or one row per instance,
-// modes 2 and 3 take none or one row per instance.
-static hipError_t launch_any(int quant_mode, const DispatchArgs &a, int src, hipStream_t stream)
+// modes 2 and 3 take none or one row per instance.  Mode 5 is mode 4 with the
+// exponents group-major: [H/512 rounded up][Bs*K rows][16 bytes].
+static hipError_t launch_any(int quant_mode, const DispatchArgs &args, int src,
+                             hipStream_t stream)
 {
+    DispatchArgs a = args;
+    const bool gm = quant_mode == 5;
+    a.sc_row = gm ? 16 : a.H / 32;
+    a.sc_group = gm ? 16 * a.Bs * a.K : 16;
     const bool pe = a.qs_kind == 3;
     switch (quant_mode) {
     case 0: return launch_mode0(a, src, false, stream);

@@ -304,6 +304,9 @@ struct DispatchArgs {
     const float *qs;             // scales input: [1], [H] or [E, H] by qs_kind, or null
     int qs_kind;                 // MOE_SCALES_*: 0 none, 1 one, 2 row, 3 one row per instance
     void *expand_x, *expand_scales;
+    // mxfp8 exponent b of row r sits at byte r * sc_row + (b / 16) * sc_group + b % 16:
+    // row-major (H / 32, 16) or group-major (16, 16 * Bs * K)
+    int sc_row, sc_group;
     int32_t *counts, *offsets, *expand_src, *assist_dst;
     int32_t *balanced_ids;       // mapped, may be null
     uint8_t *balanced_mask;      // mapped, may be null
@@ -776,9 +779,12 @@ __device__ __forceinline__ void store_row(const DispatchArgs &a, int t, bool has
                                                       (t * kChunk) / a.tile] = c.fscale;
             }
         }
-        if (MODE == 4 && (t & 1) == 0)
-            static_cast<uint8_t *>(a.expand_scales)[(size_t)rank[k] * (H / 32) + t / 2] =
+        if (MODE == 4 && (t & 1) == 0) {
+            const int b = t / 2;
+            static_cast<uint8_t *>(a.expand_scales)[(size_t)rank[k] * a.sc_row +
+                                                    (size_t)(b >> 4) * a.sc_group + (b & 15)] =
                 (uint8_t)(c.se + 127);
+        }
     }
 }
 

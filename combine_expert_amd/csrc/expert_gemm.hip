@@ -109,6 +109,11 @@ struct GemmArgs {
     uint16_t *y;             // [rows, N] bf16
     int32_t *dev_err;
     int E, rows, N, K;
+    // activation scale bytes: row r, byte offset `off` of the row-major layout, at
+    // r * x_pitch + (off / 16) * x_group + off % 16.  Row-major: (K / 32, 16); mxfp8
+    // exponents group-major ([K/512 rounded up][rows][16]): (16, 16 * rows).
+    int x_pitch;
+    size_t x_group;
 };
 
 struct Stage {
@@ -242,7 +247,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int nk = p.K / kBK;
-    const int kb = p.K / 32;                  // scale bytes per row
     const int g = lane >> 4;                  // lane group: K chunk / scale block
     const int r16 = lane & 15;
     const int wn = wave % kWavesN, wm = wave / kWavesN;   // the wave's part of the tile
@@ -283,7 +287,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
         p.w_sc + ((size_t)e * n_groups * p.N + min(n0 + (w_run ? wave : 0) * 64 + lane, p.N - 1)) * 16;
     const size_t wsc_group = (size_t)p.N * 16;   // bytes between groups
     const uint8_t *xsc_src =
-        p.a_sc + (size_t)min(m0 + (x_run ? x_idx : 0) * 64 + lane, row_hi - 1) * kb;
+        p.a_sc + (size_t)min(m0 + (x_run ? x_idx : 0) * 64 + lane, row_hi - 1) * p.x_pitch;
 
     // copies of K step s into stage s % kStages
     auto issue_data = [&](int s) {
@@ -303,12 +307,12 @@ __device__ __forceinline__ void run_tile(const GemmArgs &p, GemmSmem<GROUPED> &s
             if (kWeightStepScales && w_run)
                 dma16(wsc_src + (off >> 4) * wsc_group, lds_addr(&sc.w[wave * 64][0]));
             if (x_run)
-                dma16(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
+                dma16(xsc_src + (off >> 4) * p.x_group, lds_addr(&sc.x[x_idx * 64][0]));
         } else {
             if (kWeightStepScales && w_run)
                 dma4(wsc_src + (off >> 4) * wsc_group + (off & 15), lds_addr(&sc.w[wave * 64][0]));
             if (x_run)
-                dma4(xsc_src + off, lds_addr(&sc.x[x_idx * 64][0]));
+                dma4(xsc_src + (off >> 4) * p.x_group + (off & 15), lds_addr(&sc.x[x_idx * 64][0]));
         }
     };
 
@@ -688,7 +692,6 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int nk = p.K / kBK;
-    const int kb = p.K / 32;
     const int n_groups = nk / kScaleGroup;       // K % 512 == 0 on this path
     const int g = lane >> 4;
     const int r16 = lane & 15;
@@ -707,7 +710,7 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
     const int wj = wave - kWBM / 64;
     const bool w_run = wj >= 0 && wj < BN / 64;
     const uint8_t *xsc_src =
-        p.a_sc + (size_t)min(m0 + (x_run ? wave : 0) * 64 + lane, row_hi - 1) * kb;
+        p.a_sc + (size_t)min(m0 + (x_run ? wave : 0) * 64 + lane, row_hi - 1) * p.x_pitch;
     const uint8_t *wsc_src =
         p.w_sc + ((size_t)e * n_groups * p.N + min(n0 + (w_run ? wj : 0) * 64 + lane, p.N - 1)) * 16;
     const size_t wsc_group = (size_t)p.N * 16;
@@ -731,7 +734,7 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
     auto issue_scales = [&](int gi) {
         WScales &sc = sm.scale[gi & 1];
         if (x_run)
-            dma16(xsc_src + 16 * gi, lds_addr(&sc.x[wave * 64][0]));
+            dma16(xsc_src + gi * p.x_group, lds_addr(&sc.x[wave * 64][0]));
         if (w_run)
             dma16(wsc_src + gi * wsc_group, lds_addr(&sc.w[wj * 64][0]));
     };
@@ -947,9 +950,14 @@ hipError_t launch_expert_gemm(int quant_mode, const void *a, const void *a_sc,
                               const void *w_sc, int N, int K, uint16_t *y, int32_t *dev_err,
                               hipStream_t stream)
 {
+    // mode 5: mxfp8 with the activation exponents group-major, as the dispatch writes them
+    // for a buffer of `rows` rows
+    const bool x_gm = quant_mode == 5;
     GemmArgs p{static_cast<const uint8_t *>(a), static_cast<const uint8_t *>(a_sc), offsets,
                static_cast<const uint8_t *>(w), static_cast<const uint8_t *>(w_sc), y, dev_err,
-               E, rows, N, K};
+               E, rows, N, K, x_gm ? 16 : K / 32, x_gm ? (size_t)16 * rows : (size_t)16};
+    if (x_gm)
+        quant_mode = kModeMx;
     // Upper bound on row tiles: sum of ceil(rows_e / 128) <= ceil(rows / 128) + E.
     const long m_cap = (rows + kBM - 1) / kBM + E;
     const long tiles_cap = m_cap * ((N + kBN - 1) / kBN);

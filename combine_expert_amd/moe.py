@@ -18,6 +18,8 @@ from . import build as _build
 
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ELAUNCH = 0, 1, 2, 3
 QUANT_NONE, QUANT_STATIC, QUANT_INT8_TOKEN, QUANT_INT8_TILE, QUANT_MXFP8 = 0, 1, 2, 3, 4
+QUANT_MXFP8_GM = 5   # the mxfp8 codes, exponents group-major [ceil(H/512), rows, 16]
+_MX = (QUANT_MXFP8, QUANT_MXFP8_GM)
 SCALES_NONE, SCALES_ONE, SCALES_ROW, SCALES_EXPERT = 0, 1, 2, 3
 SHARED_PAGE, SHARED_ADD = 0, 1
 ERR_ID, ERR_TABLE, ERR_MASK1D, ERR_ROW, ERR_OFFSETS = 1, 2, 4, 8, 16
@@ -102,7 +104,7 @@ def _dispatch_args(x, expert_ids, Bs, H, K, E, quant_mode, tile, quant_scales, o
          N * H)
     ns = n_scale_entries(quant_mode, H, tile) if quant_mode != QUANT_INT8_TILE or tile > 0 else 0
     _arg(out.get("expand_scales"), "expand_scales",
-         (torch.uint8,) if quant_mode == QUANT_MXFP8 else _F32, N * ns, required=ns > 0)
+         (torch.uint8,) if quant_mode in _MX else _F32, N * ns, required=ns > 0)
     _arg(out["expert_counts"], "expert_counts", _I32, E)
     _arg(out["expert_offsets"], "expert_offsets", _I32, E + 1)
     _arg(out["expand_src"], "expand_src", _I32, N)
@@ -131,6 +133,8 @@ def n_scale_entries(quant_mode: int, H: int, tile: int = 0) -> int:
         return -(-H // tile)
     if quant_mode == QUANT_MXFP8:
         return H // 32
+    if quant_mode == QUANT_MXFP8_GM:
+        return -(-H // 512) * 16   # padded to whole groups of 16 exponents
     return 0
 
 
@@ -165,12 +169,14 @@ def dispatch_buffers(Bs: int, H: int, K: int, E: int, quant_mode: int, tile: int
     """Allocate the dispatch outputs for a shape (capacity Bs*K rows)."""
     N = Bs * K
     dt = {QUANT_NONE: torch.bfloat16, QUANT_STATIC: torch.int8, QUANT_INT8_TOKEN: torch.int8,
-          QUANT_INT8_TILE: torch.int8, QUANT_MXFP8: torch.uint8}[quant_mode]
+          QUANT_INT8_TILE: torch.int8, QUANT_MXFP8: torch.uint8,
+          QUANT_MXFP8_GM: torch.uint8}[quant_mode]
     ns = n_scale_entries(quant_mode, H, tile)
-    sdt = torch.uint8 if quant_mode == QUANT_MXFP8 else torch.float32
+    sdt = torch.uint8 if quant_mode in _MX else torch.float32
+    sshape = (ns // 16, N, 16) if quant_mode == QUANT_MXFP8_GM else (N, ns)
     return dict(
         expand_x=torch.empty((N, H), dtype=dt, device=device),
-        expand_scales=torch.empty((N, ns), dtype=sdt, device=device) if ns else None,
+        expand_scales=torch.empty(sshape, dtype=sdt, device=device) if ns else None,
         expert_counts=torch.empty((E,), dtype=torch.int32, device=device),
         expert_offsets=torch.empty((E + 1,), dtype=torch.int32, device=device),
         expand_src=torch.empty((N,), dtype=torch.int32, device=device),
@@ -300,8 +306,10 @@ def moe_expert_gemm(expand_x, expand_scales, expert_offsets, weights, weight_sca
                     quant_mode: int = QUANT_MXFP8, y=None, dev_err=None, stream=None):
     """Grouped GEMM of the expert computation -> y bf16 [rows, N] (rows outside every
     instance's range are not written).  mxfp8: expand_x u8 [rows, H] (E4M3),
-    expand_scales u8 [rows, H/32] (E8M0), weights u8 [E, N, H], weight_scales u8
-    [E, ceil(H/512), N, 16] (pack_mx_weight_scales of the [E, N, H/32] exponents).  int8 (QUANT_INT8_TOKEN / QUANT_INT8_TILE): expand_x int8 [rows, H],
+    expand_scales u8 [rows, H/32] (E8M0; QUANT_MXFP8_GM: the dispatch's group-major
+    [ceil(H/512), rows, 16] for a dispatch of rows = Bs*K), weights u8 [E, N, H],
+    weight_scales u8 [E, ceil(H/512), N, 16] (pack_mx_weight_scales of the [E, N, H/32]
+    exponents).  int8 (QUANT_INT8_TOKEN / QUANT_INT8_TILE): expand_x int8 [rows, H],
     expand_scales f32 [rows] / [rows, H/128], weights int8 [E, N, H], weight_scales f32
     [E, N].  expert_offsets int32 [E+1]."""
     rows, H = expand_x.shape
@@ -309,10 +317,11 @@ def moe_expert_gemm(expand_x, expand_scales, expert_offsets, weights, weight_sca
     N = weights.shape[1]
     if y is None:
         y = torch.empty((rows, N), dtype=torch.bfloat16, device=expand_x.device)
-    mx = quant_mode == QUANT_MXFP8
+    mx = quant_mode in _MX
     _arg(expand_x, "expand_x", _BYTE_TYPES[:2], rows * H)
     _arg(expand_scales, "expand_scales", (torch.uint8,) if mx else _F32,
-         rows * (H // 32 if mx else H // 128 if quant_mode == QUANT_INT8_TILE else 1))
+         rows * (n_scale_entries(quant_mode, H) if mx else
+                 H // 128 if quant_mode == QUANT_INT8_TILE else 1))
     _arg(expert_offsets, "expert_offsets", _I32, E + 1)
     _arg(weights, "weights", _BYTE_TYPES[:2], E * N * H)
     _arg(weight_scales, "weight_scales", (torch.uint8,) if mx else _F32,

@@ -54,7 +54,9 @@ typedef enum {
     MOE_Q_STATIC = 1,      /* static int8: code = sat(round_half_even(x * scales))     */
     MOE_Q_INT8_TOKEN = 2,  /* per-token dynamic int8                                    */
     MOE_Q_INT8_TILE = 3,   /* per-tile dynamic int8 ("pertile" / "pergroup")            */
-    MOE_Q_MXFP8 = 4        /* mxfp8: E4M3 codes, one E8M0 exponent per 32 elements      */
+    MOE_Q_MXFP8 = 4,       /* mxfp8: E4M3 codes, one E8M0 exponent per 32 elements      */
+    MOE_Q_MXFP8_GM = 5     /* the same codes, exponents group-major (moe_expert_gemm's
+                              order): a layout of case 5, not another format           */
 } moe_quant;
 
 /* Shape of the dispatch's scales input (dispatch page 计算公式: xFp32 =
@@ -152,6 +154,11 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *                      code = E4M3(x / 2^se) rounded to nearest even and
  *                      saturated at +-448; expand_scales u8 [N, H/32] = se + 127
  *                      (E8M0 code of the dequantisation multiplier 2^se)
+ *     MOE_Q_MXFP8_GM   the codes and exponents of MOE_Q_MXFP8, the exponents
+ *                      stored group-major: expand_scales u8 [ceil(H/512), N, 16],
+ *                      exponent b of row r at [b/16][r][b%16] (the pad bytes of a
+ *                      last, partial group are not written), so that the expert
+ *                      GEMM copies one group of 64 rows' exponents as 1 KB
  * Infinities and NaNs in x (the page defines no rule): every maximum skips
  * NaN; an infinite maximum gives se = 127, or d = 127/inf = 0 with scale +inf
  * (every int8 code 0); E4M3 codes NaN as 0x7F with its sign and +-inf as
@@ -165,7 +172,7 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *   quant_scales   f32, shape by quant_scales_kind (16-byte aligned for ROW and
  *                  EXPERT), or NULL with MOE_SCALES_NONE.  MOE_Q_STATIC takes
  *                  ONE, ROW or EXPERT; MOE_Q_INT8_TOKEN / _TILE take NONE or
- *                  EXPERT; MOE_Q_NONE and MOE_Q_MXFP8 take NONE (else MOE_EINVAL).
+ *                  EXPERT; MOE_Q_NONE and the mxfp8 modes take NONE (else MOE_EINVAL).
  *   expand_x       [N, H] elements of the mode's type (out)
  *   expand_scales  see above; NULL for MOE_Q_NONE and MOE_Q_STATIC (out)
  *   expert_counts  int32 [E]  (out)      expert_offsets int32 [E+1] (out)
@@ -272,8 +279,11 @@ int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
  * integer sums are exact (int32), scaling and the sum over tiles are fp32.
  *
  *   expand_x       E4M3 or int8 [rows, H]                    16-byte aligned
- *   expand_scales  mxfp8: u8 E8M0 [rows, H/32]; per token: f32 [rows];
- *                  per tile: f32 [rows, H/128]               4-byte aligned
+ *   expand_scales  mxfp8: u8 E8M0 [rows, H/32] (MOE_Q_MXFP8), or group-major
+ *                  [H/512 rounded up, rows, 16] (MOE_Q_MXFP8_GM: the dispatch's
+ *                  layout for N = rows, so rows is the N of that call, the
+ *                  capacity Bs*K); per token: f32 [rows]; per tile: f32
+ *                  [rows, H/128]                             4-byte aligned
  *   expert_offsets int32 [n_instances+1] (moe_dispatch's offsets, or a slice
  *                  of them for a subset of instances; values are absolute rows)
  *   weights        E4M3 or int8 [n_instances, N, H]          16-byte aligned
@@ -291,8 +301,8 @@ int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
  *                  clamped into [0, rows] and the output is unspecified
  *                  (but no access leaves the buffers)
  * Limits: 1 <= n_instances <= 1024, 0 <= rows <= 4194304, H and N multiples of
- * 128 in [128, 16384], quant_mode MOE_Q_MXFP8, MOE_Q_INT8_TOKEN or
- * MOE_Q_INT8_TILE (MOE_Q_NONE and MOE_Q_STATIC: MOE_ENOTSUP).
+ * 128 in [128, 16384], quant_mode MOE_Q_MXFP8, MOE_Q_MXFP8_GM, MOE_Q_INT8_TOKEN
+ * or MOE_Q_INT8_TILE (MOE_Q_NONE and MOE_Q_STATIC: MOE_ENOTSUP).
  */
 int moe_expert_gemm(const void *expand_x, const void *expand_scales,
                     const int32_t *expert_offsets, int n_instances, int rows,

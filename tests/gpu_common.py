@@ -79,9 +79,34 @@ def gpu_dispatch(wl, ids, mask, x=None, poison=True, dev_err=None):
                           active_mask=mask, out=out, dev_err=dev_err)
 
 
+QUANT_MXFP8_GM = 5  # the mxfp8 codes with the exponents stored group-major
+
+
 def oracle_dispatch(wl, ids, mask, x_bits=None):
+    """The oracle's dispatch; the group-major mxfp8 mode is the mxfp8 case of the pages
+    stored in another order, so the oracle computes case 5 and check_dispatch permutes."""
     xb = bits(wl.x) if x_bits is None else x_bits
-    return oracle.dispatch(xb, ids, mask, wl.n_ranks, wl.local_experts, wl.quant_mode, wl.tile)
+    mode = 4 if wl.quant_mode == QUANT_MXFP8_GM else wl.quant_mode
+    return oracle.dispatch(xb, ids, mask, wl.n_ranks, wl.local_experts, mode, wl.tile)
+
+
+def gm_to_row_major(gm, N, H):
+    """Group-major exponents [ceil(H/512), N, 16] -> row-major [N, H/32] (a permutation;
+    the pad bytes of a partial last group are dropped)."""
+    G = -(-H // 512)
+    g = np.asarray(gm, dtype=np.uint8).reshape(G, N, 16)
+    return np.ascontiguousarray(g.transpose(1, 0, 2).reshape(N, G * 16)[:, :H // 32])
+
+
+def row_major_to_gm(sc, H):
+    """Row-major exponents [N, H/32] -> group-major [ceil(H/512), N, 16]; the pad bytes of a
+    partial last group hold 0xFF (the E8M0 NaN), which no reader may use."""
+    sc = np.asarray(sc, dtype=np.uint8)
+    N = sc.shape[0]
+    G = -(-H // 512)
+    padded = np.full((N, G * 16), 0xFF, np.uint8)  # pad: E8M0 NaN, never read
+    padded[:, :H // 32] = sc
+    return np.ascontiguousarray(padded.reshape(N, G, 16).transpose(1, 0, 2))
 
 
 def check_dispatch(wl, g, o):
@@ -97,8 +122,15 @@ def check_dispatch(wl, g, o):
     np.testing.assert_array_equal(gx[:total], ox[:total])
     assert np.all(gx[total:] == POISON), "rows past the total were written"
     if o["scales"] is not None:
-        gs = g["expand_scales"].view(torch.uint8).cpu().numpy().reshape(N, -1)
         os_ = o["scales"].view(np.uint8).reshape(N, -1)
+        if wl.quant_mode == QUANT_MXFP8_GM:
+            G = -(-wl.H // 512)
+            raw = g["expand_scales"].view(torch.uint8).cpu().numpy().reshape(G, N, 16)
+            gs = gm_to_row_major(raw, N, wl.H)
+            pad = raw.transpose(1, 0, 2).reshape(N, G * 16)[:, wl.H // 32:]
+            assert np.all(pad == POISON), "pad bytes of the last group were written"
+        else:
+            gs = g["expand_scales"].view(torch.uint8).cpu().numpy().reshape(N, -1)
         np.testing.assert_array_equal(gs[:total], os_[:total])
         assert np.all(gs[total:] == POISON)
     return total

@@ -100,9 +100,10 @@ def test_dispatch_rejects_out_of_range_arguments():
     g = limits()["combine_shapes"]
     bad = [dict(Bs=0), dict(Bs=g["Bs"]["max"] + 1), dict(K=0), dict(K=g["K"]["max"] + 1),
            dict(H=g["H"]["min"] - 32), dict(H=g["H"]["max"] + 32), dict(H=7168 + 16),
-           dict(R=0), dict(L=0), dict(R=64, L=17), dict(R=1, L=4, K=8), dict(q=5), dict(q=-1),
+           dict(R=0), dict(L=0), dict(R=64, L=17), dict(R=1, L=4, K=8), dict(q=6), dict(q=-1),
            dict(x=None), dict(ids=None), dict(ex=None), dict(cnt=None), dict(off=None),
            dict(src=None), dict(asg=None), dict(q=2, sc=None), dict(q=4, sc=None),
+           dict(q=5, sc=None), dict(q=5, qs=P, qk=1),
            dict(q=3, tile=128, sc=None), dict(q=3, tile=0), dict(x=P + 8), dict(ex=P + 4),
            dict(ids=P + 4), dict(q=2, sc=P + 2), dict(mask=P + 1),
            # the scales input: shape named iff present, a shape the mode takes, aligned
@@ -158,7 +159,7 @@ def test_fused_update_dispatch_rejects_out_of_range_arguments():
            dict(nl=8, K=16), dict(F=1), dict(F=514), dict(R=0), dict(R=65), dict(x=None),
            dict(ids=None), dict(ids=P + 4), dict(sc=P + 4, thr=P), dict(thr=P + 1),
            dict(bi=P + 2), dict(q=3, tile=0), dict(q=7), dict(asg=None), dict(q=1),
-           dict(q=3, qs=P, qk=1)]
+           dict(q=3, qs=P, qk=1), dict(q=5, esc=None)]
     for kw in bad:
         assert fused(**kw) == 1, kw
     # a table too large to stage in LDS, odd tiles: not supported
@@ -179,7 +180,7 @@ def test_expert_gemm_rejects_out_of_range_arguments():
     bad = [dict(a=None), dict(asc=None), dict(off=None), dict(w=None), dict(wsc=None),
            dict(y=None), dict(E=0), dict(E=1025), dict(rows=-1), dict(rows=(1 << 22) + 1),
            dict(H=7168 + 32), dict(H=0),
-           dict(H=16384 + 128), dict(N=100), dict(N=0), dict(N=16384 + 128), dict(q=5),
+           dict(H=16384 + 128), dict(N=100), dict(N=0), dict(N=16384 + 128), dict(q=6),
            dict(q=-1), dict(a=P + 8), dict(w=P + 4), dict(y=P + 8), dict(asc=P + 2),
            dict(wsc=P + 1), dict(off=P + 2), dict(err=P + 1)]
     for kw in bad:
