@@ -774,7 +774,6 @@ __device__ __forceinline__ void run_wtile(const GemmArgs &p, WSmem &sm, int e, i
             load_group(sm.scale[(s / kScaleGroup) & 1]);
 
         const WStage &st = sm.stage[s & 1];
-        const WScales &sc = sm.scale[(s / kScaleGroup) & 1];
         const int sw = s % kScaleGroup;
         // all activation fragments first (32 registers), then the weight fragments one
         // ahead of the four MFMAs that use each
