@@ -5,7 +5,8 @@ test_gpu_parity.full_chain), and through the fused mapping + dispatch
 8192 in steps of 32, K from 1 to 16, up to 1024 instances, every quant mode
 but the static one (it takes the scales input; test_gpu_scales sweeps it) with
 power-of-two tiles from 16 to 1024, pruning, prefix token masks,
-replicated tables and the shared expert drawn independently.  Shapes where
+replicated tables and the shared expert drawn independently (and 16 draws in
+the group-major mxfp8 layout).  Shapes where
 Bs*K is not a multiple of 4 exercise the scalar tail of the entry loop.
 """
 import numpy as np
@@ -52,5 +53,18 @@ def test_random_case(seed):
     wl = W.make_small(seed, c["Bs"], c["H"], c["K"], c["ranks"], c["local"], c["mode"],
                       c["tile"], prune=c["prune"], shared=c["shared"],
                       token_mask_prefix=c["prefix"], replicas=c["replicas"])
+    full_chain(wl)
+    check_fused(wl)
+
+
+@pytest.mark.parametrize("seed", range(2000, 2016))
+def test_random_case_group_major_exponents(seed):
+    """The same draws in the group-major mxfp8 layout (quant mode 5): H takes any multiple
+    of 32, so most draws end in a partial last group of exponents."""
+    c = draw(seed)
+    say(f"[sweep] {seed}, group-major mxfp8: {c}")
+    wl = W.make_small(seed, c["Bs"], c["H"], c["K"], c["ranks"], c["local"], 5, 128,
+                      prune=c["prune"], shared=c["shared"], token_mask_prefix=c["prefix"],
+                      replicas=c["replicas"])
     full_chain(wl)
     check_fused(wl)
