@@ -2,7 +2,7 @@
  * moe_calib.h -- C ABI of libmoe_calib.so: measurement kernels that move
  * bytes in the shapes of the MoE dispatch and combine kernels but compute
  * nothing the method needs.  They give the ceilings the method's kernels are
- * judged against on the same device (a plain streaming copy, streams with the
+ * compared with on the same device (a plain streaming copy, streams with the
  * read/write mix of each kernel, and the kernels' own access shapes with the
  * arithmetic taken out).  Nothing here is part of the dispatch / combine path.
  *
