@@ -503,27 +503,31 @@ def time_stack(moe, torch, n_layers, replays, warmup):
 
 # ----------------------------------------------------------------- dispatch variants
 
-VARIANTS = [  # (quant mode, scales kind, tile) at the c3 shapes
-    (1, 1, 0), (1, 2, 0), (1, 3, 0), (2, 0, 0), (2, 3, 0), (3, 0, 128), (3, 3, 128)]
+VARIANTS = [  # (quant mode, scales kind, tile) at the c3 shapes; mode 5: mxfp8, exponents
+    # in the expert GEMM's group-major order
+    (1, 1, 0), (1, 2, 0), (1, 3, 0), (2, 0, 0), (2, 3, 0), (3, 0, 128), (3, 3, 128), (4, 0, 0),
+    (5, 0, 0)]
 
 
 def dispatch_variant_bytes(Bs, H, K, E, rows, mode, kind, tile):
-    """Algorithmic bytes of one dispatch: the scales input read once, int8 rows."""
+    """Algorithmic bytes of one dispatch: the scales input read once, one byte per code."""
     N = Bs * K
     qs = {0: 0, 1: 4, 2: H * 4, 3: E * H * 4}[kind]
-    sc = {1: 0, 2: 4, 3: 4 * -(-H // tile) if tile else 0}[mode]
+    sc = {1: 0, 2: 4, 3: 4 * -(-H // tile) if tile else 0, 4: H // 32, 5: H // 32}[mode]
     return (Bs * H * 2 + N * 4 + N + qs + rows * H + rows * sc + E * 4 + (E + 1) * 4 + 2 * N * 4)
 
 
-def dispatch_variants(moe, torch, n, sets=5):
+def dispatch_variants(moe, torch, n):
     """Per-launch duration (HIP events around n back-to-back launches over
-    rotating buffer sets) of moe_dispatch in the static and scaled modes."""
+    rotating buffer sets) of moe_dispatch in the static and scaled modes, and in mxfp8
+    with either exponent layout."""
     from combine_expert_amd import workloads as W
     out = []
     for mode, kind, tile in VARIANTS:
         wl = W.make_c3(seed=3200 + mode, quant_mode=mode, with_expert_out=False)
         wl.tile = tile
         dev = torch.device("cuda")
+        sets = cold_sets(wl.Bs * wl.H * 2 + wl.Bs * wl.K * wl.H, hi=64)
         qs = W.make_quant_scales(3300 + mode * 10 + kind, kind, wl.E, wl.H)
         qs = None if qs is None else qs.to(dev)
         ids = wl.logical_ids.to(dev)  # identity table: logical ids are instance ids
@@ -551,7 +555,8 @@ def dispatch_variants(moe, torch, n, sets=5):
         nb = dispatch_variant_bytes(wl.Bs, wl.H, wl.K, wl.E, rows, mode, kind, tile)
         out.append({"quant_mode": mode, "scales": ["none", "one", "row", "per-instance"][kind],
                     "tile": tile, "avg_us": round(us, 3), "bytes": nb,
-                    "GBps": round(nb / (us * 1e-6) / 1e9, 1)})
+                    "GBps": round(nb / (us * 1e-6) / 1e9, 1), "buffer_sets": sets})
+        del bufs
     return out
 
 
