@@ -201,7 +201,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const uint8_t *active
  * Every dispatch block maps the entries it counts through an LDS copy of the
  * table, which saves the second launch but repeats the mapping in each of the
  * Bs + 1 blocks: measured on MI355X it pays off up to about Bs*K = 4096
- * entries (Bs=512, K=8: 10.2 us against 3.3 + 8.6 us for the two calls) and
+ * entries (Bs=512, K=8: 10.2 us against 3.3 + 9.0 us for the two calls) and
  * not at Bs*K = 8192 with pruning (Bs=512, K=16: 17.0 us against 3.5 + 10.9).
  * So above 4096 entries, when balanced_ids and balanced_mask are given (the
  * mask 4-byte aligned), the call enqueues the two launches itself; with either
