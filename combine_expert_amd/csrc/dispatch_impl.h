@@ -19,6 +19,13 @@ constexpr int kMaxTopK = 16;      // K limit: staged thresholds
 constexpr int kStageTab = 4;      // mapping-table words per thread staged through registers
 constexpr int kStageTok = 4;      // token-mask bytes per thread staged through registers
 
+// Above this many entries the routed dispatch loads the token's row after its id loop
+// rather than right after the first id batch.  Measured on MI355X, inputs cold: with
+// 8192 entries (Bs=512, K=16; 40 KB of ids and mask per block) the early row load held
+// the ids back (10.14 against 10.48 us), with 4096 it is the late one that costs (Bs=512,
+// K=8: 9.10 against 8.73 us; fused 11.38 against 10.16, so the mapped source keeps it early).
+constexpr int kLateRowEntries = 4096;
+
 // floor(a / d) for 0 <= a < 2^23, 1 <= d <= 1024: fp32 reciprocal estimate
 // (off by far less than one unit here) and one correction step.
 __device__ __forceinline__ int small_div(int a, int d)
@@ -788,7 +795,9 @@ __device__ __forceinline__ void store_row(const DispatchArgs &a, int t, bool has
     }
 }
 
-template <int MODE, int KMAX, typename Src, bool PE>
+// LATE: the token's row is loaded after the id loop instead of right after the first id
+// batch (routed entries above kLateRowEntries)
+template <int MODE, int KMAX, typename Src, bool PE, bool LATE>
 __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
 {
     // low 16 bits: active entries with id e; high: those before this token.
@@ -874,14 +883,22 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
             Stage<Src::kKeep> st;
             if (Src::kMapped)
                 st.issue(a);
-            const uint4 *src =
-                reinterpret_cast<const uint4 *>(a.x + (size_t)i * H) + 2 * (has ? t : 0);
-            xa = src[0];
-            xb = src[1];
+            if constexpr (!LATE) {
+                const uint4 *src =
+                    reinterpret_cast<const uint4 *>(a.x + (size_t)i * H) + 2 * (has ? t : 0);
+                xa = src[0];
+                xb = src[1];
+            }
             if (Src::kMapped)
                 st.store(a, s_tab, s_tok, s_thr);
             lds_barrier();  // histograms zeroed (and mapping data staged) before use
         });
+    if constexpr (LATE) {
+        const uint4 *src =
+            reinterpret_cast<const uint4 *>(a.x + (size_t)i * H) + 2 * (has ? t : 0);
+        xa = src[0];
+        xb = src[1];
+    }
     int my_id = -1;  // lane k: entry k's instance, -1 if not dispatched
     if constexpr (!Src::kMapped) {  // the token mask, when given, is staged in LDS
         const bool on = lane < K && (a.mask == nullptr || raw_m != 0) &&
@@ -986,29 +1003,35 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
     }
 }
 
-// routed entries (moe_dispatch); PE: one scales row per instance
-template <int MODE, int KMAX, bool PE>
+// routed entries (moe_dispatch); PE: one scales row per instance; LATE: see dispatch_body
+template <int MODE, int KMAX, bool PE, bool LATE>
 __global__ __launch_bounds__(kMaxThreads + kWave) void k_dispatch(DispatchArgs a)
 {
-    dispatch_body<MODE, KMAX, Routed, PE>(a);
+    dispatch_body<MODE, KMAX, Routed, PE, LATE>(a);
 }
 
 // mapped entries (moe_update_dispatch); KEEP: a token mask or thresholds
 template <int MODE, int KMAX, bool KEEP, bool PE>
 __global__ __launch_bounds__(kMaxThreads + kWave) void k_update_dispatch(DispatchArgs a)
 {
-    dispatch_body<MODE, KMAX, Mapped<KEEP>, PE>(a);
+    dispatch_body<MODE, KMAX, Mapped<KEEP>, PE, false>(a);
 }
 
 template <int MODE, int KMAX, typename Src, bool PE>
 void launch_kernel(const DispatchArgs &a, hipStream_t stream)
 {
     const dim3 grid(a.Bs + 1), block(dispatch_threads(a.H));
-    if constexpr (Src::kMapped)
+    if constexpr (Src::kMapped) {
         hipLaunchKernelGGL((k_update_dispatch<MODE, KMAX, Src::kKeep, PE>), grid, block,
                            (size_t)a.n_logical * a.F * sizeof(int), stream, a);
-    else
-        hipLaunchKernelGGL((k_dispatch<MODE, KMAX, PE>), grid, block, 0, stream, a);
+    } else if constexpr (KMAX == 16) {  // more than 4096 entries needs K > 8
+        if (a.Bs * a.K > kLateRowEntries)
+            hipLaunchKernelGGL((k_dispatch<MODE, KMAX, PE, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((k_dispatch<MODE, KMAX, PE, false>), grid, block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((k_dispatch<MODE, KMAX, PE, false>), grid, block, 0, stream, a);
+    }
 }
 
 template <int MODE, typename Src, bool PE>
