@@ -854,7 +854,8 @@ __device__ __forceinline__ void dispatch_body(const DispatchArgs &a)
         s_cnt[e] = 0;
 
     // 2. the packed histograms.  The token's row (16 elements per thread) is
-    //    loaded after the first batch of ids, so it stays in flight meanwhile.
+    //    loaded after the first batch of ids, so it stays in flight meanwhile
+    //    (with LATE, after the whole id loop).
     //    With the mapping fused in, the token's own entries are picked up on
     //    the way (s_my: instance or -1) and their update-expert outputs
     //    written there, which saves mapping them again after the loop.
