@@ -81,6 +81,9 @@ SMALL = [
     # (straight-line row loads) next to tokens with some or none (per-row branches)
     (118, 301, 7168, 8, 32, 8, 4, 0, True, True, 280, False),
     (119, 64, 2048, 8, 4, 8, 2, 0, True, True, None, True),
+    # above 4096 entries in the modes the larger cases do not cover
+    (120, 512, 1024, 12, 8, 16, 0, 0, True, True, None, False),
+    (121, 401, 2080, 11, 16, 8, 3, 32, False, True, 300, True),
 ]
 
 

@@ -70,6 +70,10 @@ SMALL = [
     (309, 512, 1024, 16, 1, 16, 2, 0, 3, True, False, 1.0),
     (310, 200, 1024, 2, 8, 128, 3, 1024, 3, False, True, 1.0),
     (311, 64, 2048, 4, 4, 8, 1, 0, 2, False, False, 1.0),
+    # above 4096 entries (the routed dispatch loads the row after its id loop)
+    (312, 512, 2048, 16, 8, 16, 1, 0, 1, True, False, 30.0),
+    (313, 300, 1024, 16, 4, 16, 3, 128, 3, False, True, 1.0),
+    (314, 257, 1056, 16, 16, 8, 1, 0, 3, True, False, 30.0),
 ]
 
 
