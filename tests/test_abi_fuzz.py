@@ -119,3 +119,24 @@ def test_gemm_validation(E, rows, N, H, q, o):
     got = gemm(a=ptr(a), asc=ptr(asc), off=ptr(off), E=E, rows=rows, w=ptr(w), wsc=ptr(wsc),
                N=N, H=H, q=q, y=ptr(y), err=ptr(err))
     assert got == expect
+
+
+@SETTINGS
+@given(Bs=bs, K=ks, nl=st.sampled_from([0, 1, 16, 512, 1024, 1025]),
+       F=st.sampled_from([0, 1, 2, 3, 513, 1025, 1026]),
+       ni=st.sampled_from([0, 1, 256, 1024, 1025]), sc_given=st.booleans(),
+       thr_given=st.booleans(), o=st.lists(offs, min_size=6, max_size=6))
+def test_update_expert_validation(Bs, K, nl, F, ni, sc_given, thr_given, o):
+    from tests.test_abi import update
+    ids, tab, oi, sc, thr, err = o
+    expect = ELAUNCH
+    if not (0 < Bs <= 512 and 0 < K <= 16) or nl <= 0 or nl > 1024 or K > nl:
+        expect = EINVAL
+    elif F < 2 or F > nl + 1 or ni <= 0 or ni > 1024:
+        expect = EINVAL
+    elif (ids % 4 or tab % 4 or oi % 4 or (sc_given and sc % 4) or (thr_given and thr % 4)
+          or err % 4):
+        expect = EINVAL
+    got = update(ids=ptr(ids), t=ptr(tab), oi=ptr(oi), sc=ptr(sc, not sc_given),
+                 thr=ptr(thr, not thr_given), err=ptr(err), Bs=Bs, K=K, nl=nl, F=F, ni=ni)
+    assert got == expect
