@@ -171,3 +171,22 @@ def test_chain_dispatch_to_gemm_group_major():
     yb = ys[QUANT_MXFP8_GM]
     assert_close(yb[rows], y64, abs64, H, "group-major chain")
     assert np.mean(yb[rows] == ref) > BIT_EQUAL_MIN
+
+
+def test_gemm_group_major_limits():
+    """The group pitch at the limits: K = 16384 (32 groups of exponents, the last group at
+    31 pitches), and 4194304 rows (a 64 MB group pitch; H = 128 reads part of one group,
+    so the per-step copies run), sampled against the oracle and equal to the row-major
+    launch on the sampled rows."""
+    g = W.make_gemm_case(7103, [200, 77, 129], 256, 16384)
+    say("[group-major] GEMM K = 16384")
+    y = run_gemm(g, QUANT_MXFP8_GM)
+    check_sampled(g, y, where="group-major K=16384")
+    np.testing.assert_array_equal(y, run_gemm(g, 4))
+    g = W.make_gemm_case(7106, [4194304 - 1000, 1000], 128, 128)
+    say("[group-major] GEMM 4194304 rows")
+    y = run_gemm(g, QUANT_MXFP8_GM)
+    extra = np.random.default_rng(7107).integers(0, g.rows, 64)
+    check_sampled(g, y, extra_rows=extra, where="group-major 4M rows")
+    rows = np.unique(np.concatenate([extra, [0, g.rows - 1]]))
+    np.testing.assert_array_equal(y[rows], run_gemm(g, 4)[rows])
