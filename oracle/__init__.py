@@ -141,7 +141,7 @@ def route(ids, mask, E: int):
 
 
 def n_scales(quant_mode: int, H: int, tile: int) -> int:
-    return {0: 0, 1: 0, 2: 1, 3: -(-H // tile) if tile > 0 else 0, 4: H // 32}[quant_mode]
+    return {0: 0, 1: 0, 2: 1, 3: -(-H // tile) if tile > 0 else 0, 4: H // 32, 6: 0}[quant_mode]
 
 
 SCALES_NONE, SCALES_ONE, SCALES_ROW, SCALES_EXPERT = 0, 1, 2, 3
@@ -150,9 +150,9 @@ SCALES_NONE, SCALES_ONE, SCALES_ROW, SCALES_EXPERT = 0, 1, 2, 3
 def dispatch(x_bits, ids, mask, n_ranks: int, local_experts: int, quant_mode: int,
              tile: int = 0, qscales=None, qscales_kind: int = SCALES_NONE):
     """Returns dict(expand_x, scales, counts, offsets, src, assist, err).
-    Rows past offsets[E] are zero (never written).  quant_mode 1 (static) and
-    the scales input (qscales_kind: 1 = [1], 2 = [H], 3 = [E, H]) go through
-    oracle_dispatch_scaled."""
+    Rows past offsets[E] are zero (never written).  quant_mode 1 (static int8),
+    6 (static E4M3, one coefficient) and the scales input (qscales_kind: 1 = [1],
+    2 = [H], 3 = [E, H]) go through oracle_dispatch_scaled."""
     x = _c(x_bits, np.uint16)
     Bs, H = x.shape
     ids = _c(ids, np.int32)
@@ -162,7 +162,7 @@ def dispatch(x_bits, ids, mask, n_ranks: int, local_experts: int, quant_mode: in
     E = n_ranks * local_experts
     if quant_mode == 0:
         ex = np.zeros((N, H), dtype=np.uint16)
-    elif quant_mode == 4:
+    elif quant_mode in (4, 6):
         ex = np.zeros((N, H), dtype=np.uint8)
     else:
         ex = np.zeros((N, H), dtype=np.int8)
@@ -178,7 +178,7 @@ def dispatch(x_bits, ids, mask, n_ranks: int, local_experts: int, quant_mode: in
     src = np.empty(N, dtype=np.int32)
     assist = np.empty(N, dtype=np.int32)
     err = np.zeros(1, dtype=np.int32)
-    if quant_mode == 1 or qscales_kind != SCALES_NONE:
+    if quant_mode in (1, 6) or qscales_kind != SCALES_NONE:
         qs = _c(qscales, np.float32)
         rc = lib().oracle_dispatch_scaled(_p(x), _p(ids), _p(mask), Bs, H, K, n_ranks,
                                           local_experts, quant_mode, tile, _p(qs), qscales_kind,

@@ -38,6 +38,10 @@
  *     to [-128, 127]; the scales input is one coefficient, one row of H
  *     shared by all experts, or one row per instance ([E, H], indexed by the
  *     instance a copy is sent to);
+ *   - the second static output type (garbled on the page; it takes the
+ *     (1,) scales shape only) is read as OCP E4M3, the type the mxfp8 mode
+ *     writes: the cast rounds to nearest even and saturates at +-448, and a
+ *     NaN product codes to 0x7F;
  *   - int8: dstTypeMax = 127, round half to even, clamp to [-127, 127],
  *     scale written = 1 / dynamicScales, all-zero segment -> codes 0, scale 0;
  *     if 127 / max overflows fp32 (max below about 3.7e-38), zero elements
@@ -200,6 +204,18 @@ static int8_t int8_cast(float v)
     if (r < -128.0f)
         r = -128.0f;
     return (int8_t)r;
+}
+
+/* [DSP] case 2 (static) with the second output type, read as OCP E4M3:
+ * quantOut = Cast(xFp32, E4M3), the cast of CastToFp8 (nearest, ties to the
+ * even code, saturated at +-448).  A NaN product (a NaN in x, or an infinity
+ * times a zero coefficient) codes to 0x7F: its sign is not fixed across
+ * processors, so the code does not follow it. */
+static uint8_t e4m3_static_cast(float v)
+{
+    if (v != v)
+        return 0x7F;
+    return e4m3_from_float(v);
 }
 
 /* [DSP] case 5: sharedExp = floor(log2(max|x|)) - emax with emax = 8;
@@ -444,6 +460,7 @@ int oracle_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, 
 
 /* [DSP] cases 2-4 with the scales input: xFp32 = CastToFp32(X) * scales, then
  *   quant_mode 1 (static):     code = Cast(xFp32, int8)            (int8_cast)
+ *   quant_mode 6 (static):     code = Cast(xFp32, E4M3)            (e4m3_static_cast)
  *   quant_mode 2 (per token):  the dynamic int8 quantiser on xFp32
  *   quant_mode 3 (per tile):   the same per tile of `tile` elements
  * The scale applied to element j of the copy of token i sent to instance e is
@@ -452,7 +469,10 @@ int oracle_dispatch(const uint16_t *x, const int32_t *ids, const uint8_t *mask, 
  * each one fp32 multiply.  Every (token, instance) copy is quantised on its
  * own (with kinds 0-2 all copies of a token are equal).  Outputs as
  * oracle_dispatch; quant_mode 1 writes no scales (expand_scales unused).
- * quant_mode 1 needs qscales_kind >= 1; modes 0 and 4 are oracle_dispatch's. */
+ * quant_mode 1 needs qscales_kind >= 1; modes 0 and 4 are oracle_dispatch's.
+ * quant_mode 6 (the second static output type) takes one coefficient only
+ * (qscales_kind 1: the quantMode constraints allow that type the (1,) shape
+ * alone) and writes E4M3 bytes and no scales. */
 int oracle_dispatch_scaled(const uint16_t *x, const int32_t *ids, const uint8_t *mask, int Bs,
                            int H, int K, int n_ranks, int local_experts, int quant_mode,
                            int tile, const float *qscales, int qscales_kind, void *expand_x,
@@ -461,9 +481,11 @@ int oracle_dispatch_scaled(const uint16_t *x, const int32_t *ids, const uint8_t 
 {
     if (Bs <= 0 || H <= 0 || K <= 0 || n_ranks <= 0 || local_experts <= 0)
         return -1;
-    if (quant_mode < 1 || quant_mode > 3 || qscales_kind < 0 || qscales_kind > 3)
+    if (quant_mode < 1 || (quant_mode > 3 && quant_mode != 6) || qscales_kind < 0 ||
+        qscales_kind > 3)
         return -1;
-    if ((quant_mode == 1 && qscales_kind == 0) || (qscales_kind != 0 && qscales == NULL))
+    if ((quant_mode == 1 && qscales_kind == 0) || (quant_mode == 6 && qscales_kind != 1) ||
+        (qscales_kind != 0 && qscales == NULL))
         return -1;
     if (quant_mode == 3 && tile <= 0)
         return -1;
@@ -492,7 +514,11 @@ int oracle_dispatch_scaled(const uint16_t *x, const int32_t *ids, const uint8_t 
             v[j] = qscales_kind == 0 ? bf16_value(xi[j]) : bf16_value(xi[j]) * s;
         }
         int8_t *q = (int8_t *)expand_x + (size_t)r * H;
-        if (quant_mode == 1) {
+        if (quant_mode == 6) {
+            uint8_t *c = (uint8_t *)expand_x + (size_t)r * H;
+            for (int j = 0; j < H; ++j)
+                c[j] = e4m3_static_cast(v[j]);
+        } else if (quant_mode == 1) {
             for (int j = 0; j < H; ++j)
                 q[j] = int8_cast(v[j]);
         } else if (quant_mode == 2) {

@@ -53,6 +53,10 @@ MUTANTS = [
     ("smoothing_dropped", "v[j] = qscales_kind == 0 ? bf16_value(xi[j]) : bf16_value(xi[j]) * s;",
      "v[j] = bf16_value(xi[j]);"),
     ("static_row_index", "s = qscales[j];", "s = qscales[H - 1 - j];"),
+    ("static_e4m3_nan_signed", "    if (v != v)\n        return 0x7F;\n    return e4m3_from_float(v);",
+     "    return e4m3_from_float(v);"),
+    ("static_e4m3_unscaled", "c[j] = e4m3_static_cast(v[j]);",
+     "c[j] = e4m3_static_cast(bf16_value(xi[j]));"),
     ("pruned_weight_counted", "int r = assist[i * K + k];\n                if (r < 0)\n                    continue;\n                double s = scales[i * K + k];\n                ws += s;",
      "int r = assist[i * K + k];\n                double s = scales[i * K + k];\n                ws += s;\n                if (r < 0)\n                    continue;"),
     ("e4m3_decode_bias", "v = ldexp(8.0 + m, ef - 10);", "v = ldexp(8.0 + m, ef - 9);"),

@@ -165,3 +165,112 @@ def test_rejects_static_without_scales():
     rng, x, ids, E = case(170)
     with pytest.raises(ValueError):
         oracle.dispatch(x, ids, None, 2, 3, 1, 0)
+
+
+# ---- static quantisation, second output type (read as OCP E4M3), one coefficient
+
+def e4m3_table():
+    """Value of each of the 256 E4M3 codes from the format definition (sign bit,
+    4 exponent bits with bias 7, 3 mantissa bits, exponent 0 subnormal with step
+    2^-9, S.1111.111 NaN); NaN codes as nan."""
+    c = np.arange(256)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c >= 128, -mag, mag)
+
+
+E4M3 = e4m3_table()
+
+
+def brute_e4m3(v):
+    """Nearest finite E4M3 code to each value after saturation to +-448, ties to the
+    even code (even mantissa); zeros and values that round to zero keep their sign;
+    NaN -> 0x7F."""
+    v = np.asarray(v, dtype=np.float64).ravel()
+    out = np.empty(v.size, dtype=np.uint8)
+    pos = np.arange(128)[~np.isnan(E4M3[:128])]
+    for j, x in enumerate(v):
+        if x != x:
+            out[j] = 0x7F
+            continue
+        a = min(abs(x), 448.0)
+        dist = np.abs(E4M3[pos] - a)
+        cand = pos[dist == dist.min()]
+        c = cand[0] if cand.size == 1 else cand[cand % 2 == 0][0]
+        out[j] = c | (0x80 if np.signbit(x) else 0)
+    return out
+
+
+def test_e4m3_table_against_torch():
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(np.isnan(codes), np.isnan(E4M3))
+    ok = ~np.isnan(E4M3)
+    np.testing.assert_array_equal(codes[ok].astype(np.float64), E4M3[ok])
+
+
+def test_static_e4m3_brute_force():
+    rng, x, ids, E = case(181, scale=60.0)
+    Bs, H = x.shape
+    K = ids.shape[1]
+    qs = np.array([rng.uniform(0.5, 9.0)], np.float32)
+    o = oracle.dispatch(x, ids, None, 2, 3, 6, 0, qs, 1)
+    assert o["scales"] is None and o["expand_x"].dtype == np.uint8
+    xv = bf16_vals(x)
+    for f in range(Bs * K):
+        i, r = f // K, o["assist"][f]
+        v = xv[i] * qs[0]  # numpy float32 product (IEEE)
+        np.testing.assert_array_equal(o["expand_x"][r], brute_e4m3(v))
+
+
+def test_static_e4m3_against_torch():
+    """Small, tiny and large products: the clamped fp32 product through torch's
+    float8_e4m3fn conversion (round to nearest even)."""
+    rng = np.random.default_rng(182)
+    H = 512
+    mag = np.exp2(rng.uniform(-14, 11, size=(6, H)))
+    x = bf16_bits_of(mag * rng.choice([-1.0, 1.0], size=mag.shape))
+    ids = np.arange(6, dtype=np.int32).reshape(6, 1) % 4
+    for s in (1.0, 0.3, 7.0):
+        qs = np.array([s], np.float32)
+        o = oracle.dispatch(x, ids, None, 2, 2, 6, 0, qs, 1)
+        v = np.clip(bf16_vals(x) * np.float32(s), -448.0, 448.0).astype(np.float32)
+        want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = np.stack([o["expand_x"][o["assist"][f]] for f in range(6)])
+        np.testing.assert_array_equal(got, want)
+
+
+def test_static_e4m3_hand_worked():
+    vals = [1.0, 1.0625, 1.1875, 3.0, 300.0, -300.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -10,
+            -np.inf, np.inf, 0.0, -0.0, 448.0, 464.0, 480.0, -2.0 ** -11]
+    want1 = [0x38, 0x38, 0x3A, 0x44, 0x79, 0xF9, 0x01, 0x00, 0x02, 0xFE, 0x7E, 0x00, 0x80,
+             0x7E, 0x7E, 0x7E, 0x80]
+    # times 2: 600 and 928 saturate; 1.0625 * 2 = 2.125 ties to 2.0; 2^-8 and 3 * 2^-9
+    # are still subnormal (the smallest normal is 2^-6)
+    want2 = [0x40, 0x40, 0x42, 0x4C, 0x7E, 0xFE, 0x02, 0x01, 0x03, 0xFE, 0x7E, 0x00, 0x80,
+             0x7E, 0x7E, 0x7E, 0x80]
+    n = len(vals)
+    x = bf16_bits_of([vals + [0.0] * (32 - n)])
+    assert np.array_equal(bf16_vals(x)[0, :n], np.float32(vals))  # exact in bf16
+    for s, want in ((1.0, want1), (2.0, want2)):
+        o = oracle.dispatch(x, np.array([[0]], np.int32), None, 1, 1, 6, 0,
+                            np.array([s], np.float32), 1)
+        assert o["expand_x"][0, :n].tolist() == want, s
+    # NaN inputs of either sign, and an infinity times a zero coefficient: 0x7F
+    nan = np.array([[0x7FC0, 0xFFC0, 0x7F80, 0xFF80] + [0] * 28], dtype=np.uint16)
+    o = oracle.dispatch(nan, np.array([[0]], np.int32), None, 1, 1, 6, 0,
+                        np.array([1.0], np.float32), 1)
+    assert o["expand_x"][0, :4].tolist() == [0x7F, 0x7F, 0x7E, 0xFE]
+    o = oracle.dispatch(nan, np.array([[0]], np.int32), None, 1, 1, 6, 0,
+                        np.array([0.0], np.float32), 1)
+    assert o["expand_x"][0, :4].tolist() == [0x7F, 0x7F, 0x7F, 0x7F]
+    assert o["expand_x"][0, 4:].tolist() == [0] * 28
+
+
+@pytest.mark.parametrize("kind", [0, 2, 3])
+def test_static_e4m3_takes_one_coefficient_only(kind):
+    rng, x, ids, E = case(183)
+    H = x.shape[1]
+    qs = {0: None, 2: np.ones(H, np.float32), 3: np.ones((E, H), np.float32)}[kind]
+    with pytest.raises(ValueError):
+        oracle.dispatch(x, ids, None, 2, 3, 6, 0, qs, kind)
