@@ -104,6 +104,10 @@ int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int 
         if (qs_kind == MOE_SCALES_NONE)
             return MOE_EINVAL;
         break;
+    case MOE_Q_STATIC_E4M3:
+        if (qs_kind != MOE_SCALES_ONE)
+            return MOE_EINVAL;
+        break;
     case MOE_Q_INT8_TOKEN:
     case MOE_Q_INT8_TILE:
         if (qs_kind != MOE_SCALES_NONE && qs_kind != MOE_SCALES_EXPERT)
@@ -115,6 +119,7 @@ int check_dispatch(const void *x, const int32_t *ids, int Bs, int H, int K, int 
     switch (quant_mode) {
     case MOE_Q_NONE:
     case MOE_Q_STATIC:
+    case MOE_Q_STATIC_E4M3:
         break;
     case MOE_Q_INT8_TOKEN:
     case MOE_Q_MXFP8:
@@ -255,7 +260,7 @@ int moe_expert_gemm(const void *expand_x, const void *expand_scales,
     if (H < 128 || H > kMaxGemmDim || H % 128 != 0 || N < 128 || N > kMaxGemmDim ||
         N % 128 != 0)
         return MOE_EINVAL;
-    if (quant_mode < MOE_Q_NONE || quant_mode > MOE_Q_MXFP8_GM)
+    if (quant_mode < MOE_Q_NONE || quant_mode > MOE_Q_STATIC_E4M3)
         return MOE_EINVAL;
     if (quant_mode != MOE_Q_MXFP8 && quant_mode != MOE_Q_MXFP8_GM &&
         quant_mode != MOE_Q_INT8_TOKEN && quant_mode != MOE_Q_INT8_TILE)

@@ -54,12 +54,14 @@ static hipError_t launch_any(int quant_mode, const DispatchArgs &args, int src,
 {
     DispatchArgs a = args;
     const bool gm = quant_mode == 5;
+    a.static_e4m3 = quant_mode == 6;  // the static kernel, E4M3 codes
     a.sc_row = gm ? 16 : a.H / 32;
     a.sc_group = gm ? 16 * a.Bs * a.K : 16;
     const bool pe = a.qs_kind == 3;
     switch (quant_mode) {
     case 0: return launch_mode0(a, src, false, stream);
-    case 1: return launch_mode1(a, src, pe, stream);
+    case 1:
+    case 6: return launch_mode1(a, src, pe, stream);
     case 2: return launch_mode2(a, src, pe, stream);
     case 3: return launch_mode3(a, src, pe, stream);
     default: return launch_mode4(a, src, false, stream);

@@ -310,6 +310,7 @@ struct DispatchArgs {
     int Bs, H, K, E, tile;
     const float *qs;             // scales input: [1], [H] or [E, H] by qs_kind, or null
     int qs_kind;                 // MOE_SCALES_*: 0 none, 1 one, 2 row, 3 one row per instance
+    int static_e4m3;             // mode 1: E4M3 codes in place of int8 (one coefficient)
     void *expand_x, *expand_scales;
     // mxfp8 exponent b of row r sits at byte r * sc_row + (b / 16) * sc_group + b % 16:
     // row-major (H / 32, 16) or group-major (16, 16 * Bs * K)
@@ -532,6 +533,24 @@ __device__ __forceinline__ int bf16_ilogb(uint32_t m)
     return ex ? ex - 127 : (31 - __clz((int)(m & 0x7f))) - 133;
 }
 
+// E4M3 codes of 16 fp32 values for the static mode's second output type: the
+// saturating conversion of e4m3_codes, then the NaN code 0x7F in place of each
+// NaN value (a NaN in x, or an infinity times a zero coefficient), whose sign
+// is not kept: the sign of such a product is not the same on every processor.
+__device__ __forceinline__ uint4 e4m3_static_codes(const float *v)
+{
+    uint4 code = e4m3_codes(v, 1.0f);
+    uint32_t c[4] = {code.x, code.y, code.z, code.w};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        if (v[e] != v[e]) {
+            const int sh = 8 * (e & 3);
+            c[e >> 2] = (c[e >> 2] & ~(0xffu << sh)) | (0x7fu << sh);
+        }
+    }
+    return make_uint4(c[0], c[1], c[2], c[3]);
+}
+
 // int8 codes of 16 fp32 values for the static mode: the nearest integer, ties
 // to even, saturated to [-128, 127]; NaN codes to 0.
 __device__ __forceinline__ uint4 int8_static_codes(const float *v)
@@ -717,7 +736,7 @@ __device__ __forceinline__ Coded code_row(const DispatchArgs &a, int t, bool has
 #pragma unroll
         for (int j = 0; j < 16; ++j)
             v[j] *= sv[j];
-        c.code = int8_static_codes(v);
+        c.code = a.static_e4m3 ? e4m3_static_codes(v) : int8_static_codes(v);
     } else if (MODE == 2) {
         const uint32_t m = amax_row;
         const float mf = __uint_as_float(m << 16);

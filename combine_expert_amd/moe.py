@@ -19,6 +19,7 @@ from . import build as _build
 MOE_OK, MOE_EINVAL, MOE_ENOTSUP, MOE_ELAUNCH = 0, 1, 2, 3
 QUANT_NONE, QUANT_STATIC, QUANT_INT8_TOKEN, QUANT_INT8_TILE, QUANT_MXFP8 = 0, 1, 2, 3, 4
 QUANT_MXFP8_GM = 5   # the mxfp8 codes, exponents group-major [ceil(H/512), rows, 16]
+QUANT_STATIC_E4M3 = 6  # static, E4M3 codes of x * one coefficient (no expand_scales)
 _MX = (QUANT_MXFP8, QUANT_MXFP8_GM)
 SCALES_NONE, SCALES_ONE, SCALES_ROW, SCALES_EXPERT = 0, 1, 2, 3
 SHARED_PAGE, SHARED_ADD = 0, 1
@@ -127,7 +128,7 @@ def n_scale_entries(quant_mode: int, H: int, tile: int = 0) -> int:
     """Scale entries per expand_x row for a quantisation mode."""
     if quant_mode == QUANT_INT8_TOKEN:
         return 1
-    if quant_mode == QUANT_STATIC:
+    if quant_mode in (QUANT_STATIC, QUANT_STATIC_E4M3):
         return 0
     if quant_mode == QUANT_INT8_TILE:
         return -(-H // tile)
@@ -170,7 +171,7 @@ def dispatch_buffers(Bs: int, H: int, K: int, E: int, quant_mode: int, tile: int
     N = Bs * K
     dt = {QUANT_NONE: torch.bfloat16, QUANT_STATIC: torch.int8, QUANT_INT8_TOKEN: torch.int8,
           QUANT_INT8_TILE: torch.int8, QUANT_MXFP8: torch.uint8,
-          QUANT_MXFP8_GM: torch.uint8}[quant_mode]
+          QUANT_MXFP8_GM: torch.uint8, QUANT_STATIC_E4M3: torch.uint8}[quant_mode]
     ns = n_scale_entries(quant_mode, H, tile)
     sdt = torch.uint8 if quant_mode in _MX else torch.float32
     sshape = (ns // 16, N, 16) if quant_mode == QUANT_MXFP8_GM else (N, ns)

@@ -55,8 +55,10 @@ typedef enum {
     MOE_Q_INT8_TOKEN = 2,  /* per-token dynamic int8                                    */
     MOE_Q_INT8_TILE = 3,   /* per-tile dynamic int8 ("pertile" / "pergroup")            */
     MOE_Q_MXFP8 = 4,       /* mxfp8: E4M3 codes, one E8M0 exponent per 32 elements      */
-    MOE_Q_MXFP8_GM = 5     /* the same codes, exponents group-major (moe_expert_gemm's
+    MOE_Q_MXFP8_GM = 5,    /* the same codes, exponents group-major (moe_expert_gemm's
                               order): a layout of case 5, not another format           */
+    MOE_Q_STATIC_E4M3 = 6  /* static, the second output type (read as E4M3; one
+                              coefficient only): code = E4M3(x * scale)               */
 } moe_quant;
 
 /* Shape of the dispatch's scales input (dispatch page 计算公式: xFp32 =
@@ -143,6 +145,12 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *     MOE_Q_NONE       bf16 [N, H] bit copy of x[i]
  *     MOE_Q_STATIC     int8 [N, H]: code = clamp(round_half_even(v), -128, 127),
  *                      NaN -> 0; no expand_scales (may be NULL)
+ *     MOE_Q_STATIC_E4M3  E4M3 [N, H]: code = E4M3(v) rounded to nearest even and
+ *                      saturated at +-448, a NaN v (NaN in x, or +-inf times a zero
+ *                      coefficient) -> 0x7F; no expand_scales (may be NULL).  The
+ *                      page's second static output type, whose name the extracted
+ *                      text lost, read as the E4M3 of case 5; the quantMode
+ *                      constraints give that type the one-coefficient shape only
  *     MOE_Q_INT8_TOKEN int8 [N, H]: m = max|v|, d = 127/m (fp32, IEEE),
  *                      code = clamp(round_half_even(x*d), -127, 127);
  *                      expand_scales f32 [N] = 1/d  (m == 0: codes 0, scale 0)
@@ -171,10 +179,11 @@ int moe_update_expert(const int32_t *expert_ids, const float *expert_scales,
  *   token_mask     u8 [Bs] or NULL
  *   quant_scales   f32, shape by quant_scales_kind (16-byte aligned for ROW and
  *                  EXPERT), or NULL with MOE_SCALES_NONE.  MOE_Q_STATIC takes
- *                  ONE, ROW or EXPERT; MOE_Q_INT8_TOKEN / _TILE take NONE or
- *                  EXPERT; MOE_Q_NONE and the mxfp8 modes take NONE (else MOE_EINVAL).
+ *                  ONE, ROW or EXPERT; MOE_Q_STATIC_E4M3 takes ONE;
+ *                  MOE_Q_INT8_TOKEN / _TILE take NONE or EXPERT; MOE_Q_NONE and
+ *                  the mxfp8 modes take NONE (else MOE_EINVAL).
  *   expand_x       [N, H] elements of the mode's type (out)
- *   expand_scales  see above; NULL for MOE_Q_NONE and MOE_Q_STATIC (out)
+ *   expand_scales  see above; NULL for MOE_Q_NONE and the static modes (out)
  *   expert_counts  int32 [E]  (out)      expert_offsets int32 [E+1] (out)
  *   expand_src     int32 [N]  (out)      assist_dst     int32 [N]   (out)
  *   dev_err        int32 [1] or NULL
@@ -302,7 +311,7 @@ int moe_combine_add_rmsnorm(const void *expert_out, const int32_t *assist_dst,
  *                  (but no access leaves the buffers)
  * Limits: 1 <= n_instances <= 1024, 0 <= rows <= 4194304, H and N multiples of
  * 128 in [128, 16384], quant_mode MOE_Q_MXFP8, MOE_Q_MXFP8_GM, MOE_Q_INT8_TOKEN
- * or MOE_Q_INT8_TILE (MOE_Q_NONE and MOE_Q_STATIC: MOE_ENOTSUP).
+ * or MOE_Q_INT8_TILE (MOE_Q_NONE and the static modes: MOE_ENOTSUP).
  */
 int moe_expert_gemm(const void *expand_x, const void *expand_scales,
                     const int32_t *expert_offsets, int n_instances, int rows,

@@ -104,6 +104,10 @@ int main()
     expect(dispatch(512, 4096, 8, 8, 8, MOE_Q_INT8_TOKEN, 0, nullptr, 0, tm.data()) == MOE_OK,
            "dispatch with a token mask");
     g_calls.clear();
+    expect(dispatch(512, 7168, 8, 32, 8, MOE_Q_STATIC_E4M3, 0, P<float>(), MOE_SCALES_ONE) ==
+               MOE_OK, "static E4M3 with one coefficient");
+    expect(g_calls.size() == 1 && g_last_q == MOE_Q_STATIC_E4M3, "static E4M3 launcher");
+    g_calls.clear();
     // the fused call: one launch up to 4096 entries, two above when the mapped outputs are given
     expect(fused(512, 8, 256, 2, 32, 8, MOE_Q_MXFP8, 0, true) == MOE_OK, "fused c3");
     expect(g_calls.size() == 1 && g_calls[0] == "update_dispatch", "fused c3 is one launch");
@@ -140,6 +144,8 @@ int main()
     expect(dispatch(512, 7168, 8, 32, 8, MOE_Q_INT8_TILE, 96, nullptr, 0) == MOE_ENOTSUP, "tile 96");
     expect(dispatch(512, 7168, 8, 32, 8, MOE_Q_STATIC, 0, nullptr, 0) == MOE_EINVAL,
            "static without scales");
+    expect(dispatch(512, 7168, 8, 32, 8, MOE_Q_STATIC_E4M3, 0, P<float>(), MOE_SCALES_ROW) ==
+               MOE_EINVAL, "static E4M3 with a scales row");
     expect(fused(512, 8, 256, 1, 32, 8, MOE_Q_MXFP8, 0, true) == MOE_EINVAL, "F = 1");
     expect(moe_combine_add_rmsnorm(P<void>(), P<int32_t>(), P<float>(), nullptr, P<void>(),
                                    P<void>(), -1.0f, 512, 7168, 8, 0, P<void>(), nullptr,

@@ -100,7 +100,7 @@ def test_dispatch_rejects_out_of_range_arguments():
     g = limits()["combine_shapes"]
     bad = [dict(Bs=0), dict(Bs=g["Bs"]["max"] + 1), dict(K=0), dict(K=g["K"]["max"] + 1),
            dict(H=g["H"]["min"] - 32), dict(H=g["H"]["max"] + 32), dict(H=7168 + 16),
-           dict(R=0), dict(L=0), dict(R=64, L=17), dict(R=1, L=4, K=8), dict(q=6), dict(q=-1),
+           dict(R=0), dict(L=0), dict(R=64, L=17), dict(R=1, L=4, K=8), dict(q=7), dict(q=-1),
            dict(x=None), dict(ids=None), dict(ex=None), dict(cnt=None), dict(off=None),
            dict(src=None), dict(asg=None), dict(q=2, sc=None), dict(q=4, sc=None),
            dict(q=5, sc=None), dict(q=5, qs=P, qk=1),
@@ -110,7 +110,9 @@ def test_dispatch_rejects_out_of_range_arguments():
            dict(q=1), dict(q=1, qk=1), dict(q=1, qs=P), dict(q=1, qs=P, qk=4),
            dict(q=1, qs=P, qk=-1), dict(q=0, qs=P, qk=1), dict(q=4, qs=P, qk=3),
            dict(q=2, qs=P, qk=1), dict(q=2, qs=P, qk=2), dict(q=3, tile=128, qs=P, qk=2),
-           dict(q=1, qs=P + 4, qk=2), dict(q=2, qs=P + 8, qk=3), dict(q=1, qs=P + 2, qk=1)]
+           dict(q=1, qs=P + 4, qk=2), dict(q=2, qs=P + 8, qk=3), dict(q=1, qs=P + 2, qk=1),
+           # the second static type takes one coefficient only
+           dict(q=6), dict(q=6, qs=P, qk=2), dict(q=6, qs=P, qk=3), dict(q=6, qs=P + 2, qk=1)]
     for kw in bad:
         assert dispatch(**kw) == 1, kw
     for kw in (dict(q=3, tile=96), dict(q=3, tile=8), dict(q=3, tile=2048)):
@@ -180,10 +182,10 @@ def test_expert_gemm_rejects_out_of_range_arguments():
     bad = [dict(a=None), dict(asc=None), dict(off=None), dict(w=None), dict(wsc=None),
            dict(y=None), dict(E=0), dict(E=1025), dict(rows=-1), dict(rows=(1 << 22) + 1),
            dict(H=7168 + 32), dict(H=0),
-           dict(H=16384 + 128), dict(N=100), dict(N=0), dict(N=16384 + 128), dict(q=6),
+           dict(H=16384 + 128), dict(N=100), dict(N=0), dict(N=16384 + 128), dict(q=7),
            dict(q=-1), dict(a=P + 8), dict(w=P + 4), dict(y=P + 8), dict(asc=P + 2),
            dict(wsc=P + 1), dict(off=P + 2), dict(err=P + 1)]
     for kw in bad:
         assert gemm(**kw) == 1, kw
-    for q in (0, 1):
+    for q in (0, 1, 6):
         assert gemm(q=q) == 2, q

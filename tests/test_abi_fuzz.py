@@ -57,7 +57,7 @@ def test_combine_validation(Bs, H, K, eps, mode, o, null):
 
 @SETTINGS
 @given(Bs=bs, H=hs, K=ks, R=st.sampled_from([0, 1, 2, 32, 64, 65]),
-       L=st.sampled_from([0, 1, 8, 16, 17]), q=st.sampled_from([-1, 0, 1, 2, 3, 4, 5, 6]),
+       L=st.sampled_from([0, 1, 8, 16, 17]), q=st.sampled_from([-1, 0, 1, 2, 3, 4, 5, 6, 7]),
        tile=st.sampled_from([-1, 0, 8, 16, 96, 128, 1024, 2048]),
        qk=st.sampled_from([-1, 0, 1, 2, 3, 4]), qs_null=st.booleans(), sc_null=st.booleans(),
        o=st.lists(offs, min_size=10, max_size=10))
@@ -73,9 +73,9 @@ def test_dispatch_validation(Bs, H, K, R, L, q, tile, qk, qs_null, sc_null, o):
         expect = EINVAL
     elif not qs_null and qs % (16 if qk in (2, 3) else 4):
         expect = EINVAL
-    elif q not in (0, 1, 2, 3, 4, 5):
+    elif q not in (0, 1, 2, 3, 4, 5, 6):
         expect = EINVAL
-    elif ((q in (0, 4, 5) and qk != 0) or (q == 1 and qk == 0) or
+    elif ((q in (0, 4, 5) and qk != 0) or (q == 1 and qk == 0) or (q == 6 and qk != 1) or
           (q in (2, 3) and qk not in (0, 3))):
         expect = EINVAL
     elif q in (2, 3, 4, 5) and sc_null:
@@ -101,7 +101,7 @@ def test_dispatch_validation(Bs, H, K, R, L, q, tile, qk, qs_null, sc_null, o):
        rows=st.sampled_from([-1, 0, 1, 4096, 1 << 22, (1 << 22) + 1]),
        N=st.sampled_from([0, 100, 128, 4096, 16384, 16512]),
        H=st.sampled_from([0, 128, 7168, 7200, 16384, 16512]),
-       q=st.sampled_from([-1, 0, 1, 2, 3, 4, 5, 6]),
+       q=st.sampled_from([-1, 0, 1, 2, 3, 4, 5, 6, 7]),
        o=st.lists(offs, min_size=7, max_size=7))
 def test_gemm_validation(E, rows, N, H, q, o):
     a, asc, off, w, wsc, y, err = o
@@ -110,7 +110,7 @@ def test_gemm_validation(E, rows, N, H, q, o):
         expect = EINVAL
     elif not (128 <= H <= 16384 and H % 128 == 0 and 128 <= N <= 16384 and N % 128 == 0):
         expect = EINVAL
-    elif q < 0 or q > 5:
+    elif q < 0 or q > 6:
         expect = EINVAL
     elif q not in (2, 3, 4, 5):
         expect = ENOTSUP

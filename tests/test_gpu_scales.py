@@ -1,6 +1,7 @@
 """GPU parity of the dispatch's scales input and static quantisation against
 the oracle, bit for bit: quantMode 1 with one coefficient, one shared row and
-one row per instance; quantMode 2 and 3 with one smoothing row per instance
+one row per instance, and with its second output type (E4M3, one coefficient:
+saturation, subnormals, infinities, NaN, a zero coefficient); quantMode 2 and 3 with one smoothing row per instance
 (every copy quantised on its own); through moe_dispatch and through the
 fused moe_update_dispatch.  Small ragged shapes (partial tiles, K = 1 .. 16,
 inputs large enough to saturate the static cast) and the c3 shapes.
@@ -40,8 +41,9 @@ def gpu_dispatch_scaled(wl, ids, mask, qs, fused=False):
     return out, int(err.item())
 
 
-def check(wl, kind, seed, fused=False):
-    qs = W.make_quant_scales(seed, kind, wl.E, wl.H)
+def check(wl, kind, seed, fused=False, qs=None):
+    if qs is None:
+        qs = W.make_quant_scales(seed, kind, wl.E, wl.H)
     oi, om, oe = oracle_update(wl)
     od = oracle.dispatch(oracle.bf16_bits(wl.x), oi, om, wl.n_ranks, wl.local_experts,
                          wl.quant_mode, wl.tile, None if qs is None else qs.numpy(), kind)
@@ -102,3 +104,47 @@ def test_scales_through_the_fused_call(mode, tile, kind):
     wl = W.make_small(320 + mode, 96, 2048, 6, 4, 6, mode, tile, prune=True, shared=False,
                       token_mask_prefix=90, replicas=True, x_scale=8.0)
     check(wl, kind, 330 + mode, fused=True)
+
+
+# static quantisation, second output type: E4M3 codes of x times one coefficient
+E4M3_CASES = [
+    # seed, Bs, H, K, ranks, local, x_scale, coefficient range, prune, replicas, fused
+    (341, 37, 1056, 5, 3, 4, 30.0, (0.5, 8.0), True, False, False),    # many saturate
+    (342, 64, 4128, 7, 5, 5, 1.0, (0.25, 4.0), False, True, False),
+    (343, 19, 2080, 3, 2, 3, 2e-3, (0.01, 0.2), False, False, False),  # subnormal codes
+    (344, 512, 2048, 16, 8, 16, 4.0, (1.0, 3.0), True, False, False),  # 8192 entries
+    (345, 96, 2048, 6, 4, 6, 8.0, (0.5, 8.0), True, True, True),
+    (346, 1, 8192, 16, 128, 8, 1.0, (0.25, 4.0), False, False, True),
+]
+
+
+@pytest.mark.parametrize("case", E4M3_CASES, ids=[f"e{c[0]}" for c in E4M3_CASES])
+def test_static_e4m3(case):
+    seed, Bs, H, K, R, L, xs, (lo, hi), prune, rep, fused = case
+    say(f"[scales] static e4m3 {case}")
+    wl = W.make_small(seed, Bs, H, K, R, L, 6, 0, prune=prune, shared=False, replicas=rep,
+                      x_scale=xs, token_mask_prefix=Bs - Bs // 5 if fused else None)
+    check(wl, 1, seed, fused=fused, qs=W.make_quant_scales(seed, 1, wl.E, wl.H, lo, hi))
+
+
+@pytest.mark.parametrize("coef", [3.0, 0.0, -0.5])
+@pytest.mark.parametrize("fused", [False, True])
+def test_static_e4m3_non_finite(coef, fused):
+    """Infinities and NaNs of both signs in x; a zero coefficient makes every
+    infinity a NaN product (code 0x7F), a negative one flips the signs."""
+    say(f"[scales] static e4m3 non-finite coef {coef} fused {fused}")
+    wl = W.make_small(347, 48, 1024, 4, 2, 4, 6, 0, prune=False, shared=False, x_scale=50.0)
+    xb = wl.x.view(torch.int16).clone()
+    rng = np.random.default_rng(348)
+    pos = rng.choice(xb.numel(), size=400, replace=False)
+    specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0x0000, 0x8000, 0x0001],
+                        dtype=np.uint16).view(np.int16)
+    xb.view(-1)[torch.from_numpy(pos)] = torch.from_numpy(specials[np.arange(400) % 8])
+    wl.x = xb.view(torch.bfloat16)
+    check(wl, 1, 349, fused=fused, qs=torch.tensor([coef], dtype=torch.float32))
+
+
+def test_static_e4m3_c3_shapes():
+    say("[scales] c3 shapes static e4m3")
+    wl = W.make_c3(seed=3160, quant_mode=6, with_expert_out=False, name="c3.q6")
+    check(wl, 1, 3161, qs=W.make_quant_scales(3161, 1, wl.E, wl.H, 0.5, 64.0))
