@@ -46,9 +46,10 @@ def lib():
         L.oracle_set_threads.restype = i
         L.oracle_expert_gemm_mx.argtypes = [P, P, P, i, i, P, P, i, i, P, P, P]
         L.oracle_expert_gemm_i8.argtypes = [P, P, i, P, i, i, P, P, i, i, P, P, P]
+        L.oracle_swiglu_mx.argtypes = [P, P, i, i, i, P, P, P]
         for f in (L.oracle_update_expert, L.oracle_route, L.oracle_dispatch,
                   L.oracle_dispatch_scaled, L.oracle_combine_add_rmsnorm,
-                  L.oracle_expert_gemm_mx, L.oracle_expert_gemm_i8):
+                  L.oracle_expert_gemm_mx, L.oracle_expert_gemm_i8, L.oracle_swiglu_mx):
             f.restype = C.c_int
         _lib = L
     return _lib
@@ -246,6 +247,28 @@ def expert_gemm_mx(a, a_sc, offsets, w, w_sc, y_init=None):
     if rc:
         raise ValueError(f"oracle_expert_gemm_mx rc={rc}")
     return y, y64, abs64
+
+
+def swiglu_mx(y1_bits, offsets, init=None):
+    """Activation of the expert FFN between its projections: y1 bf16 bits [rows, 2I]
+    (gate | up), offsets int32 [E+1].  Returns (act_bits uint16 [rows, I], codes u8
+    [rows, I], scales u8 [rows, I/32]); rows outside [offsets[0], offsets[E]) keep
+    `init` (a (act, codes, scales) triple) or zeros."""
+    y1 = _c(y1_bits, np.uint16)
+    rows, I2 = y1.shape
+    I = I2 // 2
+    offsets = _c(offsets, np.int32)
+    E = offsets.size - 1
+    if init is None:
+        act = np.zeros((rows, I), dtype=np.uint16)
+        codes = np.zeros((rows, I), dtype=np.uint8)
+        sc = np.zeros((rows, I // 32), dtype=np.uint8)
+    else:
+        act, codes, sc = (_c(t, d).copy() for t, d in zip(init, (np.uint16, np.uint8, np.uint8)))
+    rc = lib().oracle_swiglu_mx(_p(y1), _p(offsets), E, rows, I, _p(act), _p(codes), _p(sc))
+    if rc:
+        raise ValueError(f"oracle_swiglu_mx rc={rc}")
+    return act, codes, sc
 
 
 def expert_gemm_i8(a, a_sc, offsets, w, w_sc, y_init=None):

@@ -726,3 +726,47 @@ int oracle_expert_gemm_i8(const int8_t *a, const float *a_sc, int n_tiles, const
     }
     return 0;
 }
+
+/* [SEQ] expert computation, the activation between its two projections.  The
+ * pages name the expert step and its operand formats only; the reading here is
+ * the gated FFN of a DeepSeek-V3-shaped layer: the first projection's output
+ * row holds the gate g (columns [0, I)) and the up projection u (columns
+ * [I, 2I)) side by side, and
+ *   act[r][j] = bf16( silu(g) * u ),  silu(g) = g / (1 + exp(-g))
+ * evaluated in fp64 and rounded once to bf16.  Each act row is then coded for
+ * the second projection with the quantiser of [DSP] case 5 (blocks of 32,
+ * sharedExp = floor(log2 max|act|) - 8, E4M3 codes, E8M0 byte sharedExp + 127).
+ * For every row r in [offsets[0], offsets[E]):
+ *   y1    bf16 [rows, 2I]  (in)
+ *   act   bf16 [rows, I]   (out, may be NULL)
+ *   codes E4M3 [rows, I], scales E8M0 [rows, I/32]  (out)
+ * Rows outside that range are left untouched.  Returns -1 for bad sizes or
+ * offsets that are not non-decreasing within [0, rows]. */
+int oracle_swiglu_mx(const uint16_t *y1, const int32_t *offsets, int E, int rows, int I,
+                     uint16_t *act, uint8_t *codes, uint8_t *scales)
+{
+    if (E <= 0 || rows < 0 || I <= 0 || I % 32 != 0)
+        return -1;
+    if (offsets[0] < 0 || offsets[E] > rows)
+        return -1;
+    for (int e = 0; e < E; ++e)
+        if (offsets[e] > offsets[e + 1])
+            return -1;
+    uint16_t *a = (uint16_t *)malloc((size_t)I * sizeof(uint16_t));
+    if (!a)
+        return -2;
+    for (int r = offsets[0]; r < offsets[E]; ++r) {
+        const uint16_t *row = y1 + (size_t)r * 2 * I;
+        for (int j = 0; j < I; ++j) {
+            double g = bf16_value(row[j]), u = bf16_value(row[I + j]);
+            a[j] = bf16_from_double(g / (1.0 + exp(-g)) * u);
+        }
+        if (act)
+            memcpy(act + (size_t)r * I, a, (size_t)I * sizeof(uint16_t));
+        for (int b = 0; b < I / 32; ++b)
+            quant_mxfp8_block(a + 32 * b, 32, codes + (size_t)r * I + 32 * b,
+                              scales + (size_t)r * (I / 32) + b);
+    }
+    free(a);
+    return 0;
+}

@@ -53,6 +53,10 @@ MUTANTS = [
     ("smoothing_dropped", "v[j] = qscales_kind == 0 ? bf16_value(xi[j]) : bf16_value(xi[j]) * s;",
      "v[j] = bf16_value(xi[j]);"),
     ("static_row_index", "s = qscales[j];", "s = qscales[H - 1 - j];"),
+    ("swiglu_gate_up_swapped", "double g = bf16_value(row[j]), u = bf16_value(row[I + j]);",
+     "double u = bf16_value(row[j]), g = bf16_value(row[I + j]);"),
+    ("swiglu_sigmoid_sign", "a[j] = bf16_from_double(g / (1.0 + exp(-g)) * u);",
+     "a[j] = bf16_from_double(g / (1.0 + exp(g)) * u);"),
     ("static_e4m3_nan_signed", "    if (v != v)\n        return 0x7F;\n    return e4m3_from_float(v);",
      "    return e4m3_from_float(v);"),
     ("static_e4m3_unscaled", "c[j] = e4m3_static_cast(v[j]);",
@@ -82,7 +86,7 @@ MUTANTS = [
 
 PIN_FILES = ["tests/test_oracle_numbers.py", "tests/test_oracle_route.py",
              "tests/test_oracle_dispatch_combine.py", "tests/test_oracle_scaled.py",
-             "tests/test_oracle_gemm.py", "tests/test_golden.py"]
+             "tests/test_oracle_gemm.py", "tests/test_oracle_swiglu.py", "tests/test_golden.py"]
 
 
 def _run_mutant(name, old, new, workdir):
