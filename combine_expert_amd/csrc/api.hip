@@ -275,4 +275,28 @@ int moe_expert_gemm(const void *expand_x, const void *expand_scales,
                                             static_cast<hipStream_t>(stream)));
 }
 
+int moe_expert_swiglu(const void *y1, const int32_t *expert_offsets, int n_instances, int rows,
+                      int I, int quant_mode, void *act_codes, void *act_scales, void *act,
+                      int32_t *dev_err, void *stream)
+{
+    if (!y1 || !expert_offsets || !act_codes || !act_scales)
+        return MOE_EINVAL;
+    if (n_instances < 1 || n_instances > kMaxExperts || rows < 0 || rows > kMaxGemmRows)
+        return MOE_EINVAL;
+    if (I < 128 || I > kMaxGemmDim / 2 || I % 128 != 0)
+        return MOE_EINVAL;
+    if (quant_mode < MOE_Q_NONE || quant_mode > MOE_Q_STATIC_E4M3)
+        return MOE_EINVAL;
+    if (quant_mode != MOE_Q_MXFP8 && quant_mode != MOE_Q_MXFP8_GM)
+        return MOE_ENOTSUP;
+    if (!aligned(y1, 16) || !aligned(act_codes, 16) || (act && !aligned(act, 16)) ||
+        !aligned(expert_offsets, 4) || (dev_err && !aligned(dev_err, 4)))
+        return MOE_EINVAL;
+    return from_hip(moe::launch_expert_swiglu(
+        static_cast<const uint16_t *>(y1), expert_offsets, n_instances, rows, I,
+        quant_mode == MOE_Q_MXFP8_GM, static_cast<uint8_t *>(act_codes),
+        static_cast<uint8_t *>(act_scales), static_cast<uint16_t *>(act), dev_err,
+        static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

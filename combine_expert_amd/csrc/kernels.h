@@ -39,6 +39,10 @@ hipError_t launch_expert_gemm(int quant_mode, const void *a, const void *a_sc,
                               const void *w_sc, int N, int K, uint16_t *y, int32_t *dev_err,
                               hipStream_t stream);
 
+hipError_t launch_expert_swiglu(const uint16_t *y1, const int32_t *offsets, int E, int rows,
+                                int I, bool group_major, uint8_t *codes, uint8_t *sc,
+                                uint16_t *act, int32_t *dev_err, hipStream_t stream);
+
 // Threads per row block: one thread per 16 row elements, rounded up to
 // whole waves (64 .. 512 threads for H in [1024, 8192]).  Kernels derive
 // their block size from H with these functions instead of reading blockDim,

@@ -26,7 +26,7 @@ SHARED_PAGE, SHARED_ADD = 0, 1
 ERR_ID, ERR_TABLE, ERR_MASK1D, ERR_ROW, ERR_OFFSETS = 1, 2, 4, 8, 16
 
 EXPORTS = ("moe_update_expert", "moe_dispatch", "moe_update_dispatch", "moe_combine_add_rmsnorm",
-           "moe_expert_gemm", "moe_status_string")
+           "moe_expert_gemm", "moe_expert_swiglu", "moe_status_string")
 
 if not os.path.exists(_build.LIB):
     raise ImportError(f"{_build.LIB} is not built: run `python -m combine_expert_amd.build`")
@@ -41,8 +41,9 @@ _lib.moe_update_dispatch.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
 _lib.moe_combine_add_rmsnorm.argtypes = [_P, _P, _P, _P, _P, _P, C.c_float, _I, _I, _I, _I,
                                          _P, _P, _P, _P, _P]
 _lib.moe_expert_gemm.argtypes = [_P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _P, _P, _P]
+_lib.moe_expert_swiglu.argtypes = [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
 for _f in (_lib.moe_update_expert, _lib.moe_dispatch, _lib.moe_update_dispatch,
-           _lib.moe_combine_add_rmsnorm, _lib.moe_expert_gemm):
+           _lib.moe_combine_add_rmsnorm, _lib.moe_expert_gemm, _lib.moe_expert_swiglu):
     _f.restype = C.c_int
 _lib.moe_status_string.argtypes = [_I]
 _lib.moe_status_string.restype = C.c_char_p
@@ -334,6 +335,38 @@ def moe_expert_gemm(expand_x, expand_scales, expert_offsets, weights, weight_sca
                               _ptr(dev_err), _stream(stream))
     _check("moe_expert_gemm", rc)
     return y
+
+
+def moe_expert_swiglu(y1, expert_offsets, quant_mode: int = QUANT_MXFP8, act_codes=None,
+                      act_scales=None, act=None, want_act: bool = False, dev_err=None,
+                      stream=None):
+    """Activation between the expert FFN's projections: y1 bf16 [rows, 2I] (gate | up)
+    -> (act_codes u8 E4M3 [rows, I], act_scales u8 E8M0 [rows, I/32] or group-major
+    [ceil(I/512), rows, 16] for QUANT_MXFP8_GM, act bf16 [rows, I] or None).  Rows
+    outside [offsets[0], offsets[E]) are not written."""
+    rows, I2 = y1.shape
+    I = I2 // 2
+    E = expert_offsets.numel() - 1
+    dev = y1.device
+    ns = n_scale_entries(quant_mode, I) if quant_mode in _MX else 0
+    if act_codes is None:
+        act_codes = torch.empty((rows, I), dtype=torch.uint8, device=dev)
+    if act_scales is None and ns:
+        shape = (ns // 16, rows, 16) if quant_mode == QUANT_MXFP8_GM else (rows, ns)
+        act_scales = torch.empty(shape, dtype=torch.uint8, device=dev)
+    if act is None and want_act:
+        act = torch.empty((rows, I), dtype=torch.bfloat16, device=dev)
+    _arg(y1, "y1", _BF16, rows * 2 * I)
+    _arg(expert_offsets, "expert_offsets", _I32, E + 1)
+    _arg(act_codes, "act_codes", _BYTE_TYPES[:2], rows * I)
+    _arg(act_scales, "act_scales", (torch.uint8,), rows * ns, required=ns > 0)
+    _arg(act, "act", _BF16, rows * I, required=False)
+    _arg(dev_err, "dev_err", _I32, 1, required=False)
+    rc = _lib.moe_expert_swiglu(_ptr(y1), _ptr(expert_offsets), E, rows, I, quant_mode,
+                                _ptr(act_codes), _ptr(act_scales), _ptr(act), _ptr(dev_err),
+                                _stream(stream))
+    _check("moe_expert_swiglu", rc)
+    return act_codes, act_scales, act
 
 
 def raw():

@@ -318,6 +318,42 @@ int moe_expert_gemm(const void *expand_x, const void *expand_scales,
                     const void *weights, const void *weight_scales, int N, int H,
                     int quant_mode, void *y, int32_t *dev_err, void *stream);
 
+/*
+ * moe_expert_swiglu -- the activation between the expert computation's two
+ * projections, for the second projection's moe_expert_gemm.  The pages place
+ * the expert step in the calling sequence of "aclnnMoeUpdateExpert" without
+ * defining it; this library reads it as the gated FFN of a DeepSeek-V3-shaped
+ * layer: a first moe_expert_gemm with N = 2I whose output row holds the gate g
+ * (columns [0, I)) and the up projection u (columns [I, 2I)), this call, and a
+ * second moe_expert_gemm with H = I whose output rows are the combine's
+ * expert_out.  For every row r in [expert_offsets[0], expert_offsets[n_instances]):
+ *
+ *   act[r][j] = bf16( silu(g) * u ),  silu(g) = g / (1 + exp(-g))   (fp32, j < I)
+ *
+ * and act's row is coded with the mxfp8 quantiser of the dispatch
+ * ("aclnnMoeDistributeDispatchV2", 计算公式 case 5), with the same rules as
+ * moe_dispatch's MOE_Q_MXFP8 (infinities and NaNs included).  The fp32
+ * expression may round to a bf16 one step away from the exact value's.
+ *
+ *   y1             bf16 [rows, 2I] (the first projection's output)  16-byte aligned
+ *   expert_offsets int32 [n_instances+1] (as for moe_expert_gemm)
+ *   quant_mode     MOE_Q_MXFP8 (act_scales u8 E8M0 [rows, I/32]) or MOE_Q_MXFP8_GM
+ *                  (group-major [I/512 rounded up, rows, 16], the order the second
+ *                  moe_expert_gemm reads fastest; rows is then that call's rows);
+ *                  the int8 modes: MOE_ENOTSUP
+ *   act_codes      E4M3 [rows, I] (out)                             16-byte aligned
+ *   act_scales     E8M0 bytes, layout by quant_mode (out)
+ *   act            bf16 [rows, I] or NULL (out)                     16-byte aligned
+ *   dev_err        int32 [1] or NULL: MOE_ERR_OFFSETS when offsets[0] < 0,
+ *                  offsets[n_instances] > rows or offsets[n_instances] < offsets[0];
+ *                  the range is then clamped into [0, rows]
+ * Rows outside the range are not written.  Limits: 1 <= n_instances <= 1024,
+ * 0 <= rows <= 4194304, I a multiple of 128 in [128, 8192].
+ */
+int moe_expert_swiglu(const void *y1, const int32_t *expert_offsets, int n_instances, int rows,
+                      int I, int quant_mode, void *act_codes, void *act_scales, void *act,
+                      int32_t *dev_err, void *stream);
+
 /* A static, human-readable name for a moe_status value. */
 const char *moe_status_string(int status);
 

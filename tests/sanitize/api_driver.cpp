@@ -61,6 +61,12 @@ hipError_t launch_expert_gemm(int q, const void *, const void *, const int32_t *
 {
     return record("expert_gemm", -1, -1, q);
 }
+hipError_t launch_expert_swiglu(const uint16_t *, const int32_t *, int, int rows, int I,
+                                bool group_major, uint8_t *, uint8_t *, uint16_t *, int32_t *,
+                                hipStream_t)
+{
+    return record("expert_swiglu", rows, I, group_major ? MOE_Q_MXFP8_GM : MOE_Q_MXFP8);
+}
 }  // namespace moe
 
 namespace {
@@ -133,6 +139,17 @@ int main()
            "expert gemm");
     expect(g_calls.size() == 3 && g_calls[0] == "update_expert" && g_calls[1] == "combine" &&
                g_calls[2] == "expert_gemm", "update / combine / gemm launchers");
+    g_calls.clear();
+    expect(moe_expert_swiglu(P<void>(), P<int32_t>(), 8, 4096, 2048, MOE_Q_MXFP8_GM, P<void>(),
+                             P<void>(), nullptr, nullptr, nullptr) == MOE_OK, "expert swiglu");
+    expect(g_calls.size() == 1 && g_calls[0] == "expert_swiglu" && g_last_Bs == 4096 &&
+               g_last_K == 2048 && g_last_q == MOE_Q_MXFP8_GM, "expert swiglu launcher");
+    g_calls.clear();
+    expect(moe_expert_swiglu(P<void>(), P<int32_t>(), 8, 4096, 2000, MOE_Q_MXFP8, P<void>(),
+                             P<void>(), nullptr, nullptr, nullptr) == MOE_EINVAL, "swiglu I % 128");
+    expect(moe_expert_swiglu(P<void>(), P<int32_t>(), 8, 4096, 2048, MOE_Q_INT8_TOKEN, P<void>(),
+                             P<void>(), nullptr, nullptr, nullptr) == MOE_ENOTSUP, "swiglu int8");
+    expect(g_calls.empty(), "rejected swiglu calls launch nothing");
 
     // invalid calls: a status and no launcher
     g_calls.clear();

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["moe_combine_add_rmsnorm", "moe_dispatch",
-                                    "moe_expert_gemm", "moe_status_string",
+                                    "moe_expert_gemm", "moe_expert_swiglu", "moe_status_string",
                                     "moe_update_dispatch", "moe_update_expert"]
 
 
@@ -189,3 +189,27 @@ def test_expert_gemm_rejects_out_of_range_arguments():
         assert gemm(**kw) == 1, kw
     for q in (0, 1, 6):
         assert gemm(q=q) == 2, q
+
+
+def swiglu(**kw):
+    from combine_expert_amd import moe
+    a = dict(y1=P, off=P, E=8, rows=4096, I=2048, q=4, codes=P, sc=P, act=None, err=None)
+    a.update(kw)
+    return moe.raw().moe_expert_swiglu(a["y1"], a["off"], a["E"], a["rows"], a["I"], a["q"],
+                                       a["codes"], a["sc"], a["act"], a["err"], None)
+
+
+@pytest.mark.skipif("not _no_gpu()")
+def test_expert_swiglu_rejects_out_of_range_arguments():
+    bad = [dict(y1=None), dict(off=None), dict(codes=None), dict(sc=None), dict(E=0),
+           dict(E=1025), dict(rows=-1), dict(rows=(1 << 22) + 1), dict(I=0), dict(I=64),
+           dict(I=2000), dict(I=8192 + 128), dict(q=-1), dict(q=7), dict(y1=P + 8),
+           dict(codes=P + 4), dict(act=P + 8), dict(off=P + 2), dict(err=P + 1)]
+    for kw in bad:
+        assert swiglu(**kw) == 1, kw
+    for q in (0, 1, 2, 3, 6):
+        assert swiglu(q=q) == 2, q
+    # valid calls reach the launch (no GPU here: the launch itself fails)
+    for kw in (dict(), dict(q=5), dict(I=128), dict(I=8192), dict(act=P)):
+        assert swiglu(**kw) == 3, kw
+    assert swiglu(rows=0) == 0  # nothing to launch
