@@ -905,6 +905,84 @@ def gemm_cpu_baseline(g, np, oracle, budget_s):
             "host_cores_available": len(os.sched_getaffinity(0))}
 
 
+def ffn_figures(args, g, argv, ys, off, n_sets, K, lib, moe, W, torch, dev, stream):
+    """The whole expert FFN of the rank: this launch's output y1 = [gate | up] (N = 2I),
+    the activation (moe_expert_swiglu: bf16 silu(gate) * up coded as mxfp8, exponents
+    group-major) and the second projection back to H (moe_expert_gemm with K = I), each
+    weight set twice so the weights cannot stay in the Infinity Cache.  Reported: the
+    activation kernel against the HBM peak (its y1 input was just written by the first
+    projection, as in the FFN), the second projection against the fp8 peak, and the three
+    launches as one FFN step."""
+    I = g.N // 2
+    rows = g.rows
+    g2 = W.make_gemm_case(3300, g.counts, g.Kd, I, name="g3 second projection")
+    w2 = [torch.from_numpy(g2.w).to(dev) for _ in range(n_sets)]
+    w2s = [moe.pack_mx_weight_scales(torch.from_numpy(g2.w_sc).to(dev)) for _ in range(n_sets)]
+    codes = [torch.empty((rows, I), dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    scs = [torch.empty((-(-I // 512), rows, 16), dtype=torch.uint8, device=dev)
+           for _ in range(n_sets)]
+    y2 = [torch.empty((rows, g.Kd), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    gm = moe.QUANT_MXFP8_GM
+    act_argv = [(ys[k].data_ptr(), off.data_ptr(), g.E, rows, I, gm, codes[k].data_ptr(),
+                 scs[k].data_ptr(), None, None, stream.cuda_stream) for k in range(n_sets)]
+    g2_argv = [(codes[k].data_ptr(), scs[k].data_ptr(), off.data_ptr(), g.E, rows,
+                w2[k].data_ptr(), w2s[k].data_ptr(), g.Kd, I, gm, y2[k].data_ptr(), None,
+                stream.cuda_stream) for k in range(n_sets)]
+    act, gemm = lib.moe_expert_swiglu, lib.moe_expert_gemm
+
+    def timed(fn):
+        for k in range(args.warmup):
+            fn(k)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(K):
+            fn(k)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K
+
+    def step(k):
+        a = k % n_sets
+        if gemm(*argv[a]) | act(*act_argv[a]) | gemm(*g2_argv[a]):
+            raise RuntimeError("an expert FFN call returned a non-zero status")
+
+    def act_only(k):
+        gemm(*argv[k % n_sets])   # y1 freshly written, as in the FFN
+        if act(*act_argv[k % n_sets]):
+            raise RuntimeError("moe_expert_swiglu returned a non-zero status")
+
+    t_step = timed(step)
+    t_gemm1_act = timed(act_only)
+    t_gemm1 = timed(lambda k: gemm(*argv[k % n_sets]))
+    t_act = t_gemm1_act - t_gemm1
+    t_act_alone = timed(lambda k: act(*act_argv[k % n_sets]))
+    t_g2 = timed(lambda k: gemm(*g2_argv[k % n_sets]))
+    n = int(g.offsets[-1])
+    f1, f2 = 2.0 * n * g.N * g.Kd, 2.0 * n * g.Kd * I
+    act_bytes = n * 2 * I * 2 + n * I + n * (I // 32)
+    tf = lambda f, u: f / (u * 1e-6) / 1e12
+    return {
+        "workload": (f"the rank's expert FFN: {g.E} instances, {n} rows, H={g.Kd} -> 2I={g.N} "
+                     f"(gate | up), silu(gate) * up coded as mxfp8, I={I} -> H={g.Kd}"),
+        "step_us": round(t_step, 3),
+        "TFLOPs": round(tf(f1 + f2, t_step), 1),
+        "frac_of_fp8_peak": round(tf(f1 + f2, t_step) / FP8_PEAK_TFLOPS, 4),
+        "activation": {"kernel": "k_expert_swiglu", "bound": "hbm",
+                       "avg_us": round(t_act, 3), "bytes": act_bytes,
+                       "GBps": round(act_bytes / (t_act * 1e-6) / 1e9, 1),
+                       "frac": round(act_bytes / (t_act * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "how": "first projection + activation minus first projection alone, "
+                              "HIP events, y1 read right after the projection wrote it",
+                       "alone_us": round(t_act_alone, 3),
+                       "alone_GBps": round(act_bytes / (t_act_alone * 1e-6) / 1e9, 1),
+                       "alone_how": "back-to-back launches over the two y1 sets (67 MB: "
+                                    "partly served by the Infinity Cache)"},
+        "second_projection": {"avg_us": round(t_g2, 3), "flops": f2,
+                              "TFLOPs": round(tf(f2, t_g2), 1),
+                              "frac_of_fp8_peak": round(tf(f2, t_g2) / FP8_PEAK_TFLOPS, 4)},
+    }
+
+
 def gemm_main(args):
     import numpy as np
     import torch
@@ -989,6 +1067,8 @@ def gemm_main(args):
         variants[name] = {"avg_us": round(ui, 3), "TOPS": round(fi / (ui * 1e-6) / 1e12, 2),
                           "frac_of_int8_peak": round(fi / (ui * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
         del ti, wi2, yi
+    ffn = None if args.gemm_dense else ffn_figures(args, g, argv, ys, off, n_sets, K, lib, moe, W,
+                                                    torch, dev, stream)
     rows_total = int(g.offsets[-1])
     flops = 2.0 * rows_total * g.N * g.Kd
     tfs = flops / (us * 1e-6) / 1e12
@@ -1017,6 +1097,7 @@ def gemm_main(args):
                      "algorithmic_bytes_per_launch": alg_bytes, "avg_launch_us": round(us, 3)},
         "hbm_GBps_algorithmic": round(alg_bytes / (us * 1e-6) / 1e9, 1),
         "other_formats": variants,
+        "ffn": ffn,
         "parity_sample": "ok" if ok else "MISMATCH",
         "cpu_baseline": None,
     }
