@@ -19,13 +19,15 @@ constexpr int kMaxWaves = kMaxThreads / kWave;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// Two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+// Two fp32 -> packed bf16x2, round to nearest even: one v_cvt_pk_bf16_f32 on gfx950
+// (two scalar casts compile to one conversion each, plus the masks and shifts that
+// pack them).
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    const moe_f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, moe_bf16x2));
 }
 
 __device__ __forceinline__ uint4 pack8_bf16(const float *f)

@@ -21,21 +21,6 @@ namespace moe {
 
 constexpr int kActThreads = 256;
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// 8 fp32 -> 8 bf16, round to nearest even, one v_cvt_pk_bf16_f32 per pair
-__device__ __forceinline__ uint4 pack8_bf16_pairs(const float *f)
-{
-    uint32_t w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f32x2 v = {f[2 * q], f[2 * q + 1]};
-        w[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 __global__ __launch_bounds__(kActThreads) void k_expert_swiglu(
     const uint16_t *__restrict__ y1, const int32_t *__restrict__ offsets, int E, int rows,
     int I, int sc_row, int sc_group, uint8_t *__restrict__ codes, uint8_t *__restrict__ sc,
@@ -90,7 +75,7 @@ __global__ __launch_bounds__(kActThreads) void k_expert_swiglu(
             a[j] = s * uv[j];
         }
     }
-    const uint4 xa = pack8_bf16_pairs(a), xb = pack8_bf16_pairs(a + 8);
+    const uint4 xa = pack8_bf16(a), xb = pack8_bf16(a + 8);
 
     // the case-5 coder on the bf16 values, as the dispatch codes a token's row
     float v[16];
