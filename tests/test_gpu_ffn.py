@@ -188,3 +188,16 @@ def test_layer_with_the_ffn(case):
     g = gpu_combine(wl, gd["assist_dst"], y2.cpu())
     o = oracle_combine(wl, od["assist"], y2.cpu())
     check_combine(g, o)
+
+
+def test_swiglu_is_bitwise_repeatable():
+    say("[ffn] swiglu twice on the same input")
+    rows, I = 256, 1024
+    rng = np.random.default_rng(905)
+    y1 = torch.from_numpy(rng.normal(0.0, 4.0, size=(rows, 2 * I)).astype(np.float32))
+    y1 = y1.bfloat16().cuda()
+    off = torch.tensor([0, 100, 256], dtype=torch.int32).cuda()
+    a = run_swiglu(y1, off, QUANT_MXFP8_GM, rows, I)
+    b = run_swiglu(y1, off, QUANT_MXFP8_GM, rows, I)
+    for x, y in zip(a[:3], b[:3]):
+        np.testing.assert_array_equal(x, y)
