@@ -201,3 +201,57 @@ def test_swiglu_is_bitwise_repeatable():
     b = run_swiglu(y1, off, QUANT_MXFP8_GM, rows, I)
     for x, y in zip(a[:3], b[:3]):
         np.testing.assert_array_equal(x, y)
+
+
+def test_ffn_replays_from_a_graph():
+    """The rank's FFN (first projection, activation, second projection) captured in one
+    HIP graph: every replay, with eager work between them, equals the eager run bitwise."""
+    say("[ffn] graph capture and replays")
+    m = M()
+    rng = np.random.default_rng(906)
+    E, H, I = 4, 1024, 256
+    counts = np.array([40, 0, 130, 86], np.int32)
+    rows = int(counts.sum()) + 8
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    a = torch.from_numpy(W.e4m3_codes(rng, (rows, H))).cuda()
+    a_sc = torch.from_numpy(W.e8m0_codes(rng, (rows, H // 32), 120, 124)).cuda()
+    w1, w1_sc = mx_weights(907, E, 2 * I, H)
+    w2, w2_sc = mx_weights(908, E, H, I)
+    w1, w2 = torch.from_numpy(w1).cuda(), torch.from_numpy(w2).cuda()
+    w1_sc = m.pack_mx_weight_scales(torch.from_numpy(w1_sc).cuda())
+    w2_sc = m.pack_mx_weight_scales(torch.from_numpy(w2_sc).cuda())
+    y1 = torch.zeros((rows, 2 * I), dtype=torch.bfloat16, device="cuda")
+    codes = torch.zeros((rows, I), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((-(-I // 512), rows, 16), dtype=torch.uint8, device="cuda")
+    y2 = torch.zeros((rows, H), dtype=torch.bfloat16, device="cuda")
+
+    def ffn():
+        m.moe_expert_gemm(a, a_sc, off, w1, w1_sc, y=y1)
+        m.moe_expert_swiglu(y1, off, QUANT_MXFP8_GM, act_codes=codes, act_scales=sc)
+        m.moe_expert_gemm(codes, sc, off, w2, w2_sc, quant_mode=QUANT_MXFP8_GM, y=y2)
+
+    total = int(counts.sum())  # the spare rows past it are written by no kernel
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ffn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = (u16(y1)[:total], codes.cpu().numpy()[:total], sc.cpu().numpy(), u16(y2)[:total])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ffn()
+    other = torch.randn(1 << 20, device="cuda")
+    for rep in range(3):
+        for t in (y1, y2):
+            t.view(torch.int16).fill_(rep + 1)
+        codes.fill_(rep + 7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (u16(y1)[:total], codes.cpu().numpy()[:total], sc.cpu().numpy(), u16(y2)[:total])
+        for x, y in zip(ref, got):
+            np.testing.assert_array_equal(x, y)
+        other.mul_(1.0001).add_(0.5)
+        ffn()
+        torch.cuda.synchronize()
