@@ -153,7 +153,10 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 // every later LDS read, and every LDS fence, wait for all such copies in
 // flight, which caps the pipeline at one step; here the waits are explicit.
 // The asm has no output registers (the data goes to LDS), and the address
-// registers are read when the instruction issues.
+// registers are read when the instruction issues.  M0 is listed as clobbered, so
+// the compiler assumes nothing about it after the statement and sets it again
+// before any use of its own (LDS-direct or message instructions); the kernel's
+// own LDS accesses are ordinary ds_ instructions, which do not read M0 on gfx950.
 __device__ __forceinline__ void dma16(const uint8_t *src, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
